@@ -1,0 +1,197 @@
+/*
+ * ssd.h - C ABI of libssdv: batched speculative-decoding verification and the
+ * SAGUARO speculation-cache build on one AMD MI355X (gfx950) GPU.
+ *
+ * Sources (page title, then section):
+ *   [SD-notes]  brentwoodlivery.com, "Speculative decoding" study notes
+ *   [SD-why]    til.phipham141.dev, "Why does speculative decoding exist?"
+ *   [SSD-notes] papernotes.org, "Speculative Speculative Decoding" (ICLR 2026 notes)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Logits.  Row-major [B, rows, V] with the vocabulary contiguous; rows of one
+ *   batch element are V elements apart; consecutive batch elements are
+ *   `*_bstride` ELEMENTS apart (0 broadcasts one batch element to all B).
+ *   dtype is SSD_F32 (float) or SSD_BF16 (bfloat16 bits). Values must be
+ *   finite or -inf (a masked token); NaN and +inf are undefined.
+ * Temperature.  x = logits / tau for target and draft alike, tau > 0 finite
+ *   ([SD-notes] Temperature and Sampling).
+ * Memory.  Every pointer documented "device" is device memory owned by the
+ *   caller; "host" pointers are read during the call only. The library never
+ *   allocates. Workspace: a device buffer (256-byte aligned) of at least the
+ *   size returned by the matching *_workspace_size query. Its layout depends
+ *   on the entry point and on (B, K, V, dtype); it must be ZERO-FILLED before
+ *   its first use with a given entry point and shape. Each completed call
+ *   leaves the completion counters it uses at zero, so the buffer can be
+ *   reused for the same entry point and shape without clearing; zero it again
+ *   before using it with another entry point or shape. A workspace that was
+ *   not zero-filled gives wrong outputs but never makes the kernels address
+ *   memory outside the caller's buffers. One workspace must not be used by
+ *   two calls that may run at the same time.
+ * Streams.  Calls enqueue kernels on `hip_stream` (a hipStream_t; NULL = the
+ *   default stream) and return without synchronising. Only ssd_fanout runs on
+ *   the host. Graph capture is supported (no memset or allocation inside).
+ * Errors.  Functions return SSD_OK (0) or a negative status; arguments are
+ *   checked on the host before anything is enqueued, and ssd_last_error()
+ *   gives a message for the calling thread's last failure. A drafted token
+ *   outside [0, V) is a data error found on the device: that batch row gets
+ *   accepted = -1, all its out_tokens = -1, hit = 0 and slot = -1; other rows
+ *   are unaffected.
+ * Determinism.  No floating-point atomics; identical inputs on the same
+ *   device give bit-identical outputs.
+ * Limits.  1 <= B < 2^24, 1 <= K <= 64, 1 <= V < 2^31, 0 <= F_k <= min(V, 64).
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define SSD_API __attribute__((visibility("default")))
+#else
+#define SSD_API
+#endif
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+enum {
+  SSD_OK = 0,
+  SSD_EINVAL = -1,     /* bad size, pointer, temperature, C, fan-out ... */
+  SSD_EDTYPE = -2,     /* unknown dtype */
+  SSD_EWORKSPACE = -3, /* workspace missing, too small or misaligned (256 B) */
+  SSD_EHIP = -4        /* the HIP runtime refused a launch */
+};
+
+enum { SSD_MAX_K = 64, SSD_MAX_F = 64 };
+
+/* Position of one token in the top-F order of a draft row: an order-preserving
+ * integer image of the logit (dtype specific) and the token index. Produced
+ * by ssd_build_cache, consumed by ssd_verify / ssd_residual_sample; opaque. */
+typedef struct {
+  uint32_t key;
+  int32_t idx;
+} ssd_rowkey;
+
+/* sigma_{F,C} reshaping of the draft distribution ([SSD-notes] key design 2):
+ * q(t) is proportional to C*exp(x_t) for t among the F_k largest draft logits
+ * of row k (ties: smaller index first), exp(x_t) otherwise. Passed to verify
+ * and residual sampling to use the reshaped q; both arrays come from
+ * ssd_build_cache run on the same draft logits with the same tau. */
+typedef struct {
+  float C;                    /* down-weight in [0, 1] */
+  const ssd_rowkey* thr;      /* device [B, K+1]: last member of each top-F_k set */
+  const double* draft_stats;  /* device [B, K+1, 3]: zmax, S_top, S_rest (see ssd_build_cache) */
+} ssd_sigma;
+
+/* Message for the calling thread's last non-OK return ("" if none). */
+SSD_API const char* ssd_last_error(void);
+
+/* Geometric fan-out of a cache budget over acceptance lengths k = 0..K
+ * ([SSD-notes] key design 1): real-valued F_k = F_0 a_p^(k/(1+r)) for k < K,
+ * F_K = F_0 a_p^(K/(1+r)) (1-a_p)^(-1/(1+r)), with F_0 chosen so the values
+ * sum to n_budget; rounded by largest remainder (ties to the smaller k), so
+ * the integers sum to n_budget exactly.
+ * n_budget >= 0, 1 <= K <= 64, 0 < a_p < 1, r > -1, both finite.
+ * F_out: host int32[K+1]. Returns sum(F) (= n_budget) or a negative status. */
+SSD_API int ssd_fanout(int32_t n_budget, int32_t K, double a_p, double r, int32_t* F_out);
+
+/* Bytes of workspace ssd_verify needs for this shape (any mode). */
+SSD_API size_t ssd_verify_workspace_size(int32_t B, int32_t K, int32_t V, int dtype);
+
+/* Batched verification ([SD-notes] The Algorithm, step 3; Batching
+ * Speculation; [SD-why] How it works, Fixes 2 and 3).
+ * For each batch row b and position i = 0..K-1, with p_i = softmax(target row
+ * i / tau) and q_i = softmax(draft row i / tau) (or its sigma_{F_i,C} form):
+ * the drafted token d = draft_tokens[b,i] is kept iff u_acc[b,i]*q_i(d) <
+ * p_i(d) (accept with probability min(1, p/q)); the scan stops at the first
+ * rejection. With a = number kept, the extra token t* is drawn from
+ * max(0, p_a - q_a)/Z if a < K, or from p_K if a = K, by inverse CDF in token
+ * order: the smallest v whose running mass exceeds u_res[b]*Z. If that
+ * residual has no mass the draw uses p_a; if p_a has none, t* = -1.
+ *   target_logits  device [B, K+1, V]  (row K feeds the bonus)
+ *   draft_logits   device [B, >=K, V]  (rows 0..K-1 used; ignored with sigma
+ *                                        except row a for the residual)
+ *   draft_tokens   device int32 [B, K]
+ *   u_acc          device float [B, K] in [0, 1);  u_res device float [B] in [0, 1)
+ *   sigma          NULL for plain softmax q, else host pointer (see ssd_sigma)
+ * Outputs (device):
+ *   accepted    int32 [B]: a in 0..K, or -1 for a flagged row
+ *   out_tokens  int32 [B, K+1]: d_1..d_a, t*, then -1 padding
+ *   probs       float [B, K, 2] or NULL: (p_i(d), q_i(d)) for every i < K
+ *   resid_mass  float [B] or NULL: Z of the final draw (probability units;
+ *               1 for a bonus, 0 when the residual was empty)
+ *   row_lse     float [B, 2K+1] or NULL: log-sum-exp of x over target rows
+ *               0..K, then draft rows 0..K-1 (sigma form when sigma given)
+ * Launches two kernels on hip_stream. */
+SSD_API int ssd_verify(const void* target_logits, int64_t target_bstride,
+                       const void* draft_logits, int64_t draft_bstride, int dtype,
+                       int32_t B, int32_t K, int32_t V, float tau,
+                       const int32_t* draft_tokens, const float* u_acc, const float* u_res,
+                       const ssd_sigma* sigma,
+                       int32_t* accepted, int32_t* out_tokens, float* probs,
+                       float* resid_mass, float* row_lse,
+                       void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* Bytes of workspace ssd_residual_sample needs. */
+SSD_API size_t ssd_residual_workspace_size(int32_t B, int32_t K, int32_t V, int dtype);
+
+/* One draw per batch row from position row[b] (0..K) ([SD-notes] step 3 and
+ * Derivation of Acceptance Criterion): from max(0, p - q)/Z when row[b] < K
+ * and draft_logits is given (q optionally sigma-reshaped), otherwise from p
+ * of that target row (the bonus form). Same inverse-CDF convention and
+ * fallbacks as ssd_verify.
+ *   target_logits device [B, K+1, V]; draft_logits device [B, >=K, V] or NULL
+ *   row device int32 [B]; u device float [B]
+ *   token_out device int32 [B]; mass_out device float [B] or NULL (Z). */
+SSD_API int ssd_residual_sample(const void* target_logits, int64_t target_bstride,
+                                const void* draft_logits, int64_t draft_bstride, int dtype,
+                                int32_t B, int32_t K, int32_t V, float tau,
+                                const int32_t* row, const ssd_sigma* sigma, const float* u,
+                                int32_t* token_out, float* mass_out,
+                                void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* Bytes of workspace ssd_build_cache needs. */
+SSD_API size_t ssd_build_cache_workspace_size(int32_t B, int32_t K, int32_t V, int dtype);
+
+/* Speculation-cache keys ([SSD-notes] framework; key designs 1 and 2): for
+ * every batch row b and acceptance length k = 0..K, the F_k tokens with the
+ * largest draft logits on draft row k (order: logit descending, index
+ * ascending) - the guessed bonus tokens prepared for outcome (k, t*).
+ *   draft_logits device [B, >=K+1, V] (rows 0..K read)
+ *   F host int32 [K+1] (e.g. from ssd_fanout), 0 <= F_k <= min(V, 64)
+ * Outputs (device):
+ *   cache_tokens int32 [B, sum F]: row b holds the K+1 segments in k order,
+ *                segment k sorted in top-F order
+ *   thr          ssd_rowkey [B, K+1]: the F_k-th member (or an empty marker)
+ *   draft_stats  double [B, K+1, 3]: zmax = max logit of the row; S_top and
+ *                S_rest = sums of exp((z - zmax)/tau) over the top-F_k set and
+ *                over the other tokens (zmax taken as 0 if the row is all
+ *                -inf). ln(C S_top + S_rest) + zmax/tau is the log-normaliser
+ *                of sigma_{F_k,C}.
+ * One kernel launch on hip_stream. */
+SSD_API int ssd_build_cache(const void* draft_logits, int64_t draft_bstride, int dtype,
+                            int32_t B, int32_t K, int32_t V, float tau, const int32_t* F,
+                            int32_t* cache_tokens, ssd_rowkey* thr, double* draft_stats,
+                            void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* Cache hit of the realised outcome ([SSD-notes] framework: the round's
+ * outcome (k, t*) hits iff it is among the prepared keys): hit[b] = 1 iff
+ * t* = out_tokens[b, a] lies in segment a of cache_tokens row b, with
+ * a = accepted[b]; slot[b] = its position in that segment, else -1.
+ *   cache_tokens device int32 [B, sum F]; F host int32 [K+1]
+ *   accepted device int32 [B]; out_tokens device int32 [B, K+1]
+ *   hit device uint8 [B]; slot device int32 [B] or NULL. One kernel launch. */
+SSD_API int ssd_cache_lookup(const int32_t* cache_tokens, const int32_t* F, int32_t B, int32_t K,
+                             const int32_t* accepted, const int32_t* out_tokens,
+                             uint8_t* hit, int32_t* slot, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H */

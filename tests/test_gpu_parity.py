@@ -1,0 +1,328 @@
+"""GPU parity: the HIP library (through its C ABI) against the float64 oracle.
+
+Integer outputs (accepted length, emitted tokens, cache tokens, hits, slots)
+must match exactly, except batch rows whose deciding margin in the oracle is
+below 1e-6 (counted and printed); probabilities within 1e-5 relative, row
+log-sum-exps within 1e-5, residual mass within 1e-5 relative.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from gpu_utils import compare_verify, fvec, ivec, log, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module")
+def S():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import verify_speculation_cache_amd as lib
+    lib.lib()
+    return lib
+
+
+def _ln(rows):
+    with np.errstate(divide="ignore"):
+        return np.log(np.asarray(rows, dtype=np.float64)).astype(np.float32)
+
+
+def _run_verify(S, d, sigma=None, oracle_sigma=None, rows=None, label=""):
+    tgt, dft = to_dev(d["target"], torch), to_dev(d["draft"], torch)
+    got = S.ssd_verify(tgt, dft, ivec(d["tokens"], torch), fvec(d["u_acc"], torch),
+                       fvec(d["u_res"], torch), d["tau"], sigma)
+    torch.cuda.synchronize()
+    sel = list(range(d["tokens"].shape[0])) if rows is None else list(rows)
+    ref = O.verify(d["target"][sel], d["draft"][sel], d["tokens"][sel], d["u_acc"][sel],
+                   d["u_res"][sel], d["tau"], oracle_sigma)
+    n_exc = compare_verify(ref, got, d["tokens"].shape[1], rows=sel, label=label)
+    return got, ref, n_exc
+
+
+# ---------------------------------------------------------------------------
+# printed worked examples
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["worked_example_4token.json", "paris_example.json"])
+def test_worked_examples(S, name):
+    fx = json.load(open(os.path.join(GOLDEN, name)))
+    log(f"[gpu] worked example {name}")
+    for case in fx["cases"]:
+        n = 16
+        us = np.linspace(0.0, 0.999, n).astype(np.float32)
+        d = {"target": np.broadcast_to(_ln(fx["p_rows"]), (n, fx["K"] + 1, fx["V"])).copy(),
+             "draft": np.broadcast_to(_ln(fx["q_rows"]), (n, fx["K"], fx["V"])).copy(),
+             "tokens": np.tile(np.array(fx["draft_tokens"], dtype=np.int32), (n, 1)),
+             "u_acc": np.tile(np.array(case["u_acc"], dtype=np.float32), (n, 1)),
+             "u_res": us, "tau": fx["tau"]}
+        got, ref, _ = _run_verify(S, d, label=name)
+        acc = got["accepted"].cpu().numpy()
+        out = got["out_tokens"].cpu().numpy()
+        if "expect_accepted" in case:
+            assert np.all(acc == case["expect_accepted"])
+            assert np.all(out == np.array(case["expect_out"]))
+        else:
+            assert np.all(acc >= case["expect_accepted_at_least"])
+
+
+# ---------------------------------------------------------------------------
+# small sizes the oracle finishes quickly, spanning several chunks with a ragged tail
+# ---------------------------------------------------------------------------
+def _random_case(seed, B, K, V, dtype, tau, mask_frac=0.0, draft_sd=0.7, Kd=None):
+    rng = np.random.default_rng(seed)
+    Kd = K if Kd is None else Kd
+    t = (rng.standard_normal((B, K + 1, V)) * 2.5).astype(np.float32)
+    d = (t[:, :Kd] + rng.standard_normal((B, Kd, V)).astype(np.float32) * draft_sd).astype(np.float32)
+    if mask_frac > 0:
+        t[rng.random(t.shape) < mask_frac] = -np.inf
+        d[rng.random(d.shape) < mask_frac] = -np.inf
+    if dtype == "bf16":
+        t, d = W.f32_to_bf16_bits(t), W.f32_to_bf16_bits(d)
+    toks = np.zeros((B, K), dtype=np.int32)
+    for b in range(B):
+        for i in range(K):
+            toks[b, i] = O.sample_draft(d[b, i], tau, rng.random())
+    return {"target": t, "draft": d, "tokens": toks,
+            "u_acc": rng.random((B, K)).astype(np.float32),
+            "u_res": rng.random(B).astype(np.float32), "tau": float(np.float32(tau))}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V,K,B", [(20000, 4, 6), (8192, 3, 4), (16385, 2, 3), (1000, 5, 8),
+                                   (61, 6, 5), (7, 1, 9), (1, 2, 3)])
+def test_verify_small(S, dtype, V, K, B):
+    log(f"[gpu] verify small dtype={dtype} V={V} K={K} B={B}")
+    d = _random_case(V * 7 + K, B, K, V, dtype, 0.8)
+    _run_verify(S, d, label=f"small-{dtype}-{V}")
+
+
+def test_verify_masked_and_unaligned(S):
+    # masked tokens and an odd V (rows not 16-byte aligned -> scalar loads)
+    for V, dtype in ((12347, "bf16"), (9001, "f32"), (33, "bf16")):
+        log(f"[gpu] masked V={V} {dtype}")
+        d = _random_case(V, 5, 3, V, dtype, 0.6, mask_frac=0.3)
+        _run_verify(S, d, label=f"mask-{V}")
+
+
+def test_verify_extremes(S):
+    # K = 64 (largest), identical target/draft (everything accepted), tau extremes
+    log("[gpu] K=64")
+    d = _random_case(1, 2, 64, 3000, "bf16", 1.0, draft_sd=0.05)
+    _run_verify(S, d, label="K64")
+    for tau in (0.05, 5.0):
+        log(f"[gpu] tau={tau}")
+        d = _random_case(2, 4, 3, 5000, "f32", tau)
+        _run_verify(S, d, label=f"tau{tau}")
+    log("[gpu] identical rows")
+    d = _random_case(3, 4, 4, 4000, "bf16", 0.7, draft_sd=0.0)
+    got, _, _ = _run_verify(S, d, label="identical")
+    assert np.all(got["accepted"].cpu().numpy() == 4)
+
+
+def test_verify_flagged_tokens(S):
+    log("[gpu] out-of-range drafted tokens")
+    d = _random_case(4, 6, 3, 2000, "bf16", 1.0)
+    d["tokens"][1, 2] = 2000
+    d["tokens"][3, 0] = -5
+    got, _, _ = _run_verify(S, d, label="flagged")
+    acc = got["accepted"].cpu().numpy()
+    out = got["out_tokens"].cpu().numpy()
+    assert acc[1] == -1 and acc[3] == -1 and np.all(out[1] == -1) and np.all(out[3] == -1)
+    assert np.all(acc[[0, 2, 4, 5]] >= 0)
+
+
+def test_fully_masked_rows(S):
+    # a target row with no mass: p = 0 there, so its drafted token is rejected and
+    # the residual (from p = 0) is empty -> token -1
+    log("[gpu] fully masked target row")
+    d = _random_case(5, 3, 2, 3000, "f32", 1.0)
+    d["target"][1, 0, :] = -np.inf
+    got, _, _ = _run_verify(S, d, label="fullmask")
+    assert got["accepted"].cpu().numpy()[1] == 0
+    assert got["out_tokens"].cpu().numpy()[1, 0] == -1
+
+
+def test_determinism(S):
+    log("[gpu] determinism")
+    d = _random_case(6, 8, 4, 30000, "bf16", 0.7)
+    tgt, dft = to_dev(d["target"], torch), to_dev(d["draft"], torch)
+    args = (ivec(d["tokens"], torch), fvec(d["u_acc"], torch), fvec(d["u_res"], torch), d["tau"])
+    r1 = S.ssd_verify(tgt, dft, *args)
+    o1 = {k: v.clone() for k, v in r1.items() if v is not None}
+    # another shape in between (its own workspace)
+    d2 = _random_case(7, 3, 2, 500, "bf16", 0.7)
+    S.ssd_verify(to_dev(d2["target"], torch), to_dev(d2["draft"], torch), ivec(d2["tokens"], torch),
+                 fvec(d2["u_acc"], torch), fvec(d2["u_res"], torch), d2["tau"])
+    r2 = S.ssd_verify(tgt, dft, *args)
+    torch.cuda.synchronize()
+    for k, v in o1.items():
+        assert torch.equal(v, r2[k]), k
+
+
+# ---------------------------------------------------------------------------
+# residual sampling entry point
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_residual_sample(S, dtype):
+    log(f"[gpu] residual_sample {dtype}")
+    d = _random_case(8, 10, 3, 17000, dtype, 0.9)
+    rows = np.array([0, 1, 2, 3, 0, 1, 2, 3, 1, 0], dtype=np.int32)
+    u = np.random.default_rng(1).random(10).astype(np.float32)
+    tgt, dft = to_dev(d["target"], torch), to_dev(d["draft"], torch)
+    for use_draft in (True, False):
+        got = S.ssd_residual_sample(tgt, dft if use_draft else None, ivec(rows, torch), fvec(u, torch),
+                                    d["tau"])
+        torch.cuda.synchronize()
+        ref = O.residual_sample(d["target"], d["draft"] if use_draft else None, rows, u, d["tau"])
+        tg = got["tokens"].cpu().numpy()
+        mg = got["mass"].cpu().numpy()
+        for b in range(10):
+            if tg[b] != ref["tokens"][b]:
+                assert ref["margin"][b] < 1e-6, (b, tg[b], ref["tokens"][b], ref["margin"][b])
+            if ref["Z"][b] >= 1e-2:
+                assert abs(mg[b] - ref["Z"][b]) <= 1e-5 * ref["Z"][b]
+
+
+# ---------------------------------------------------------------------------
+# cache build, sigma verify and lookup
+# ---------------------------------------------------------------------------
+def _check_cache(cache, ref, F, rows, label):
+    ct = cache["cache_tokens"].cpu().numpy()
+    thr = cache["thr"].cpu().numpy()
+    st = cache["draft_stats"].cpu().numpy()
+    sumF = sum(F)
+    for j, b in enumerate(rows):
+        assert np.array_equal(ct[b, :sumF], ref["cache_tokens"][j]), f"{label} row {b} cache tokens"
+        assert np.array_equal(thr[b, :, 1], ref["thr_idx"][j]), f"{label} row {b} thr"
+        for k in range(len(F)):
+            zr, tr, rr = ref["stats"][j, k]
+            zg, tg, rg = st[b, k]
+            assert zg == zr or (np.isinf(zg) and np.isinf(zr)), f"{label} zmax"
+            assert abs(tg - tr) <= 1e-5 * abs(tr) + 1e-300, f"{label} row {b} k {k} S_top {tg} vs {tr}"
+            assert abs(rg - rr) <= 1e-5 * abs(rr) + 1e-300, f"{label} row {b} k {k} S_rest {rg} vs {rr}"
+
+
+def _cache_case(S, d, F, C, rows=None, label=""):
+    K = d["tokens"].shape[1]
+    sel = list(range(d["tokens"].shape[0])) if rows is None else list(rows)
+    dft = to_dev(d["draft"], torch)
+    cache = S.ssd_build_cache(dft, d["tau"], F)
+    torch.cuda.synchronize()
+    ref = O.build_cache(d["draft"][sel], d["tau"], F, C)
+    _check_cache(cache, ref, F, sel, label)
+    sigma = S.sigma_from_cache(cache, C)
+    got, vref, n_exc = _run_verify(S, d, sigma, {"F": F, "C": C}, rows=sel, label=label)
+    look = S.ssd_cache_lookup(cache["cache_tokens"], F, got["accepted"], got["out_tokens"])
+    torch.cuda.synchronize()
+    hit_r, slot_r = O.cache_lookup(ref["cache_tokens"], F, vref["accepted"], vref["out_tokens"])
+    hg = look["hit"].cpu().numpy()
+    sg = look["slot"].cpu().numpy()
+    acc_g = got["accepted"].cpu().numpy()
+    out_g = got["out_tokens"].cpu().numpy()
+    # lookup on the GPU's own outcome must match the oracle lookup of that outcome
+    hit_own, slot_own = O.cache_lookup(ref["cache_tokens"], F, acc_g[sel], out_g[sel])
+    assert np.array_equal(hg[sel], hit_own) and np.array_equal(sg[sel], slot_own), label
+    agree = (acc_g[sel] == vref["accepted"]) & np.all(out_g[sel] == vref["out_tokens"], axis=1)
+    assert np.array_equal(hg[sel][agree], hit_r[agree]), label
+    return cache, got, hg
+
+
+def test_cache_small(S):
+    for (V, K, B, dtype, N, C) in ((20000, 3, 5, "bf16", 40, 0.5), (9000, 2, 4, "f32", 30, 0.0),
+                                   (300, 4, 6, "bf16", 64, 1.0), (70, 2, 3, "bf16", 9, 0.3)):
+        log(f"[gpu] cache small V={V} K={K} B={B} {dtype} N={N} C={C}")
+        F = S.ssd_fanout(N, K, 0.75, 1.0)
+        F = [min(f, 64, V) for f in F]
+        d = _random_case(V + K, B, K, V, dtype, 0.7, Kd=K + 1)
+        _cache_case(S, d, F, C, label=f"cache-{V}")
+
+
+def test_cache_ties_and_limits(S):
+    # all-equal rows (every token ties), F_k = 0 and F_k = 64 segments
+    log("[gpu] cache ties")
+    B, K, V = 3, 3, 20000
+    d = _random_case(11, B, K, V, "bf16", 1.0, Kd=K + 1)
+    d["draft"][0, :, :] = W.f32_to_bf16_bits(np.full((K + 1, V), 0.5, dtype=np.float32))
+    d["draft"][1, 1, ::2] = W.f32_to_bf16_bits(np.full(V // 2, 3.0, dtype=np.float32))
+    F = [64, 0, 17, 64]
+    _cache_case(S, d, F, 0.4, label="ties")
+    log("[gpu] cache f32 ties")
+    d = _random_case(12, B, K, 5000, "f32", 1.0, Kd=K + 1)
+    d["draft"][2] = np.round(d["draft"][2])
+    _cache_case(S, d, [5, 64, 1, 33], 0.2, label="ties-f32")
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size
+# ---------------------------------------------------------------------------
+def test_cfg1(S):
+    cfg = W.get_config(1)
+    log(f"[gpu] {cfg.name}")
+    d = W.make_inputs(cfg)
+    _run_verify(S, d, label=cfg.name)
+    # many uniform draws on the same logits (batch stride 0 broadcast)
+    n = 256
+    ua = np.random.default_rng(5).random((n, cfg.K)).astype(np.float32)
+    ur = np.random.default_rng(6).random(n).astype(np.float32)
+    tgt = to_dev(d["target"], torch).expand(n, -1, -1)
+    dft = to_dev(d["draft"], torch).expand(n, -1, -1)
+    toks = np.tile(d["tokens"], (n, 1))
+    got = S.ssd_verify(tgt, dft, ivec(toks, torch), fvec(ua, torch), fvec(ur, torch), d["tau"])
+    torch.cuda.synchronize()
+    ref = O.verify(np.broadcast_to(d["target"], (n,) + d["target"].shape[1:]),
+                   np.broadcast_to(d["draft"], (n,) + d["draft"].shape[1:]), toks, ua, ur, d["tau"])
+    compare_verify(ref, got, cfg.K, label="cfg1-broadcast")
+
+
+def test_cfg2(S):
+    cfg = W.get_config(2)
+    log(f"[gpu] {cfg.name}")
+    d = W.make_inputs(cfg)
+    _run_verify(S, d, label=cfg.name)
+
+
+def test_cfg2_cache(S):
+    cfg = W.get_config(2)
+    log(f"[gpu] {cfg.name} cache build")
+    d = W.make_inputs(cfg)
+    F = S.ssd_fanout(cfg.n_budget, cfg.K, cfg.a_p, cfg.r)
+    _cache_case(S, d, F, cfg.C, rows=range(0, 64, 4), label="cfg2-cache")
+
+
+def test_cfg3(S):
+    cfg = W.get_config(3)
+    log(f"[gpu] {cfg.name}")
+    d = W.make_inputs(cfg)
+    F = S.ssd_fanout(cfg.n_budget, cfg.K, cfg.a_p, cfg.r)
+    assert F == [10, 9, 8, 8, 7, 6, 5, 11]
+    _, _, hits = _cache_case(S, d, F, cfg.C, label=cfg.name)
+    log(f"[gpu] cfg3 hit rate {hits.mean():.3f}")
+    _run_verify(S, d, label=cfg.name + "-plain")
+
+
+def test_cfg4(S):
+    cfg = W.get_config(4)
+    log(f"[gpu] {cfg.name}")
+    d = W.make_inputs(cfg)
+    rows = list(range(0, 512, 23))
+    _run_verify(S, d, rows=rows, label=cfg.name)
+
+
+@pytest.mark.parametrize("tau", [0.5, 1.0])
+def test_cfg5(S, tau):
+    cfg = W.get_config(5)
+    log(f"[gpu] {cfg.name} tau={tau}")
+    d = W.make_inputs(cfg, tau=tau)
+    F = S.ssd_fanout(cfg.n_budget, cfg.K, cfg.a_p, cfg.r)
+    assert F == [29, 23, 18, 15, 11, 9, 7, 6, 10]
+    rows = list(range(0, 256, 29))
+    _, _, hits = _cache_case(S, d, F, cfg.C, rows=rows, label=f"cfg5-{tau}")
+    log(f"[gpu] cfg5 tau={tau} hit rate {hits.mean():.3f}")

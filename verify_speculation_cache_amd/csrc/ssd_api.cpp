@@ -1,0 +1,376 @@
+// C-ABI layer of libssdv: argument checks, workspace carving and kernel
+// launches on the caller's stream. Every check runs on the host before the
+// first HIP call, so bad arguments never reach the device.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "ssd_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return SSD_OK;
+}
+
+constexpr double kLog2e = 1.4426950408889634073599246810018921;
+
+bool dtype_ok(int dtype) { return dtype == SSD_F32 || dtype == SSD_BF16; }
+
+int check_shape(int32_t B, int32_t K, int32_t V) {
+  if (B < 1 || B >= (1 << 24)) return fail(SSD_EINVAL, "B=%d outside [1, 2^24)", B);
+  if (K < 1 || K > SSD_MAX_K) return fail(SSD_EINVAL, "K=%d outside [1, %d]", K, SSD_MAX_K);
+  if (V < 1) return fail(SSD_EINVAL, "V=%d must be >= 1", V);
+  return SSD_OK;
+}
+
+int check_tau(float tau) {
+  if (!(tau > 0.0f) || !std::isfinite(tau)) return fail(SSD_EINVAL, "tau=%g must be finite and > 0", double(tau));
+  return SSD_OK;
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return SSD_OK;
+  if (ws == nullptr) return fail(SSD_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(SSD_EWORKSPACE, "workspace not 256-byte aligned");
+  if (have < need) return fail(SSD_EWORKSPACE, "workspace %zu bytes < %zu needed", have, need);
+  return SSD_OK;
+}
+
+int check_sigma(const ssd_sigma* s) {
+  if (s == nullptr) return SSD_OK;
+  if (!(s->C >= 0.0f && s->C <= 1.0f)) return fail(SSD_EINVAL, "sigma C=%g outside [0, 1]", double(s->C));
+  if (s->thr == nullptr || s->draft_stats == nullptr) return fail(SSD_EINVAL, "sigma thr/draft_stats is NULL");
+  return SSD_OK;
+}
+
+// grid dimension x is limited to 2^32-1 workgroups
+int check_grid(int64_t wgs) {
+  if (wgs > int64_t(0xFFFFFFFFll)) return fail(SSD_EINVAL, "problem too large for one launch (%lld workgroups)", (long long)wgs);
+  return SSD_OK;
+}
+
+int check_fanout_vec(const int32_t* F, int32_t K, int32_t V, int* sumF) {
+  if (F == nullptr) return fail(SSD_EINVAL, "F is NULL");
+  long long s = 0;
+  for (int k = 0; k <= K; ++k) {
+    if (F[k] < 0 || F[k] > SSD_MAX_F || F[k] > V)
+      return fail(SSD_EINVAL, "F[%d]=%d outside [0, min(V=%d, %d)]", k, F[k], V, SSD_MAX_F);
+    s += F[k];
+  }
+  *sumF = int(s);
+  return SSD_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SSD_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+using namespace ssd;
+
+extern "C" {
+
+SSD_API const char* ssd_last_error(void) { return g_err.c_str(); }
+
+SSD_API int ssd_fanout(int32_t n_budget, int32_t K, double a_p, double r, int32_t* F_out) {
+  if (F_out == nullptr) return fail(SSD_EINVAL, "F_out is NULL");
+  if (n_budget < 0) return fail(SSD_EINVAL, "budget %d < 0", n_budget);
+  if (K < 1 || K > SSD_MAX_K) return fail(SSD_EINVAL, "K=%d outside [1, %d]", K, SSD_MAX_K);
+  if (!(a_p > 0.0 && a_p < 1.0) || !std::isfinite(a_p)) return fail(SSD_EINVAL, "a_p=%g outside (0, 1)", a_p);
+  if (!(r > -1.0) || !std::isfinite(r)) return fail(SSD_EINVAL, "r=%g must be finite and > -1", r);
+  // weights of the geometric shape: a_p^(k/(1+r)) for k < K, and the
+  // all-accept length a_p^(K/(1+r)) (1 - a_p)^(-1/(1+r))
+  const double e = 1.0 / (1.0 + r);
+  std::vector<double> wgt(K + 1);
+  double tot = 0.0;
+  for (int k = 0; k < K; ++k) {
+    wgt[k] = std::pow(a_p, double(k) * e);
+    tot += wgt[k];
+  }
+  wgt[K] = std::pow(a_p, double(K) * e) * std::pow(1.0 - a_p, -e);
+  tot += wgt[K];
+  const double f0 = double(n_budget) / tot;
+  std::vector<double> frac(K + 1);
+  long long used = 0;
+  for (int k = 0; k <= K; ++k) {
+    const double v = f0 * wgt[k];
+    const double fl = std::floor(v);
+    F_out[k] = int32_t(fl);
+    frac[k] = v - fl;
+    used += F_out[k];
+  }
+  // leftover units to the largest fractional parts, ties to the smaller k
+  long long left = (long long)n_budget - used;
+  std::vector<char> taken(K + 1, 0);
+  for (; left > 0; --left) {
+    int best = -1;
+    for (int k = 0; k <= K; ++k)
+      if (!taken[k] && (best < 0 || frac[k] > frac[best])) best = k;
+    if (best < 0) break;
+    taken[best] = 1;
+    F_out[best] += 1;
+  }
+  ok();
+  return n_budget;
+}
+
+SSD_API size_t ssd_verify_workspace_size(int32_t B, int32_t K, int32_t V, int dtype) {
+  if (check_shape(B, K, V) != SSD_OK || !dtype_ok(dtype)) return 0;
+  const int64_t S = chunks_per_row(V);
+  const StatsWs sw(B, 2 * K + 1, S);
+  const ResidWs rw(B, S);
+  return sw.total + rw.total;
+}
+
+SSD_API size_t ssd_residual_workspace_size(int32_t B, int32_t K, int32_t V, int dtype) {
+  if (check_shape(B, K, V) != SSD_OK || !dtype_ok(dtype)) return 0;
+  const int64_t S = chunks_per_row(V);
+  const StatsWs sw(B, 2, S);
+  const ResidWs rw(B, S);
+  return sw.total + rw.total;
+}
+
+SSD_API size_t ssd_build_cache_workspace_size(int32_t B, int32_t K, int32_t V, int dtype) {
+  if (check_shape(B, K, V) != SSD_OK || !dtype_ok(dtype)) return 0;
+  return CacheWs(B, K, chunks_per_row(V)).total;
+}
+
+SSD_API int ssd_verify(const void* target_logits, int64_t target_bstride,
+                       const void* draft_logits, int64_t draft_bstride, int dtype,
+                       int32_t B, int32_t K, int32_t V, float tau,
+                       const int32_t* draft_tokens, const float* u_acc, const float* u_res,
+                       const ssd_sigma* sigma,
+                       int32_t* accepted, int32_t* out_tokens, float* probs,
+                       float* resid_mass, float* row_lse,
+                       void* workspace, size_t ws_bytes, void* hip_stream) {
+  int st;
+  if (!dtype_ok(dtype)) return fail(SSD_EDTYPE, "unknown dtype %d", dtype);
+  if ((st = check_shape(B, K, V)) != SSD_OK) return st;
+  if ((st = check_tau(tau)) != SSD_OK) return st;
+  if ((st = check_sigma(sigma)) != SSD_OK) return st;
+  if (!target_logits || !draft_logits || !draft_tokens || !u_acc || !u_res || !accepted || !out_tokens)
+    return fail(SSD_EINVAL, "a required pointer is NULL");
+  if (target_bstride < 0 || draft_bstride < 0) return fail(SSD_EINVAL, "negative batch stride");
+  const int64_t S = chunks_per_row(V);
+  const bool sig = sigma != nullptr;
+  const int NR = sig ? K + 1 : 2 * K + 1;
+  const StatsWs sw(B, 2 * K + 1, S);
+  const ResidWs rw(B, S);
+  if ((st = check_ws(workspace, ws_bytes, sw.total + rw.total)) != SSD_OK) return st;
+  if ((st = check_grid(int64_t(B) * NR * S)) != SSD_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+
+  StatsArgs a{};
+  a.target = target_logits;
+  a.tb = target_bstride;
+  a.draft = draft_logits;
+  a.db = draft_bstride;
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.S = int(S);
+  a.NR = NR;
+  a.mode = sig ? kModeVerifySigma : kModeVerify;
+  a.c64 = kLog2e / double(tau);
+  a.c32 = float(a.c64);
+  a.inv_tau = 1.0 / double(tau);
+  a.tokens = draft_tokens;
+  a.u_acc = u_acc;
+  a.use_sigma = sig ? 1 : 0;
+  a.C = sig ? sigma->C : 1.0f;
+  a.thr = sig ? sigma->thr : nullptr;
+  a.dstats = sig ? sigma->draft_stats : nullptr;
+  a.accepted = accepted;
+  a.out_tokens = out_tokens;
+  a.probs = probs;
+  a.row_lse = row_lse;
+  a.part = reinterpret_cast<RowPartial*>(ws + sw.part);
+  a.cnt = reinterpret_cast<uint32_t*>(ws + sw.cnt);
+  a.info = reinterpret_cast<RowInfo*>(ws + sw.info);
+  hipStream_t stream = as_stream(hip_stream);
+  if ((st = hip_status(launch_stats(a, dtype, stream), "stats launch")) != SSD_OK) return st;
+
+  ResidArgs r{};
+  r.target = target_logits;
+  r.tb = target_bstride;
+  r.draft = draft_logits;
+  r.db = draft_bstride;
+  r.B = B;
+  r.K = K;
+  r.V = V;
+  r.S = int(S);
+  r.c32 = a.c32;
+  r.u = u_res;
+  r.info = a.info;
+  r.cmass = reinterpret_cast<double*>(ws + sw.total + rw.cmass);
+  r.cnt = reinterpret_cast<uint32_t*>(ws + sw.total + rw.cnt);
+  r.tok_out = out_tokens;
+  r.tok_stride = K + 1;
+  r.tok_at_a = 1;
+  r.mass_out = resid_mass;
+  return hip_status(launch_resid(r, dtype, sig, stream), "residual launch");
+}
+
+SSD_API int ssd_residual_sample(const void* target_logits, int64_t target_bstride,
+                                const void* draft_logits, int64_t draft_bstride, int dtype,
+                                int32_t B, int32_t K, int32_t V, float tau,
+                                const int32_t* row, const ssd_sigma* sigma, const float* u,
+                                int32_t* token_out, float* mass_out,
+                                void* workspace, size_t ws_bytes, void* hip_stream) {
+  int st;
+  if (!dtype_ok(dtype)) return fail(SSD_EDTYPE, "unknown dtype %d", dtype);
+  if ((st = check_shape(B, K, V)) != SSD_OK) return st;
+  if ((st = check_tau(tau)) != SSD_OK) return st;
+  if ((st = check_sigma(sigma)) != SSD_OK) return st;
+  if (!target_logits || !row || !u || !token_out) return fail(SSD_EINVAL, "a required pointer is NULL");
+  if (sigma && !draft_logits) return fail(SSD_EINVAL, "sigma given without draft logits");
+  if (target_bstride < 0 || draft_bstride < 0) return fail(SSD_EINVAL, "negative batch stride");
+  const int64_t S = chunks_per_row(V);
+  const StatsWs sw(B, 2, S);
+  const ResidWs rw(B, S);
+  if ((st = check_ws(workspace, ws_bytes, sw.total + rw.total)) != SSD_OK) return st;
+  if ((st = check_grid(int64_t(B) * 2 * S)) != SSD_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  const bool sig = sigma != nullptr;
+
+  StatsArgs a{};
+  a.target = target_logits;
+  a.tb = target_bstride;
+  a.draft = draft_logits;
+  a.db = draft_bstride;
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.S = int(S);
+  a.NR = 2;
+  a.mode = kModeRows;
+  a.c64 = kLog2e / double(tau);
+  a.c32 = float(a.c64);
+  a.inv_tau = 1.0 / double(tau);
+  a.rows_in = row;
+  a.use_draft = draft_logits != nullptr ? 1 : 0;
+  a.use_sigma = sig ? 1 : 0;
+  a.C = sig ? sigma->C : 1.0f;
+  a.thr = sig ? sigma->thr : nullptr;
+  a.dstats = sig ? sigma->draft_stats : nullptr;
+  a.part = reinterpret_cast<RowPartial*>(ws + sw.part);
+  a.cnt = reinterpret_cast<uint32_t*>(ws + sw.cnt);
+  a.info = reinterpret_cast<RowInfo*>(ws + sw.info);
+  hipStream_t stream = as_stream(hip_stream);
+  if ((st = hip_status(launch_stats(a, dtype, stream), "stats launch")) != SSD_OK) return st;
+
+  ResidArgs r{};
+  r.target = target_logits;
+  r.tb = target_bstride;
+  r.draft = draft_logits;
+  r.db = draft_bstride;
+  r.B = B;
+  r.K = K;
+  r.V = V;
+  r.S = int(S);
+  r.c32 = a.c32;
+  r.u = u;
+  r.info = a.info;
+  r.cmass = reinterpret_cast<double*>(ws + sw.total + rw.cmass);
+  r.cnt = reinterpret_cast<uint32_t*>(ws + sw.total + rw.cnt);
+  r.tok_out = token_out;
+  r.tok_stride = 1;
+  r.tok_at_a = 0;
+  r.mass_out = mass_out;
+  return hip_status(launch_resid(r, dtype, sig, stream), "residual launch");
+}
+
+SSD_API int ssd_build_cache(const void* draft_logits, int64_t draft_bstride, int dtype,
+                            int32_t B, int32_t K, int32_t V, float tau, const int32_t* F,
+                            int32_t* cache_tokens, ssd_rowkey* thr, double* draft_stats,
+                            void* workspace, size_t ws_bytes, void* hip_stream) {
+  int st;
+  if (!dtype_ok(dtype)) return fail(SSD_EDTYPE, "unknown dtype %d", dtype);
+  if ((st = check_shape(B, K, V)) != SSD_OK) return st;
+  if ((st = check_tau(tau)) != SSD_OK) return st;
+  int sumF = 0;
+  if ((st = check_fanout_vec(F, K, V, &sumF)) != SSD_OK) return st;
+  if (!draft_logits || !thr || !draft_stats || (sumF > 0 && !cache_tokens))
+    return fail(SSD_EINVAL, "a required pointer is NULL");
+  if (draft_bstride < 0) return fail(SSD_EINVAL, "negative batch stride");
+  const int64_t S = chunks_per_row(V);
+  const CacheWs cw(B, K, S);
+  if ((st = check_ws(workspace, ws_bytes, cw.total)) != SSD_OK) return st;
+  if ((st = check_grid(int64_t(B) * (K + 1) * S)) != SSD_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  CacheArgs a{};
+  a.draft = draft_logits;
+  a.db = draft_bstride;
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.S = int(S);
+  a.sumF = sumF;
+  a.c64 = kLog2e / double(tau);
+  a.c32 = float(a.c64);
+  int acc = 0;
+  for (int k = 0; k <= K; ++k) {
+    a.F[k] = F[k];
+    a.off[k] = acc;
+    acc += F[k];
+  }
+  a.off[K + 1] = acc;
+  a.cache_tokens = cache_tokens;
+  a.thr = thr;
+  a.dstats = draft_stats;
+  a.part = reinterpret_cast<CachePartial*>(ws + cw.part);
+  a.cand = reinterpret_cast<Cand*>(ws + cw.cand);
+  a.cnt = reinterpret_cast<uint32_t*>(ws + cw.cnt);
+  return hip_status(launch_cache(a, dtype, as_stream(hip_stream)), "cache build launch");
+}
+
+SSD_API int ssd_cache_lookup(const int32_t* cache_tokens, const int32_t* F, int32_t B, int32_t K,
+                             const int32_t* accepted, const int32_t* out_tokens,
+                             uint8_t* hit, int32_t* slot, void* hip_stream) {
+  if (B < 1 || B >= (1 << 24)) return fail(SSD_EINVAL, "B=%d outside [1, 2^24)", B);
+  if (K < 1 || K > SSD_MAX_K) return fail(SSD_EINVAL, "K=%d outside [1, %d]", K, SSD_MAX_K);
+  if (F == nullptr) return fail(SSD_EINVAL, "F is NULL");
+  LookupArgs a{};
+  int acc = 0;
+  for (int k = 0; k <= K; ++k) {
+    if (F[k] < 0 || F[k] > SSD_MAX_F) return fail(SSD_EINVAL, "F[%d]=%d outside [0, %d]", k, F[k], SSD_MAX_F);
+    a.F[k] = F[k];
+    a.off[k] = acc;
+    acc += F[k];
+  }
+  a.off[K + 1] = acc;
+  if (!accepted || !out_tokens || !hit || (acc > 0 && !cache_tokens))
+    return fail(SSD_EINVAL, "a required pointer is NULL");
+  a.cache_tokens = cache_tokens;
+  a.B = B;
+  a.K = K;
+  a.sumF = acc;
+  a.accepted = accepted;
+  a.out_tokens = out_tokens;
+  a.hit = hit;
+  a.slot = slot;
+  return hip_status(launch_lookup(a, as_stream(hip_stream)), "lookup launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,165 @@
+// Internal interface between the C-ABI layer (ssd_api.cpp) and the HIP
+// kernels: argument blocks, workspace layout and launcher declarations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ssd.h"
+
+namespace ssd {
+
+// One workgroup = 256 lanes = four wave64s; every thread holds 32 logits of
+// its chunk in registers, so a chunk is 8192 vocabulary entries.
+constexpr int kThreads = 256;
+constexpr int kPerThread = 32;
+constexpr int kChunk = kThreads * kPerThread;   // 8192
+constexpr int kMaxRows = 2 * SSD_MAX_K + 1;     // rows one verify batch element touches
+
+inline int64_t chunks_per_row(int64_t V) { return (V + kChunk - 1) / kChunk; }
+
+// Per-(row, chunk) statistics: chunk max of the raw logits and the chunk's
+// sum of exp2((z - pivot) * log2(e)/tau), pivot = chunk max (0 if -inf).
+struct alignas(16) RowPartial {
+  float m;
+  float pad;
+  double s;
+};
+
+// Everything the residual kernel needs about one batch row.
+struct alignas(16) RowInfo {
+  int32_t a;        // accepted length (-1: flagged row, skip)
+  int32_t bonus;    // 1: draw from p of target row `a`; 0: from max(0, p - q)
+  float piv_t;      // pivot of target row a (raw logit units)
+  float piv_d;      // pivot of draft row a
+  double s_t;       // sum exp2((z - piv_t) c) over target row a
+  double s_d;       // sigma-weighted draft normaliser of row a (same units)
+  uint32_t thr_key; // sigma membership threshold of draft row a
+  int32_t thr_idx;
+  float C;          // weight of members (1 when no sigma)
+  int32_t pad;
+};
+
+struct alignas(16) CachePartial {
+  float m;
+  float pad;
+  double s_rest;   // sum over the chunk's tokens that are not its top-F candidates
+};
+
+struct Cand {
+  uint32_t key;
+  int32_t idx;
+};
+
+enum StatsMode { kModeVerify = 0, kModeVerifySigma = 1, kModeRows = 2 };
+
+struct StatsArgs {
+  const void* target;
+  int64_t tb;
+  const void* draft;
+  int64_t db;
+  int B, K, V, S, NR, mode;
+  float c32;        // log2(e) / tau
+  double c64;       // log2(e) / tau in double
+  double inv_tau;   // 1 / tau
+  const int32_t* tokens;
+  const float* u_acc;
+  const int32_t* rows_in;   // kModeRows: position per batch row
+  int use_draft;            // kModeRows: residual form (else bonus form)
+  int use_sigma;
+  float C;
+  const ssd_rowkey* thr;
+  const double* dstats;
+  int32_t* accepted;
+  int32_t* out_tokens;
+  float* probs;
+  float* row_lse;
+  RowPartial* part;   // [B, NR, S]
+  uint32_t* cnt;      // [B]
+  RowInfo* info;      // [B]
+};
+
+struct ResidArgs {
+  const void* target;
+  int64_t tb;
+  const void* draft;
+  int64_t db;
+  int B, K, V, S;
+  float c32;
+  const float* u;
+  const RowInfo* info;
+  double* cmass;       // [B, S, 2]: residual mass, target mass per chunk
+  uint32_t* cnt;       // [B]
+  int32_t* tok_out;    // token written at tok_out[b * tok_stride + (tok_at_a ? a : 0)]
+  int64_t tok_stride;
+  int tok_at_a;
+  float* mass_out;     // nullable [B]
+};
+
+struct CacheArgs {
+  const void* draft;
+  int64_t db;
+  int B, K, V, S, sumF;
+  float c32;
+  double c64;
+  int F[SSD_MAX_K + 1];
+  int off[SSD_MAX_K + 2];
+  int32_t* cache_tokens;
+  ssd_rowkey* thr;
+  double* dstats;
+  CachePartial* part;   // [B, K+1, S]
+  Cand* cand;           // [B, K+1, S, SSD_MAX_F]
+  uint32_t* cnt;        // [B, K+1]
+};
+
+struct LookupArgs {
+  const int32_t* cache_tokens;
+  int B, K, sumF;
+  int F[SSD_MAX_K + 1];
+  int off[SSD_MAX_K + 2];
+  const int32_t* accepted;
+  const int32_t* out_tokens;
+  uint8_t* hit;
+  int32_t* slot;
+};
+
+// Workspace layouts (byte offsets, each 256-aligned).
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct StatsWs {
+  size_t part, cnt, info, total;
+  StatsWs(int64_t B, int64_t NR, int64_t S) {
+    part = 0;
+    cnt = align256(part + sizeof(RowPartial) * B * NR * S);
+    info = align256(cnt + sizeof(uint32_t) * B);
+    total = align256(info + sizeof(RowInfo) * B);
+  }
+};
+
+struct ResidWs {
+  size_t cmass, cnt, total;
+  ResidWs(int64_t B, int64_t S) {
+    cmass = 0;
+    cnt = align256(cmass + sizeof(double) * 2 * B * S);
+    total = align256(cnt + sizeof(uint32_t) * B);
+  }
+};
+
+struct CacheWs {
+  size_t part, cand, cnt, total;
+  CacheWs(int64_t B, int64_t K, int64_t S) {
+    part = 0;
+    cand = align256(part + sizeof(CachePartial) * B * (K + 1) * S);
+    cnt = align256(cand + sizeof(Cand) * B * (K + 1) * S * SSD_MAX_F);
+    total = align256(cnt + sizeof(uint32_t) * B * (K + 1));
+  }
+};
+
+// Launchers (return the hipError_t of the launch).
+hipError_t launch_stats(const StatsArgs& a, int dtype, hipStream_t st);
+hipError_t launch_resid(const ResidArgs& a, int dtype, bool sigma, hipStream_t st);
+hipError_t launch_cache(const CacheArgs& a, int dtype, hipStream_t st);
+hipError_t launch_lookup(const LookupArgs& a, hipStream_t st);
+
+}  // namespace ssd
