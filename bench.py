@@ -1,0 +1,258 @@
+"""Throughput of the speculative verification + SAGUARO cache path on one GPU.
+
+One step = one pass of the whole path over one batch:
+  ssd_fanout (host)  ->  ssd_build_cache (draft rows 0..K)  ->
+  ssd_verify with sigma_{F,C}  ->  ssd_cache_lookup.
+Default workload: B=64 sequences, K=5 drafted tokens, V=128256, bf16 logits,
+tau=0.7, cache budget 64 split with a_p=0.8, r=1, C=0.5.
+
+Inputs are resident in HBM before timing; NCOPY rotating copies (more than
+the 256 MB Infinity Cache holds) make each step read its logits from HBM.
+Each copy's step is captured once in a HIP graph and replayed. Timing uses
+HIP events on the stream the library launches on.
+
+Prints one JSON line (rank 0).
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0   # MI355X HBM3E peak, GB/s
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--eager", action="store_true", help="launch eagerly instead of graph replay")
+    ap.add_argument("--profile-loop", type=int, default=0,
+                    help="after the bench, run this many extra eager steps (for profilers)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(every batch row is independent, so more GPUs would each run this same "
+              "kernel on B/N rows)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import verify_speculation_cache_amd as S
+    import workloads as W
+
+    cfg = W.get_config(args.config)
+    if not cfg.has_cache:   # the cache build reads draft row K: use cfg3's cache parameters
+        raise SystemExit("bench workload needs cache parameters (use --config 2, 3 or 5)")
+    B, K, V = cfg.B, cfg.K, cfg.V
+    tau = cfg.taus[0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    d = W.make_inputs(cfg, tau=tau)
+    gen_s = time.time() - t0
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    tgt0, dft0 = up(d["target"]), up(d["draft"][:, :K + 1])
+    step_bytes = tgt0.numel() * tgt0.element_size() + dft0.numel() * dft0.element_size()
+    ncopy = int(math.ceil(MALL_BYTES / step_bytes)) + 1
+    tgts = [tgt0] + [tgt0.clone() for _ in range(ncopy - 1)]
+    dfts = [dft0] + [dft0.clone() for _ in range(ncopy - 1)]
+    toks = torch.from_numpy(d["tokens"]).to(dev)
+    ua = torch.from_numpy(d["u_acc"]).to(dev)
+    ur = torch.from_numpy(d["u_res"]).to(dev)
+    F = S.ssd_fanout(cfg.n_budget, K, cfg.a_p, cfg.r)
+    C = cfg.C
+
+    outs = []
+    for j in range(ncopy):
+        cache = S.ssd_build_cache(dfts[j], tau, F)
+        res = S.ssd_verify(tgts[j], dfts[j], toks, ua, ur, tau, S.sigma_from_cache(cache, C))
+        look = S.ssd_cache_lookup(cache["cache_tokens"], F, res["accepted"], res["out_tokens"])
+        outs.append((cache, res, look))
+    torch.cuda.synchronize()
+
+    def step(j):
+        cache, res, look = outs[j]
+        S.ssd_build_cache(dfts[j], tau, F, out=cache)
+        S.ssd_verify(tgts[j], dfts[j], toks, ua, ur, tau, S.sigma_from_cache(cache, C), out=res)
+        S.ssd_cache_lookup(cache["cache_tokens"], F, res["accepted"], res["out_tokens"], out=look)
+
+    stream = torch.cuda.Stream()
+    graphs = []
+    if not args.eager:
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            for j in range(ncopy):     # warm the per-shape workspaces on this stream
+                step(j)
+        torch.cuda.synchronize()
+        for j in range(ncopy):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                step(j)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(n, offset=0):
+        for i in range(n):
+            j = (offset + i) % ncopy
+            F_host = S.ssd_fanout(cfg.n_budget, K, cfg.a_p, cfg.r)   # host row of the step
+            assert F_host == F
+            if graphs:
+                graphs[j].replay()
+            else:
+                step(j)
+
+    run(args.warmup)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run(args.steps, args.warmup)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # replays must reproduce the eager outputs
+    ref = [(o[1]["accepted"].clone(), o[1]["out_tokens"].clone(), o[2]["hit"].clone()) for o in outs]
+
+    # per-entry-point durations (eager, events on the launching stream)
+    def time_call(fn, n=60):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record()
+            fn(i % ncopy)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in ev)
+        return float(np.mean(ts[n // 10: n - n // 10]))   # trimmed mean, ms
+
+    def call_build(j):
+        S.ssd_build_cache(dfts[j], tau, F, out=outs[j][0])
+
+    def call_verify(j):
+        S.ssd_verify(tgts[j], dfts[j], toks, ua, ur, tau, S.sigma_from_cache(outs[j][0], C), out=outs[j][1])
+
+    def call_plain(j):
+        S.ssd_verify(tgts[j], dfts[j], toks, ua, ur, tau, out=plain_out[j])
+
+    def call_lookup(j):
+        cache, res, look = outs[j]
+        S.ssd_cache_lookup(cache["cache_tokens"], F, res["accepted"], res["out_tokens"], out=look)
+
+    plain_out = [S.ssd_verify(tgts[j], dfts[j], toks, ua, ur, tau) for j in range(ncopy)]
+    torch.cuda.synchronize()
+    for _ in range(2):
+        time_call(call_build, 10), time_call(call_verify, 10), time_call(call_plain, 10)
+    t_build = time_call(call_build)
+    t_verify = time_call(call_verify)
+    t_plain = time_call(call_plain)
+    t_lookup = time_call(call_lookup)
+    for j, o in enumerate(outs):
+        assert torch.equal(o[1]["accepted"], ref[j][0]) and torch.equal(o[1]["out_tokens"], ref[j][1])
+        assert torch.equal(o[2]["hit"], ref[j][2])
+
+    if args.profile_loop:
+        for i in range(args.profile_loop):
+            step(i % ncopy)
+            call_plain(i % ncopy)
+        torch.cuda.synchronize()
+
+    acc = outs[0][1]["accepted"].cpu().numpy()
+    hit = outs[0][2]["hit"].cpu().numpy()
+
+    # single-read algorithmic bytes
+    elem = 2 if cfg.dtype == "bf16" else 4
+    row_bytes = V * elem
+    bytes_build = B * (K + 1) * row_bytes            # draft rows 0..K
+    bytes_verify_sigma = B * (K + 1) * row_bytes     # target rows 0..K (draft stats reused)
+    bytes_plain = B * (2 * K + 1) * row_bytes        # target 0..K + draft 0..K-1
+    s_step = ms_step / 1e3
+    gbps = step_bytes / s_step / 1e9
+
+    # dominant kernel: the cache build (one kernel per call)
+    dom_ms = t_build
+    dom_gbps = bytes_build / (dom_ms / 1e3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(dom_gbps / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "k_cache<bf16> (ssd_build_cache)", "bytes_per_launch": bytes_build,
+                "avg_launch_ms": round(dom_ms, 5)}
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(cfg, d, F, C, tau, args.cpu_seconds)
+
+    line = {
+        "metric": "verified rows/sec + logits HBM GB/s (% of peak), B=64 K=5 V=128256 bf16",
+        "value": round(B / s_step, 1),
+        "unit": "verified rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded Gaussian + Zipf-rank logits, draft = target + noise)",
+        "config": {"workload": "ssd_step_fanout_buildcache_verify_sigma_lookup", "B": B, "K": K, "V": V,
+                   "logits": cfg.dtype, "tau": tau, "cache": {"budget": cfg.n_budget, "a_p": cfg.a_p,
+                                                                "r": cfg.r, "C": C, "F": F},
+                   "rotating_copies": ncopy, "graph_replay": not args.eager},
+        "logits_gbps": round(gbps, 1),
+        "pct_peak_hbm": round(100 * gbps / PEAK_HBM_GBS, 2),
+        "bytes_per_step": step_bytes,
+        "roofline": roofline,
+        "per_call_ms": {"ssd_build_cache": round(t_build, 5), "ssd_verify_sigma": round(t_verify, 5),
+                        "ssd_cache_lookup": round(t_lookup, 5)},
+        "verify_only": {"ms": round(t_plain, 5), "rows_per_s": round(B / (t_plain / 1e3), 1),
+                        "bytes": bytes_plain,
+                        "gbps": round(bytes_plain / (t_plain / 1e3) / 1e9, 1),
+                        "pct_peak_hbm": round(100 * bytes_plain / (t_plain / 1e3) / 1e9 / PEAK_HBM_GBS, 2)},
+        "verify_sigma_gbps": round(bytes_verify_sigma / (t_verify / 1e3) / 1e9, 1),
+        "mean_accepted_plus_1": round(float(np.mean(acc + 1)), 4),
+        "hit_rate": round(float(np.mean(hit)), 4),
+        "cpu_baseline": cpu,
+        "gen_s": round(gen_s, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(cfg, d, F, C, tau, budget_s):
+    """The float64 oracle on the host, same workload, single thread, bounded sample."""
+    import oracle as O
+    t0 = time.time()
+    n = 0
+    while n < cfg.B and (time.time() - t0) < budget_s:
+        b = slice(n, n + 1)
+        cache = O.build_cache(d["draft"][b], tau, F, C)
+        ref = O.verify(d["target"][b], d["draft"][b], d["tokens"][b], d["u_acc"][b], d["u_res"][b],
+                       tau, {"F": F, "C": C})
+        O.cache_lookup(cache["cache_tokens"], F, ref["accepted"], ref["out_tokens"])
+        n += 1
+    dt = time.time() - t0
+    return {"value": round(n / dt, 3), "unit": "verified rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} of {cfg.B} batch rows of the same step (fan-out, cache build, "
+                      f"sigma verify, lookup), float64 NumPy, {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

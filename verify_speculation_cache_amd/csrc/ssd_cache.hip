@@ -31,14 +31,27 @@ namespace ssd {
 constexpr int kSurvCap = 1024;    // survivor list capacity (entries)
 constexpr int kMergeCap = 4096;   // candidates staged in LDS for the merge
 
-template <int DT>
-__device__ __forceinline__ bool surv_fast(float x, float f0, int64_t idx, int64_t V, bool tail) {
-  return (x >= f0) && (!tail || idx < V);
+__device__ __forceinline__ uint64_t cand_bits(Cand e) {
+  return uint64_t(e.key) | (uint64_t(uint32_t(e.idx)) << 32);
+}
+__device__ __forceinline__ Cand bits_cand(uint64_t w) {
+  Cand e;
+  e.key = uint32_t(w);
+  e.idx = int32_t(uint32_t(w >> 32));
+  return e;
 }
 
+// Position of entry q of thread tid inside its chunk (strided layout).
 template <int DT>
-__device__ __forceinline__ uint64_t local_comp(float x, int64_t idx, int64_t c0) {
-  return (uint64_t(key_of<DT>(x)) << 13) | uint64_t(kChunk - 1 - int(idx - c0));
+__device__ __forceinline__ int local_of(int tid, int q) {
+  constexpr int PV = Dt<DT>::kPerVec;
+  return ((q / PV) * kThreads + tid) * PV + (q % PV);
+}
+
+// chunk-local rank key for the exact search: key, then the smaller offset
+template <int DT>
+__device__ __forceinline__ uint64_t local_comp(float x, int loc) {
+  return (uint64_t(key_of<DT>(x)) << 13) | uint64_t(kChunk - 1 - loc);
 }
 
 template <int DT>
@@ -52,6 +65,8 @@ __global__ __launch_bounds__(kThreads) void k_cache(CacheArgs a) {
   __shared__ int sm_last;
   __shared__ double s_sel_e[SSD_MAX_F];
   __shared__ Cand s_sel[SSD_MAX_F];
+  __shared__ float sm_mrow;
+  __shared__ double sm_srest;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int KP = a.K + 1;
@@ -63,14 +78,13 @@ __global__ __launch_bounds__(kThreads) void k_cache(CacheArgs a) {
   const int F = a.F[k];
   const int64_t rowid = int64_t(b) * KP + k;
   const T* row = static_cast<const T*>(a.draft) + int64_t(b) * a.db + int64_t(k) * a.V;
-  const int64_t V = a.V;
 
   const int64_t c0 = int64_t(c) * kChunk;
-  const bool full = c0 + kChunk <= V;
-  const bool tail = !full;
-  const bool vec = full && ((reinterpret_cast<uintptr_t>(row) & 15u) == 0);
+  const int nvalid = int(min(int64_t(kChunk), int64_t(a.V) - c0));   // entries of this chunk
+  const bool full = nvalid == kChunk;
+  const bool vec = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
   float x[kPerThread];
-  load_strided<DT>(row, c0, V, vec, tid, x);
+  load_strided<DT>(row, c0, a.V, vec, tid, x);
   float lm = x[0];
 #pragma unroll
   for (int q = 1; q < kPerThread; ++q) lm = fmaxf(lm, x[q]);
@@ -78,11 +92,10 @@ __global__ __launch_bounds__(kThreads) void k_cache(CacheArgs a) {
   const float piv = pivot_of(mc);
   const float c32 = a.c32;
 
-  // ---- step 2: per-wave threshold from lane maxima ----
+  // ---- per-wave threshold from lane maxima ----
   float f0 = __builtin_inff();   // F == 0: no survivors
   if (F > 0) {
-    const bool lane_valid = Strided<DT>::index(c0, tid, 0) < V;
-    const uint32_t kl = lane_valid ? key_of<DT>(lm) : 0u;
+    const uint32_t kl = local_of<DT>(tid, 0) < nvalid ? key_of<DT>(lm) : 0u;
     uint32_t t = 0;
     for (int bit = Dt<DT>::kKeyBits - 1; bit >= 0; --bit) {
       const uint32_t cand = t | (1u << bit);
@@ -90,48 +103,45 @@ __global__ __launch_bounds__(kThreads) void k_cache(CacheArgs a) {
     }
     f0 = (t <= key_of<DT>(-__builtin_inff())) ? -__builtin_inff() : value_of_key<DT>(t);
   }
-  int nt = 0;
+  // survivor mask: bit q set when entry q may be among the chunk's top-F
+  uint32_t smask = 0;
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q)
-    nt += surv_fast<DT>(x[q], f0, Strided<DT>::index(c0, tid, q), V, tail) ? 1 : 0;
-  int n = block_sum_i(nt, sm_i);
+    if (x[q] >= f0 && (full || local_of<DT>(tid, q) < nvalid)) smask |= 1u << q;
+  int n = block_sum_i(__popc(smask), sm_i);
 
-  // ---- exact fallback: chunk-level F-th (key, index) by bitwise search ----
-  bool exact = n > kSurvCap;
-  uint64_t thr = 0;
-  if (exact) {   // uniform per workgroup
+  // ---- exact fallback (ties beyond LDS capacity): chunk-level F-th (key, offset) ----
+  if (n > kSurvCap) {   // uniform per workgroup
     constexpr int kBits = Dt<DT>::kKeyBits + 13;
+    uint64_t thr = 0;
     for (int bit = kBits - 1; bit >= 0; --bit) {
       const uint64_t cand = thr | (uint64_t(1) << bit);
       int cnt = 0;
 #pragma unroll
       for (int q = 0; q < kPerThread; ++q) {
-        const int64_t idx = Strided<DT>::index(c0, tid, q);
-        if (idx < V && local_comp<DT>(x[q], idx, c0) >= cand) ++cnt;
+        const int loc = local_of<DT>(tid, q);
+        if (loc < nvalid && local_comp<DT>(x[q], loc) >= cand) ++cnt;
       }
       if (block_sum_i(cnt, sm_i) >= F) thr = cand;
     }
-  }
-  auto is_surv = [&](int q) -> bool {
-    const int64_t idx = Strided<DT>::index(c0, tid, q);
-    if (exact) return idx < V && local_comp<DT>(x[q], idx, c0) >= thr;
-    return surv_fast<DT>(x[q], f0, idx, V, tail);
-  };
-  if (exact) {
-    nt = 0;
+    smask = 0;
 #pragma unroll
-    for (int q = 0; q < kPerThread; ++q) nt += is_surv(q) ? 1 : 0;
+    for (int q = 0; q < kPerThread; ++q) {
+      const int loc = local_of<DT>(tid, q);
+      if (loc < nvalid && local_comp<DT>(x[q], loc) >= thr) smask |= 1u << q;
+    }
   }
 
-  // ---- step 4a: mass of non-survivors ----
+  // ---- mass of the entries that are not survivors ----
   float sn = 0.0f;
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
     const float e = __builtin_amdgcn_exp2f((x[q] - piv) * c32);
-    sn += is_surv(q) ? 0.0f : e;
+    sn += ((smask >> q) & 1u) ? 0.0f : e;
   }
 
-  // ---- step 3: compaction of survivors into LDS ----
+  // ---- compaction of survivors into LDS ----
+  const int nt = __popc(smask);
   const int incl = wave_incl_scan_i(nt, lane);
   __syncthreads();
   if (lane == 63) sm_wcnt[w] = incl;
@@ -142,10 +152,10 @@ __global__ __launch_bounds__(kThreads) void k_cache(CacheArgs a) {
   int pos = woff + incl - nt;
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
-    if (is_surv(q)) {
+    if ((smask >> q) & 1u) {
       Cand e;
       e.key = key_of<DT>(x[q]);
-      e.idx = int32_t(Strided<DT>::index(c0, tid, q));
+      e.idx = int32_t(c0) + local_of<DT>(tid, q);
       s_list[pos++] = e;
     }
   }
@@ -159,50 +169,43 @@ __global__ __launch_bounds__(kThreads) void k_cache(CacheArgs a) {
     const uint64_t rk = rank_key(e.key, e.idx);
     int rank = 0;
     for (int j = 0; j < n; ++j) rank += (rank_key(s_list[j].key, s_list[j].idx) > rk) ? 1 : 0;
-    if (rank < F) out[rank] = e;
+    if (rank < F) dev_store(reinterpret_cast<uint64_t*>(out + rank), cand_bits(e));
     else sdrop += double(__builtin_amdgcn_exp2f((value_of_key<DT>(e.key) - piv) * c32));
   }
   for (int r = n + tid; r < F; r += kThreads) {
     Cand e;
     e.key = 0u;
     e.idx = -1;
-    out[r] = e;
+    dev_store(reinterpret_cast<uint64_t*>(out + r), cand_bits(e));
   }
   const double s_rest = block_sum(double(sn), sm_d) + block_sum(sdrop, sm_d);
   if (tid == 0) {
-    CachePartial p;
-    p.m = mc;
-    p.pad = 0.0f;
-    p.s_rest = s_rest;
-    a.part[rowid * a.S + c] = p;
+    uint64_t* wp = reinterpret_cast<uint64_t*>(a.part + rowid * a.S + c);
+    dev_store(wp, pack2(mc, 0.0f));
+    dev_store(wp + 1, dbits(s_rest));
   }
 
-  if (!arrive_last(&a.cnt[rowid], uint32_t(a.S), &sm_last)) return;
+  if (!arrive_last(&a.cnt[rowid * kCntStride], uint32_t(a.S), &sm_last)) return;
 
   // ---------------- merge: last workgroup of row (b, k) ----------------
-  const CachePartial* pp = a.part + rowid * a.S;
-  float mrow = -__builtin_inff();
-  for (int cc = 0; cc < a.S; ++cc) mrow = fmaxf(mrow, pp[cc].m);
-  const float prow = pivot_of(mrow);
   const double c64 = a.c64;
-  double srest_chunks = 0.0;
-  if (tid == 0) {
-    for (int cc = 0; cc < a.S; ++cc) {
-      const CachePartial q = pp[cc];
-      if (q.s_rest > 0.0) srest_chunks += q.s_rest * exp2((double(pivot_of(q.m)) - double(prow)) * c64);
-    }
-  }
-  const Cand* cl = a.cand + rowid * a.S * SSD_MAX_F;
+  const uint64_t* cl = reinterpret_cast<const uint64_t*>(a.cand + rowid * a.S * SSD_MAX_F);
   const int L = a.S * F;
   const bool staged = L <= kMergeCap;
-  __syncthreads();
-  if (staged) {
-    for (int i = tid; i < L; i += kThreads) s_list[i] = cl[(i / F) * SSD_MAX_F + (i % F)];
-    __syncthreads();
+  if (w == 0) {   // chunk maxima and non-candidate masses, one lane per chunk
+    __shared__ float sm_pv;
+    merge_rows<1>(reinterpret_cast<const uint64_t*>(a.part + rowid * a.S), 1, a.S, c32, &sm_pv,
+                  &sm_srest, &sm_mrow);
   }
+  if (staged) {
+    for (int i = tid; i < L; i += kThreads) s_list[i] = bits_cand(dev_load(cl + (i / F) * SSD_MAX_F + (i % F)));
+  }
+  __syncthreads();
   auto cand_at = [&](int list, int i) -> Cand {
-    return staged ? s_list[list * F + i] : cl[list * SSD_MAX_F + i];
+    return staged ? s_list[list * F + i] : bits_cand(dev_load(cl + list * SSD_MAX_F + i));
   };
+  const float mrow = sm_mrow;
+  const float prow = pivot_of(mrow);
   double s_unsel = 0.0;
   for (int e = tid; e < L; e += kThreads) {
     const int li = e / F, ii = e - li * F;
@@ -222,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void k_cache(CacheArgs a) {
       }
       rank += lo;
     }
-    const double ev = exp2((double(value_of_key<DT>(me.key)) - double(prow)) * c64);
+    const double ev = exp2(double(value_of_key<DT>(me.key) - prow) * double(c32));
     if (rank < F) {
       s_sel[rank] = me;
       s_sel_e[rank] = ev;
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void k_cache(CacheArgs a) {
     double* ds = a.dstats + rowid * 3;
     ds[0] = double(mrow);
     ds[1] = s_top;
-    ds[2] = srest_chunks + unsel;
+    ds[2] = sm_srest + unsel;
   }
 }
 

@@ -69,33 +69,92 @@ struct Strided {
   }
 };
 
+// Unpack one 16-byte vector into floats x[o .. o + kPerVec).
+template <int DT>
+__device__ __forceinline__ void unpack16(const uint4& r, float* x) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if constexpr (DT == 1) {
+      x[2 * q] = __uint_as_float(w[q] << 16);
+      x[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+    } else {
+      x[q] = __uint_as_float(w[q]);
+    }
+  }
+}
+
+// Entry i of a row as float, or -inf past the end. The index is clamped so
+// the load is unconditional (in bounds) and can be batched with the others.
+template <int DT>
+__device__ __forceinline__ float load_elem(const typename Dt<DT>::T* __restrict__ row, int64_t i,
+                                           int64_t V) {
+  const float v = Dt<DT>::to_f(row[i < V ? i : V - 1]);
+  return i < V ? v : -__builtin_inff();
+}
+
+// Load a chunk in the strided layout. `aligned`: the row start is 16-byte
+// aligned, so every vector lying wholly inside the row is one 16-byte load;
+// entries past the row end read as -inf, and a vector straddling the end (V
+// not a multiple of the vector width) or an unaligned row is read per entry.
 template <int DT>
 __device__ __forceinline__ void load_strided(const typename Dt<DT>::T* __restrict__ row, int64_t c0,
-                                             int64_t V, bool vec, int tid, float (&x)[kPerThread]) {
+                                             int64_t V, bool aligned, int tid, float (&x)[kPerThread]) {
   using S = Strided<DT>;
-  if (vec) {
+  constexpr int PV = S::PV;
+  const int64_t rem = V - c0;
+  if (aligned && rem >= kChunk) {
     const uint4* p = reinterpret_cast<const uint4*>(row + c0);
     uint4 raw[S::NV];
 #pragma unroll
     for (int j = 0; j < S::NV; ++j) raw[j] = p[j * kThreads + tid];
+    // keep every load in flight before the first use (the scheduler would
+    // otherwise wait on the first load before issuing the rest)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < S::NV; ++j) unpack16<DT>(raw[j], x + j * PV);
+  } else if (aligned) {
+    const int nvalid = int(rem);   // < kChunk
+    const uint4* p = reinterpret_cast<const uint4*>(row + c0);
+    uint4 raw[S::NV];
 #pragma unroll
     for (int j = 0; j < S::NV; ++j) {
-      const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+      const int loc = (j * kThreads + tid) * PV;
+      raw[j] = (loc + PV <= nvalid) ? p[j * kThreads + tid] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if constexpr (DT == 1) {
-          x[j * 8 + 2 * q] = __uint_as_float(w[q] << 16);
-          x[j * 8 + 2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
-        } else {
-          x[j * 4 + q] = __uint_as_float(w[q]);
+    for (int j = 0; j < S::NV; ++j) unpack16<DT>(raw[j], x + j * PV);
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+      const int loc = ((k / PV) * kThreads + tid) * PV + (k % PV);
+      if (loc >= nvalid) x[k] = -__builtin_inff();
+    }
+    const int gs = nvalid / PV;   // vector straddling the end, if any
+    if ((nvalid % PV) != 0 && (gs % kThreads) == tid) {
+#pragma unroll
+      for (int j = 0; j < S::NV; ++j) {
+        if (j == gs / kThreads) {
+#pragma unroll
+          for (int e = 0; e < PV; ++e)
+            if (gs * PV + e < nvalid) x[j * PV + e] = Dt<DT>::to_f(row[c0 + gs * PV + e]);
         }
       }
     }
   } else {
+    // unaligned row (rare): per-entry loads at 32-bit offsets from the
+    // (uniform) chunk start, one vector's worth at a time to bound registers
+    const typename Dt<DT>::T* base = row + c0;
+    const int lim = rem < kChunk ? int(rem) : kChunk;
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-      const int64_t i = S::index(c0, tid, k);
-      x[k] = (i < V) ? Dt<DT>::to_f(row[i]) : -__builtin_inff();
+    for (int j = 0; j < S::NV; ++j) {
+#pragma unroll
+      for (int e = 0; e < PV; ++e) {
+        const int loc = (j * kThreads + tid) * PV + e;
+        const float v = Dt<DT>::to_f(base[loc < lim ? loc : lim - 1]);
+        x[j * PV + e] = loc < lim ? v : -__builtin_inff();
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -103,31 +162,32 @@ __device__ __forceinline__ void load_strided(const typename Dt<DT>::T* __restric
 // Contiguous layout: thread t holds entries c0 + t*kPerThread + k.
 template <int DT>
 __device__ __forceinline__ void load_run(const typename Dt<DT>::T* __restrict__ row, int64_t c0,
-                                         int64_t V, bool vec, int tid, float (&x)[kPerThread]) {
+                                         int64_t V, bool aligned, int tid, float (&x)[kPerThread]) {
+  constexpr int PV = Dt<DT>::kPerVec;
+  constexpr int NV = kPerThread / PV;
   const int64_t base = c0 + int64_t(tid) * kPerThread;
-  if (vec) {
-    constexpr int PV = Dt<DT>::kPerVec;
-    constexpr int NV = kPerThread / PV;
+  if (aligned && base + kPerThread <= V) {
     const uint4* p = reinterpret_cast<const uint4*>(row + base);
+    uint4 raw[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) raw[j] = p[j];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) unpack16<DT>(raw[j], x + j * PV);
+  } else {
+    const typename Dt<DT>::T* cb = row + c0;
+    const int64_t rem = V - c0;
+    const int lim = rem < kChunk ? int(rem) : kChunk;
+    const int t0 = tid * kPerThread;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const uint4 r = p[j];
-      const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if constexpr (DT == 1) {
-          x[j * 8 + 2 * q] = __uint_as_float(w[q] << 16);
-          x[j * 8 + 2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
-        } else {
-          x[j * 4 + q] = __uint_as_float(w[q]);
-        }
+      for (int e = 0; e < PV; ++e) {
+        const int loc = t0 + j * PV + e;
+        const float v = Dt<DT>::to_f(cb[loc < lim ? loc : lim - 1]);
+        x[j * PV + e] = loc < lim ? v : -__builtin_inff();
       }
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-      const int64_t i = base + k;
-      x[k] = (i < V) ? Dt<DT>::to_f(row[i]) : -__builtin_inff();
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -192,23 +252,107 @@ __device__ __forceinline__ int block_sum_i(int v, int* sm4) {
   return (sm4[0] + sm4[1]) + (sm4[2] + sm4[3]);
 }
 
-// Publish this workgroup's results and count it in; returns true in every
-// thread of the workgroup that arrives last (it then sees all the others'
-// writes). The last arrival also re-arms the counter for the next call.
-// No workgroup ever waits for another, so this cannot deadlock.
+// ---- cross-workgroup exchange inside one kernel ----
+// Workgroups on different XCDs do not share an L2, so partial results that
+// another workgroup of the same launch reads are stored and loaded with
+// device-scope (sc1) accesses, which are coherent across the XCDs' L2s.
+// A device-scope release fence would also work but writes back the whole L2
+// of the XCD on every arrival, which serialises thousands of workgroups.
+__device__ __forceinline__ void dev_store(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t dev_load(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t pack2(float a, float b) {
+  return uint64_t(__float_as_uint(a)) | (uint64_t(__float_as_uint(b)) << 32);
+}
+__device__ __forceinline__ float lo_f(uint64_t w) { return __uint_as_float(uint32_t(w)); }
+__device__ __forceinline__ uint64_t dbits(double v) { return uint64_t(__double_as_longlong(v)); }
+__device__ __forceinline__ double bits_d(uint64_t w) { return __longlong_as_double((long long)w); }
+
+// Weight that moves a sum of exp2((z - pa) * c) onto pivot pb (pa <= pb):
+// 2^((pa - pb) * c), with the same float c as the per-entry exponentials so
+// that the merged sum equals the sum taken with pivot pb directly.
+__device__ __forceinline__ double rescale(float pa, float pb, float c32) {
+  return double(__builtin_amdgcn_exp2f((pa - pb) * c32));
+}
+
+// Merge per-chunk (max, sum of exp2((z - pivot) * c)) partials of NR rows:
+// row r's S partials sit at part + (r * S + chunk) * 2 (two 64-bit words:
+// max in the low half of the first, sum in the second). One wave handles
+// RPW rows at a time with one lane per chunk; a lane folds chunks lane,
+// lane+64, ... in order, then fixed butterflies combine the lanes, so the
+// result is the same on every run. Writes the merged row max (m_out, may be
+// nullptr), its pivot and the sum relative to that pivot.
+template <int RPW>
+__device__ void merge_rows(const uint64_t* part, int NR, int S, float c32, float* piv_out,
+                           double* s_out, float* m_out) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int r0 = w * RPW; r0 < NR; r0 += 4 * RPW) {
+    float ml[RPW];
+    double sl[RPW];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      ml[j] = -__builtin_inff();
+      sl[j] = 0.0;
+    }
+    for (int cc = lane; cc < S; cc += 64) {
+      float qm[RPW];
+      double qs[RPW];
+#pragma unroll
+      for (int j = 0; j < RPW; ++j) {
+        qm[j] = -__builtin_inff();
+        qs[j] = 0.0;
+        if (r0 + j < NR) {
+          const uint64_t* p = part + (int64_t(r0 + j) * S + cc) * 2;
+          qm[j] = lo_f(dev_load(p));
+          qs[j] = bits_d(dev_load(p + 1));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < RPW; ++j) {
+        const float nm = fmaxf(ml[j], qm[j]);
+        const float pn = pivot_of(nm);
+        double acc = 0.0;
+        if (sl[j] > 0.0) acc += sl[j] * rescale(pivot_of(ml[j]), pn, c32);
+        if (qs[j] > 0.0) acc += qs[j] * rescale(pivot_of(qm[j]), pn, c32);
+        ml[j] = nm;
+        sl[j] = acc;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const float m = wave_max(ml[j]);
+      const float pm = pivot_of(m);
+      const double t = sl[j] > 0.0 ? sl[j] * rescale(pivot_of(ml[j]), pm, c32) : 0.0;
+      const double sum = wave_sum(t);
+      if (lane == 0 && r0 + j < NR) {
+        piv_out[r0 + j] = pm;
+        s_out[r0 + j] = sum;
+        if (m_out) m_out[r0 + j] = m;
+      }
+    }
+  }
+}
+
+// Count this workgroup in; returns true in every thread of the workgroup that
+// arrives last, which then reads the others' partials with dev_load. Each
+// thread first waits until its own device-scope stores have completed, so
+// they are visible before the counter moves. The last arrival re-arms the
+// counter for the next launch. No workgroup waits for another, so this
+// cannot deadlock.
 __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, int* sm_flag) {
-  __threadfence();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t prev = atomicAdd(counter, 1u);
+    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = (prev == expected - 1u);
-    if (last) *counter = 0u;
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *sm_flag = last ? 1 : 0;
   }
   __syncthreads();
-  const bool last = *sm_flag != 0;
-  if (last) __threadfence();
-  return last;
+  return *sm_flag != 0;
 }
 
 }  // namespace ssd

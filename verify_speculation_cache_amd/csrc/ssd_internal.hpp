@@ -76,7 +76,7 @@ struct StatsArgs {
   float* probs;
   float* row_lse;
   RowPartial* part;   // [B, NR, S]
-  uint32_t* cnt;      // [B]
+  uint32_t* cnt;      // [B] (kCntStride apart)
   RowInfo* info;      // [B]
 };
 
@@ -90,7 +90,7 @@ struct ResidArgs {
   const float* u;
   const RowInfo* info;
   double* cmass;       // [B, S, 2]: residual mass, target mass per chunk
-  uint32_t* cnt;       // [B]
+  uint32_t* cnt;       // [B] (kCntStride apart)
   int32_t* tok_out;    // token written at tok_out[b * tok_stride + (tok_at_a ? a : 0)]
   int64_t tok_stride;
   int tok_at_a;
@@ -110,7 +110,7 @@ struct CacheArgs {
   double* dstats;
   CachePartial* part;   // [B, K+1, S]
   Cand* cand;           // [B, K+1, S, SSD_MAX_F]
-  uint32_t* cnt;        // [B, K+1]
+  uint32_t* cnt;        // [B, K+1] (kCntStride apart)
 };
 
 struct LookupArgs {
@@ -127,12 +127,17 @@ struct LookupArgs {
 // Workspace layouts (byte offsets, each 256-aligned).
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Completion counters sit kCntStride uint32 apart (4 KiB): device-scope
+// atomics on one cache line serialise, so every counter gets its own line
+// and memory channel.
+constexpr int kCntStride = 1024;
+
 struct StatsWs {
   size_t part, cnt, info, total;
   StatsWs(int64_t B, int64_t NR, int64_t S) {
     part = 0;
     cnt = align256(part + sizeof(RowPartial) * B * NR * S);
-    info = align256(cnt + sizeof(uint32_t) * B);
+    info = align256(cnt + sizeof(uint32_t) * kCntStride * B);
     total = align256(info + sizeof(RowInfo) * B);
   }
 };
@@ -142,7 +147,7 @@ struct ResidWs {
   ResidWs(int64_t B, int64_t S) {
     cmass = 0;
     cnt = align256(cmass + sizeof(double) * 2 * B * S);
-    total = align256(cnt + sizeof(uint32_t) * B);
+    total = align256(cnt + sizeof(uint32_t) * kCntStride * B);
   }
 };
 
@@ -152,7 +157,7 @@ struct CacheWs {
     part = 0;
     cand = align256(part + sizeof(CachePartial) * B * (K + 1) * S);
     cnt = align256(cand + sizeof(Cand) * B * (K + 1) * S * SSD_MAX_F);
-    total = align256(cnt + sizeof(uint32_t) * B * (K + 1));
+    total = align256(cnt + sizeof(uint32_t) * kCntStride * B * (K + 1));
   }
 };
 

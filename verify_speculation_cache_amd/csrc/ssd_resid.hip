@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void k_resid(ResidArgs a) {
   if (inf.a >= 0) {
     const int64_t c0 = int64_t(c) * kChunk;
     const bool full = c0 + kChunk <= a.V;
-    const bool vt = full && ((reinterpret_cast<uintptr_t>(rowT) & 15u) == 0);
+    const bool vt = (reinterpret_cast<uintptr_t>(rowT) & 15u) == 0;
     float xt[kPerThread];
     load_strided<DT>(rowT, c0, a.V, vt, tid, xt);
     float rs = 0.0f, ts = 0.0f;
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void k_resid(ResidArgs a) {
       for (int q = 0; q < kPerThread; ++q) ts += target_elem<DT>(k, xt[q]);
       rs = ts;
     } else {
-      const bool vd = full && ((reinterpret_cast<uintptr_t>(rowD) & 15u) == 0);
+      const bool vd = (reinterpret_cast<uintptr_t>(rowD) & 15u) == 0;
       float xd[kPerThread];
       load_strided<DT>(rowD, c0, a.V, vd, tid, xd);
 #pragma unroll
@@ -124,12 +124,13 @@ __global__ __launch_bounds__(kThreads) void k_resid(ResidArgs a) {
     const double R = block_sum(double(rs), sm_d);
     const double P = block_sum(double(ts), sm_d);
     if (tid == 0) {
-      a.cmass[(int64_t(b) * a.S + c) * 2 + 0] = R;
-      a.cmass[(int64_t(b) * a.S + c) * 2 + 1] = P;
+      uint64_t* w = reinterpret_cast<uint64_t*>(a.cmass + (int64_t(b) * a.S + c) * 2);
+      dev_store(w, dbits(R));
+      dev_store(w + 1, dbits(P));
     }
   }
 
-  if (!arrive_last(&a.cnt[b], uint32_t(a.S), &sm_last)) return;
+  if (!arrive_last(&a.cnt[int64_t(b) * kCntStride], uint32_t(a.S), &sm_last)) return;
 
   // ---------------- phase B: last workgroup of batch row b ----------------
   if (inf.a < 0) {
@@ -139,48 +140,59 @@ __global__ __launch_bounds__(kThreads) void k_resid(ResidArgs a) {
     }
     return;
   }
-  if (tid == 0) {
-    const double* cm = a.cmass + int64_t(b) * a.S * 2;
-    double z = 0.0;
-    for (int cc = 0; cc < a.S; ++cc) z += cm[cc * 2 + 0];
-    int useres = 1;
-    double tot = z;
-    if (!(z > 0.0)) {
-      useres = 0;
-      tot = 0.0;
-      for (int cc = 0; cc < a.S; ++cc) tot += cm[cc * 2 + 1];
+  // chunk masses in parallel (one lane per chunk), prefix sums by a fixed
+  // wave scan, then the first chunk whose running mass exceeds u * Z.
+  if (tid < 64) {
+    const int lane = tid;
+    const uint64_t* cmw = reinterpret_cast<const uint64_t*>(a.cmass + int64_t(b) * a.S * 2);
+    double zres = 0.0, ztgt = 0.0;   // running totals over chunk groups
+    for (int g = 0; g < a.S; g += 64) {
+      const int cc = g + lane;
+      const double r = cc < a.S ? bits_d(dev_load(cmw + cc * 2)) : 0.0;
+      const double t = cc < a.S ? bits_d(dev_load(cmw + cc * 2 + 1)) : 0.0;
+      zres += __shfl(wave_incl_scan_d(r, lane), 63);
+      ztgt += __shfl(wave_incl_scan_d(t, lane), 63);
     }
+    const int useres = zres > 0.0 ? 1 : 0;
+    const double tot = useres ? zres : ztgt;
+    const double target = double(a.u[b]) * tot;
     int cs = -1;
     double pre = 0.0;
-    const double target = double(a.u[b]) * tot;
     if (tot > 0.0) {
-      double run = 0.0;
+      double base = 0.0;
       int lastpos = -1;
       double lastpre = 0.0;
-      for (int cc = 0; cc < a.S; ++cc) {
-        const double mc = cm[cc * 2 + (useres ? 0 : 1)];
-        const double nxt = run + mc;
-        if (mc > 0.0) {
-          lastpos = cc;
-          lastpre = run;
+      for (int g = 0; g < a.S && cs < 0; g += 64) {
+        const int cc = g + lane;
+        const double mc = cc < a.S ? bits_d(dev_load(cmw + cc * 2 + (useres ? 0 : 1))) : 0.0;
+        const double incl = wave_incl_scan_d(mc, lane);
+        const double prev = __shfl_up(incl, 1);   // all lanes shuffle (lane 0 reads itself)
+        const double excl = base + (lane > 0 ? prev : 0.0);
+        const uint64_t crossing = __ballot(cc < a.S && base + incl > target);
+        const uint64_t pos = __ballot(cc < a.S && mc > 0.0);
+        if (crossing) {
+          const int l = __ffsll((unsigned long long)crossing) - 1;
+          cs = g + l;
+          pre = __shfl(excl, l);
+        } else if (pos) {
+          const int l = 63 - __clzll((long long)pos);
+          lastpos = g + l;
+          lastpre = __shfl(excl, l);
         }
-        if (nxt > target) {
-          cs = cc;
-          pre = run;
-          break;
-        }
-        run = nxt;
+        base += __shfl(incl, 63);
       }
-      if (cs < 0) {
+      if (cs < 0) {   // rounding left u*Z past the last crossing: last chunk with mass
         cs = lastpos;
         pre = lastpre;
       }
     }
-    sm_c = cs;
-    sm_pre = pre;
-    sm_target = target;
-    sm_useres = useres;
-    if (a.mass_out) a.mass_out[b] = useres ? float(z / inf.s_t) : 0.0f;
+    if (lane == 0) {
+      sm_c = cs;
+      sm_pre = pre;
+      sm_target = target;
+      sm_useres = useres;
+      if (a.mass_out) a.mass_out[b] = useres ? float(zres / inf.s_t) : 0.0f;
+    }
   }
   __syncthreads();
   const int cs = sm_c;
@@ -190,9 +202,9 @@ __global__ __launch_bounds__(kThreads) void k_resid(ResidArgs a) {
     const bool full = c0 + kChunk <= a.V;
     const bool useres = sm_useres != 0 && !inf.bonus;
     float xt[kPerThread], xd[kPerThread];
-    load_run<DT>(rowT, c0, a.V, full && ((reinterpret_cast<uintptr_t>(rowT) & 15u) == 0), tid, xt);
+    load_run<DT>(rowT, c0, a.V, (reinterpret_cast<uintptr_t>(rowT) & 15u) == 0, tid, xt);
     if (useres)
-      load_run<DT>(rowD, c0, a.V, full && ((reinterpret_cast<uintptr_t>(rowD) & 15u) == 0), tid, xd);
+      load_run<DT>(rowD, c0, a.V, (reinterpret_cast<uintptr_t>(rowD) & 15u) == 0, tid, xd);
     const int64_t base_idx = c0 + int64_t(tid) * kPerThread;
     float v[kPerThread];
 #pragma unroll

@@ -65,8 +65,7 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsArgs a) {
   const typename Dt<DT>::T* row = stats_row_ptr<DT>(a, b, r);
   if (row != nullptr) {  // uniform per workgroup
     const int64_t c0 = int64_t(c) * kChunk;
-    const bool vec = a.S > 0 && (c0 + kChunk <= a.V) &&
-                     ((reinterpret_cast<uintptr_t>(row) & 15u) == 0);
+    const bool vec = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
     float x[kPerThread];
     load_strided<DT>(row, c0, a.V, vec, tid, x);
     float m = x[0];
@@ -79,30 +78,17 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsArgs a) {
     for (int k = 0; k < kPerThread; ++k) s += __builtin_amdgcn_exp2f((x[k] - piv) * a.c32);
     const double sd = block_sum(double(s), sm_d);
     if (tid == 0) {
-      RowPartial p;
-      p.m = m;
-      p.pad = 0.0f;
-      p.s = sd;
-      a.part[(int64_t(b) * a.NR + r) * a.S + c] = p;
+      uint64_t* w = reinterpret_cast<uint64_t*>(a.part + (int64_t(b) * a.NR + r) * a.S + c);
+      dev_store(w, pack2(m, 0.0f));
+      dev_store(w + 1, dbits(sd));
     }
   }
 
-  if (!arrive_last(&a.cnt[b], uint32_t(per_b), &sm_last)) return;
+  if (!arrive_last(&a.cnt[int64_t(b) * kCntStride], uint32_t(per_b), &sm_last)) return;
 
   // ---------------- epilogue: last workgroup of batch row b ----------------
-  for (int rr = tid; rr < a.NR; rr += kThreads) {
-    const RowPartial* pp = a.part + (int64_t(b) * a.NR + rr) * a.S;
-    float mm = -__builtin_inff();
-    for (int cc = 0; cc < a.S; ++cc) mm = fmaxf(mm, pp[cc].m);
-    const float pv = pivot_of(mm);
-    double ss = 0.0;
-    for (int cc = 0; cc < a.S; ++cc) {
-      const RowPartial q = pp[cc];
-      if (q.s > 0.0) ss += q.s * exp2((double(pivot_of(q.m)) - double(pv)) * a.c64);
-    }
-    e_piv[rr] = pv;
-    e_s[rr] = ss;
-  }
+  merge_rows<2>(reinterpret_cast<const uint64_t*>(a.part) + int64_t(b) * a.NR * a.S * 2, a.NR, a.S,
+                a.c32, e_piv, e_s, nullptr);
   __syncthreads();
 
   const int K = a.K;
@@ -153,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsArgs a) {
         const float zt = load_one<DT>(a.target, int64_t(b) * a.tb + int64_t(i) * a.V + d);
         const float zd = load_one<DT>(a.draft, int64_t(b) * a.db + int64_t(i) * a.V + d);
         const double st = e_s[i];
-        pd = st > 0.0 ? exp2((double(zt) - double(e_piv[i])) * a.c64) / st : 0.0;
+        pd = st > 0.0 ? exp2(double(zt - e_piv[i]) * double(a.c32)) / st : 0.0;
         double pivd, sdn, w = 1.0;
         if (a.use_sigma) {
           const double* sp = a.dstats + (int64_t(b) * (K + 1) + i) * 3;
@@ -165,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsArgs a) {
           pivd = double(e_piv[K + 1 + i]);
           sdn = e_s[K + 1 + i];
         }
-        qd = sdn > 0.0 ? w * exp2((double(zd) - pivd) * a.c64) / sdn : 0.0;
+        qd = sdn > 0.0 ? w * exp2(double(zd - float(pivd)) * double(a.c32)) / sdn : 0.0;
         acc = double(a.u_acc[int64_t(b) * K + i]) * qd < pd;
       }
     }
