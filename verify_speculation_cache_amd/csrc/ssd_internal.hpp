@@ -41,11 +41,14 @@ struct alignas(16) RowInfo {
   int32_t pad;
 };
 
-struct alignas(16) CachePartial {
-  float m;
-  float pad;
-  double s_rest;   // sum over the chunk's tokens that are not its top-F candidates
+// Per-(row, chunk) record of the cache build, four 64-bit words:
+//  [0] chunk max (low 32 bits, float) | chunk threshold key T0 (high 32 bits)
+//  [1] sum of exp2((z - max) * c) over the chunk entries that are not candidates
+//  [2] number of candidates written for the chunk
+struct alignas(32) CachePartial {
+  uint64_t w[4];
 };
+constexpr int kCandCap = 128;   // candidate slots per (row, chunk)
 
 struct Cand {
   uint32_t key;
@@ -109,7 +112,7 @@ struct CacheArgs {
   ssd_rowkey* thr;
   double* dstats;
   CachePartial* part;   // [B, K+1, S]
-  Cand* cand;           // [B, K+1, S, SSD_MAX_F]
+  Cand* cand;           // [B, K+1, S, kCandCap]
   uint32_t* cnt;        // [B, K+1] (kCntStride apart)
 };
 
@@ -156,7 +159,7 @@ struct CacheWs {
   CacheWs(int64_t B, int64_t K, int64_t S) {
     part = 0;
     cand = align256(part + sizeof(CachePartial) * B * (K + 1) * S);
-    cnt = align256(cand + sizeof(Cand) * B * (K + 1) * S * SSD_MAX_F);
+    cnt = align256(cand + sizeof(Cand) * B * (K + 1) * S * kCandCap);
     total = align256(cnt + sizeof(uint32_t) * kCntStride * B * (K + 1));
   }
 };
