@@ -159,6 +159,139 @@ __device__ __forceinline__ void load_strided(const typename Dt<DT>::T* __restric
   }
 }
 
+// Raw dtype bits of one entry (bf16: the 16 stored bits).
+template <int DT> __device__ __forceinline__ uint32_t raw_bits(typename Dt<DT>::T v);
+template <> __device__ __forceinline__ uint32_t raw_bits<0>(float v) { return __float_as_uint(v); }
+template <> __device__ __forceinline__ uint32_t raw_bits<1>(uint16_t v) { return uint32_t(v); }
+// -inf as a packed 32-bit word of the dtype
+template <int DT> __device__ __forceinline__ constexpr uint32_t neg_inf_word() {
+  return DT == 1 ? 0xFF80FF80u : 0xFF800000u;
+}
+
+// One 16-byte vector built from per-entry reads of base[loc0 .. loc0+PV);
+// entries at or past `lim` read as -inf. Indices are clamped so every read
+// is unconditional and in bounds (lim >= 1).
+template <int DT>
+__device__ __forceinline__ uint4 gather_vec(const typename Dt<DT>::T* __restrict__ base, int loc0, int lim) {
+  constexpr uint32_t kNeg = DT == 1 ? 0xFF80u : 0xFF800000u;
+  uint32_t e[Dt<DT>::kPerVec];
+#pragma unroll
+  for (int q = 0; q < Dt<DT>::kPerVec; ++q) {
+    const int l = loc0 + q;
+    const uint32_t v = raw_bits<DT>(base[uint32_t(l < lim ? l : lim - 1)]);
+    e[q] = l < lim ? v : kNeg;
+  }
+  if constexpr (DT == 1)
+    return make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
+  else
+    return make_uint4(e[0], e[1], e[2], e[3]);
+}
+
+// A chunk held as raw 16-byte vectors, so callers need not keep 32 floats
+// per row live. STRIDED: vector j of thread t covers chunk entries
+// (j*256 + t)*PV .. +PV (each wave load is one contiguous 1 KiB span);
+// contiguous: entries t*32 + j*PV .. +PV. Entries past the row end read as
+// -inf. Whole vectors of a 16-byte aligned row are single loads, all issued
+// before the first use; a vector straddling the row end, or any vector of
+// an unaligned row, is read per entry.
+template <int DT, bool STRIDED>
+struct ChunkVecs {
+  static constexpr int PV = Dt<DT>::kPerVec;
+  static constexpr int NV = kPerThread / PV;
+  uint4 raw[NV];
+
+  __device__ static int local(int tid, int j) {
+    return STRIDED ? (j * kThreads + tid) * PV : tid * kPerThread + j * PV;
+  }
+  __device__ static int64_t first(int64_t c0, int tid, int j) { return c0 + local(tid, j); }
+
+  __device__ void issue_full(const typename Dt<DT>::T* __restrict__ row, int64_t c0, int tid) {
+    const typename Dt<DT>::T* base = row + c0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) raw[j] = *reinterpret_cast<const uint4*>(base + uint32_t(local(tid, j)));
+  }
+  __device__ void load(const typename Dt<DT>::T* __restrict__ row, int64_t c0, int64_t V, bool aligned, int tid) {
+    if (aligned && V - c0 >= kChunk) {
+      issue_full(row, c0, tid);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      load_partial(row, c0, V, aligned, tid);
+    }
+  }
+  // Tail chunk of an aligned row: whole vectors inside the row are single
+  // loads (masked per lane), vectors wholly past the end read -inf; the one
+  // vector straddling the end is filled in by patch_tail.
+  __device__ void issue_tail(const typename Dt<DT>::T* __restrict__ row, int64_t c0, int lim, int tid) {
+    const typename Dt<DT>::T* base = row + c0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int l = local(tid, j);
+      raw[j].x = raw[j].y = raw[j].z = raw[j].w = neg_inf_word<DT>();
+      if (l + PV <= lim) raw[j] = *reinterpret_cast<const uint4*>(base + uint32_t(l));
+    }
+  }
+  __device__ void patch_tail(const typename Dt<DT>::T* __restrict__ row, int64_t c0, int lim, int tid) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int l = local(tid, j);
+      if (l < lim && l + PV > lim) raw[j] = gather_vec<DT>(row + c0, l, lim);
+    }
+  }
+  // unaligned row: per-entry reads, one vector at a time (rare path)
+  __device__ void gather_all(const typename Dt<DT>::T* __restrict__ row, int64_t c0, int lim, int tid) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      raw[j] = gather_vec<DT>(row + c0, local(tid, j), lim);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // tail chunk (entries past V read -inf) or unaligned row
+  __device__ void load_partial(const typename Dt<DT>::T* __restrict__ row, int64_t c0, int64_t V, bool aligned,
+                               int tid) {
+    const int64_t rem = V - c0;
+    const int lim = rem < kChunk ? int(rem) : kChunk;
+    if (aligned) {
+      issue_tail(row, c0, lim, tid);
+      __builtin_amdgcn_sched_barrier(0);
+      patch_tail(row, c0, lim, tid);
+    } else {
+      gather_all(row, c0, lim, tid);
+    }
+  }
+  __device__ void get(int j, float (&v)[PV]) const { unpack16<DT>(raw[j], v); }
+  // Make the held vectors opaque to the optimiser, so values derived from
+  // them are recomputed afterwards instead of being kept live in registers.
+  __device__ void opaque() {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) asm volatile("" : "+v"(raw[j].x), "+v"(raw[j].y), "+v"(raw[j].z), "+v"(raw[j].w));
+  }
+};
+
+// The same chunk of two rows, with all loads of both in flight together
+// when both rows are 16-byte aligned and the chunk is full.
+template <int DT, bool STRIDED>
+__device__ __forceinline__ void load_pair(ChunkVecs<DT, STRIDED>& x, const typename Dt<DT>::T* __restrict__ rx,
+                                          ChunkVecs<DT, STRIDED>& y, const typename Dt<DT>::T* __restrict__ ry,
+                                          int64_t c0, int64_t V, int tid) {
+  const bool ax = (reinterpret_cast<uintptr_t>(rx) & 15u) == 0;
+  const bool ay = (reinterpret_cast<uintptr_t>(ry) & 15u) == 0;
+  if (ax && ay && V - c0 >= kChunk) {
+    x.issue_full(rx, c0, tid);
+    y.issue_full(ry, c0, tid);
+    __builtin_amdgcn_sched_barrier(0);
+  } else if (ax && ay) {
+    const int lim = int(V - c0);
+    x.issue_tail(rx, c0, lim, tid);
+    y.issue_tail(ry, c0, lim, tid);
+    __builtin_amdgcn_sched_barrier(0);
+    x.patch_tail(rx, c0, lim, tid);
+    y.patch_tail(ry, c0, lim, tid);
+  } else {
+    x.load_partial(rx, c0, V, ax, tid);
+    y.load_partial(ry, c0, V, ay, tid);
+  }
+}
+
 // Contiguous layout: thread t holds entries c0 + t*kPerThread + k.
 template <int DT>
 __device__ __forceinline__ void load_run(const typename Dt<DT>::T* __restrict__ row, int64_t c0,

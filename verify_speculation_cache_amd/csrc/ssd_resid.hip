@@ -28,9 +28,9 @@ namespace ssd {
 struct ResidConsts {
   float piv_t, piv_d, c32;
   float rho_hi, rho_lo, rhoC_hi, rhoC_lo;
-  uint32_t thr_key;
+  float thr_val;     // sigma threshold as a logit value (key order = value order)
   int32_t thr_idx;
-  int bonus;
+  bool plain;        // value is e_t itself (bonus draw, or no residual mass)
 };
 
 __device__ __forceinline__ void split2(double v, float& hi, float& lo) {
@@ -38,23 +38,26 @@ __device__ __forceinline__ void split2(double v, float& hi, float& lo) {
   lo = float(v - double(hi));
 }
 
-template <int DT, bool SIG>
-__device__ __forceinline__ float resid_elem(const ResidConsts& k, float xt, float xd, int64_t idx) {
+// Residual (or, when plain, target) mass of one entry in target units.
+// Sigma membership "key > thr, or key == thr and index <= thr_idx" is taken
+// on values: for non-NaN logits the order of keys is the order of values,
+// with -0 and +0 equal in both.
+template <bool SIG>
+__device__ __forceinline__ float resid_elem(const ResidConsts& k, float xt, float xd, int idx) {
   const float et = __builtin_amdgcn_exp2f((xt - k.piv_t) * k.c32);
   const float ed = __builtin_amdgcn_exp2f((xd - k.piv_d) * k.c32);
   float hi = k.rho_hi, lo = k.rho_lo;
   if constexpr (SIG) {
-    const uint32_t kk = key_of<DT>(xd);
-    const bool mem = (kk > k.thr_key) || (kk == k.thr_key && idx <= int64_t(k.thr_idx));
+    // bitwise, not short-circuit: keeps the test branch-free
+    const bool mem = (xd > k.thr_val) | ((xd == k.thr_val) & (idx <= k.thr_idx));
     hi = mem ? k.rhoC_hi : hi;
     lo = mem ? k.rhoC_lo : lo;
   }
   float r = __builtin_fmaf(-hi, ed, et);
   r = __builtin_fmaf(-lo, ed, r);
-  return fmaxf(r, 0.0f);
+  return k.plain ? et : fmaxf(r, 0.0f);
 }
 
-template <int DT>
 __device__ __forceinline__ float target_elem(const ResidConsts& k, float xt) {
   return __builtin_amdgcn_exp2f((xt - k.piv_t) * k.c32);
 }
@@ -62,15 +65,19 @@ __device__ __forceinline__ float target_elem(const ResidConsts& k, float xt) {
 template <int DT, bool SIG>
 __global__ __launch_bounds__(kThreads) void k_resid(ResidArgs a) {
   using T = typename Dt<DT>::T;
-  __shared__ double sm_d[4];
+  constexpr int PV = Dt<DT>::kPerVec;
+  constexpr int NV = kPerThread / PV;
+  __shared__ double sm_pair[8];
   __shared__ int sm_i[4];
   __shared__ int sm_last;
   __shared__ double sm_scan[4];
   __shared__ int sm_pick[4];
   __shared__ double sm_pre, sm_target;
-  __shared__ int sm_c, sm_useres, sm_tok;
+  __shared__ int sm_c, sm_useres, sm_tok, sm_lastpos;
+  __shared__ uint4 sm_run[2][NV];   // the crossing thread's 32 target / draft entries
+  __shared__ double sm_base;
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = blockIdx.x / a.S;
   const int c = blockIdx.x - b * a.S;
   RowInfo inf = a.info[b];
@@ -80,53 +87,62 @@ __global__ __launch_bounds__(kThreads) void k_resid(ResidArgs a) {
   if (inf.a < -1 || inf.a > a.K) inf.a = -1;
   if (inf.a == a.K || a.draft == nullptr) inf.bonus = 1;
 
+  // A bonus row has no draft: it reads the target row twice with rho = 0,
+  // so both rows take the same load and arithmetic path.
   ResidConsts k{};
   const T* rowT = nullptr;
   const T* rowD = nullptr;
   if (inf.a >= 0) {
     rowT = static_cast<const T*>(a.target) + int64_t(b) * a.tb + int64_t(inf.a) * a.V;
     k.piv_t = inf.piv_t;
-    k.piv_d = inf.piv_d;
     k.c32 = a.c32;
-    k.bonus = inf.bonus;
-    k.thr_key = inf.thr_key;
+    k.thr_val = value_of_key<DT>(inf.thr_key);
     k.thr_idx = inf.thr_idx;
-    if (!inf.bonus) {
+    if (inf.bonus) {
+      rowD = rowT;
+      k.piv_d = inf.piv_t;
+      k.plain = true;
+    } else {
       rowD = static_cast<const T*>(a.draft) + int64_t(b) * a.db + int64_t(inf.a) * a.V;
+      k.piv_d = inf.piv_d;
       const double rho = inf.s_d > 0.0 ? inf.s_t / inf.s_d : 0.0;
       split2(rho, k.rho_hi, k.rho_lo);
       split2(rho * double(inf.C), k.rhoC_hi, k.rhoC_lo);
     }
   }
+  // sigma thresholds that admit no entry (key above that of +inf)
+  if (SIG && inf.thr_key > key_of<DT>(__builtin_inff())) k.thr_val = __builtin_nanf("");
 
   // ---------------- phase A: chunk masses ----------------
   if (inf.a >= 0) {
     const int64_t c0 = int64_t(c) * kChunk;
-    const bool full = c0 + kChunk <= a.V;
-    const bool vt = (reinterpret_cast<uintptr_t>(rowT) & 15u) == 0;
-    float xt[kPerThread];
-    load_strided<DT>(rowT, c0, a.V, vt, tid, xt);
+    ChunkVecs<DT, true> vt, vd;
+    load_pair(vt, rowT, vd, rowD, c0, a.V, tid);
     float rs = 0.0f, ts = 0.0f;
-    if (inf.bonus) {
 #pragma unroll
-      for (int q = 0; q < kPerThread; ++q) ts += target_elem<DT>(k, xt[q]);
-      rs = ts;
-    } else {
-      const bool vd = (reinterpret_cast<uintptr_t>(rowD) & 15u) == 0;
-      float xd[kPerThread];
-      load_strided<DT>(rowD, c0, a.V, vd, tid, xd);
+    for (int j = 0; j < NV; ++j) {
+      float xt[PV], xd[PV];
+      vt.get(j, xt);
+      vd.get(j, xd);
+      const int i0 = int(c0) + ChunkVecs<DT, true>::local(tid, j);
 #pragma unroll
-      for (int q = 0; q < kPerThread; ++q) {
-        ts += target_elem<DT>(k, xt[q]);
-        rs += resid_elem<DT, SIG>(k, xt[q], xd[q], Strided<DT>::index(c0, tid, q));
+      for (int e = 0; e < PV; ++e) {
+        ts += target_elem(k, xt[e]);
+        rs += resid_elem<SIG>(k, xt[e], xd[e], i0 + e);
       }
     }
-    const double R = block_sum(double(rs), sm_d);
-    const double P = block_sum(double(ts), sm_d);
+    // both sums across the workgroup with one barrier
+    const double R = wave_sum(double(rs));
+    const double P = wave_sum(double(ts));
+    if (lane == 0) {
+      sm_pair[w] = R;
+      sm_pair[4 + w] = P;
+    }
+    __syncthreads();
     if (tid == 0) {
-      uint64_t* w = reinterpret_cast<uint64_t*>(a.cmass + (int64_t(b) * a.S + c) * 2);
-      dev_store(w, dbits(R));
-      dev_store(w + 1, dbits(P));
+      uint64_t* wp = reinterpret_cast<uint64_t*>(a.cmass + (int64_t(b) * a.S + c) * 2);
+      dev_store(wp, dbits((sm_pair[0] + sm_pair[1]) + (sm_pair[2] + sm_pair[3])));
+      dev_store(wp + 1, dbits((sm_pair[4] + sm_pair[5]) + (sm_pair[6] + sm_pair[7])));
     }
   }
 
@@ -140,16 +156,21 @@ __global__ __launch_bounds__(kThreads) void k_resid(ResidArgs a) {
     }
     return;
   }
-  // chunk masses in parallel (one lane per chunk), prefix sums by a fixed
-  // wave scan, then the first chunk whose running mass exceeds u * Z.
-  if (tid < 64) {
-    const int lane = tid;
+  // chunk masses (one lane per chunk, one round trip for S <= 64), prefix
+  // sums by a fixed wave scan, then the first chunk whose running mass
+  // exceeds u * Z
+  if (w == 0) {
     const uint64_t* cmw = reinterpret_cast<const uint64_t*>(a.cmass + int64_t(b) * a.S * 2);
-    double zres = 0.0, ztgt = 0.0;   // running totals over chunk groups
+    double zres = 0.0, ztgt = 0.0;   // totals over chunk groups
+    double r0 = 0.0, t0 = 0.0;        // this lane's masses in the first group
     for (int g = 0; g < a.S; g += 64) {
       const int cc = g + lane;
       const double r = cc < a.S ? bits_d(dev_load(cmw + cc * 2)) : 0.0;
       const double t = cc < a.S ? bits_d(dev_load(cmw + cc * 2 + 1)) : 0.0;
+      if (g == 0) {
+        r0 = r;
+        t0 = t;
+      }
       zres += __shfl(wave_incl_scan_d(r, lane), 63);
       ztgt += __shfl(wave_incl_scan_d(t, lane), 63);
     }
@@ -164,7 +185,9 @@ __global__ __launch_bounds__(kThreads) void k_resid(ResidArgs a) {
       double lastpre = 0.0;
       for (int g = 0; g < a.S && cs < 0; g += 64) {
         const int cc = g + lane;
-        const double mc = cc < a.S ? bits_d(dev_load(cmw + cc * 2 + (useres ? 0 : 1))) : 0.0;
+        double mc;
+        if (g == 0) mc = useres ? r0 : t0;
+        else mc = cc < a.S ? bits_d(dev_load(cmw + cc * 2 + (useres ? 0 : 1))) : 0.0;
         const double incl = wave_incl_scan_d(mc, lane);
         const double prev = __shfl_up(incl, 1);   // all lanes shuffle (lane 0 reads itself)
         const double excl = base + (lane > 0 ? prev : 0.0);
@@ -198,59 +221,67 @@ __global__ __launch_bounds__(kThreads) void k_resid(ResidArgs a) {
   const int cs = sm_c;
   int tok = -1;
   if (cs >= 0) {
+    if (!sm_useres) k.plain = true;
     const int64_t c0 = int64_t(cs) * kChunk;
-    const bool full = c0 + kChunk <= a.V;
-    const bool useres = sm_useres != 0 && !inf.bonus;
-    float xt[kPerThread], xd[kPerThread];
-    load_run<DT>(rowT, c0, a.V, (reinterpret_cast<uintptr_t>(rowT) & 15u) == 0, tid, xt);
-    if (useres)
-      load_run<DT>(rowD, c0, a.V, (reinterpret_cast<uintptr_t>(rowD) & 15u) == 0, tid, xd);
-    const int64_t base_idx = c0 + int64_t(tid) * kPerThread;
-    float v[kPerThread];
-#pragma unroll
-    for (int q = 0; q < kPerThread; ++q)
-      v[q] = useres ? resid_elem<DT, SIG>(k, xt[q], xd[q], base_idx + q) : target_elem<DT>(k, xt[q]);
+    // each thread owns 32 consecutive tokens of the chunk
+    ChunkVecs<DT, false> vt, vd;
+    load_pair(vt, rowT, vd, rowD, c0, a.V, tid);
+    const int i0 = int(c0) + tid * kPerThread;
     double tot = 0.0;
     int lastpos = -1;
 #pragma unroll
-    for (int q = 0; q < kPerThread; ++q) {
-      tot += double(v[q]);
-      if (v[q] > 0.0f) lastpos = q;
+    for (int j = 0; j < NV; ++j) {
+      float xt[PV], xd[PV];
+      vt.get(j, xt);
+      vd.get(j, xd);
+#pragma unroll
+      for (int e = 0; e < PV; ++e) {
+        const float v = resid_elem<SIG>(k, xt[e], xd[e], i0 + j * PV + e);
+        tot += double(v);
+        if (v > 0.0f) lastpos = j * PV + e;
+      }
     }
     // exclusive scan of thread totals (thread order = token order)
-    const int lane = tid & 63, w = tid >> 6;
     const double incl_w = wave_incl_scan_d(tot, lane);
     if (lane == 63) sm_scan[w] = incl_w;
     __syncthreads();
     double wbase = 0.0;
     for (int ww = 0; ww < w; ++ww) wbase += sm_scan[ww];
-    const double excl = wbase + (incl_w - tot);
-    const double base = sm_pre + excl;
+    const double base = sm_pre + wbase + (incl_w - tot);
     const double target = sm_target;
-    const bool cross = (base + tot) > target;
-    // first crossing thread
-    const uint64_t cm = __ballot(cross);
+    // first thread whose running mass crosses u * Z
+    const uint64_t cm = __ballot((base + tot) > target);
     if (lane == 0) sm_pick[w] = cm ? (w * 64 + __ffsll((unsigned long long)cm) - 1) : 0x7FFFFFFF;
     __syncthreads();
     const int first = min(min(sm_pick[0], sm_pick[1]), min(sm_pick[2], sm_pick[3]));
-    __syncthreads();
     if (first != 0x7FFFFFFF) {
+      // the crossing thread hands its run to wave 0 (one entry per lane),
+      // which rescans it in parallel from the thread's base
       if (tid == first) {
-        double run = 0.0;   // same association as `tot`, so q = 31 reproduces `cross`
-        int pick = lastpos;
-        for (int q = 0; q < kPerThread; ++q) {
-          run += double(v[q]);
-          if (base + run > target) {
-            pick = q;
-            break;
-          }
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+          sm_run[0][q] = vt.raw[q];
+          sm_run[1][q] = vd.raw[q];
         }
-        sm_tok = int(base_idx + pick);
+        sm_base = base;
+        sm_lastpos = lastpos;
+      }
+      __syncthreads();
+      if (w == 0) {
+        const int q = lane & 31;
+        const T* rt = reinterpret_cast<const T*>(&sm_run[0][0]);
+        const T* rd = reinterpret_cast<const T*>(&sm_run[1][0]);
+        const int f0 = int(c0) + first * kPerThread;
+        const float v = resid_elem<SIG>(k, Dt<DT>::to_f(rt[q]), Dt<DT>::to_f(rd[q]), f0 + q);
+        const double cum = sm_base + wave_incl_scan_d(lane < 32 ? double(v) : 0.0, lane);
+        const uint64_t cr = __ballot(lane < 32 && cum > target);
+        // if rounding keeps the rescan at or below u * Z through the run, the
+        // crossing is at the run's end: its last token with mass
+        if (lane == 0) sm_tok = f0 + (cr ? __ffsll((unsigned long long)cr) - 1 : sm_lastpos);
       }
     } else {
       // rounding left u*Z past this chunk's scan: last token with mass
-      const int cand = lastpos >= 0 ? int(base_idx + lastpos) : -1;
-      int best = cand;
+      int best = lastpos >= 0 ? i0 + lastpos : -1;
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) best = max(best, __shfl_xor(best, o));
       if (lane == 0) sm_i[w] = best;
