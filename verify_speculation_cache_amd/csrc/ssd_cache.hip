@@ -461,14 +461,60 @@ __global__ __launch_bounds__(kThreads) void k_cache_merge(CacheArgs a) {
   }
 }
 
+// Candidate test, count and non-candidate exp-mass of one thread's entries.
+// Entries past the row end read as -inf: they add no mass, and they can only
+// pass the candidate test when f0 = -inf, a case the caller handles apart.
+template <int DT>
+__device__ __forceinline__ void chunk_pass(const float (&x)[kPerThread], float f0, float piv, float c32, int& cnt,
+                                           float& sn) {
+  constexpr int PV = Dt<DT>::kPerVec;
+  cnt = 0;
+  sn = 0.0f;
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const bool cand = x[q] >= f0;
+    const float e = __builtin_amdgcn_exp2f((x[q] - piv) * c32);
+    cnt += cand ? 1 : 0;
+    sn += cand ? 0.0f : e;
+    // a vector at a time: keeps the exp temporaries short-lived
+    if (q % PV == PV - 1) __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Writes this thread's candidates (entries >= f0 inside the row) from
+// position pos on. Only vectors whose maximum reaches f0 are visited.
+template <int DT>
+__device__ __forceinline__ void chunk_store(const float (&x)[kPerThread], const float (&vm)[kPerThread / Dt<DT>::kPerVec],
+                                            float f0, int tid, int nvalid, int c0, uint64_t* out, int pos) {
+  constexpr int PV = Dt<DT>::kPerVec;
+  constexpr int NV = kPerThread / PV;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    if (vm[j] >= f0) {   // rare: the vector holds a candidate
+#pragma unroll
+      for (int e = 0; e < PV; ++e) {
+        const int q = j * PV + e;
+        const int loc = local_of<DT>(tid, q);
+        if ((x[q] >= f0) & (loc < nvalid)) {
+          out[uint32_t(pos)] = cand_bits(key_of<DT>(x[q]), c0 + loc);
+          ++pos;
+        }
+      }
+    }
+    // one vector at a time keeps the key/address temporaries short-lived
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_cache_chunk(CacheArgs a) {
   using T = typename Dt<DT>::T;
+  constexpr int PV = Dt<DT>::kPerVec;
+  constexpr int NV = kPerThread / PV;
   __shared__ float sm_wmax[4];
   __shared__ uint32_t sm_wthr[4];
   __shared__ int sm_wcnt[4];
-  __shared__ double sm_d[4];
-  __shared__ int sm_i[4];
+  __shared__ double sm_ws[4];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int KP = a.K + 1;
@@ -485,15 +531,31 @@ __global__ __launch_bounds__(kThreads) void k_cache_chunk(CacheArgs a) {
   const int nvalid = int(min(int64_t(kChunk), int64_t(a.V) - c0));
   const bool full = nvalid == kChunk;
   float x[kPerThread];
-  load_strided<DT>(row, c0, a.V, (reinterpret_cast<uintptr_t>(row) & 15u) == 0, tid, x);
-  float lm = x[0];
+  float vm[NV];   // per-vector maxima (padding is -inf)
+  {
+    ChunkVecs<DT, true> cv;
+    cv.load(row, c0, a.V, (reinterpret_cast<uintptr_t>(row) & 15u) == 0, tid);
 #pragma unroll
-  for (int q = 1; q < kPerThread; ++q) lm = fmaxf(lm, x[q]);
+    for (int j = 0; j < NV; ++j) {
+      float v[PV];
+      cv.get(j, v);
+      float m = v[0];
+#pragma unroll
+      for (int e = 0; e < PV; ++e) {
+        x[j * PV + e] = v[e];
+        m = fmaxf(m, v[e]);
+      }
+      vm[j] = m;
+    }
+  }
+  float lm = vm[0];
+#pragma unroll
+  for (int j = 1; j < NV; ++j) lm = fmaxf(lm, vm[j]);
   const float c32 = a.c32;
 
   // ---- per-wave max and threshold T0_w; chunk max and T0 ----
   {
-    const float wm = wave_max(lm);
+    const float wm = wave_max_u(lm);
     uint32_t t = 0;
     if (F > 0) {
       const uint32_t kl = local_of<DT>(tid, 0) < nvalid ? key_of<DT>(lm) : 0u;
@@ -511,49 +573,41 @@ __global__ __launch_bounds__(kThreads) void k_cache_chunk(CacheArgs a) {
   const float mc = fmaxf(fmaxf(sm_wmax[0], sm_wmax[1]), fmaxf(sm_wmax[2], sm_wmax[3]));
   const uint32_t t0 = max(max(sm_wthr[0], sm_wthr[1]), max(sm_wthr[2], sm_wthr[3]));
   const float piv = pivot_of(mc);
-  float f0 = __builtin_inff();   // F == 0: no candidates
+  float f0 = __builtin_nanf("");   // F == 0: compares false, nothing is a candidate
   if (F > 0) f0 = (t0 <= key_of<DT>(-__builtin_inff())) ? -__builtin_inff() : value_of_key<DT>(t0);
 
-  uint32_t smask = 0;
+  // ---- candidate count and exp-mass of the non-candidates ----
+  int nt;
+  float sn;
+  if (!full && f0 == -__builtin_inff()) {
+    // every entry inside the row is a candidate (padding would pass too)
+    nt = 0;
 #pragma unroll
-  for (int q = 0; q < kPerThread; ++q)
-    if (x[q] >= f0 && (full || local_of<DT>(tid, q) < nvalid)) smask |= 1u << q;
-  int n = block_sum_i(__popc(smask), sm_i);
-
-  const bool overflow = n > kCandCap;   // ties: the merge re-reads this chunk
-
-  // ---- exp-mass of the non-candidates ----
-  float sn = 0.0f;
-#pragma unroll
-  for (int q = 0; q < kPerThread; ++q) {
-    const float e = __builtin_amdgcn_exp2f((x[q] - piv) * c32);
-    sn += ((smask >> q) & 1u) ? 0.0f : e;
+    for (int q = 0; q < kPerThread; ++q) nt += local_of<DT>(tid, q) < nvalid ? 1 : 0;
+    sn = 0.0f;
+  } else {
+    chunk_pass<DT>(x, f0, piv, c32, nt, sn);
   }
-
-  // ---- candidates out, in a fixed order (wave, lane, entry) ----
-  const int nt = __popc(smask);
-  const int incl = wave_incl_scan_i(nt, lane);
-  if (lane == 63) sm_wcnt[w] = incl;
+  const int incl = wave_scan_i(nt);
+  const double ws = wave_sum_u(double(sn));
+  if (lane == 63) {
+    sm_wcnt[w] = incl;
+    sm_ws[w] = ws;
+  }
   __syncthreads();
   int woff = 0;
   for (int ww = 0; ww < w; ++ww) woff += sm_wcnt[ww];
-  n = (sm_wcnt[0] + sm_wcnt[1]) + (sm_wcnt[2] + sm_wcnt[3]);
-  uint64_t* out = reinterpret_cast<uint64_t*>(a.cand + (rowid * a.S + c) * kCandCap);
-  if (!overflow && smask != 0u) {
-    int pos = woff + incl - nt;
-    constexpr int PV = Dt<DT>::kPerVec;
-#pragma unroll
-    for (int q = 0; q < kPerThread; ++q) {
-      if ((smask >> q) & 1u) {
-        out[pos] = cand_bits(key_of<DT>(x[q]), int32_t(c0) + local_of<DT>(tid, q));
-        ++pos;
-      }
-      // one vector at a time keeps the key/address temporaries short-lived
-      if (q % PV == PV - 1) __builtin_amdgcn_sched_barrier(0);
-    }
+  const int n = (sm_wcnt[0] + sm_wcnt[1]) + (sm_wcnt[2] + sm_wcnt[3]);
+  const bool overflow = n > kCandCap;   // ties: the merge re-reads this chunk
+
+  // ---- candidates out, in a fixed order (wave, lane, entry) ----
+  if (!overflow && nt > 0) {
+    uint64_t* out = reinterpret_cast<uint64_t*>(a.cand + (rowid * a.S + c) * kCandCap);
+    const int pos = woff + incl - nt;
+    chunk_store<DT>(x, vm, f0, tid, nvalid, int(c0), out, pos);
   }
-  const double s_rest = block_sum(double(sn), sm_d);
   if (tid == 0) {
+    const double s_rest = (sm_ws[0] + sm_ws[1]) + (sm_ws[2] + sm_ws[3]);
     uint64_t* wp = reinterpret_cast<uint64_t*>(a.part + rowid * a.S + c);
     wp[0] = uint64_t(__float_as_uint(mc)) | (uint64_t(t0) << 32);
     wp[1] = dbits(s_rest);

@@ -325,6 +325,77 @@ __device__ __forceinline__ void load_run(const typename Dt<DT>::T* __restrict__ 
   }
 }
 
+// ---- wave64 reductions on DPP lane moves (no LDS traffic) ----
+// Within each row of 16 lanes: quad swaps, half-row mirror, row mirror;
+// across rows: row_bcast15 / row_bcast31 fold rows 0+1 and 2+3, then 0..3.
+// The full result lands in lane 63 (read with readlane: wave-uniform).
+// Rows a row_mask leaves out keep `old`, which is the operation's identity.
+namespace dpp {
+constexpr int kXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;
+constexpr int kMirror = 0x140;
+constexpr int kBcast15 = 0x142;
+constexpr int kBcast31 = 0x143;
+constexpr int shr(int n) { return 0x110 + n; }
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int mov(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float movf(float old, float v) {
+  return __int_as_float(mov<CTRL, ROWS>(__float_as_int(old), __float_as_int(v)));
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ double movd(double v) {   // 0.0 where the row is masked
+  const uint64_t b = uint64_t(__double_as_longlong(v));
+  const int lo = mov<CTRL, ROWS>(0, int(uint32_t(b)));
+  const int hi = mov<CTRL, ROWS>(0, int(uint32_t(b >> 32)));
+  return __longlong_as_double(int64_t((uint64_t(uint32_t(hi)) << 32) | uint32_t(lo)));
+}
+__device__ __forceinline__ float lane63f(float v) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63)); }
+__device__ __forceinline__ double lane63d(double v) {
+  const uint64_t b = uint64_t(__double_as_longlong(v));
+  const uint32_t lo = __builtin_amdgcn_readlane(int(uint32_t(b)), 63);
+  const uint32_t hi = __builtin_amdgcn_readlane(int(uint32_t(b >> 32)), 63);
+  return __longlong_as_double(int64_t((uint64_t(hi) << 32) | lo));
+}
+}  // namespace dpp
+
+// wave max of a float, uniform result (fmaxf ignores NaN operands)
+__device__ __forceinline__ float wave_max_u(float v) {
+  using namespace dpp;
+  v = fmaxf(v, movf<kXor1>(v, v));
+  v = fmaxf(v, movf<kXor2>(v, v));
+  v = fmaxf(v, movf<kHalfMirror>(v, v));
+  v = fmaxf(v, movf<kMirror>(v, v));
+  v = fmaxf(v, movf<kBcast15, 0xA>(v, v));
+  v = fmaxf(v, movf<kBcast31, 0xC>(v, v));
+  return lane63f(v);
+}
+// wave sum of a double, uniform result (fixed order: deterministic)
+__device__ __forceinline__ double wave_sum_u(double v) {
+  using namespace dpp;
+  v += movd<kXor1>(v);
+  v += movd<kXor2>(v);
+  v += movd<kHalfMirror>(v);
+  v += movd<kMirror>(v);
+  v += movd<kBcast15, 0xA>(v);
+  v += movd<kBcast31, 0xC>(v);
+  return lane63d(v);
+}
+// inclusive prefix sum of an int over lanes 0..63
+__device__ __forceinline__ int wave_scan_i(int v) {
+  using namespace dpp;
+  v += mov<shr(1)>(0, v);
+  v += mov<shr(2)>(0, v);
+  v += mov<shr(4)>(0, v);
+  v += mov<shr(8)>(0, v);
+  v += mov<kBcast15, 0xA>(0, v);
+  v += mov<kBcast31, 0xC>(0, v);
+  return v;
+}
+
 // ---- wave64 reductions (butterflies: every lane ends with the same bits) ----
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
