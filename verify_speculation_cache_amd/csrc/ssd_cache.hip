@@ -461,49 +461,44 @@ __global__ __launch_bounds__(kThreads) void k_cache_merge(CacheArgs a) {
   }
 }
 
-// Candidate test, count and non-candidate exp-mass of one thread's entries.
-// Entries past the row end read as -inf: they add no mass, and they can only
-// pass the candidate test when f0 = -inf, a case the caller handles apart.
+// Exp-mass of the entries below f0 (the non-candidates). Entries past the
+// row end read as -inf and add nothing; with f0 = NaN (no candidates) every
+// entry counts.
 template <int DT>
-__device__ __forceinline__ void chunk_pass(const float (&x)[kPerThread], float f0, float piv, float c32, int& cnt,
-                                           float& sn) {
+__device__ __forceinline__ float chunk_rest_mass(const float (&x)[kPerThread], float f0, float piv, float c32) {
   constexpr int PV = Dt<DT>::kPerVec;
-  cnt = 0;
-  sn = 0.0f;
+  float sn = 0.0f;
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
-    const bool cand = x[q] >= f0;
     const float e = __builtin_amdgcn_exp2f((x[q] - piv) * c32);
-    cnt += cand ? 1 : 0;
-    sn += cand ? 0.0f : e;
+    sn += (x[q] >= f0) ? 0.0f : e;
     // a vector at a time: keeps the exp temporaries short-lived
     if (q % PV == PV - 1) __builtin_amdgcn_sched_barrier(0);
   }
+  return sn;
 }
 
-// Writes this thread's candidates (entries >= f0 inside the row) from
-// position pos on. Only vectors whose maximum reaches f0 are visited.
-template <int DT>
-__device__ __forceinline__ void chunk_store(const float (&x)[kPerThread], const float (&vm)[kPerThread / Dt<DT>::kPerVec],
-                                            float f0, int tid, int nvalid, int c0, uint64_t* out, int pos) {
-  constexpr int PV = Dt<DT>::kPerVec;
-  constexpr int NV = kPerThread / PV;
+// Compacts one wave's candidates (entries >= f0; with CHECK also inside the
+// row) into its LDS staging list, in (entry, lane) order; entries past
+// kCandCap are counted but not kept. Returns the wave's count.
+template <int DT, bool CHECK>
+__device__ __forceinline__ uint32_t wave_compact(const float (&x)[kPerThread], float f0, int tid, int nvalid, int c0,
+                                                 uint64_t* wlist) {
+  uint32_t cw = 0;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    if (vm[j] >= f0) {   // rare: the vector holds a candidate
-#pragma unroll
-      for (int e = 0; e < PV; ++e) {
-        const int q = j * PV + e;
-        const int loc = local_of<DT>(tid, q);
-        if ((x[q] >= f0) & (loc < nvalid)) {
-          out[uint32_t(pos)] = cand_bits(key_of<DT>(x[q]), c0 + loc);
-          ++pos;
-        }
+  for (int q = 0; q < kPerThread; ++q) {
+    const int loc = local_of<DT>(tid, q);
+    const bool cand = CHECK ? ((x[q] >= f0) & (loc < nvalid)) : (x[q] >= f0);
+    const uint64_t m = __builtin_amdgcn_ballot_w64(cand);
+    if (m != 0) {   // wave-uniform
+      if (cand) {
+        const uint32_t p = cw + __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+        if (p < uint32_t(kCandCap)) wlist[p] = cand_bits(key_of<DT>(x[q]), c0 + loc);
       }
+      cw += uint32_t(__popcll(m));
     }
-    // one vector at a time keeps the key/address temporaries short-lived
-    __builtin_amdgcn_sched_barrier(0);
   }
+  return cw;
 }
 
 template <int DT>
@@ -514,7 +509,8 @@ __global__ __launch_bounds__(kThreads) void k_cache_chunk(CacheArgs a) {
   __shared__ float sm_wmax[4];
   __shared__ uint32_t sm_wthr[4];
   __shared__ int sm_wcnt[4];
-  __shared__ double sm_ws[4];
+  __shared__ float sm_ws[4];
+  __shared__ uint64_t sm_list[4][kCandCap];   // per-wave candidate staging
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int KP = a.K + 1;
@@ -529,7 +525,6 @@ __global__ __launch_bounds__(kThreads) void k_cache_chunk(CacheArgs a) {
 
   const int64_t c0 = int64_t(c) * kChunk;
   const int nvalid = int(min(int64_t(kChunk), int64_t(a.V) - c0));
-  const bool full = nvalid == kChunk;
   float x[kPerThread];
   float vm[NV];   // per-vector maxima (padding is -inf)
   {
@@ -576,22 +571,16 @@ __global__ __launch_bounds__(kThreads) void k_cache_chunk(CacheArgs a) {
   float f0 = __builtin_nanf("");   // F == 0: compares false, nothing is a candidate
   if (F > 0) f0 = (t0 <= key_of<DT>(-__builtin_inff())) ? -__builtin_inff() : value_of_key<DT>(t0);
 
-  // ---- candidate count and exp-mass of the non-candidates ----
-  int nt;
-  float sn;
-  if (!full && f0 == -__builtin_inff()) {
-    // every entry inside the row is a candidate (padding would pass too)
-    nt = 0;
-#pragma unroll
-    for (int q = 0; q < kPerThread; ++q) nt += local_of<DT>(tid, q) < nvalid ? 1 : 0;
-    sn = 0.0f;
-  } else {
-    chunk_pass<DT>(x, f0, piv, c32, nt, sn);
-  }
-  const int incl = wave_scan_i(nt);
-  const double ws = wave_sum_u(double(sn));
-  if (lane == 63) {
-    sm_wcnt[w] = incl;
+  // ---- candidates (per-wave compaction) and exp-mass of the rest ----
+  uint32_t cw;
+  if (nvalid < kChunk && f0 == -__builtin_inff())   // padding would pass the test
+    cw = wave_compact<DT, true>(x, f0, tid, nvalid, int(c0), sm_list[w]);
+  else
+    cw = wave_compact<DT, false>(x, f0, tid, nvalid, int(c0), sm_list[w]);
+  const float sn = chunk_rest_mass<DT>(x, f0, piv, c32);
+  const float ws = wave_sum_uf(sn);
+  if (lane == 0) {
+    sm_wcnt[w] = int(cw);
     sm_ws[w] = ws;
   }
   __syncthreads();
@@ -600,14 +589,13 @@ __global__ __launch_bounds__(kThreads) void k_cache_chunk(CacheArgs a) {
   const int n = (sm_wcnt[0] + sm_wcnt[1]) + (sm_wcnt[2] + sm_wcnt[3]);
   const bool overflow = n > kCandCap;   // ties: the merge re-reads this chunk
 
-  // ---- candidates out, in a fixed order (wave, lane, entry) ----
-  if (!overflow && nt > 0) {
-    uint64_t* out = reinterpret_cast<uint64_t*>(a.cand + (rowid * a.S + c) * kCandCap);
-    const int pos = woff + incl - nt;
-    chunk_store<DT>(x, vm, f0, tid, nvalid, int(c0), out, pos);
+  // ---- candidates out: each wave copies its list, in order ----
+  if (!overflow) {
+    uint64_t* out = reinterpret_cast<uint64_t*>(a.cand + (rowid * a.S + c) * kCandCap) + woff;
+    for (int i = lane; i < int(cw); i += 64) out[i] = sm_list[w][i];
   }
   if (tid == 0) {
-    const double s_rest = (sm_ws[0] + sm_ws[1]) + (sm_ws[2] + sm_ws[3]);
+    const double s_rest = (double(sm_ws[0]) + double(sm_ws[1])) + (double(sm_ws[2]) + double(sm_ws[3]));
     uint64_t* wp = reinterpret_cast<uint64_t*>(a.part + rowid * a.S + c);
     wp[0] = uint64_t(__float_as_uint(mc)) | (uint64_t(t0) << 32);
     wp[1] = dbits(s_rest);

@@ -373,6 +373,17 @@ __device__ __forceinline__ float wave_max_u(float v) {
   v = fmaxf(v, movf<kBcast31, 0xC>(v, v));
   return lane63f(v);
 }
+// wave sum of a float, uniform result (fixed order: deterministic)
+__device__ __forceinline__ float wave_sum_uf(float v) {
+  using namespace dpp;
+  v += movf<kXor1>(0.0f, v);
+  v += movf<kXor2>(0.0f, v);
+  v += movf<kHalfMirror>(0.0f, v);
+  v += movf<kMirror>(0.0f, v);
+  v += movf<kBcast15, 0xA>(0.0f, v);
+  v += movf<kBcast31, 0xC>(0.0f, v);
+  return lane63f(v);
+}
 // wave sum of a double, uniform result (fixed order: deterministic)
 __device__ __forceinline__ double wave_sum_u(double v) {
   using namespace dpp;
