@@ -137,17 +137,15 @@ SSD_API int ssd_fanout(int32_t n_budget, int32_t K, double a_p, double r, int32_
 
 SSD_API size_t ssd_verify_workspace_size(int32_t B, int32_t K, int32_t V, int dtype) {
   if (check_shape(B, K, V) != SSD_OK || !dtype_ok(dtype)) return 0;
-  const int64_t S = chunks_per_row(V);
-  const StatsWs sw(B, 2 * K + 1, S);
-  const ResidWs rw(B, S);
+  const StatsWs sw(B, 2 * K + 1, stats_chunks_per_row(V), K);
+  const ResidWs rw(B, chunks_per_row(V));
   return sw.total + rw.total;
 }
 
 SSD_API size_t ssd_residual_workspace_size(int32_t B, int32_t K, int32_t V, int dtype) {
   if (check_shape(B, K, V) != SSD_OK || !dtype_ok(dtype)) return 0;
-  const int64_t S = chunks_per_row(V);
-  const StatsWs sw(B, 2, S);
-  const ResidWs rw(B, S);
+  const StatsWs sw(B, 2, stats_chunks_per_row(V), K);
+  const ResidWs rw(B, chunks_per_row(V));
   return sw.total + rw.total;
 }
 
@@ -173,12 +171,14 @@ SSD_API int ssd_verify(const void* target_logits, int64_t target_bstride,
     return fail(SSD_EINVAL, "a required pointer is NULL");
   if (target_bstride < 0 || draft_bstride < 0) return fail(SSD_EINVAL, "negative batch stride");
   const int64_t S = chunks_per_row(V);
+  const int64_t SS = stats_chunks_per_row(V);
   const bool sig = sigma != nullptr;
   const int NR = sig ? K + 1 : 2 * K + 1;
-  const StatsWs sw(B, 2 * K + 1, S);
+  const StatsWs sw(B, 2 * K + 1, SS, K);
   const ResidWs rw(B, S);
   if ((st = check_ws(workspace, ws_bytes, sw.total + rw.total)) != SSD_OK) return st;
-  if ((st = check_grid(int64_t(B) * NR * S)) != SSD_OK) return st;
+  if ((st = check_grid(int64_t(B) * NR * SS)) != SSD_OK) return st;
+  if ((st = check_grid(int64_t(B) * S)) != SSD_OK) return st;
   char* ws = static_cast<char*>(workspace);
 
   StatsArgs a{};
@@ -189,7 +189,7 @@ SSD_API int ssd_verify(const void* target_logits, int64_t target_bstride,
   a.B = B;
   a.K = K;
   a.V = V;
-  a.S = int(S);
+  a.S = int(SS);
   a.NR = NR;
   a.mode = sig ? kModeVerifySigma : kModeVerify;
   a.c64 = kLog2e / double(tau);
@@ -208,6 +208,7 @@ SSD_API int ssd_verify(const void* target_logits, int64_t target_bstride,
   a.part = reinterpret_cast<RowPartial*>(ws + sw.part);
   a.cnt = reinterpret_cast<uint32_t*>(ws + sw.cnt);
   a.info = reinterpret_cast<RowInfo*>(ws + sw.info);
+  a.zg = reinterpret_cast<uint64_t*>(ws + sw.zg);
   hipStream_t stream = as_stream(hip_stream);
   if ((st = hip_status(launch_stats(a, dtype, stream), "stats launch")) != SSD_OK) return st;
 
@@ -247,10 +248,12 @@ SSD_API int ssd_residual_sample(const void* target_logits, int64_t target_bstrid
   if (sigma && !draft_logits) return fail(SSD_EINVAL, "sigma given without draft logits");
   if (target_bstride < 0 || draft_bstride < 0) return fail(SSD_EINVAL, "negative batch stride");
   const int64_t S = chunks_per_row(V);
-  const StatsWs sw(B, 2, S);
+  const int64_t SS = stats_chunks_per_row(V);
+  const StatsWs sw(B, 2, SS, K);
   const ResidWs rw(B, S);
   if ((st = check_ws(workspace, ws_bytes, sw.total + rw.total)) != SSD_OK) return st;
-  if ((st = check_grid(int64_t(B) * 2 * S)) != SSD_OK) return st;
+  if ((st = check_grid(int64_t(B) * 2 * SS)) != SSD_OK) return st;
+  if ((st = check_grid(int64_t(B) * S)) != SSD_OK) return st;
   char* ws = static_cast<char*>(workspace);
   const bool sig = sigma != nullptr;
 
@@ -262,7 +265,7 @@ SSD_API int ssd_residual_sample(const void* target_logits, int64_t target_bstrid
   a.B = B;
   a.K = K;
   a.V = V;
-  a.S = int(S);
+  a.S = int(SS);
   a.NR = 2;
   a.mode = kModeRows;
   a.c64 = kLog2e / double(tau);
@@ -277,6 +280,7 @@ SSD_API int ssd_residual_sample(const void* target_logits, int64_t target_bstrid
   a.part = reinterpret_cast<RowPartial*>(ws + sw.part);
   a.cnt = reinterpret_cast<uint32_t*>(ws + sw.cnt);
   a.info = reinterpret_cast<RowInfo*>(ws + sw.info);
+  a.zg = reinterpret_cast<uint64_t*>(ws + sw.zg);
   hipStream_t stream = as_stream(hip_stream);
   if ((st = hip_status(launch_stats(a, dtype, stream), "stats launch")) != SSD_OK) return st;
 

@@ -509,7 +509,7 @@ __global__ __launch_bounds__(kThreads) void k_cache_chunk(CacheArgs a) {
   __shared__ float sm_wmax[4];
   __shared__ uint32_t sm_wthr[4];
   __shared__ int sm_wcnt[4];
-  __shared__ float sm_ws[4];
+  __shared__ double sm_ws[4];
   __shared__ uint64_t sm_list[4][kCandCap];   // per-wave candidate staging
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -578,7 +578,7 @@ __global__ __launch_bounds__(kThreads) void k_cache_chunk(CacheArgs a) {
   else
     cw = wave_compact<DT, false>(x, f0, tid, nvalid, int(c0), sm_list[w]);
   const float sn = chunk_rest_mass<DT>(x, f0, piv, c32);
-  const float ws = wave_sum_uf(sn);
+  const double ws = wave_sum_u(double(sn));   // double across threads
   if (lane == 0) {
     sm_wcnt[w] = int(cw);
     sm_ws[w] = ws;
@@ -595,7 +595,7 @@ __global__ __launch_bounds__(kThreads) void k_cache_chunk(CacheArgs a) {
     for (int i = lane; i < int(cw); i += 64) out[i] = sm_list[w][i];
   }
   if (tid == 0) {
-    const double s_rest = (double(sm_ws[0]) + double(sm_ws[1])) + (double(sm_ws[2]) + double(sm_ws[3]));
+    const double s_rest = (sm_ws[0] + sm_ws[1]) + (sm_ws[2] + sm_ws[3]);
     uint64_t* wp = reinterpret_cast<uint64_t*>(a.part + rowid * a.S + c);
     wp[0] = uint64_t(__float_as_uint(mc)) | (uint64_t(t0) << 32);
     wp[1] = dbits(s_rest);

@@ -187,21 +187,22 @@ __device__ __forceinline__ uint4 gather_vec(const typename Dt<DT>::T* __restrict
     return make_uint4(e[0], e[1], e[2], e[3]);
 }
 
-// A chunk held as raw 16-byte vectors, so callers need not keep 32 floats
-// per row live. STRIDED: vector j of thread t covers chunk entries
+// A chunk of 256 x PT entries held as raw 16-byte vectors, so callers need
+// not keep PT floats per row live. STRIDED: vector j of thread t covers chunk entries
 // (j*256 + t)*PV .. +PV (each wave load is one contiguous 1 KiB span);
 // contiguous: entries t*32 + j*PV .. +PV. Entries past the row end read as
 // -inf. Whole vectors of a 16-byte aligned row are single loads, all issued
 // before the first use; a vector straddling the row end, or any vector of
 // an unaligned row, is read per entry.
-template <int DT, bool STRIDED>
+template <int DT, bool STRIDED, int PT = kPerThread>
 struct ChunkVecs {
   static constexpr int PV = Dt<DT>::kPerVec;
-  static constexpr int NV = kPerThread / PV;
+  static constexpr int NV = PT / PV;
+  static constexpr int kSpan = kThreads * PT;   // entries per chunk
   uint4 raw[NV];
 
   __device__ static int local(int tid, int j) {
-    return STRIDED ? (j * kThreads + tid) * PV : tid * kPerThread + j * PV;
+    return STRIDED ? (j * kThreads + tid) * PV : tid * PT + j * PV;
   }
   __device__ static int64_t first(int64_t c0, int tid, int j) { return c0 + local(tid, j); }
 
@@ -211,7 +212,7 @@ struct ChunkVecs {
     for (int j = 0; j < NV; ++j) raw[j] = *reinterpret_cast<const uint4*>(base + uint32_t(local(tid, j)));
   }
   __device__ void load(const typename Dt<DT>::T* __restrict__ row, int64_t c0, int64_t V, bool aligned, int tid) {
-    if (aligned && V - c0 >= kChunk) {
+    if (aligned && V - c0 >= kSpan) {
       issue_full(row, c0, tid);
       __builtin_amdgcn_sched_barrier(0);
     } else {
@@ -249,7 +250,7 @@ struct ChunkVecs {
   __device__ void load_partial(const typename Dt<DT>::T* __restrict__ row, int64_t c0, int64_t V, bool aligned,
                                int tid) {
     const int64_t rem = V - c0;
-    const int lim = rem < kChunk ? int(rem) : kChunk;
+    const int lim = rem < kSpan ? int(rem) : kSpan;
     if (aligned) {
       issue_tail(row, c0, lim, tid);
       __builtin_amdgcn_sched_barrier(0);
@@ -269,13 +270,13 @@ struct ChunkVecs {
 
 // The same chunk of two rows, with all loads of both in flight together
 // when both rows are 16-byte aligned and the chunk is full.
-template <int DT, bool STRIDED>
-__device__ __forceinline__ void load_pair(ChunkVecs<DT, STRIDED>& x, const typename Dt<DT>::T* __restrict__ rx,
-                                          ChunkVecs<DT, STRIDED>& y, const typename Dt<DT>::T* __restrict__ ry,
+template <int DT, bool STRIDED, int PT>
+__device__ __forceinline__ void load_pair(ChunkVecs<DT, STRIDED, PT>& x, const typename Dt<DT>::T* __restrict__ rx,
+                                          ChunkVecs<DT, STRIDED, PT>& y, const typename Dt<DT>::T* __restrict__ ry,
                                           int64_t c0, int64_t V, int tid) {
   const bool ax = (reinterpret_cast<uintptr_t>(rx) & 15u) == 0;
   const bool ay = (reinterpret_cast<uintptr_t>(ry) & 15u) == 0;
-  if (ax && ay && V - c0 >= kChunk) {
+  if (ax && ay && V - c0 >= ChunkVecs<DT, STRIDED, PT>::kSpan) {
     x.issue_full(rx, c0, tid);
     y.issue_full(ry, c0, tid);
     __builtin_amdgcn_sched_barrier(0);
@@ -289,39 +290,6 @@ __device__ __forceinline__ void load_pair(ChunkVecs<DT, STRIDED>& x, const typen
   } else {
     x.load_partial(rx, c0, V, ax, tid);
     y.load_partial(ry, c0, V, ay, tid);
-  }
-}
-
-// Contiguous layout: thread t holds entries c0 + t*kPerThread + k.
-template <int DT>
-__device__ __forceinline__ void load_run(const typename Dt<DT>::T* __restrict__ row, int64_t c0,
-                                         int64_t V, bool aligned, int tid, float (&x)[kPerThread]) {
-  constexpr int PV = Dt<DT>::kPerVec;
-  constexpr int NV = kPerThread / PV;
-  const int64_t base = c0 + int64_t(tid) * kPerThread;
-  if (aligned && base + kPerThread <= V) {
-    const uint4* p = reinterpret_cast<const uint4*>(row + base);
-    uint4 raw[NV];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) raw[j] = p[j];
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < NV; ++j) unpack16<DT>(raw[j], x + j * PV);
-  } else {
-    const typename Dt<DT>::T* cb = row + c0;
-    const int64_t rem = V - c0;
-    const int lim = rem < kChunk ? int(rem) : kChunk;
-    const int t0 = tid * kPerThread;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-#pragma unroll
-      for (int e = 0; e < PV; ++e) {
-        const int loc = t0 + j * PV + e;
-        const float v = Dt<DT>::to_f(cb[loc < lim ? loc : lim - 1]);
-        x[j * PV + e] = loc < lim ? v : -__builtin_inff();
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
   }
 }
 
@@ -551,16 +519,48 @@ __device__ void merge_rows(const uint64_t* part, int NR, int S, float c32, float
   }
 }
 
+// merge_rows for S <= 64 chunks per row, all partials in one round trip:
+// each row gets a segment of G lanes (G = S rounded up to a power of two),
+// one lane per chunk; segmented butterflies give the row max and the
+// rescaled sum (fixed order, deterministic).
+__device__ inline void merge_rows_seg(const uint64_t* part, int NR, int S, float c32, float* piv_out,
+                                      double* s_out) {
+  int G = 1;
+  while (G < S) G <<= 1;
+  const int per_wave = 64 / G;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int seg = lane / G, cl = lane - seg * G;
+  for (int r0 = w * per_wave; r0 < NR; r0 += 4 * per_wave) {
+    const int r = r0 + seg;
+    float m = -__builtin_inff();
+    double s = 0.0;
+    if (r < NR && cl < S) {
+      const uint64_t* p = part + (int64_t(r) * S + cl) * 2;
+      m = lo_f(dev_load(p));
+      s = bits_d(dev_load(p + 1));
+    }
+    float mr = m;
+    for (int o = 1; o < G; o <<= 1) mr = fmaxf(mr, __shfl_xor(mr, o));
+    const float pr = pivot_of(mr);
+    double t = s > 0.0 ? s * rescale(pivot_of(m), pr, c32) : 0.0;
+    for (int o = 1; o < G; o <<= 1) t += __shfl_xor(t, o);
+    if (cl == 0 && r < NR) {
+      piv_out[r] = pr;
+      s_out[r] = t;
+    }
+  }
+}
+
 // Count this workgroup in; returns true in every thread of the workgroup that
-// arrives last, which then reads the others' partials with dev_load. Each
-// thread first waits until its own device-scope stores have completed, so
-// they are visible before the counter moves. The last arrival re-arms the
-// counter for the next launch. No workgroup waits for another, so this
-// cannot deadlock.
+// arrives last, which then reads the others' partials with dev_load. All
+// data a workgroup leaves for others is stored by its thread 0 with
+// dev_store, and thread 0 waits for those stores to complete before it
+// moves the counter, so they are visible to whoever arrives last. The last
+// arrival re-arms the counter for the next launch. No workgroup waits for
+// another, so this cannot deadlock.
 __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, int* sm_flag) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
   if (threadIdx.x == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = (prev == expected - 1u);
     if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -569,5 +569,6 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected
   __syncthreads();
   return *sm_flag != 0;
 }
+
 
 }  // namespace ssd

@@ -19,6 +19,13 @@ constexpr int kMaxRows = 2 * SSD_MAX_K + 1;     // rows one verify batch element
 
 inline int64_t chunks_per_row(int64_t V) { return (V + kChunk - 1) / kChunk; }
 
+// The row-statistics pass reads 64 entries per thread: twice the bytes per
+// workgroup, half the workgroups (dispatching workgroups, not HBM, bounds a
+// one-chunk-per-workgroup pass at this size).
+constexpr int kStatsPerThread = 64;
+constexpr int kStatsChunk = kThreads * kStatsPerThread;   // 16384
+inline int64_t stats_chunks_per_row(int64_t V) { return (V + kStatsChunk - 1) / kStatsChunk; }
+
 // Per-(row, chunk) statistics: chunk max of the raw logits and the chunk's
 // sum of exp2((z - pivot) * log2(e)/tau), pivot = chunk max (0 if -inf).
 struct alignas(16) RowPartial {
@@ -78,9 +85,10 @@ struct StatsArgs {
   int32_t* out_tokens;
   float* probs;
   float* row_lse;
-  RowPartial* part;   // [B, NR, S]
+  RowPartial* part;   // [B, NR, S] (S = stats chunks per row)
   uint32_t* cnt;      // [B] (kCntStride apart)
   RowInfo* info;      // [B]
+  uint64_t* zg;       // [B, K]: target | draft logit at the drafted token (floats)
 };
 
 struct ResidArgs {
@@ -136,12 +144,13 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr int kCntStride = 1024;
 
 struct StatsWs {
-  size_t part, cnt, info, total;
-  StatsWs(int64_t B, int64_t NR, int64_t S) {
+  size_t part, cnt, info, zg, total;
+  StatsWs(int64_t B, int64_t NR, int64_t S, int64_t K) {
     part = 0;
     cnt = align256(part + sizeof(RowPartial) * B * NR * S);
     info = align256(cnt + sizeof(uint32_t) * kCntStride * B);
-    total = align256(info + sizeof(RowInfo) * B);
+    zg = align256(info + sizeof(RowInfo) * B);
+    total = align256(zg + sizeof(uint64_t) * B * K);
   }
 };
 

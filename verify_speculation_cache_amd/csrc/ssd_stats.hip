@@ -48,14 +48,15 @@ __device__ __forceinline__ bool in_top(float x, int32_t idx, uint32_t tkey, int3
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_stats(StatsArgs a) {
+  constexpr int PV = Dt<DT>::kPerVec;
   __shared__ float sm_f[4];
-  __shared__ double sm_d[4];
+  __shared__ double sm_s[4];
   __shared__ int sm_last;
   __shared__ float e_piv[kMaxRows];
   __shared__ double e_s[kMaxRows];
   __shared__ int sm_a;
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int per_b = a.NR * a.S;
   const int b = blockIdx.x / per_b;
   const int rem = blockIdx.x - b * per_b;
@@ -64,34 +65,87 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsArgs a) {
 
   const typename Dt<DT>::T* row = stats_row_ptr<DT>(a, b, r);
   if (row != nullptr) {  // uniform per workgroup
-    const int64_t c0 = int64_t(c) * kChunk;
-    const bool vec = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
-    float x[kPerThread];
-    load_strided<DT>(row, c0, a.V, vec, tid, x);
-    float m = x[0];
+    using CV = ChunkVecs<DT, true, kStatsPerThread>;
+    const int64_t c0 = int64_t(c) * kStatsChunk;
+    // The workgroup whose chunk holds drafted token d_r (target row r < K)
+    // also fetches z_t(d_r) and z_d(d_r) for the accept test, so the
+    // epilogue finds them with the partials.
+    int32_t dtok = -1;
+    if (a.mode != kModeRows && r < a.K) dtok = a.tokens[int64_t(b) * a.K + r];
+    const bool owns = dtok >= 0 && dtok < a.V && int64_t(dtok) >= c0 && int64_t(dtok) < c0 + kStatsChunk;
+    float gzt = 0.0f, gzd = 0.0f;
+    if (owns && tid == 0) {
+      gzt = load_one<DT>(a.target, int64_t(b) * a.tb + int64_t(r) * a.V + dtok);
+      gzd = load_one<DT>(a.draft, int64_t(b) * a.db + int64_t(r) * a.V + dtok);
+    }
+    CV cv;
+    cv.load(row, c0, a.V, (reinterpret_cast<uintptr_t>(row) & 15u) == 0, tid);
+    float m = -__builtin_inff();
 #pragma unroll
-    for (int k = 1; k < kPerThread; ++k) m = fmaxf(m, x[k]);
-    m = block_max(m, sm_f);
+    for (int j = 0; j < CV::NV; ++j) {
+      float v[PV];
+      cv.get(j, v);
+#pragma unroll
+      for (int e = 0; e < PV; ++e) m = fmaxf(m, v[e]);
+    }
+    m = wave_max_u(m);
+    if (lane == 0) sm_f[w] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(sm_f[0], sm_f[1]), fmaxf(sm_f[2], sm_f[3]));
     const float piv = pivot_of(m);
-    float s = 0.0f;
+    float sum = 0.0f;
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) s += __builtin_amdgcn_exp2f((x[k] - piv) * a.c32);
-    const double sd = block_sum(double(s), sm_d);
+    for (int j = 0; j < CV::NV; ++j) {
+      float v[PV];
+      cv.get(j, v);
+#pragma unroll
+      for (int e = 0; e < PV; ++e) sum += __builtin_amdgcn_exp2f((v[e] - piv) * a.c32);
+    }
+    // per-thread sums in float, double across threads
+    const double wsum = wave_sum_u(double(sum));
+    if (lane == 0) sm_s[w] = wsum;
+    __syncthreads();
     if (tid == 0) {
-      uint64_t* w = reinterpret_cast<uint64_t*>(a.part + (int64_t(b) * a.NR + r) * a.S + c);
-      dev_store(w, pack2(m, 0.0f));
-      dev_store(w + 1, dbits(sd));
+      const double sd = (sm_s[0] + sm_s[1]) + (sm_s[2] + sm_s[3]);
+      uint64_t* wp = reinterpret_cast<uint64_t*>(a.part + (int64_t(b) * a.NR + r) * a.S + c);
+      dev_store(wp, pack2(m, 0.0f));
+      dev_store(wp + 1, dbits(sd));
+      if (owns) dev_store(a.zg + int64_t(b) * a.K + r, pack2(gzt, gzd));
     }
   }
 
   if (!arrive_last(&a.cnt[int64_t(b) * kCntStride], uint32_t(per_b), &sm_last)) return;
 
   // ---------------- epilogue: last workgroup of batch row b ----------------
-  merge_rows<2>(reinterpret_cast<const uint64_t*>(a.part) + int64_t(b) * a.NR * a.S * 2, a.NR, a.S,
-                a.c32, e_piv, e_s, nullptr);
+  const int K = a.K;
+  // per drafted position (wave 0, lane i < K): inputs of the accept test,
+  // loaded before the merge so that all loads share one round trip
+  int32_t d = -1;
+  float ua = 0.0f, zt = 0.0f, zd = 0.0f;
+  double sp0 = 0.0, sp1 = 0.0, sp2 = 0.0;
+  ssd_rowkey tk{0xFFFFFFFFu, -1};
+  if (a.mode != kModeRows && tid < K) {
+    const int i = tid;
+    d = a.tokens[int64_t(b) * K + i];
+    ua = a.u_acc[int64_t(b) * K + i];
+    const uint64_t g = dev_load(a.zg + int64_t(b) * K + i);   // valid only for 0 <= d < V
+    zt = lo_f(g);
+    zd = __uint_as_float(uint32_t(g >> 32));
+    if (a.use_sigma) {
+      const double* sp = a.dstats + (int64_t(b) * (K + 1) + i) * 3;
+      sp0 = sp[0];
+      sp1 = sp[1];
+      sp2 = sp[2];
+      tk = a.thr[int64_t(b) * (K + 1) + i];
+    }
+  }
+  {
+    const uint64_t* pb = reinterpret_cast<const uint64_t*>(a.part) + int64_t(b) * a.NR * a.S * 2;
+    if (a.S <= 64) merge_rows_seg(pb, a.NR, a.S, a.c32, e_piv, e_s);
+    else merge_rows<2>(pb, a.NR, a.S, a.c32, e_piv, e_s, nullptr);
+  }
   __syncthreads();
 
-  const int K = a.K;
   if (a.mode == kModeRows) {
     if (tid == 0) {
       RowInfo inf{};
@@ -131,28 +185,22 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsArgs a) {
     const int i = tid;
     bool bad = false, acc = true;
     double pd = 0.0, qd = 0.0;
-    int32_t d = -1;
     if (i < K) {
-      d = a.tokens[int64_t(b) * K + i];
       bad = (d < 0 || d >= a.V);
       if (!bad) {
-        const float zt = load_one<DT>(a.target, int64_t(b) * a.tb + int64_t(i) * a.V + d);
-        const float zd = load_one<DT>(a.draft, int64_t(b) * a.db + int64_t(i) * a.V + d);
         const double st = e_s[i];
         pd = st > 0.0 ? exp2(double(zt - e_piv[i]) * double(a.c32)) / st : 0.0;
-        double pivd, sdn, w = 1.0;
+        double pivd, sdn, wgt = 1.0;
         if (a.use_sigma) {
-          const double* sp = a.dstats + (int64_t(b) * (K + 1) + i) * 3;
-          pivd = double(pivot_of(float(sp[0])));
-          sdn = double(a.C) * sp[1] + sp[2];
-          const ssd_rowkey tk = a.thr[int64_t(b) * (K + 1) + i];
-          if (in_top<DT>(zd, d, tk.key, tk.idx)) w = double(a.C);
+          pivd = double(pivot_of(float(sp0)));
+          sdn = double(a.C) * sp1 + sp2;
+          if (in_top<DT>(zd, d, tk.key, tk.idx)) wgt = double(a.C);
         } else {
           pivd = double(e_piv[K + 1 + i]);
           sdn = e_s[K + 1 + i];
         }
-        qd = sdn > 0.0 ? w * exp2(double(zd - float(pivd)) * double(a.c32)) / sdn : 0.0;
-        acc = double(a.u_acc[int64_t(b) * K + i]) * qd < pd;
+        qd = sdn > 0.0 ? wgt * exp2(double(zd - float(pivd)) * double(a.c32)) / sdn : 0.0;
+        acc = double(ua) * qd < pd;
       }
     }
     const uint64_t badm = __ballot(i < K && bad);
