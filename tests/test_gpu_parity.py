@@ -260,6 +260,37 @@ def test_cache_ties_and_limits(S):
     _cache_case(S, d, [5, 64, 1, 33], 0.2, label="ties-f32")
 
 
+@pytest.mark.parametrize("K,F", [(64, [5] * 65), (4, [64] * 5), (3, [0, 10, 0, 64]), (1, [1, 0])])
+def test_cache_lookup_direct(S, K, F):
+    """Lookup against the oracle on synthetic caches: rows whose cache holds
+    more than 256 tokens, K = 64 (outcome at position 64), empty segments,
+    flagged rows and misses."""
+    log(f"[gpu] lookup K={K} sumF={sum(F)}")
+    rng = np.random.default_rng(1000 + K)
+    B, V = 97, 50000
+    off = np.concatenate([[0], np.cumsum(F)])
+    cache = np.full((B, sum(F)), -1, dtype=np.int32)
+    for b in range(B):
+        for k in range(K + 1):
+            cache[b, off[k]:off[k + 1]] = rng.choice(V, size=F[k], replace=False)
+    acc = rng.integers(-1, K + 1, size=B).astype(np.int32)
+    acc[:3] = K
+    out = rng.integers(0, V, size=(B, K + 1)).astype(np.int32)
+    for b in range(B):
+        a = int(acc[b])
+        if a >= 0 and F[a] > 0 and b % 2 == 0:
+            out[b, a] = cache[b, off[a] + rng.integers(0, F[a])]
+        if b % 7 == 3 and a >= 0:
+            out[b, a] = -1
+    got = S.ssd_cache_lookup(torch.from_numpy(cache).cuda(), F, torch.from_numpy(acc).cuda(),
+                             torch.from_numpy(out).cuda())
+    torch.cuda.synchronize()
+    hit_r, slot_r = O.cache_lookup(cache, F, acc, out)
+    assert np.array_equal(got["hit"].cpu().numpy(), hit_r)
+    assert np.array_equal(got["slot"].cpu().numpy().astype(np.int64), slot_r)
+    assert hit_r.sum() >= 10   # the case exercises hits, not only misses
+
+
 # ---------------------------------------------------------------------------
 # the five workloads at full size
 # ---------------------------------------------------------------------------

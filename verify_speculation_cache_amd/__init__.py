@@ -288,8 +288,8 @@ def ssd_cache_lookup(cache_tokens, F: Sequence[int], accepted, out_tokens, *, ou
     K = len(F) - 1
     B = int(accepted.shape[0])
     dev = accepted.device
-    if cache_tokens.dim() != 2 or cache_tokens.shape[0] != B or cache_tokens.shape[1] < sum(F):
-        raise ValueError("cache_tokens must be [B, >= sum F]")
+    if cache_tokens.dim() != 2 or cache_tokens.shape[0] != B or cache_tokens.shape[1] != sum(F):
+        raise ValueError("cache_tokens must be [B, sum F] (row stride sum F)")
     if not cache_tokens.is_contiguous() or cache_tokens.dtype != torch.int32:
         raise ValueError("cache_tokens must be contiguous int32")
     if out is None:

@@ -603,27 +603,53 @@ __global__ __launch_bounds__(kThreads) void k_cache_chunk(CacheArgs a) {
   }
 }
 
+// One wave per batch row. Everything the row needs (its accepted length,
+// its outcome tokens and, when the row's cache holds at most 256 tokens, the
+// whole cache row) is loaded in one round trip; the outcome (k, t*) is then
+// matched against segment k with a ballot. Segment tokens are distinct, so
+// at most one slot matches.
+constexpr int kLookupPre = 4;   // cache slots per lane loaded up front
+
 __global__ __launch_bounds__(kThreads) void k_lookup(LookupArgs a) {
-  const int b = blockIdx.x * kThreads + threadIdx.x;
-  if (b >= a.B) return;
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (b >= a.B) return;   // whole wave
+  const int32_t* orow = a.out_tokens + int64_t(b) * (a.K + 1);
+  const int32_t* crow = a.cache_tokens + int64_t(b) * a.sumF;
+  const bool pre = a.sumF <= 64 * kLookupPre;
   const int av = a.accepted[b];
+  const int32_t ot = lane <= a.K ? orow[lane] : -1;
+  const int32_t ot64 = (lane == 0 && a.K >= 64) ? orow[64] : -1;
+  int32_t cv[kLookupPre];
+#pragma unroll
+  for (int r = 0; r < kLookupPre; ++r) {
+    const int idx = r * 64 + lane;
+    cv[r] = (pre && idx < a.sumF) ? crow[idx] : -1;
+  }
   uint8_t h = 0;
   int32_t s = -1;
-  if (av >= 0 && av <= a.K) {
-    const int32_t t = a.out_tokens[int64_t(b) * (a.K + 1) + av];
-    const int32_t* seg = a.cache_tokens + int64_t(b) * a.sumF + a.off[av];
-    if (t >= 0) {
-      for (int j = 0; j < a.F[av]; ++j) {
-        if (seg[j] == t) {
-          h = 1;
-          s = j;
-          break;
+  if (av >= 0 && av <= a.K) {   // wave-uniform
+    const int32_t t = av < 64 ? __shfl(ot, av) : __shfl(ot64, 0);
+    const int lo = a.off[av], n = a.F[av];
+    if (t >= 0 && n > 0) {
+      if (pre) {
+#pragma unroll
+        for (int r = 0; r < kLookupPre; ++r) {
+          const int idx = r * 64 + lane;
+          const uint64_t m = __ballot(idx >= lo && idx < lo + n && cv[r] == t);
+          if (m != 0 && s < 0) s = r * 64 + (__ffsll((unsigned long long)m) - 1) - lo;
         }
+      } else {
+        const uint64_t m = __ballot(lane < n && crow[lo + lane] == t);
+        if (m != 0) s = __ffsll((unsigned long long)m) - 1;
       }
+      h = s >= 0 ? 1 : 0;
     }
   }
-  a.hit[b] = h;
-  if (a.slot) a.slot[b] = s;
+  if (lane == 0) {
+    a.hit[b] = h;
+    if (a.slot) a.slot[b] = s;
+  }
 }
 
 hipError_t launch_cache(const CacheArgs& a, int dtype, hipStream_t st) {
@@ -640,7 +666,8 @@ hipError_t launch_cache(const CacheArgs& a, int dtype, hipStream_t st) {
 }
 
 hipError_t launch_lookup(const LookupArgs& a, hipStream_t st) {
-  const unsigned grid = unsigned((a.B + kThreads - 1) / kThreads);
+  const unsigned rows_per_wg = kThreads / 64;
+  const unsigned grid = unsigned((a.B + rows_per_wg - 1) / rows_per_wg);
   hipLaunchKernelGGL(k_lookup, dim3(grid), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
