@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of graph replay")
     ap.add_argument("--profile-loop", type=int, default=0,
                     help="after the bench, run this many extra eager steps (for profilers)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="first run a plain 256 MiB read + 256 MiB write elementwise kernel (torch.neg on "
+                         "bf16) three times: the known-size reference that scales hardware byte counters")
     return ap.parse_args()
 
 
@@ -62,6 +65,14 @@ def main():
     tau = cfg.taus[0]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.calib_copy:
+        src = torch.ones(128 << 20, dtype=torch.bfloat16, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     t0 = time.time()
     d = W.make_inputs(cfg, tau=tau)
@@ -192,7 +203,7 @@ def main():
     dom_ms = t_build
     dom_gbps = bytes_build / (dom_ms / 1e3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(dom_gbps / PEAK_HBM_GBS, 4), "traffic": None,
+                "frac": round(dom_gbps / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
                 "kernel": "ssd_build_cache (k_cache_chunk + k_cache_merge, bf16)", "bytes_per_launch": bytes_build,
                 "avg_launch_ms": round(dom_ms, 5)}
 
@@ -234,6 +245,24 @@ def main():
         "gen_s": round(gen_s, 2),
     }
     print(json.dumps(line), flush=True)
+
+
+HBM_BYTES_PROFILE = os.path.join(ROOT, "profiles", "ssd_build_cache_B64_K5_V128256_bf16_hbm_bytes.md")
+
+
+def measured_traffic():
+    """HBM bytes per ssd_build_cache call from the committed FETCH_SIZE / WRITE_SIZE
+    counter summary, or None when the kernel sources changed since it was taken."""
+    import hashlib
+    try:
+        text = open(HBM_BYTES_PROFILE).read()
+        rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+        h = hashlib.sha256()
+        for p in rec["sources"]:
+            h.update(open(os.path.join(ROOT, p), "rb").read())
+    except (OSError, ValueError, KeyError, IndexError):
+        return None
+    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["source_sha256"] else None
 
 
 def cpu_baseline(cfg, d, F, C, tau, budget_s):
