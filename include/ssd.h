@@ -155,6 +155,28 @@ SSD_API int ssd_residual_sample(const void* target_logits, int64_t target_bstrid
                                 int32_t* token_out, float* mass_out,
                                 void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* Bytes of workspace ssd_draft_sample needs. */
+SSD_API size_t ssd_draft_sample_workspace_size(int32_t B, int32_t K, int32_t V, int dtype);
+
+/* The draft phase's sampling ([SD-notes] The Algorithm, step 1; with sigma,
+ * [SSD-notes] key design 2: the top-F_i tokens of draft row i keep weight C,
+ * the others weight 1, and the draw is from the renormalised result): for
+ * every batch row b and position i = 0..K-1, d[b,i] is drawn from
+ * q_i = softmax(draft row i / tau), or its sigma_{F_i,C} form, by inverse CDF
+ * in token order with u[b,i] (the smallest v whose running mass exceeds
+ * u*Z). A row without mass (all -inf) draws -1.
+ *   draft_logits device [B, >=K, V] (rows 0..K-1 read)
+ *   sigma        NULL for the plain softmax, else host pointer whose thr comes
+ *                from ssd_build_cache on the same draft rows (draft_stats is
+ *                not read)
+ *   u            device float [B, K] in [0, 1)
+ *   tokens_out   device int32 [B, K]
+ * One kernel launch on hip_stream. */
+SSD_API int ssd_draft_sample(const void* draft_logits, int64_t draft_bstride, int dtype,
+                             int32_t B, int32_t K, int32_t V, float tau, const ssd_sigma* sigma,
+                             const float* u, int32_t* tokens_out,
+                             void* workspace, size_t ws_bytes, void* hip_stream);
+
 /* Bytes of workspace ssd_build_cache needs. */
 SSD_API size_t ssd_build_cache_workspace_size(int32_t B, int32_t K, int32_t V, int dtype);
 
@@ -173,7 +195,7 @@ SSD_API size_t ssd_build_cache_workspace_size(int32_t B, int32_t K, int32_t V, i
  *                over the other tokens (zmax taken as 0 if the row is all
  *                -inf). ln(C S_top + S_rest) + zmax/tau is the log-normaliser
  *                of sigma_{F_k,C}.
- * One kernel launch on hip_stream. */
+ * Two kernel launches on hip_stream (chunk pass, then per-row merge). */
 SSD_API int ssd_build_cache(const void* draft_logits, int64_t draft_bstride, int dtype,
                             int32_t B, int32_t K, int32_t V, float tau, const int32_t* F,
                             int32_t* cache_tokens, ssd_rowkey* thr, double* draft_stats,

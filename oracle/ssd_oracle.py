@@ -45,7 +45,7 @@ __all__ = [
     "as_f64", "row_stats", "softmax", "top_f", "sigma_weights", "draft_probs",
     "sigma_row_stats", "accept_scan", "inverse_cdf", "verify_row", "verify",
     "residual_sample", "fanout", "fanout_real", "build_cache", "cache_lookup",
-    "alpha", "expected_tokens", "p_hit_row", "sample_draft", "segment_offsets",
+    "alpha", "expected_tokens", "p_hit_row", "sample_draft", "draft_sample", "segment_offsets",
 ]
 
 
@@ -466,3 +466,22 @@ def sample_draft(z: np.ndarray, tau: float, u: float, F: Optional[int] = None,
     q = draft_probs(z, tau, F, C)
     t, _, _ = inverse_cdf(q, u)
     return t
+
+
+def draft_sample(draft: np.ndarray, tau: float, u: np.ndarray, F: Optional[Sequence[int]] = None,
+                 C: float = 1.0):
+    """The draft phase for a batch ([SD-notes] The Algorithm, step 1; with F,
+    the sigma_{F_i,C} reshaping of [SSD-notes] key design 2): for every
+    sequence b and position i < K, d[b, i] is drawn from the draft
+    distribution of row i by inverse CDF with u[b, i]. Returns tokens [B, K]
+    (-1 for a row without mass) and the margins of the draws."""
+    B, K = u.shape
+    tokens = np.full((B, K), -1, dtype=np.int64)
+    margins = np.full((B, K), math.inf)
+    for b in range(B):
+        for i in range(K):
+            q = draft_probs(draft[b, i], tau, None if F is None else int(F[i]), C)
+            t, _, mg = inverse_cdf(q, float(u[b, i]))
+            tokens[b, i] = t
+            margins[b, i] = mg
+    return tokens, margins

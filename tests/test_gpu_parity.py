@@ -14,7 +14,7 @@ import pytest
 
 import oracle as O
 import workloads as W
-from gpu_utils import compare_verify, fvec, ivec, log, to_dev
+from gpu_utils import EXCUSE, compare_verify, fvec, ivec, log, to_dev
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -357,3 +357,89 @@ def test_cfg5(S, tau):
     rows = list(range(0, 256, 29))
     _, _, hits = _cache_case(S, d, F, cfg.C, rows=rows, label=f"cfg5-{tau}")
     log(f"[gpu] cfg5 tau={tau} hit rate {hits.mean():.3f}")
+
+
+# ---------------------------------------------------------------------------
+# the draft phase on the GPU (sigma-aware drafting)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V,K,B,sig", [(20000, 3, 5, True), (20000, 3, 5, False), (16385, 2, 3, True),
+                                       (300, 4, 6, True), (8192, 2, 4, False), (7, 2, 4, False),
+                                       (70000, 2, 3, True)])
+def test_draft_sample(S, dtype, V, K, B, sig):
+    log(f"[gpu] draft sample V={V} K={K} B={B} {dtype} sigma={sig}")
+    d = _random_case(V + 3 * K + B, B, K, V, dtype, 0.7, Kd=K + 1)
+    rng = np.random.default_rng(V + K)
+    u = rng.random((B, K)).astype(np.float32)
+    u[0, 0] = 0.0
+    u[-1, -1] = np.float32(0.99999994)
+    draft = to_dev(d["draft"], torch)
+    C = 0.3 if sig else 1.0
+    F = [min(f, 64, V) for f in S.ssd_fanout(40, K, 0.75, 1.0)] if sig else None
+    sg = S.sigma_from_cache(S.ssd_build_cache(draft, d["tau"], F), C) if sig else None
+    got = S.ssd_draft_sample(draft, fvec(u, torch), d["tau"], sg).cpu().numpy()
+    ref, mg = O.draft_sample(d["draft"], d["tau"], u, F, C)
+    bad = (got != ref) & ~(mg < EXCUSE)
+    assert not bad.any(), (np.argwhere(bad), got[bad], ref[bad])
+    log(f"[gpu] draft sample excused {int(((got != ref) & (mg < EXCUSE)).sum())}")
+
+
+def test_draft_sample_masked_rows(S):
+    log("[gpu] draft sample masked rows")
+    B, K, V = 3, 2, 9000
+    d = _random_case(5, B, K, V, "bf16", 1.0, Kd=K)
+    dd = W.bf16_bits_to_f32(d["draft"])
+    dd[0, 0, :] = -np.inf               # no mass: draws -1
+    dd[1, 1, ::3] = -np.inf             # masked tokens are never drawn
+    dd[2, 0, :-1] = -np.inf             # only the last token has mass
+    d["draft"] = W.f32_to_bf16_bits(dd)
+    u = np.array([[0.5, 0.0], [0.3, 0.7], [0.9, 0.1]], dtype=np.float32)
+    got = S.ssd_draft_sample(to_dev(d["draft"], torch), fvec(u, torch), 1.0).cpu().numpy()
+    ref, mg = O.draft_sample(d["draft"], 1.0, u)
+    assert got[0, 0] == -1 and got[2, 0] == V - 1 and got[1, 1] % 3 != 0
+    assert np.array_equal(got[mg >= EXCUSE], ref[mg >= EXCUSE])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("tau", [0.5, 1.0])
+def test_cfg5_expected_tokens_and_hits(S, tau):
+    """Config 5's statistical checks: the empirical mean of (accepted + 1)
+    and the empirical cache-hit rate over many uniform draws (drafts sampled
+    on the GPU from q_sigma, verified against q_sigma) fall within 4 standard
+    errors of the exact expectations mean_b E_b[tokens] and mean_b P_b(hit)
+    computed by the oracle; the closed form with the mean alpha is printed."""
+    cfg = W.get_config(5)
+    nb, reps, rounds = 32, 32, 16            # 32 rows x 32 copies x 16 rounds = 16384 samples
+    log(f"[gpu] cfg5 statistics tau={tau}: {nb} rows x {reps * rounds} draws")
+    d = W.make_inputs(cfg, tau=tau, draw_tokens=False, b_rows=range(nb))
+    F = S.ssd_fanout(cfg.n_budget, cfg.K, cfg.a_p, cfg.r)
+    K, tau32 = cfg.K, d["tau"]
+    ex = [O.p_hit_row(d["target"][b], d["draft"][b], tau32, F, cfg.C) for b in range(nb)]
+    e_tok = float(np.mean([e["e_tokens"] for e in ex]))
+    p_hit = float(np.mean([e["p_hit"] for e in ex]))
+    abar = float(np.mean([np.mean(e["alphas"]) for e in ex]))
+    closed = (1 - abar ** (K + 1)) / (1 - abar)
+    tgt = to_dev(d["target"], torch).repeat(reps, 1, 1)
+    dft = to_dev(d["draft"], torch).repeat(reps, 1, 1)
+    B = nb * reps
+    cache = S.ssd_build_cache(dft, tau32, F)
+    sg = S.sigma_from_cache(cache, cfg.C)
+    rng = np.random.default_rng(4000 + int(tau * 10))
+    lens, hits = [], []
+    for _ in range(rounds):
+        toks = S.ssd_draft_sample(dft, fvec(rng.random((B, K)), torch), tau32, sg)
+        res = S.ssd_verify(tgt, dft, toks, fvec(rng.random((B, K)), torch), fvec(rng.random(B), torch),
+                           tau32, sg)
+        look = S.ssd_cache_lookup(cache["cache_tokens"], F, res["accepted"], res["out_tokens"])
+        lens.append(res["accepted"].cpu().numpy() + 1)
+        hits.append(look["hit"].cpu().numpy())
+    lens = np.concatenate(lens).astype(np.float64)
+    hits = np.concatenate(hits).astype(np.float64)
+    assert lens.min() >= 1
+    se_t = lens.std(ddof=1) / math.sqrt(lens.size)
+    se_h = math.sqrt(max(p_hit * (1 - p_hit), 1e-12) / hits.size)
+    log(f"[gpu] cfg5 tau={tau}: mean tokens {lens.mean():.4f} vs exact {e_tok:.4f} (4 SE {4 * se_t:.4f}); "
+        f"closed form with mean alpha {abar:.4f}: {closed:.4f}; hit rate {hits.mean():.4f} vs exact "
+        f"{p_hit:.4f} (4 SE {4 * se_h:.4f})")
+    assert abs(lens.mean() - e_tok) <= 4 * se_t
+    assert abs(hits.mean() - p_hit) <= 4 * se_h

@@ -98,7 +98,7 @@ def test_verify_argument_checks():
     assert _verify(sigma=ctypes.byref(sig)) == -1      # C outside [0, 1]
     sig = S._Sigma(0.5, None, 0x1000)
     assert _verify(sigma=ctypes.byref(sig)) == -1
-    assert b"tau" in S.lib().ssd_last_error() or True
+    assert b"thr" in S.lib().ssd_last_error()
 
 
 def test_build_cache_and_lookup_argument_checks():
@@ -127,6 +127,32 @@ def test_build_cache_and_lookup_argument_checks():
     r = L.ssd_residual_sample(FAKE, 0, None, 0, S.SSD_BF16, 2, 3, 100, 1.0, FAKE, ctypes.byref(sig),
                               FAKE, FAKE, None, FAKE, 1 << 30, None)
     assert r == -1                                      # sigma without draft
+
+
+def test_draft_sample_argument_checks():
+    L = S.lib()
+
+    def call(**kw):
+        a = dict(d=FAKE, db=0, dtype=S.SSD_BF16, B=2, K=3, V=100, tau=1.0, sigma=None, u=FAKE, out=FAKE,
+                 ws=FAKE, wsz=1 << 30)
+        a.update(kw)
+        return L.ssd_draft_sample(a["d"], a["db"], a["dtype"], a["B"], a["K"], a["V"], a["tau"], a["sigma"],
+                                  a["u"], a["out"], a["ws"], a["wsz"], None)
+
+    assert call(tau=0.0) == -1
+    assert call(tau=float("inf")) == -1
+    assert call(dtype=7) == -2
+    assert call(K=0) == -1 and call(K=65) == -1
+    assert call(u=None) == -1 and call(out=None) == -1 and call(d=None) == -1
+    assert call(db=-1) == -1
+    assert call(ws=None, wsz=0) == -3
+    assert call(wsz=16) == -3
+    sig = S._Sigma(-0.1, 0x1000, None)
+    assert call(sigma=ctypes.byref(sig)) == -1
+    sig = S._Sigma(0.5, None, None)
+    assert call(sigma=ctypes.byref(sig)) == -1 and b"thr" in L.ssd_last_error()
+    assert S.ssd_draft_sample_workspace_size(2, 3, 100, S.SSD_BF16) > 0
+    assert S.ssd_draft_sample_workspace_size(0, 3, 100, S.SSD_BF16) == 0
 
 
 def test_oracle_not_imported_by_product():

@@ -337,6 +337,27 @@ def test_inverse_cdf_edges():
     assert O.inverse_cdf(np.zeros(4), 0.5)[0] == -1
 
 
+def test_draft_sample_distribution():
+    # Drafts over a stratified grid of u reproduce q (plain) and q_sigma: the
+    # sigma form written out by hand here (top-2 by logit get weight C).
+    z = np.log(np.array([[0.30, 0.05, 0.25, 0.10, 0.20, 0.10]], dtype=np.float64)).astype(np.float32)
+    draft = np.broadcast_to(z, (1, 1, 6))
+    N = 20000
+    u = ((np.arange(N) + 0.5) / N).reshape(N, 1)
+    for F, C in ((None, 1.0), ([2], 0.3), ([2], 0.0), ([6], 0.5)):
+        toks, _ = O.draft_sample(np.broadcast_to(draft, (N, 1, 6)), 1.0, u, F, C)
+        hist = np.bincount(toks[:, 0], minlength=6) / N
+        w = np.exp(z[0].astype(np.float64))
+        if F is not None:
+            w[[0, 2]] *= C if F[0] == 2 else 1.0
+            if F[0] == 6:
+                w = w * C
+        q = w / w.sum()
+        assert np.max(np.abs(hist - q)) <= 1.0 / N + 1e-12, (F, C, hist, q)
+    toks, _ = O.draft_sample(np.full((1, 1, 4), -np.inf, dtype=np.float32), 1.0, np.array([[0.5]]))
+    assert toks[0, 0] == -1
+
+
 def test_zero_residual_falls_back_to_p():
     # identical target and draft rows, drafted token masked in both: p = q = 0 -> reject,
     # the residual is empty, the draw comes from p of that row

@@ -14,15 +14,17 @@ import os
 from typing import Optional, Sequence
 
 __all__ = ["SSD_F32", "SSD_BF16", "SsdError", "lib", "ssd_fanout", "ssd_verify",
-           "ssd_residual_sample", "ssd_build_cache", "ssd_cache_lookup", "Sigma",
+           "ssd_residual_sample", "ssd_build_cache", "ssd_cache_lookup", "ssd_draft_sample", "Sigma",
            "ssd_verify_workspace_size", "ssd_residual_workspace_size",
-           "ssd_build_cache_workspace_size", "EXPORTS", "library_path"]
+           "ssd_build_cache_workspace_size", "ssd_draft_sample_workspace_size", "EXPORTS",
+           "library_path"]
 
 SSD_F32, SSD_BF16 = 0, 1
 SSD_MAX_K, SSD_MAX_F = 64, 64
 EXPORTS = ("ssd_last_error", "ssd_fanout", "ssd_verify_workspace_size", "ssd_verify",
            "ssd_residual_workspace_size", "ssd_residual_sample",
-           "ssd_build_cache_workspace_size", "ssd_build_cache", "ssd_cache_lookup")
+           "ssd_build_cache_workspace_size", "ssd_build_cache", "ssd_cache_lookup",
+           "ssd_draft_sample_workspace_size", "ssd_draft_sample")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -60,6 +62,9 @@ _SIGS = {
     "ssd_build_cache": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _i32, _i32, _i32, _f32, _vp,
                                        _vp, _vp, _vp, _vp, _sz, _vp]),
     "ssd_cache_lookup": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "ssd_draft_sample_workspace_size": (_sz, [_i32, _i32, _i32, ctypes.c_int]),
+    "ssd_draft_sample": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _i32, _i32, _i32, _f32, _vp, _vp, _vp,
+                                        _vp, _sz, _vp]),
 }
 
 _lib = None
@@ -252,6 +257,33 @@ def ssd_residual_sample(target, draft, row, u, tau: float, sigma: Optional[Sigma
     _check(lib().ssd_residual_sample(tp, tb, dp, db, dt, B, K, V, float(tau), rp, sig, up,
                                      tok.data_ptr(), mass.data_ptr(), ws, wsz, _stream(stream)))
     return {"tokens": tok, "mass": mass}
+
+
+def ssd_draft_sample_workspace_size(B, K, V, dtype) -> int:
+    return int(lib().ssd_draft_sample_workspace_size(B, K, V, dtype))
+
+
+def ssd_draft_sample(draft, u, tau: float, sigma: Optional[Sigma] = None, *, out=None, stream=None):
+    """Drafted tokens [B, K] int32: d[b, i] drawn from softmax(draft row i / tau),
+    or its sigma form, by inverse CDF with u [B, K]."""
+    torch = _torch()
+    if u.dim() != 2:
+        raise ValueError("u must be [B, K]")
+    B, K = int(u.shape[0]), int(u.shape[1])
+    V = int(draft.shape[2])
+    dt = _dtype_code(draft)
+    if draft.shape[0] != B:
+        raise ValueError("draft batch size differs from u")
+    dp, db = _logits(draft, "draft", K)
+    up = _dev(u, torch.float32, (B, K), "u")
+    if out is None:
+        out = torch.empty((B, K), dtype=torch.int32, device=draft.device)
+    _dev(out, torch.int32, (B, K), "out")
+    sig = ctypes.byref(sigma._c()) if sigma is not None else None
+    ws, wsz = _workspace(ssd_draft_sample_workspace_size(B, K, V, dt), draft.device, ("sample", B, K, V, dt), stream)
+    _check(lib().ssd_draft_sample(dp, db, dt, B, K, V, float(tau), sig, up, out.data_ptr(), ws, wsz,
+                                  _stream(stream)))
+    return out
 
 
 def ssd_build_cache(draft, tau: float, F: Sequence[int], *, out: Optional[dict] = None,

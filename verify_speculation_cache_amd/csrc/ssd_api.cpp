@@ -305,6 +305,45 @@ SSD_API int ssd_residual_sample(const void* target_logits, int64_t target_bstrid
   return hip_status(launch_resid(r, dtype, sig, stream), "residual launch");
 }
 
+SSD_API size_t ssd_draft_sample_workspace_size(int32_t B, int32_t K, int32_t V, int dtype) {
+  if (check_shape(B, K, V) != SSD_OK || !dtype_ok(dtype)) return 0;
+  return SampleWs(int64_t(B) * K, chunks_per_row(V)).total;
+}
+
+SSD_API int ssd_draft_sample(const void* draft_logits, int64_t draft_bstride, int dtype,
+                             int32_t B, int32_t K, int32_t V, float tau, const ssd_sigma* sigma,
+                             const float* u, int32_t* tokens_out,
+                             void* workspace, size_t ws_bytes, void* hip_stream) {
+  int st;
+  if (!dtype_ok(dtype)) return fail(SSD_EDTYPE, "unknown dtype %d", dtype);
+  if ((st = check_shape(B, K, V)) != SSD_OK) return st;
+  if ((st = check_tau(tau)) != SSD_OK) return st;
+  if (sigma != nullptr && (!(sigma->C >= 0.0f && sigma->C <= 1.0f) || sigma->thr == nullptr))
+    return fail(SSD_EINVAL, "sigma needs C in [0, 1] and thr");
+  if (!draft_logits || !u || !tokens_out) return fail(SSD_EINVAL, "a required pointer is NULL");
+  if (draft_bstride < 0) return fail(SSD_EINVAL, "negative batch stride");
+  const int64_t S = chunks_per_row(V);
+  const SampleWs sw(int64_t(B) * K, S);
+  if ((st = check_ws(workspace, ws_bytes, sw.total)) != SSD_OK) return st;
+  if ((st = check_grid(int64_t(B) * K * S)) != SSD_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  SampleArgs a{};
+  a.draft = draft_logits;
+  a.db = draft_bstride;
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.S = int(S);
+  a.c32 = float(kLog2e / double(tau));
+  a.C = sigma ? sigma->C : 1.0f;
+  a.thr = sigma ? sigma->thr : nullptr;
+  a.u = u;
+  a.tok_out = tokens_out;
+  a.part = reinterpret_cast<RowPartial*>(ws + sw.part);
+  a.cnt = reinterpret_cast<uint32_t*>(ws + sw.cnt);
+  return hip_status(launch_sample(a, dtype, as_stream(hip_stream)), "sample launch");
+}
+
 SSD_API int ssd_build_cache(const void* draft_logits, int64_t draft_bstride, int dtype,
                             int32_t B, int32_t K, int32_t V, float tau, const int32_t* F,
                             int32_t* cache_tokens, ssd_rowkey* thr, double* draft_stats,

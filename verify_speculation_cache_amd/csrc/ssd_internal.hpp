@@ -124,6 +124,19 @@ struct CacheArgs {
   uint32_t* cnt;        // [B, K+1] (kCntStride apart)
 };
 
+struct SampleArgs {
+  const void* draft;
+  int64_t db;
+  int B, K, V, S;
+  float c32;
+  float C;                  // sigma weight of the top-F members (1: plain softmax)
+  const ssd_rowkey* thr;    // [B, K+1] sigma thresholds (nullptr: plain)
+  const float* u;           // [B, K]
+  int32_t* tok_out;         // [B, K]
+  RowPartial* part;         // [B*K, S]
+  uint32_t* cnt;            // [B*K] (kCntStride apart)
+};
+
 struct LookupArgs {
   const int32_t* cache_tokens;
   int B, K, sumF;
@@ -173,10 +186,20 @@ struct CacheWs {
   }
 };
 
+struct SampleWs {
+  size_t part, cnt, total;
+  SampleWs(int64_t rows, int64_t S) {
+    part = 0;
+    cnt = align256(part + sizeof(RowPartial) * rows * S);
+    total = align256(cnt + sizeof(uint32_t) * kCntStride * rows);
+  }
+};
+
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_stats(const StatsArgs& a, int dtype, hipStream_t st);
 hipError_t launch_resid(const ResidArgs& a, int dtype, bool sigma, hipStream_t st);
 hipError_t launch_cache(const CacheArgs& a, int dtype, hipStream_t st);
 hipError_t launch_lookup(const LookupArgs& a, hipStream_t st);
+hipError_t launch_sample(const SampleArgs& a, int dtype, hipStream_t st);
 
 }  // namespace ssd

@@ -21,7 +21,7 @@
 // If rounding leaves no crossing inside the chosen chunk the last token of
 // that chunk with positive mass is taken. With no residual mass at all the
 // draw uses p (e_t) instead; with no mass in p either the token is -1.
-#include "ssd_device.hpp"
+#include "ssd_cdf.hpp"
 
 namespace ssd {
 
@@ -68,14 +68,10 @@ __global__ __launch_bounds__(kThreads) void k_resid(ResidArgs a) {
   constexpr int PV = Dt<DT>::kPerVec;
   constexpr int NV = kPerThread / PV;
   __shared__ double sm_pair[8];
-  __shared__ int sm_i[4];
   __shared__ int sm_last;
-  __shared__ double sm_scan[4];
-  __shared__ int sm_pick[4];
   __shared__ double sm_pre, sm_target;
-  __shared__ int sm_c, sm_useres, sm_tok, sm_lastpos;
-  __shared__ uint4 sm_run[2][NV];   // the crossing thread's 32 target / draft entries
-  __shared__ double sm_base;
+  __shared__ int sm_c, sm_useres;
+  __shared__ PickLds<DT, 2> sm_pk;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = blockIdx.x / a.S;
@@ -180,34 +176,12 @@ __global__ __launch_bounds__(kThreads) void k_resid(ResidArgs a) {
     int cs = -1;
     double pre = 0.0;
     if (tot > 0.0) {
-      double base = 0.0;
-      int lastpos = -1;
-      double lastpre = 0.0;
-      for (int g = 0; g < a.S && cs < 0; g += 64) {
-        const int cc = g + lane;
-        double mc;
-        if (g == 0) mc = useres ? r0 : t0;
-        else mc = cc < a.S ? bits_d(dev_load(cmw + cc * 2 + (useres ? 0 : 1))) : 0.0;
-        const double incl = wave_incl_scan_d(mc, lane);
-        const double prev = __shfl_up(incl, 1);   // all lanes shuffle (lane 0 reads itself)
-        const double excl = base + (lane > 0 ? prev : 0.0);
-        const uint64_t crossing = __ballot(cc < a.S && base + incl > target);
-        const uint64_t pos = __ballot(cc < a.S && mc > 0.0);
-        if (crossing) {
-          const int l = __ffsll((unsigned long long)crossing) - 1;
-          cs = g + l;
-          pre = __shfl(excl, l);
-        } else if (pos) {
-          const int l = 63 - __clzll((long long)pos);
-          lastpos = g + l;
-          lastpre = __shfl(excl, l);
-        }
-        base += __shfl(incl, 63);
-      }
-      if (cs < 0) {   // rounding left u*Z past the last crossing: last chunk with mass
-        cs = lastpos;
-        pre = lastpre;
-      }
+      chunk_crossing(
+          [&](int cc, int g) -> double {
+            if (g == 0) return useres ? r0 : t0;
+            return cc < a.S ? bits_d(dev_load(cmw + cc * 2 + (useres ? 0 : 1))) : 0.0;
+          },
+          a.S, target, lane, cs, pre);
     }
     if (lane == 0) {
       sm_c = cs;
@@ -224,72 +198,11 @@ __global__ __launch_bounds__(kThreads) void k_resid(ResidArgs a) {
     if (!sm_useres) k.plain = true;
     const int64_t c0 = int64_t(cs) * kChunk;
     // each thread owns 32 consecutive tokens of the chunk
-    ChunkVecs<DT, false> vt, vd;
-    load_pair(vt, rowT, vd, rowD, c0, a.V, tid);
-    const int i0 = int(c0) + tid * kPerThread;
-    double tot = 0.0;
-    int lastpos = -1;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      float xt[PV], xd[PV];
-      vt.get(j, xt);
-      vd.get(j, xd);
-#pragma unroll
-      for (int e = 0; e < PV; ++e) {
-        const float v = resid_elem<SIG>(k, xt[e], xd[e], i0 + j * PV + e);
-        tot += double(v);
-        if (v > 0.0f) lastpos = j * PV + e;
-      }
-    }
-    // exclusive scan of thread totals (thread order = token order)
-    const double incl_w = wave_incl_scan_d(tot, lane);
-    if (lane == 63) sm_scan[w] = incl_w;
-    __syncthreads();
-    double wbase = 0.0;
-    for (int ww = 0; ww < w; ++ww) wbase += sm_scan[ww];
-    const double base = sm_pre + wbase + (incl_w - tot);
-    const double target = sm_target;
-    // first thread whose running mass crosses u * Z
-    const uint64_t cm = __ballot((base + tot) > target);
-    if (lane == 0) sm_pick[w] = cm ? (w * 64 + __ffsll((unsigned long long)cm) - 1) : 0x7FFFFFFF;
-    __syncthreads();
-    const int first = min(min(sm_pick[0], sm_pick[1]), min(sm_pick[2], sm_pick[3]));
-    if (first != 0x7FFFFFFF) {
-      // the crossing thread hands its run to wave 0 (one entry per lane),
-      // which rescans it in parallel from the thread's base
-      if (tid == first) {
-#pragma unroll
-        for (int q = 0; q < NV; ++q) {
-          sm_run[0][q] = vt.raw[q];
-          sm_run[1][q] = vd.raw[q];
-        }
-        sm_base = base;
-        sm_lastpos = lastpos;
-      }
-      __syncthreads();
-      if (w == 0) {
-        const int q = lane & 31;
-        const T* rt = reinterpret_cast<const T*>(&sm_run[0][0]);
-        const T* rd = reinterpret_cast<const T*>(&sm_run[1][0]);
-        const int f0 = int(c0) + first * kPerThread;
-        const float v = resid_elem<SIG>(k, Dt<DT>::to_f(rt[q]), Dt<DT>::to_f(rd[q]), f0 + q);
-        const double cum = sm_base + wave_incl_scan_d(lane < 32 ? double(v) : 0.0, lane);
-        const uint64_t cr = __ballot(lane < 32 && cum > target);
-        // if rounding keeps the rescan at or below u * Z through the run, the
-        // crossing is at the run's end: its last token with mass
-        if (lane == 0) sm_tok = f0 + (cr ? __ffsll((unsigned long long)cr) - 1 : sm_lastpos);
-      }
-    } else {
-      // rounding left u*Z past this chunk's scan: last token with mass
-      int best = lastpos >= 0 ? i0 + lastpos : -1;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) best = max(best, __shfl_xor(best, o));
-      if (lane == 0) sm_i[w] = best;
-      __syncthreads();
-      if (tid == 0) sm_tok = max(max(sm_i[0], sm_i[1]), max(sm_i[2], sm_i[3]));
-    }
-    __syncthreads();
-    tok = sm_tok;
+    ChunkVecs<DT, false> cv[2];
+    load_pair(cv[0], rowT, cv[1], rowD, c0, a.V, tid);
+    tok = chunk_pick<DT, 2>(cv, c0, sm_pre, sm_target,
+                            [&](const float (&x)[2], int idx) { return resid_elem<SIG>(k, x[0], x[1], idx); },
+                            sm_pk);
   }
   if (tid == 0) a.tok_out[int64_t(b) * a.tok_stride + (a.tok_at_a ? inf.a : 0)] = tok;
 }

@@ -1,0 +1,180 @@
+// Drafting from the sigma-reshaped draft distribution.
+//
+// SAGUARO reshapes the draft distribution before sampling: the top-F tokens
+// of draft row k (the tokens the cache prepares for) keep weight C, all
+// others weight 1, and the drafted token d_{k+1} is drawn from the
+// renormalised result (papernotes.org "Speculative Speculative Decoding",
+// key design 2). The verifier then uses the same q_sigma, which keeps the
+// output distribution exact (brentwoodlivery.com "Speculative decoding",
+// Derivation of Acceptance Criterion). Without sigma the draw is from the
+// plain softmax of draft row k at temperature tau.
+//
+// The draw is by inverse CDF in token-index order: the smallest v whose
+// running mass exceeds u * Z. One workgroup per (batch row b, position i,
+// 8192-chunk c) sums the chunk's weighted mass against the chunk's own max;
+// the last workgroup of row (b, i) rescales the chunk masses to the row max,
+// finds the crossing chunk and picks the token inside it. A row without mass
+// (all logits -inf) draws -1.
+#include "ssd_cdf.hpp"
+
+namespace ssd {
+
+struct SigmaTest {
+  float val;   // threshold as a logit value (NaN: no member)
+  int32_t idx;
+  float C;
+  // sigma weight of token idx with logit x: C for members (key above the
+  // threshold, or equal with index at most idx), else 1; bitwise tests keep
+  // it branch-free
+  __device__ float weight(float x, int i) const {
+    const bool mem = (x > val) | ((x == val) & (i <= idx));
+    return mem ? C : 1.0f;
+  }
+};
+
+template <int DT, bool SIG>
+__device__ __forceinline__ SigmaTest sigma_test(const SampleArgs& a, int b, int i) {
+  SigmaTest t{__builtin_nanf(""), -1, 1.0f};
+  if (SIG) {
+    const ssd_rowkey tk = a.thr[int64_t(b) * (a.K + 1) + i];
+    t.val = tk.key > key_of<DT>(__builtin_inff()) ? __builtin_nanf("") : value_of_key<DT>(tk.key);
+    t.idx = tk.idx;
+    t.C = a.C;
+  }
+  return t;
+}
+
+template <int DT, bool SIG>
+__global__ __launch_bounds__(kThreads) void k_sample(SampleArgs a) {
+  using T = typename Dt<DT>::T;
+  constexpr int PV = Dt<DT>::kPerVec;
+  constexpr int NV = kPerThread / PV;
+  __shared__ float sm_f[4];
+  __shared__ double sm_s[4];
+  __shared__ int sm_last;
+  __shared__ int sm_c;
+  __shared__ double sm_pre, sm_target;
+  __shared__ float sm_piv;
+  __shared__ PickLds<DT, 1> sm_pk;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t rowid = blockIdx.x / a.S;
+  const int c = int(blockIdx.x - rowid * a.S);
+  const int b = int(rowid / a.K);
+  const int i = int(rowid - int64_t(b) * a.K);
+  const T* row = static_cast<const T*>(a.draft) + int64_t(b) * a.db + int64_t(i) * a.V;
+  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+  const SigmaTest sg = sigma_test<DT, SIG>(a, b, i);
+
+  // ---------------- phase A: chunk max and weighted chunk mass ----------------
+  {
+    const int64_t c0 = int64_t(c) * kChunk;
+    ChunkVecs<DT, true> cv;
+    cv.load(row, c0, a.V, aligned, tid);
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      float v[PV];
+      cv.get(j, v);
+#pragma unroll
+      for (int e = 0; e < PV; ++e) m = fmaxf(m, v[e]);
+    }
+    m = wave_max_u(m);
+    if (lane == 0) sm_f[w] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(sm_f[0], sm_f[1]), fmaxf(sm_f[2], sm_f[3]));
+    const float pc = pivot_of(m);
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      float v[PV];
+      cv.get(j, v);
+      const int i0 = int(c0) + ChunkVecs<DT, true>::local(tid, j);
+#pragma unroll
+      for (int e = 0; e < PV; ++e) {
+        const float ex = __builtin_amdgcn_exp2f((v[e] - pc) * a.c32);
+        sum += SIG ? sg.weight(v[e], i0 + e) * ex : ex;
+      }
+    }
+    const double ws = wave_sum_u(double(sum));
+    if (lane == 0) sm_s[w] = ws;
+    __syncthreads();
+    if (tid == 0) {
+      uint64_t* wp = reinterpret_cast<uint64_t*>(a.part + rowid * a.S + c);
+      dev_store(wp, pack2(m, 0.0f));
+      dev_store(wp + 1, dbits((sm_s[0] + sm_s[1]) + (sm_s[2] + sm_s[3])));
+    }
+  }
+  if (!arrive_last(&a.cnt[rowid * kCntStride], uint32_t(a.S), &sm_last)) return;
+
+  // ---------------- phase B: last workgroup of row (b, i) ----------------
+  if (w == 0) {
+    const uint64_t* pw = reinterpret_cast<const uint64_t*>(a.part + rowid * a.S);
+    // chunk partials (the first 64 stay in registers: one round trip for S <= 64)
+    float m0 = -__builtin_inff();
+    double s0 = 0.0;
+    float mx = -__builtin_inff();
+    for (int g = 0; g < a.S; g += 64) {
+      const int cc = g + lane;
+      const float mc = cc < a.S ? lo_f(dev_load(pw + cc * 2)) : -__builtin_inff();
+      if (g == 0) {
+        m0 = mc;
+        s0 = cc < a.S ? bits_d(dev_load(pw + cc * 2 + 1)) : 0.0;
+      }
+      mx = fmaxf(mx, mc);
+    }
+    const float P = pivot_of(wave_max(mx));
+    auto mass = [&](int cc, int g) -> double {
+      float mc = m0;
+      double sc = s0;
+      if (g != 0) {
+        mc = cc < a.S ? lo_f(dev_load(pw + cc * 2)) : -__builtin_inff();
+        sc = cc < a.S ? bits_d(dev_load(pw + cc * 2 + 1)) : 0.0;
+      }
+      return sc > 0.0 ? sc * rescale(pivot_of(mc), P, a.c32) : 0.0;
+    };
+    double Z = 0.0;
+    for (int g = 0; g < a.S; g += 64) Z += __shfl(wave_incl_scan_d(mass(g + lane, g), lane), 63);
+    const double target = double(a.u[rowid]) * Z;
+    int cs = -1;
+    double pre = 0.0;
+    if (Z > 0.0) chunk_crossing(mass, a.S, target, lane, cs, pre);
+    if (lane == 0) {
+      sm_c = cs;
+      sm_pre = pre;
+      sm_target = target;
+      sm_piv = P;
+    }
+  }
+  __syncthreads();
+  const int cs = sm_c;
+  int tok = -1;
+  if (cs >= 0) {
+    const int64_t c0 = int64_t(cs) * kChunk;
+    const float P = sm_piv, c32 = a.c32;
+    ChunkVecs<DT, false> cv[1];
+    cv[0].load(row, c0, a.V, aligned, tid);
+    tok = chunk_pick<DT, 1>(cv, c0, sm_pre, sm_target,
+                            [&](const float (&x)[1], int idx) {
+                              const float ex = __builtin_amdgcn_exp2f((x[0] - P) * c32);
+                              return SIG ? sg.weight(x[0], idx) * ex : ex;
+                            },
+                            sm_pk);
+  }
+  if (tid == 0) a.tok_out[rowid] = tok;
+}
+
+hipError_t launch_sample(const SampleArgs& a, int dtype, hipStream_t st) {
+  const unsigned grid = unsigned(int64_t(a.B) * a.K * a.S);
+  const bool sig = a.thr != nullptr;
+  if (dtype == SSD_BF16) {
+    if (sig) hipLaunchKernelGGL((k_sample<1, true>), dim3(grid), dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((k_sample<1, false>), dim3(grid), dim3(kThreads), 0, st, a);
+  } else {
+    if (sig) hipLaunchKernelGGL((k_sample<0, true>), dim3(grid), dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((k_sample<0, false>), dim3(grid), dim3(kThreads), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ssd
