@@ -155,6 +155,26 @@ SSD_API int ssd_residual_sample(const void* target_logits, int64_t target_bstrid
                                 int32_t* token_out, float* mass_out,
                                 void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* Bytes of workspace ssd_verify_greedy needs. */
+SSD_API size_t ssd_verify_greedy_workspace_size(int32_t B, int32_t K, int32_t V, int dtype);
+
+/* Greedy verification ([SD-why] How it works, Fix 2: the drafted token is
+ * kept iff it is also the target's argmax): for each batch row b, d_i =
+ * draft_tokens[b,i] is kept iff it is the argmax of target row i (largest
+ * logit, ties to the smaller index); the scan stops at the first mismatch a,
+ * and the argmax of target row a (the correction, or the bonus from row K
+ * when a = K) is emitted. A target row with no finite logit has no argmax:
+ * its drafted token is rejected and the emitted token is -1. No temperature
+ * and no draft logits.
+ *   target_logits device [B, K+1, V]; draft_tokens device int32 [B, K]
+ *   accepted device int32 [B]: a in 0..K, or -1 for a flagged row
+ *   out_tokens device int32 [B, K+1]: d_1..d_a, argmax of row a, then -1
+ * One kernel launch on hip_stream. */
+SSD_API int ssd_verify_greedy(const void* target_logits, int64_t target_bstride, int dtype,
+                              int32_t B, int32_t K, int32_t V, const int32_t* draft_tokens,
+                              int32_t* accepted, int32_t* out_tokens,
+                              void* workspace, size_t ws_bytes, void* hip_stream);
+
 /* Bytes of workspace ssd_draft_sample needs. */
 SSD_API size_t ssd_draft_sample_workspace_size(int32_t B, int32_t K, int32_t V, int dtype);
 

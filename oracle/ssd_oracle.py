@@ -46,6 +46,7 @@ __all__ = [
     "sigma_row_stats", "accept_scan", "inverse_cdf", "verify_row", "verify",
     "residual_sample", "fanout", "fanout_real", "build_cache", "cache_lookup",
     "alpha", "expected_tokens", "p_hit_row", "sample_draft", "draft_sample", "segment_offsets",
+    "argmax_token", "verify_greedy",
 ]
 
 
@@ -485,3 +486,41 @@ def draft_sample(draft: np.ndarray, tau: float, u: np.ndarray, F: Optional[Seque
             tokens[b, i] = t
             margins[b, i] = mg
     return tokens, margins
+
+
+# ---------------------------------------------------------------------------
+# greedy verification   [SD-why] How it works, Fix 2
+# ---------------------------------------------------------------------------
+def argmax_token(z: np.ndarray) -> int:
+    """The target's greedy token: the largest logit, ties to the smaller index
+    (the same order as top_f). A row with no finite logit has none: -1."""
+    zf = as_f64(z)
+    if not np.any(zf > -math.inf):
+        return -1
+    return int(top_f(z, 1)[0])
+
+
+def verify_greedy(target: np.ndarray, tokens: np.ndarray) -> dict:
+    """Greedy verification: keep drafted token d_i iff it is the target's
+    argmax at position i, stop at the first mismatch, and emit the target's
+    argmax at the stopping position (the correction, or the bonus from row K
+    when all K are kept). Temperature plays no part. A row with a drafted
+    token outside [0, V) is flagged (accepted -1, all outputs -1).
+    Returns accepted [B] and out_tokens [B, K+1]."""
+    B, K = tokens.shape
+    V = target.shape[-1]
+    acc = np.full(B, -1, dtype=np.int64)
+    out = np.full((B, K + 1), -1, dtype=np.int64)
+    for b in range(B):
+        if any(int(d) < 0 or int(d) >= V for d in tokens[b]):
+            continue
+        g = [argmax_token(target[b, i]) for i in range(K + 1)]
+        a = K
+        for i in range(K):
+            if int(tokens[b, i]) != g[i]:
+                a = i
+                break
+        acc[b] = a
+        out[b, :a] = tokens[b, :a]
+        out[b, a] = g[a]
+    return {"accepted": acc, "out_tokens": out}

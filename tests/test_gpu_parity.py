@@ -443,3 +443,50 @@ def test_cfg5_expected_tokens_and_hits(S, tau):
         f"{p_hit:.4f} (4 SE {4 * se_h:.4f})")
     assert abs(lens.mean() - e_tok) <= 4 * se_t
     assert abs(hits.mean() - p_hit) <= 4 * se_h
+
+
+# ---------------------------------------------------------------------------
+# greedy verification
+# ---------------------------------------------------------------------------
+def _greedy_case(seed, B, K, V, dtype, ties=False):
+    rng = np.random.default_rng(seed)
+    t = (rng.standard_normal((B, K + 1, V)) * 2.5).astype(np.float32)
+    if ties:
+        t = np.round(t).astype(np.float32)   # many equal maxima: the smaller index wins
+    if dtype == "bf16":
+        t = W.bf16_bits_to_f32(W.f32_to_bf16_bits(t))
+    g = np.array([[O.argmax_token(t[b, i]) for i in range(K)] for b in range(B)], dtype=np.int32).reshape(B, K)
+    toks = np.where(rng.random((B, K)) < 0.75, g, rng.integers(0, max(V, 1), (B, K))).astype(np.int32)
+    tt = W.f32_to_bf16_bits(t) if dtype == "bf16" else t
+    return tt, toks
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V,K,B,ties", [(20000, 4, 6, False), (20000, 4, 6, True), (16385, 2, 3, True),
+                                        (40000, 3, 4, True), (7, 3, 5, True), (1, 2, 3, False),
+                                        (100, 64, 2, True)])
+def test_verify_greedy(S, dtype, V, K, B, ties):
+    log(f"[gpu] greedy V={V} K={K} B={B} {dtype} ties={ties}")
+    t, toks = _greedy_case(V + K + B, B, K, V, dtype, ties)
+    if B >= 3 and V > 4:
+        t[1, 0] = W.f32_to_bf16_bits(np.full(V, -np.inf, np.float32)) if dtype == "bf16" else -np.inf
+        toks[2, K - 1] = V + 5                          # flagged row
+    got = S.ssd_verify_greedy(to_dev(t, torch), ivec(toks, torch))
+    torch.cuda.synchronize()
+    ref = O.verify_greedy(t, toks)
+    assert np.array_equal(got["accepted"].cpu().numpy(), ref["accepted"])
+    assert np.array_equal(got["out_tokens"].cpu().numpy(), ref["out_tokens"])
+
+
+def test_verify_greedy_cfg2(S):
+    cfg = W.get_config(2)
+    log("[gpu] greedy cfg2")
+    d = W.make_inputs(cfg, draw_tokens=False)
+    g = np.array([[O.argmax_token(d["target"][b, i]) for i in range(cfg.K)] for b in range(cfg.B)],
+                 dtype=np.int32)
+    rng = np.random.default_rng(22)
+    toks = np.where(rng.random(g.shape) < 0.8, g, rng.integers(0, cfg.V, g.shape)).astype(np.int32)
+    got = S.ssd_verify_greedy(to_dev(d["target"], torch), ivec(toks, torch))
+    ref = O.verify_greedy(d["target"], toks)
+    assert np.array_equal(got["accepted"].cpu().numpy(), ref["accepted"])
+    assert np.array_equal(got["out_tokens"].cpu().numpy(), ref["out_tokens"])

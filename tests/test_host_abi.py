@@ -155,6 +155,23 @@ def test_draft_sample_argument_checks():
     assert S.ssd_draft_sample_workspace_size(0, 3, 100, S.SSD_BF16) == 0
 
 
+def test_verify_greedy_argument_checks():
+    L = S.lib()
+
+    def call(**kw):
+        a = dict(t=FAKE, tb=0, dtype=S.SSD_F32, B=2, K=3, V=100, tok=FAKE, acc=FAKE, out=FAKE, ws=FAKE, wsz=1 << 30)
+        a.update(kw)
+        return L.ssd_verify_greedy(a["t"], a["tb"], a["dtype"], a["B"], a["K"], a["V"], a["tok"], a["acc"],
+                                   a["out"], a["ws"], a["wsz"], None)
+
+    assert call(dtype=5) == -2
+    assert call(B=0) == -1 and call(K=65) == -1 and call(V=0) == -1
+    assert call(t=None) == -1 and call(tok=None) == -1 and call(acc=None) == -1 and call(out=None) == -1
+    assert call(tb=-4) == -1
+    assert call(ws=None, wsz=0) == -3 and call(wsz=8) == -3
+    assert S.ssd_verify_greedy_workspace_size(2, 3, 100, S.SSD_F32) > 0
+
+
 def test_oracle_not_imported_by_product():
     import sys
     src_dir = os.path.join(ROOT, "verify_speculation_cache_amd")

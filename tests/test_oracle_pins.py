@@ -358,6 +358,35 @@ def test_draft_sample_distribution():
     assert toks[0, 0] == -1
 
 
+def test_greedy_is_the_zero_temperature_limit():
+    # With well separated target logits, sampling verification at a tiny
+    # temperature has one-hot p: it keeps d iff d is the argmax, and the
+    # residual max(0, p - q) (or p_K) puts all mass on the argmax. So the
+    # sampling oracle at tau -> 0 must reproduce greedy verification.
+    rng = np.random.default_rng(7)
+    B, K, V = 40, 4, 12
+    target = rng.permuted(np.tile(np.arange(V, dtype=np.float32) * 3.0, (B, K + 1, 1)), axis=2)
+    draft = (target[:, :K] + rng.standard_normal((B, K, V)).astype(np.float32)).astype(np.float32)
+    g = np.argmax(target, axis=2)
+    tokens = np.where(rng.random((B, K)) < 0.7, g[:, :K], rng.integers(0, V, (B, K))).astype(np.int32)
+    gr = O.verify_greedy(target, tokens)
+    sm = O.verify(target, draft, tokens, rng.random((B, K)).astype(np.float32),
+                  rng.random(B).astype(np.float32), 1e-3)
+    assert np.array_equal(gr["accepted"], sm["accepted"])
+    assert np.array_equal(gr["out_tokens"], sm["out_tokens"])
+    # the argmax order and the degenerate rows
+    assert O.argmax_token(np.array([1.0, 3.0, 3.0, 2.0], dtype=np.float32)) == 1
+    assert O.argmax_token(np.full(5, -np.inf, dtype=np.float32)) == -1
+    t = np.zeros((1, 3, 4), dtype=np.float32)
+    t[0, :, 2] = 1.0
+    r = O.verify_greedy(t, np.array([[2, 0]], dtype=np.int32))
+    assert r["accepted"][0] == 1 and list(r["out_tokens"][0]) == [2, 2, -1]
+    r = O.verify_greedy(t, np.array([[2, 2]], dtype=np.int32))
+    assert r["accepted"][0] == 2 and list(r["out_tokens"][0]) == [2, 2, 2]
+    r = O.verify_greedy(t, np.array([[2, 9]], dtype=np.int32))
+    assert r["accepted"][0] == -1 and list(r["out_tokens"][0]) == [-1, -1, -1]
+
+
 def test_zero_residual_falls_back_to_p():
     # identical target and draft rows, drafted token masked in both: p = q = 0 -> reject,
     # the residual is empty, the draw comes from p of that row

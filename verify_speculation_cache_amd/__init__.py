@@ -14,9 +14,10 @@ import os
 from typing import Optional, Sequence
 
 __all__ = ["SSD_F32", "SSD_BF16", "SsdError", "lib", "ssd_fanout", "ssd_verify",
-           "ssd_residual_sample", "ssd_build_cache", "ssd_cache_lookup", "ssd_draft_sample", "Sigma",
+           "ssd_residual_sample", "ssd_build_cache", "ssd_cache_lookup", "ssd_draft_sample", "ssd_verify_greedy", "Sigma",
            "ssd_verify_workspace_size", "ssd_residual_workspace_size",
-           "ssd_build_cache_workspace_size", "ssd_draft_sample_workspace_size", "EXPORTS",
+           "ssd_build_cache_workspace_size", "ssd_draft_sample_workspace_size",
+           "ssd_verify_greedy_workspace_size", "EXPORTS",
            "library_path"]
 
 SSD_F32, SSD_BF16 = 0, 1
@@ -24,7 +25,8 @@ SSD_MAX_K, SSD_MAX_F = 64, 64
 EXPORTS = ("ssd_last_error", "ssd_fanout", "ssd_verify_workspace_size", "ssd_verify",
            "ssd_residual_workspace_size", "ssd_residual_sample",
            "ssd_build_cache_workspace_size", "ssd_build_cache", "ssd_cache_lookup",
-           "ssd_draft_sample_workspace_size", "ssd_draft_sample")
+           "ssd_draft_sample_workspace_size", "ssd_draft_sample",
+           "ssd_verify_greedy_workspace_size", "ssd_verify_greedy")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -63,6 +65,9 @@ _SIGS = {
                                        _vp, _vp, _vp, _vp, _sz, _vp]),
     "ssd_cache_lookup": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "ssd_draft_sample_workspace_size": (_sz, [_i32, _i32, _i32, ctypes.c_int]),
+    "ssd_verify_greedy_workspace_size": (_sz, [_i32, _i32, _i32, ctypes.c_int]),
+    "ssd_verify_greedy": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz,
+                                         _vp]),
     "ssd_draft_sample": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _i32, _i32, _i32, _f32, _vp, _vp, _vp,
                                         _vp, _sz, _vp]),
 }
@@ -257,6 +262,31 @@ def ssd_residual_sample(target, draft, row, u, tau: float, sigma: Optional[Sigma
     _check(lib().ssd_residual_sample(tp, tb, dp, db, dt, B, K, V, float(tau), rp, sig, up,
                                      tok.data_ptr(), mass.data_ptr(), ws, wsz, _stream(stream)))
     return {"tokens": tok, "mass": mass}
+
+
+def ssd_verify_greedy_workspace_size(B, K, V, dtype) -> int:
+    return int(lib().ssd_verify_greedy_workspace_size(B, K, V, dtype))
+
+
+def ssd_verify_greedy(target, draft_tokens, *, out: Optional[dict] = None, stream=None) -> dict:
+    """Greedy verification: returns accepted [B] and out_tokens [B, K+1]."""
+    torch = _torch()
+    B, K = int(draft_tokens.shape[0]), int(draft_tokens.shape[1])
+    V = int(target.shape[2])
+    dt = _dtype_code(target)
+    if target.shape[0] != B:
+        raise ValueError("target batch size differs from draft_tokens")
+    tp, tb = _logits(target, "target", K + 1)
+    kp = _dev(draft_tokens, torch.int32, (B, K), "draft_tokens")
+    if out is None:
+        out = {"accepted": torch.empty(B, dtype=torch.int32, device=target.device),
+               "out_tokens": torch.empty((B, K + 1), dtype=torch.int32, device=target.device)}
+    ws, wsz = _workspace(ssd_verify_greedy_workspace_size(B, K, V, dt), target.device, ("greedy", B, K, V, dt),
+                         stream)
+    _check(lib().ssd_verify_greedy(tp, tb, dt, B, K, V, kp, _dev(out["accepted"], torch.int32, (B,), "accepted"),
+                                   _dev(out["out_tokens"], torch.int32, (B, K + 1), "out_tokens"), ws, wsz,
+                                   _stream(stream)))
+    return out
 
 
 def ssd_draft_sample_workspace_size(B, K, V, dtype) -> int:

@@ -305,6 +305,41 @@ SSD_API int ssd_residual_sample(const void* target_logits, int64_t target_bstrid
   return hip_status(launch_resid(r, dtype, sig, stream), "residual launch");
 }
 
+SSD_API size_t ssd_verify_greedy_workspace_size(int32_t B, int32_t K, int32_t V, int dtype) {
+  if (check_shape(B, K, V) != SSD_OK || !dtype_ok(dtype)) return 0;
+  return GreedyWs(B, K, stats_chunks_per_row(V)).total;
+}
+
+SSD_API int ssd_verify_greedy(const void* target_logits, int64_t target_bstride, int dtype,
+                              int32_t B, int32_t K, int32_t V, const int32_t* draft_tokens,
+                              int32_t* accepted, int32_t* out_tokens,
+                              void* workspace, size_t ws_bytes, void* hip_stream) {
+  int st;
+  if (!dtype_ok(dtype)) return fail(SSD_EDTYPE, "unknown dtype %d", dtype);
+  if ((st = check_shape(B, K, V)) != SSD_OK) return st;
+  if (!target_logits || !draft_tokens || !accepted || !out_tokens)
+    return fail(SSD_EINVAL, "a required pointer is NULL");
+  if (target_bstride < 0) return fail(SSD_EINVAL, "negative batch stride");
+  const int64_t SS = stats_chunks_per_row(V);
+  const GreedyWs gw(B, K, SS);
+  if ((st = check_ws(workspace, ws_bytes, gw.total)) != SSD_OK) return st;
+  if ((st = check_grid(int64_t(B) * (K + 1) * SS)) != SSD_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  GreedyArgs a{};
+  a.target = target_logits;
+  a.tb = target_bstride;
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.S = int(SS);
+  a.tokens = draft_tokens;
+  a.accepted = accepted;
+  a.out_tokens = out_tokens;
+  a.part = reinterpret_cast<uint64_t*>(ws + gw.part);
+  a.cnt = reinterpret_cast<uint32_t*>(ws + gw.cnt);
+  return hip_status(launch_greedy(a, dtype, as_stream(hip_stream)), "greedy launch");
+}
+
 SSD_API size_t ssd_draft_sample_workspace_size(int32_t B, int32_t K, int32_t V, int dtype) {
   if (check_shape(B, K, V) != SSD_OK || !dtype_ok(dtype)) return 0;
   return SampleWs(int64_t(B) * K, chunks_per_row(V)).total;

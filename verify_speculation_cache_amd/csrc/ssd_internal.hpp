@@ -186,6 +186,26 @@ struct CacheWs {
   }
 };
 
+struct GreedyArgs {
+  const void* target;
+  int64_t tb;
+  int B, K, V, S;            // S = stats chunks per row
+  const int32_t* tokens;     // [B, K]
+  int32_t* accepted;         // [B]
+  int32_t* out_tokens;       // [B, K+1]
+  uint64_t* part;            // [B, K+1, S]: chunk max (float bits) | argmax index << 32
+  uint32_t* cnt;             // [B] (kCntStride apart)
+};
+
+struct GreedyWs {
+  size_t part, cnt, total;
+  GreedyWs(int64_t B, int64_t K, int64_t S) {
+    part = 0;
+    cnt = align256(part + sizeof(uint64_t) * B * (K + 1) * S);
+    total = align256(cnt + sizeof(uint32_t) * kCntStride * B);
+  }
+};
+
 struct SampleWs {
   size_t part, cnt, total;
   SampleWs(int64_t rows, int64_t S) {
@@ -201,5 +221,6 @@ hipError_t launch_resid(const ResidArgs& a, int dtype, bool sigma, hipStream_t s
 hipError_t launch_cache(const CacheArgs& a, int dtype, hipStream_t st);
 hipError_t launch_lookup(const LookupArgs& a, hipStream_t st);
 hipError_t launch_sample(const SampleArgs& a, int dtype, hipStream_t st);
+hipError_t launch_greedy(const GreedyArgs& a, int dtype, hipStream_t st);
 
 }  // namespace ssd
