@@ -100,6 +100,32 @@ SSD_API const char* ssd_last_error(void);
  * F_out: host int32[K+1]. Returns sum(F) (= n_budget) or a negative status. */
 SSD_API int ssd_fanout(int32_t n_budget, int32_t K, double a_p, double r, int32_t* F_out);
 
+/* Uniform fan-out, the baseline cache shape of [SSD-notes] (ablation: cache
+ * topology): n_budget split evenly over k = 0..K, the remainder going to the
+ * smallest k (largest remainder with ties to the smaller k, as ssd_fanout).
+ * F_out: host int32[K+1]. Returns sum(F) (= n_budget) or a negative status. */
+SSD_API int ssd_fanout_uniform(int32_t n_budget, int32_t K, int32_t* F_out);
+
+/* Expected speedup of SSD over the verifier alone ([SSD-notes] theoretical
+ * analysis): (p E_hit + (1-p) E_miss) / (q max(1, T_p) + (1-q)(1 + T_b)) with
+ * p = p_hit, and q = p_hit^batch the probability that every sequence of a
+ * batch hits ([SSD-notes] batch-size-aware fallback); batch = 1 is the
+ * single-sequence formula. T_p, T_b: primary and backup speculator times
+ * relative to one verification; E_hit, E_miss: tokens per round on a hit or
+ * a miss. 0 <= p_hit <= 1, E_* >= 0, T_* >= 0, batch >= 1. Writes *out;
+ * returns SSD_OK or a negative status. Host only. */
+SSD_API int ssd_speedup(double p_hit, double e_hit, double e_miss, double t_p, double t_b, int32_t batch,
+                        double* out);
+
+/* Per-length cache statistics of one round: counts[k][0] = rows whose
+ * accepted length is k, counts[k][1] = those among them that hit (hit[b] = 1),
+ * k = 0..K; flagged rows (accepted < 0) are not counted. Exact integer
+ * counts (order-independent).
+ *   accepted device int32 [B]; hit device uint8 [B]
+ *   counts device uint32 [K+1, 2] (fully written). One kernel launch. */
+SSD_API int ssd_cache_stats(const int32_t* accepted, const uint8_t* hit, int32_t B, int32_t K,
+                            uint32_t* counts, void* hip_stream);
+
 /* Bytes of workspace ssd_verify needs for this shape (any mode). */
 SSD_API size_t ssd_verify_workspace_size(int32_t B, int32_t K, int32_t V, int dtype);
 

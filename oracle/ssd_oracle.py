@@ -46,7 +46,7 @@ __all__ = [
     "sigma_row_stats", "accept_scan", "inverse_cdf", "verify_row", "verify",
     "residual_sample", "fanout", "fanout_real", "build_cache", "cache_lookup",
     "alpha", "expected_tokens", "p_hit_row", "sample_draft", "draft_sample", "segment_offsets",
-    "argmax_token", "verify_greedy",
+    "argmax_token", "verify_greedy", "fanout_uniform", "cache_stats", "ssd_speedup",
 ]
 
 
@@ -524,3 +524,42 @@ def verify_greedy(target: np.ndarray, tokens: np.ndarray) -> dict:
         out[b, :a] = tokens[b, :a]
         out[b, a] = g[a]
     return {"accepted": acc, "out_tokens": out}
+
+
+# ---------------------------------------------------------------------------
+# cache statistics and policy   [SSD-notes] theoretical analysis; ablations
+# ---------------------------------------------------------------------------
+def fanout_uniform(n_budget: int, K: int) -> list:
+    """The uniform cache shape (the baseline of the cache-topology ablation):
+    real F_k = budget / (K+1) for every k, rounded like fanout (floors, then
+    the leftover to the largest fractional parts, ties to the smaller k)."""
+    real = [float(n_budget) / (K + 1)] * (K + 1)
+    F = [int(math.floor(v)) for v in real]
+    left = int(n_budget) - sum(F)
+    order = sorted(range(K + 1), key=lambda k: (-(real[k] - math.floor(real[k])), k))
+    for k in order[:left]:
+        F[k] += 1
+    return F
+
+
+def cache_stats(accepted: np.ndarray, hit: np.ndarray, K: int) -> np.ndarray:
+    """counts[k] = (rows with accepted length k, hits among them), k = 0..K;
+    flagged rows (accepted < 0) are not counted."""
+    counts = np.zeros((K + 1, 2), dtype=np.int64)
+    for a, h in zip(accepted, hit):
+        if 0 <= int(a) <= K:
+            counts[int(a), 0] += 1
+            counts[int(a), 1] += int(h != 0)
+    return counts
+
+
+def ssd_speedup(p_hit: float, e_hit: float, e_miss: float, t_p: float, t_b: float, batch: int = 1) -> float:
+    """Expected SSD speedup ([SSD-notes] theoretical analysis):
+    (p E_hit + (1-p) E_miss) / (p max(1, T_p) + (1-p)(1 + T_b)); for a batch
+    of b sequences the round waits on a miss unless every sequence hits, so
+    the time terms use p_hit^b ([SSD-notes] batch-size-aware fallback) while
+    the tokens per sequence keep p_hit (a reading: the page states only that
+    p_hit^b takes over the latency expectation)."""
+    q = float(p_hit) ** int(batch)
+    num = float(p_hit) * e_hit + (1.0 - float(p_hit)) * e_miss
+    return num / (q * max(1.0, float(t_p)) + (1.0 - q) * (1.0 + float(t_b)))

@@ -490,3 +490,26 @@ def test_verify_greedy_cfg2(S):
     ref = O.verify_greedy(d["target"], toks)
     assert np.array_equal(got["accepted"].cpu().numpy(), ref["accepted"])
     assert np.array_equal(got["out_tokens"].cpu().numpy(), ref["out_tokens"])
+
+
+# ---------------------------------------------------------------------------
+# per-length cache statistics
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,K", [(1, 1), (97, 5), (5000, 8), (3, 64)])
+def test_cache_stats(S, B, K):
+    log(f"[gpu] cache stats B={B} K={K}")
+    rng = np.random.default_rng(B + K)
+    acc = rng.integers(-1, K + 1, size=B).astype(np.int32)
+    hit = (rng.random(B) < 0.6).astype(np.uint8)
+    got = S.ssd_cache_stats(torch.from_numpy(acc).cuda(), torch.from_numpy(hit).cuda(), K)
+    assert np.array_equal(got.cpu().numpy().astype(np.int64), O.cache_stats(acc, hit, K))
+
+
+def test_uniform_fanout_cache_hits(S):
+    # the uniform shape drives the same cache build and lookup (cfg3 rows)
+    cfg = W.get_config(3)
+    log("[gpu] uniform fan-out cache on cfg3 rows")
+    F = S.ssd_fanout_uniform(cfg.n_budget, cfg.K)
+    assert F == O.fanout_uniform(cfg.n_budget, cfg.K)
+    d = W.make_inputs(cfg, b_rows=range(0, 32, 4))
+    _cache_case(S, d, F, cfg.C, label="cfg3-uniform")

@@ -172,6 +172,26 @@ def test_verify_greedy_argument_checks():
     assert S.ssd_verify_greedy_workspace_size(2, 3, 100, S.SSD_F32) > 0
 
 
+def test_cache_policy_host_calls_match_oracle():
+    for n, K in ((64, 7), (128, 8), (5, 3), (0, 4), (1000, 64)):
+        assert S.ssd_fanout_uniform(n, K) == O.fanout_uniform(n, K)
+    for args in ((0.8, 3.6, 1.9, 0.7, 0.1, 1), (0.95, 4.0, 1.2, 1.5, 0.0, 16), (0.0, 2.0, 1.0, 0.3, 0.4, 3),
+                 (1.0, 5.0, 1.0, 0.0, 2.0, 64)):
+        assert abs(S.ssd_speedup(*args) - O.ssd_speedup(*args)) <= 1e-15 * O.ssd_speedup(*args)
+    L = S.lib()
+    out = ctypes.c_double()
+    assert L.ssd_speedup(1.5, 1.0, 1.0, 0.0, 0.0, 1, ctypes.byref(out)) == -1
+    assert L.ssd_speedup(0.5, -1.0, 1.0, 0.0, 0.0, 1, ctypes.byref(out)) == -1
+    assert L.ssd_speedup(0.5, 1.0, 1.0, 0.0, 0.0, 0, ctypes.byref(out)) == -1
+    assert L.ssd_speedup(0.5, 1.0, 1.0, float("nan"), 0.0, 1, ctypes.byref(out)) == -1
+    assert L.ssd_speedup(0.5, 1.0, 1.0, 0.0, 0.0, 1, None) == -1
+    F = (ctypes.c_int32 * 2)()
+    assert L.ssd_fanout_uniform(-1, 1, F) == -1 and L.ssd_fanout_uniform(4, 0, F) == -1
+    assert L.ssd_cache_stats(FAKE, FAKE, 0, 3, FAKE, None) == -1
+    assert L.ssd_cache_stats(FAKE, None, 4, 3, FAKE, None) == -1
+    assert L.ssd_cache_stats(FAKE, FAKE, 4, 65, FAKE, None) == -1
+
+
 def test_oracle_not_imported_by_product():
     import sys
     src_dir = os.path.join(ROOT, "verify_speculation_cache_amd")

@@ -387,6 +387,30 @@ def test_greedy_is_the_zero_temperature_limit():
     assert r["accepted"][0] == -1 and list(r["out_tokens"][0]) == [-1, -1, -1]
 
 
+def test_cache_policy_helpers():
+    # uniform shape: sums to the budget, differs by at most one, extra units first
+    for n, K in ((64, 7), (128, 8), (5, 3), (0, 4), (9, 8)):
+        F = O.fanout_uniform(n, K)
+        assert sum(F) == n and max(F) - min(F) <= 1 and F == sorted(F, reverse=True)
+    assert O.fanout_uniform(10, 3) == [3, 3, 2, 2]
+    # speedup: all hits with a primary no slower than the verifier give E_hit;
+    # all misses give E_miss / (1 + T_b); batch 1 is the single-sequence form;
+    # a large batch almost never has every sequence hit
+    assert O.ssd_speedup(1.0, 4.0, 1.5, 0.5, 0.2) == 4.0
+    assert O.ssd_speedup(1.0, 4.0, 1.5, 2.0, 0.2) == 2.0
+    assert abs(O.ssd_speedup(0.0, 4.0, 1.5, 0.5, 0.2) - 1.5 / 1.2) < 1e-15
+    p, Eh, Em, Tp, Tb = 0.8, 3.6, 1.9, 0.7, 0.1
+    single = (p * Eh + (1 - p) * Em) / (p * 1.0 + (1 - p) * (1 + Tb))
+    assert abs(O.ssd_speedup(p, Eh, Em, Tp, Tb, 1) - single) < 1e-15
+    big = O.ssd_speedup(p, Eh, Em, Tp, Tb, 200)
+    assert abs(big - (p * Eh + (1 - p) * Em) / (1 + Tb)) < 1e-12
+    assert O.ssd_speedup(p, Eh, Em, Tp, Tb, 2) < single
+    # per-length counts on a hand example
+    acc = np.array([0, 2, 2, -1, 3, 2, 0])
+    hit = np.array([1, 0, 1, 1, 1, 1, 0], dtype=np.uint8)
+    assert O.cache_stats(acc, hit, 3).tolist() == [[2, 1], [0, 0], [3, 2], [1, 1]]
+
+
 def test_zero_residual_falls_back_to_p():
     # identical target and draft rows, drafted token masked in both: p = q = 0 -> reject,
     # the residual is empty, the draw comes from p of that row

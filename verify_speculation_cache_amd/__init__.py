@@ -14,7 +14,8 @@ import os
 from typing import Optional, Sequence
 
 __all__ = ["SSD_F32", "SSD_BF16", "SsdError", "lib", "ssd_fanout", "ssd_verify",
-           "ssd_residual_sample", "ssd_build_cache", "ssd_cache_lookup", "ssd_draft_sample", "ssd_verify_greedy", "Sigma",
+           "ssd_residual_sample", "ssd_build_cache", "ssd_cache_lookup", "ssd_draft_sample", "ssd_verify_greedy", "ssd_fanout_uniform",
+           "ssd_speedup", "ssd_cache_stats", "Sigma",
            "ssd_verify_workspace_size", "ssd_residual_workspace_size",
            "ssd_build_cache_workspace_size", "ssd_draft_sample_workspace_size",
            "ssd_verify_greedy_workspace_size", "EXPORTS",
@@ -26,7 +27,8 @@ EXPORTS = ("ssd_last_error", "ssd_fanout", "ssd_verify_workspace_size", "ssd_ver
            "ssd_residual_workspace_size", "ssd_residual_sample",
            "ssd_build_cache_workspace_size", "ssd_build_cache", "ssd_cache_lookup",
            "ssd_draft_sample_workspace_size", "ssd_draft_sample",
-           "ssd_verify_greedy_workspace_size", "ssd_verify_greedy")
+           "ssd_verify_greedy_workspace_size", "ssd_verify_greedy", "ssd_fanout_uniform", "ssd_speedup",
+           "ssd_cache_stats")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -66,6 +68,9 @@ _SIGS = {
     "ssd_cache_lookup": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "ssd_draft_sample_workspace_size": (_sz, [_i32, _i32, _i32, ctypes.c_int]),
     "ssd_verify_greedy_workspace_size": (_sz, [_i32, _i32, _i32, ctypes.c_int]),
+    "ssd_fanout_uniform": (ctypes.c_int, [_i32, _i32, _vp]),
+    "ssd_speedup": (ctypes.c_int, [_f64, _f64, _f64, _f64, _f64, _i32, _vp]),
+    "ssd_cache_stats": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
     "ssd_verify_greedy": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz,
                                          _vp]),
     "ssd_draft_sample": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _i32, _i32, _i32, _f32, _vp, _vp, _vp,
@@ -262,6 +267,33 @@ def ssd_residual_sample(target, draft, row, u, tau: float, sigma: Optional[Sigma
     _check(lib().ssd_residual_sample(tp, tb, dp, db, dt, B, K, V, float(tau), rp, sig, up,
                                      tok.data_ptr(), mass.data_ptr(), ws, wsz, _stream(stream)))
     return {"tokens": tok, "mass": mass}
+
+
+def ssd_fanout_uniform(n_budget: int, K: int) -> list:
+    """Uniform fan-out F[0..K] (host call)."""
+    arr = (ctypes.c_int32 * (K + 1))()
+    _check(lib().ssd_fanout_uniform(int(n_budget), int(K), arr))
+    return list(arr)
+
+
+def ssd_speedup(p_hit: float, e_hit: float, e_miss: float, t_p: float, t_b: float, batch: int = 1) -> float:
+    """Expected SSD speedup with the batch all-hit probability p_hit**batch (host call)."""
+    out = ctypes.c_double()
+    _check(lib().ssd_speedup(float(p_hit), float(e_hit), float(e_miss), float(t_p), float(t_b), int(batch),
+                             ctypes.byref(out)))
+    return out.value
+
+
+def ssd_cache_stats(accepted, hit, K: int, *, out=None, stream=None):
+    """Per-length counts [K+1, 2] (int32 view of uint32): outcomes at length k, hits among them."""
+    torch = _torch()
+    B = int(accepted.shape[0])
+    if out is None:
+        out = torch.empty((K + 1, 2), dtype=torch.int32, device=accepted.device)
+    _check(lib().ssd_cache_stats(_dev(accepted, torch.int32, (B,), "accepted"),
+                                 _dev(hit, torch.uint8, (B,), "hit"), B, int(K),
+                                 _dev(out, torch.int32, (K + 1, 2), "out"), _stream(stream)))
+    return out
 
 
 def ssd_verify_greedy_workspace_size(B, K, V, dtype) -> int:

@@ -1,6 +1,7 @@
 // C-ABI layer of libssdv: argument checks, workspace carving and kernel
 // launches on the caller's stream. Every check runs on the host before the
 // first HIP call, so bad arguments never reach the device.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -133,6 +134,47 @@ SSD_API int ssd_fanout(int32_t n_budget, int32_t K, double a_p, double r, int32_
   }
   ok();
   return n_budget;
+}
+
+SSD_API int ssd_fanout_uniform(int32_t n_budget, int32_t K, int32_t* F_out) {
+  if (F_out == nullptr) return fail(SSD_EINVAL, "F_out is NULL");
+  if (n_budget < 0) return fail(SSD_EINVAL, "budget %d < 0", n_budget);
+  if (K < 1 || K > SSD_MAX_K) return fail(SSD_EINVAL, "K=%d outside [1, %d]", K, SSD_MAX_K);
+  // equal real shares; every fractional part ties, so the leftover units go
+  // to the smallest lengths
+  const int32_t base = n_budget / (K + 1), left = n_budget - base * (K + 1);
+  for (int k = 0; k <= K; ++k) F_out[k] = base + (k < left ? 1 : 0);
+  ok();
+  return n_budget;
+}
+
+SSD_API int ssd_speedup(double p_hit, double e_hit, double e_miss, double t_p, double t_b, int32_t batch,
+                        double* out) {
+  if (out == nullptr) return fail(SSD_EINVAL, "out is NULL");
+  if (!(p_hit >= 0.0 && p_hit <= 1.0)) return fail(SSD_EINVAL, "p_hit=%g outside [0, 1]", p_hit);
+  if (!(e_hit >= 0.0) || !(e_miss >= 0.0) || !std::isfinite(e_hit) || !std::isfinite(e_miss))
+    return fail(SSD_EINVAL, "E_hit, E_miss must be finite and >= 0");
+  if (!(t_p >= 0.0) || !(t_b >= 0.0) || !std::isfinite(t_p) || !std::isfinite(t_b))
+    return fail(SSD_EINVAL, "T_p, T_b must be finite and >= 0");
+  if (batch < 1) return fail(SSD_EINVAL, "batch=%d < 1", batch);
+  const double q = std::pow(p_hit, double(batch));   // every sequence of the batch hits
+  *out = (p_hit * e_hit + (1.0 - p_hit) * e_miss) / (q * std::max(1.0, t_p) + (1.0 - q) * (1.0 + t_b));
+  ok();
+  return SSD_OK;
+}
+
+SSD_API int ssd_cache_stats(const int32_t* accepted, const uint8_t* hit, int32_t B, int32_t K,
+                            uint32_t* counts, void* hip_stream) {
+  if (!accepted || !hit || !counts) return fail(SSD_EINVAL, "a required pointer is NULL");
+  if (B < 1 || B >= (1 << 24)) return fail(SSD_EINVAL, "B=%d outside [1, 2^24)", B);
+  if (K < 1 || K > SSD_MAX_K) return fail(SSD_EINVAL, "K=%d outside [1, %d]", K, SSD_MAX_K);
+  CacheStatsArgs a{};
+  a.accepted = accepted;
+  a.hit = hit;
+  a.B = B;
+  a.K = K;
+  a.counts = counts;
+  return hip_status(launch_cache_stats(a, as_stream(hip_stream)), "cache stats launch");
 }
 
 SSD_API size_t ssd_verify_workspace_size(int32_t B, int32_t K, int32_t V, int dtype) {

@@ -652,6 +652,28 @@ __global__ __launch_bounds__(kThreads) void k_lookup(LookupArgs a) {
   }
 }
 
+// Per-length outcome and hit counts of one round: one workgroup, LDS
+// histogram with integer atomics (exact, order-independent), fully written.
+__global__ __launch_bounds__(kThreads) void k_cache_stats(CacheStatsArgs a) {
+  __shared__ uint32_t h[SSD_MAX_K + 1][2];
+  for (int i = threadIdx.x; i < (a.K + 1) * 2; i += kThreads) h[i >> 1][i & 1] = 0u;
+  __syncthreads();
+  for (int b = threadIdx.x; b < a.B; b += kThreads) {
+    const int av = a.accepted[b];
+    if (av >= 0 && av <= a.K) {
+      atomicAdd(&h[av][0], 1u);
+      if (a.hit[b]) atomicAdd(&h[av][1], 1u);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < (a.K + 1) * 2; i += kThreads) a.counts[i] = h[i >> 1][i & 1];
+}
+
+hipError_t launch_cache_stats(const CacheStatsArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_cache_stats, dim3(1), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_cache(const CacheArgs& a, int dtype, hipStream_t st) {
   const unsigned grid = unsigned(int64_t(a.B) * (a.K + 1) * a.S);
   const unsigned rows = unsigned(int64_t(a.B) * (a.K + 1));

@@ -186,6 +186,13 @@ struct CacheWs {
   }
 };
 
+struct CacheStatsArgs {
+  const int32_t* accepted;
+  const uint8_t* hit;
+  int B, K;
+  uint32_t* counts;   // [K+1, 2]
+};
+
 struct GreedyArgs {
   const void* target;
   int64_t tb;
@@ -222,5 +229,6 @@ hipError_t launch_cache(const CacheArgs& a, int dtype, hipStream_t st);
 hipError_t launch_lookup(const LookupArgs& a, hipStream_t st);
 hipError_t launch_sample(const SampleArgs& a, int dtype, hipStream_t st);
 hipError_t launch_greedy(const GreedyArgs& a, int dtype, hipStream_t st);
+hipError_t launch_cache_stats(const CacheStatsArgs& a, hipStream_t st);
 
 }  // namespace ssd
