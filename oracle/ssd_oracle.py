@@ -47,6 +47,7 @@ __all__ = [
     "residual_sample", "fanout", "fanout_real", "build_cache", "cache_lookup",
     "alpha", "expected_tokens", "p_hit_row", "sample_draft", "draft_sample", "segment_offsets",
     "argmax_token", "verify_greedy", "fanout_uniform", "cache_stats", "ssd_speedup",
+    "tree_children", "tree_depth", "verify_tree_row", "verify_tree",
 ]
 
 
@@ -563,3 +564,122 @@ def ssd_speedup(p_hit: float, e_hit: float, e_miss: float, t_p: float, t_b: floa
     q = float(p_hit) ** int(batch)
     num = float(p_hit) * e_hit + (1.0 - float(p_hit)) * e_miss
     return num / (q * max(1.0, float(t_p)) + (1.0 - q) * (1.0 + float(t_b)))
+
+
+# ---------------------------------------------------------------------------
+# token-tree verification   [SD-notes] Extensions and Variants, Multi-candidate
+#                           speculation; [SSD-yc] Where SSD sits in the
+#                           inference stack (token trees)
+# ---------------------------------------------------------------------------
+def tree_children(parent: Sequence[int]) -> list:
+    """Children of every node of a token tree, in node-index order.
+    parent[0] = -1 (the root, the position after the committed context) and
+    0 <= parent[n] < n for n >= 1."""
+    ch = [[] for _ in range(len(parent))]
+    for n in range(1, len(parent)):
+        ch[int(parent[n])].append(n)
+    return ch
+
+
+def tree_depth(parent: Sequence[int]) -> list:
+    """Depth of every node (root 0)."""
+    d = [0] * len(parent)
+    for n in range(1, len(parent)):
+        d[n] = d[int(parent[n])] + 1
+    return d
+
+
+def _after_rejection(P: np.ndarray, q: np.ndarray, p: np.ndarray):
+    """The distribution the next sibling is tested against once a child drawn
+    from q was rejected under P: max(0, P - q) / Z ([SD-notes] step 3 and the
+    Derivation of the acceptance criterion), or p of the node when the
+    residual has no mass (reading, as for one candidate). Returns (P', r) with
+    r the unnormalised residual (None on the fallback)."""
+    r = np.maximum(0.0, P - q)
+    Z = float(np.sum(r))
+    if Z > 0.0:
+        return r / Z, r
+    return p, None
+
+
+def verify_tree_row(target: np.ndarray, draft: np.ndarray, parent: Sequence[int],
+                    tokens: Sequence[int], u_acc: Sequence[float], u_res: float,
+                    tau: float) -> dict:
+    """Verify one sequence's token tree ([SD-notes] Extensions and Variants,
+    Multi-candidate speculation: the target checks every drafted branch in
+    one pass).
+
+    target [N, V]: target logits after each node's path; draft [N, V]: draft
+    logits at each node (the distribution its children were drawn from; rows
+    of leaves are not read). tokens[n] is node n's token (n >= 1), u_acc[n]
+    the uniform of node n's test, u_res the uniform of the final draw.
+
+    The walk applies the page's one-candidate rule ([SD-notes] The Algorithm,
+    step 3) to the children of the current node in index order, each against
+    the distribution left by the previous rejection (readings):
+      P = p of the node; for each child c: keep c iff u_acc[c] q(x_c) < P(x_c);
+      on a rejection P <- max(0, P - q) / Z; if that leaves no mass
+      (Z <= 0) P <- p of the node.
+    A kept child becomes the current node (its token is emitted); when every
+    child of the current node was rejected, or it has none, one more token is
+    drawn from the last P by inverse CDF with u_res: the residual
+    max(0, P - q) of the last rejection, or p of the node (the bonus) when
+    nothing was rejected there. With siblings drawn independently from q this
+    keeps the emitted token distributed as p.
+    Returns a = depth reached, out [N] (emitted tokens, -1 padding), nodes [N]
+    (nodes on the kept path, root first, -1 padding), the margin of every
+    test taken (nan for nodes not tested), the residual margin and Z.
+    A token outside [0, V) at any node >= 1 flags the row (a = -1, all -1).
+    """
+    N = len(parent)
+    V = target.shape[-1]
+    out = np.full(N, -1, dtype=np.int64)
+    nodes = np.full(N, -1, dtype=np.int64)
+    res = {"a": -1, "out": out, "nodes": nodes, "acc_margin": np.full(N, np.nan),
+           "res_margin": math.nan, "Z": math.nan}
+    if any(int(tokens[n]) < 0 or int(tokens[n]) >= V for n in range(1, N)):
+        return res
+    ch = tree_children(parent)
+    node, depth = 0, 0
+    nodes[0] = 0
+    while True:
+        p = softmax(target[node], tau)
+        P = p
+        last_r = None                    # unnormalised residual of the last rejection
+        kept = None
+        if ch[node]:
+            q = softmax(draft[node], tau)
+            for c in ch[node]:
+                x = int(tokens[c])
+                u = float(u_acc[c])
+                res["acc_margin"][c] = abs(P[x] - u * q[x])
+                if u * q[x] < P[x]:
+                    kept = c
+                    break
+                P, last_r = _after_rejection(P, q, p)
+        if kept is None:
+            t, Z, mg = inverse_cdf(P if last_r is None else last_r, u_res)
+            out[depth] = t
+            res.update(a=depth, res_margin=mg, Z=Z)
+            return res
+        out[depth] = int(tokens[kept])
+        depth += 1
+        nodes[depth] = kept
+        node = kept
+
+
+def verify_tree(target: np.ndarray, draft: np.ndarray, parent: Sequence[int], tokens: np.ndarray,
+                u_acc: np.ndarray, u_res: np.ndarray, tau: float) -> dict:
+    """Batched token-tree verification: every sequence walks its own tree
+    (same topology, its own tokens, logits and uniforms). Loops over the batch."""
+    B, N = tokens.shape
+    rows = [verify_tree_row(target[b], draft[b], parent, tokens[b], u_acc[b], float(u_res[b]), tau)
+            for b in range(B)]
+    return {
+        "accepted": np.array([r["a"] for r in rows], dtype=np.int64),
+        "out_tokens": np.stack([r["out"] for r in rows]),
+        "out_nodes": np.stack([r["nodes"] for r in rows]),
+        "acc_margin": np.stack([r["acc_margin"] for r in rows]),
+        "res_margin": np.array([r["res_margin"] for r in rows]),
+        "Z": np.array([r["Z"] for r in rows]),
+    }

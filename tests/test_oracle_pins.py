@@ -502,3 +502,153 @@ def test_planted_mistakes_are_caught(monkeypatch, golden_dir):
             return orig_vr(t2, draft, tokens, u_acc, u_res, tau, sigma)
         m.setattr(OM, "verify_row", bad_vr)
         _expect_fail(check_lossless, 400)
+
+
+# ---------------------------------------------------------------------------
+# token-tree verification
+# ---------------------------------------------------------------------------
+def _tree_logits(prob_rows):
+    return _ln_rows(prob_rows)
+
+
+def check_tree_hand_cases():
+    """Small trees worked by hand from the one-candidate rule applied to each
+    sibling in turn (temperature 1, logits ln(prob)).
+
+    p = (0.5, 0.3, 0.2), q = (0.2, 0.2, 0.6) at the root; root children are
+    nodes 1 and 2, both leaves. A token-2 child is kept iff 0.6 u < 0.2.
+    After rejecting it the residual is (0.3, 0.1, 0)/0.4 = (0.75, 0.25, 0),
+    where a token-1 child is kept iff 0.2 u < 0.25 (always) and a token-2
+    child never; rejecting that as well leaves max(0, (0.75, 0.25, 0) - q) =
+    (0.55, 0.05, 0), Z = 0.6, so the final draw is token 0 for u_res Z < 0.55
+    and token 1 above.
+    """
+    p = [0.5, 0.3, 0.2]
+    q = [0.2, 0.2, 0.6]
+    leaf1 = [0.5, 0.5, 0.0]      # target after node 1 (bonus row)
+    leaf2 = [0.1, 0.1, 0.8]      # target after node 2
+    T = _tree_logits([p, leaf1, leaf2])
+    D = _tree_logits([q, q, q])
+    par = [-1, 0, 0]
+    cases = [
+        # tokens, u_acc, u_res, a, out, nodes
+        ([0, 2, 1], [0, 0.5, 0.9], 0.3, 1, [1, 2, -1], [0, 2, -1]),   # reject, keep, bonus 2
+        ([0, 2, 2], [0, 0.5, 0.2], 0.5, 0, [0, -1, -1], [0, -1, -1]),  # both rejected, 0.30 < 0.55
+        ([0, 2, 2], [0, 0.5, 0.2], 0.95, 0, [1, -1, -1], [0, -1, -1]), # 0.57 in (0.55, 0.6]
+        ([0, 2, 2], [0, 0.2, 0.2], 0.9, 1, [2, 1, -1], [0, 1, -1]),   # 0.12 < 0.2: keep node 1
+    ]
+    for toks, ua, ur, a, out, nodes in cases:
+        r = O.verify_tree_row(T, D, par, toks, ua, ur, 1.0)
+        assert r["a"] == a and list(r["out"]) == out and list(r["nodes"]) == nodes, (toks, ua, ur, r)
+    r = O.verify_tree_row(T, D, par, [0, 2, 2], [0, 0.5, 0.2], 0.5, 1.0)
+    assert abs(r["Z"] - 0.6) < 1e-6
+    # empty residual: p = q = (1, 0); a token-1 child has p = q = 0 and is
+    # rejected; max(0, p - q) = 0, so the draw uses p: token 0
+    one = _tree_logits([[1.0, 0.0]] * 2)
+    r = O.verify_tree_row(one, one, [-1, 0], [0, 1], [0, 0.3], 0.7, 1.0)
+    assert r["a"] == 0 and list(r["out"]) == [0, -1]
+    # root only: the bonus from p of the root, (0.5, 0.8, 1.0] -> token 1
+    r = O.verify_tree_row(_tree_logits([p]), _tree_logits([q]), [-1], [0], [0.0], 0.6, 1.0)
+    assert r["a"] == 0 and list(r["out"]) == [1]
+    # a token outside [0, V) anywhere flags the row
+    r = O.verify_tree_row(T, D, par, [0, 1, 3], [0, 0.1, 0.1], 0.5, 1.0)
+    assert r["a"] == -1 and list(r["out"]) == [-1, -1, -1]
+
+
+def test_tree_hand_cases():
+    check_tree_hand_cases()
+
+
+def check_tree_chain(n=150, seed=3):
+    """A tree that is one chain is the single-path algorithm: same kept
+    length and tokens as verify_row on the same rows and uniforms."""
+    rng = np.random.default_rng(seed)
+    for it in range(n):
+        K = int(rng.integers(1, 6))
+        V = int(rng.integers(2, 40))
+        tau = float(rng.choice([0.5, 0.8, 1.3]))
+        zt = (rng.standard_normal((K + 1, V)) * 1.5).astype(np.float32)
+        zd = (zt + rng.standard_normal((K + 1, V)).astype(np.float32) * 0.7).astype(np.float32)
+        toks = rng.integers(0, V, K)
+        ua = rng.random(K)
+        ur = float(rng.random())
+        lin = O.verify_row(zt, zd[:K], toks, ua, ur, tau)
+        par = [-1] + list(range(K))
+        tr = O.verify_tree_row(zt, zd, par, [0] + list(toks), [0.0] + list(ua), ur, tau)
+        assert tr["a"] == lin["a"], it
+        assert list(tr["out"]) == list(lin["out"]), it
+        assert list(tr["nodes"][:tr["a"] + 1]) == list(range(tr["a"] + 1))
+
+
+def test_tree_chain_is_linear_verification():
+    check_tree_chain()
+
+
+def check_tree_lossless(T=12000, seed=11):
+    """Siblings drawn independently from the draft: the first emitted token
+    follows p of the root, and after a kept first token x the next emitted
+    token follows p after x (chi-square at 1e-4, fixed seed). Rows depend on
+    the token path only, as a model's would."""
+    import scipy.stats
+    rng = np.random.default_rng(seed)
+    V = 4
+    dirich = lambda: rng.dirichlet(np.full(V, 0.8))
+    p0, q0 = dirich(), dirich()
+    p1 = [dirich() for _ in range(V)]           # target after token x
+    q1 = [dirich() for _ in range(V)]           # draft after token x
+    p2 = [[dirich() for _ in range(V)] for _ in range(V)]
+    lg = lambda v: _tree_logits([v])[0]
+    # root with 3 children, each child with 2 children: N = 10
+    par = [-1, 0, 0, 0, 1, 1, 2, 2, 3, 3]
+    first = np.zeros(V)
+    second = np.zeros((V, V))
+    for _ in range(T):
+        toks = [0] * 10
+        for c in (1, 2, 3):
+            toks[c] = int(rng.choice(V, p=q0))
+        for c in range(4, 10):
+            toks[c] = int(rng.choice(V, p=q1[toks[par[c]]]))
+        tgt = np.zeros((10, V), dtype=np.float32)
+        dft = np.zeros((10, V), dtype=np.float32)
+        tgt[0], dft[0] = lg(p0), lg(q0)
+        for c in range(1, 10):
+            if par[c] == 0:
+                tgt[c], dft[c] = lg(p1[toks[c]]), lg(q1[toks[c]])
+            else:
+                tgt[c], dft[c] = lg(p2[toks[par[c]]][toks[c]]), lg(q0)
+        r = O.verify_tree_row(tgt, dft, par, toks, rng.random(10), float(rng.random()), 1.0)
+        first[r["out"][0]] += 1
+        if r["a"] >= 1:
+            second[r["out"][0], r["out"][1]] += 1
+    assert scipy.stats.chisquare(first, p0 * T).pvalue > 1e-4, (first / T, p0)
+    for x in range(V):
+        n = second[x].sum()
+        if n >= 200:
+            assert scipy.stats.chisquare(second[x], p1[x] * n).pvalue > 1e-4, (x, second[x] / n, p1[x])
+
+
+def test_tree_lossless_montecarlo():
+    check_tree_lossless()
+
+
+def test_tree_planted_mistakes_are_caught(monkeypatch):
+    # siblings all tested against p (no residual update between them)
+    with monkeypatch.context() as m:
+        m.setattr(OM, "_after_rejection", lambda P, q, p: (P, None))
+        _expect_fail(check_tree_hand_cases)
+        _expect_fail(check_tree_lossless, 6000)
+    # residual left unnormalised
+    with monkeypatch.context() as m:
+        def unnorm(P, q, p):
+            r = np.maximum(0.0, P - q)
+            return (r, r) if r.sum() > 0 else (p, None)
+        m.setattr(OM, "_after_rejection", unnorm)
+        _expect_fail(check_tree_lossless, 6000)
+    # residual taken from p of the node instead of the current distribution
+    with monkeypatch.context() as m:
+        def from_p(P, q, p):
+            r = np.maximum(0.0, p - q)
+            return (r / r.sum(), r) if r.sum() > 0 else (p, None)
+        m.setattr(OM, "_after_rejection", from_p)
+        _expect_fail(check_tree_hand_cases)
+        _expect_fail(check_tree_lossless, 6000)
