@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--workload", choices=["step", "tree"], default="step",
+                    help="step: the verification + cache step (default); tree: token-tree verification")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of graph replay")
@@ -53,6 +55,9 @@ def main():
               "(every batch row is independent, so more GPUs would each run this same "
               "kernel on B/N rows)", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "tree":
+        return bench_tree(args)
 
     import torch
     import verify_speculation_cache_amd as S
@@ -241,6 +246,126 @@ def main():
         "verify_sigma_gbps": round(bytes_verify_sigma / (t_verify / 1e3) / 1e9, 1),
         "mean_accepted_plus_1": round(float(np.mean(acc + 1)), 4),
         "hit_rate": round(float(np.mean(hit)), 4),
+        "cpu_baseline": cpu,
+        "gen_s": round(gen_s, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_tree(args):
+    """Token-tree verification on its workload: B=32 sequences, a 29-node
+    tree (4 first-token candidates, 2 continuations each, then chains to
+    depth 4), V=128256, bf16, tau=0.7. One step = one ssd_verify_tree call
+    (the statistics pass, then the residual rounds the topology needs)."""
+    import torch
+    import verify_speculation_cache_amd as S
+    import workloads as W
+
+    cfg = W.TREE_CONFIGS["tree"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    d = W.make_tree_inputs(cfg)
+    gen_s = time.time() - t0
+    B, N, V = cfg.B, cfg.N, cfg.V
+    parent = d["parent"]
+    inner = sum(1 for n in range(N) if n in set(parent[1:]))
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    tgt0 = up(d["target"])
+    # only inner nodes' draft rows are read; the rest of the buffer is never touched
+    dft0 = up(d["draft"])
+    row_bytes = V * 2
+    bytes_single = B * (N + inner) * row_bytes       # every statistics row once
+    ncopy = int(math.ceil(MALL_BYTES / bytes_single)) + 1
+    tgts = [tgt0] + [tgt0.clone() for _ in range(ncopy - 1)]
+    dfts = [dft0] + [dft0.clone() for _ in range(ncopy - 1)]
+    toks = torch.from_numpy(d["tokens"]).to(dev)
+    ua = torch.from_numpy(d["u_acc"]).to(dev)
+    ur = torch.from_numpy(d["u_res"]).to(dev)
+    outs = [S.ssd_verify_tree(tgts[j], dfts[j], parent, toks, ua, ur, cfg.tau) for j in range(ncopy)]
+    torch.cuda.synchronize()
+    ref = [(o["accepted"].clone(), o["out_tokens"].clone()) for o in outs]
+
+    def step(j):
+        S.ssd_verify_tree(tgts[j], dfts[j], parent, toks, ua, ur, cfg.tau, out=outs[j])
+
+    stream = torch.cuda.Stream()
+    graphs = []
+    if not args.eager:
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            for j in range(ncopy):
+                step(j)
+        torch.cuda.synchronize()
+        for j in range(ncopy):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                step(j)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(n, offset=0):
+        for i in range(n):
+            j = (offset + i) % ncopy
+            if graphs:
+                graphs[j].replay()
+            else:
+                step(j)
+
+    run(args.warmup)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run(args.steps, args.warmup)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    for j, o in enumerate(outs):
+        assert torch.equal(o["accepted"], ref[j][0]) and torch.equal(o["out_tokens"], ref[j][1])
+    if args.profile_loop:
+        for i in range(args.profile_loop):
+            step(i % ncopy)
+        torch.cuda.synchronize()
+    acc = outs[0]["accepted"].cpu().numpy()
+    gbps = bytes_single / (ms_step / 1e3) / 1e9
+    cpu = None
+    if not args.no_cpu:
+        import oracle as O
+        t0 = time.time()
+        n = 0
+        while n < B and (time.time() - t0) < args.cpu_seconds:
+            sl = slice(n, n + 1)
+            O.verify_tree(d["target"][sl], d["draft"][sl], parent, d["tokens"][sl], d["u_acc"][sl],
+                          d["u_res"][sl], d["tau"])
+            n += 1
+        dt = time.time() - t0
+        cpu = {"value": round(n / dt, 3), "unit": "verified trees/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {n} of {B} batch rows of the same step, float64 NumPy, {dt:.1f} s"}
+    line = {
+        "metric": "verified trees/sec, B=32 N=29 V=128256 bf16",
+        "value": round(B / (ms_step / 1e3), 1),
+        "unit": "verified trees/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded Gaussian + Zipf-rank logits, draft = target + noise, siblings drawn "
+                "independently from the parent's draft distribution)",
+        "config": {"workload": "ssd_verify_tree", "B": B, "N": N, "branching": list(cfg.branching), "V": V,
+                   "logits": cfg.dtype, "tau": cfg.tau, "rounds": S.ssd_tree_rounds(parent),
+                   "rotating_copies": ncopy, "graph_replay": not args.eager},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "ssd_verify_tree (k_tree_stats + rounds of k_tree_round, bf16)",
+                     "bytes_per_launch": bytes_single, "avg_launch_ms": round(ms_step, 5)},
+        "mean_accepted_plus_1": round(float(np.mean(acc + 1)), 4),
         "cpu_baseline": cpu,
         "gen_s": round(gen_s, 2),
     }

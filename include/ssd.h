@@ -39,7 +39,8 @@
  *   are unaffected.
  * Determinism.  No floating-point atomics; identical inputs on the same
  *   device give bit-identical outputs.
- * Limits.  1 <= B < 2^24, 1 <= K <= 64, 1 <= V < 2^31, 0 <= F_k <= min(V, 64).
+ * Limits.  1 <= B < 2^24, 1 <= K <= 64, 1 <= V < 2^31, 0 <= F_k <= min(V, 64),
+ *   token trees of 1 <= N <= 64 nodes.
  */
 #ifndef SSD_H
 #define SSD_H
@@ -67,7 +68,7 @@ enum {
   SSD_EHIP = -4        /* the HIP runtime refused a launch */
 };
 
-enum { SSD_MAX_K = 64, SSD_MAX_F = 64 };
+enum { SSD_MAX_K = 64, SSD_MAX_F = 64, SSD_MAX_TREE = 64 };
 
 /* Position of one token in the top-F order of a draft row: an order-preserving
  * integer image of the logit (dtype specific) and the token index. Produced
@@ -222,6 +223,50 @@ SSD_API int ssd_draft_sample(const void* draft_logits, int64_t draft_bstride, in
                              int32_t B, int32_t K, int32_t V, float tau, const ssd_sigma* sigma,
                              const float* u, int32_t* tokens_out,
                              void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* Number of round kernels ssd_verify_tree launches for this topology (the
+ * most vocabulary passes one walk can need), or a negative status for an
+ * invalid parent array. Host only. */
+SSD_API int ssd_tree_rounds(const int32_t* parent, int32_t N);
+
+/* Bytes of workspace ssd_verify_tree needs (any topology of N nodes). */
+SSD_API size_t ssd_verify_tree_workspace_size(int32_t B, int32_t N, int32_t V, int dtype);
+
+/* Token-tree verification ([SD-notes] Extensions and Variants, Multi-
+ * candidate speculation: the draft proposes a tree of candidates and the
+ * target checks every path in one pass).
+ * Topology (host, shared by the batch): N nodes, node 0 the root (the
+ * position after the committed context), parent[0] = -1, 0 <= parent[n] < n.
+ * Node n >= 1 holds token tokens[b,n], drawn from the draft distribution at
+ * its parent; siblings are expected to be independent draws. For each batch
+ * row the walk starts at the root with P = p of the node (softmax of its
+ * target row / tau) and tests the node's children in index order with the
+ * one-candidate rule ([SD-notes] The Algorithm, step 3): child x is kept iff
+ * u_acc[b,x] * q(x) < P(x), q = softmax of the node's draft row / tau. After
+ * a rejection P becomes max(0, P - q)/Z (or p of the node if that has no
+ * mass) and the next sibling is tested. A kept child becomes the current
+ * node and its token is emitted. When the current node has no child left to
+ * test, one more token is drawn from P by inverse CDF in token order with
+ * u_res[b]: the residual of the last rejection, or p of the node (the bonus)
+ * when none of its children was tested; -1 if P has no mass.
+ *   target_logits device [B, N, V]: row n = target logits after node n's path
+ *   draft_logits  device [B, N, V]: row n = draft logits at node n (read only
+ *                 for nodes with children; may be NULL when N = 1)
+ *   tokens device int32 [B, N]; u_acc device float [B, N] in [0, 1) (entry 0
+ *   of both unused); u_res device float [B] in [0, 1)
+ * Outputs (device):
+ *   accepted   int32 [B]: depth a of the final node (tokens kept), -1 flagged
+ *   out_tokens int32 [B, N]: the a kept tokens, the drawn token, then -1
+ *   out_nodes  int32 [B, N] or NULL: nodes on the kept path, root first
+ *              (a+1 entries), then -1
+ * A token outside [0, V) at any node >= 1 flags the row (everything -1).
+ * Launches 1 + ssd_tree_rounds(parent, N) kernels on hip_stream. */
+SSD_API int ssd_verify_tree(const void* target_logits, int64_t target_bstride,
+                            const void* draft_logits, int64_t draft_bstride, int dtype,
+                            int32_t B, int32_t N, int32_t V, float tau, const int32_t* parent,
+                            const int32_t* tokens, const float* u_acc, const float* u_res,
+                            int32_t* accepted, int32_t* out_tokens, int32_t* out_nodes,
+                            void* workspace, size_t ws_bytes, void* hip_stream);
 
 /* Bytes of workspace ssd_build_cache needs. */
 SSD_API size_t ssd_build_cache_workspace_size(int32_t B, int32_t K, int32_t V, int dtype);

@@ -200,3 +200,55 @@ def test_oracle_not_imported_by_product():
             if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.replace("oracle-free", ""), f
+
+
+def _max_passes(children, node):
+    # brute force over walk outcomes: each rejection costs one vocabulary
+    # pass; all children rejected ends with the draw in the last one's pass;
+    # a node without children needs one pass for its bonus draw
+    ch = children[node]
+    best = max(len(ch), 1)
+    for i, c in enumerate(ch):
+        best = max(best, i + _max_passes(children, c))
+    return best
+
+
+def test_tree_rounds_match_bruteforce():
+    rng = np.random.default_rng(4)
+    cases = [[-1], [-1, 0], [-1, 0, 1, 2, 3], [-1] + [0] * 63, [-1, 0, 0, 1, 1, 2, 2]]
+    for _ in range(300):
+        N = int(rng.integers(1, 65))
+        cases.append([-1] + [int(rng.integers(0, n)) for n in range(1, N)])
+    for par in cases:
+        ch = O.tree_children(par)
+        assert S.ssd_tree_rounds(par) == _max_passes(ch, 0), par
+
+
+def test_verify_tree_argument_checks():
+    L = S.lib()
+
+    def call(parent=(-1, 0, 0), **kw):
+        a = dict(t=FAKE, tb=0, d=FAKE, db=0, dtype=S.SSD_BF16, B=2, V=100, tau=1.0, tok=FAKE, ua=FAKE, ur=FAKE,
+                 acc=FAKE, out=FAKE, nodes=None, ws=FAKE, wsz=1 << 30)
+        a.update(kw)
+        N = kw.pop("N", len(parent))
+        arr = (ctypes.c_int32 * max(len(parent), 1))(*parent)
+        return L.ssd_verify_tree(a["t"], a["tb"], a["d"], a["db"], a["dtype"], a["B"], N, a["V"], a["tau"], arr,
+                                 a["tok"], a["ua"], a["ur"], a["acc"], a["out"], a["nodes"], a["ws"], a["wsz"],
+                                 None)
+
+    assert call(dtype=3) == -2
+    assert call(B=0) == -1 and call(V=0) == -1
+    assert call(tau=0.0) == -1 and call(tau=float("nan")) == -1
+    assert call(parent=(0, 0, 0)) == -1 and b"root" in L.ssd_last_error()
+    assert call(parent=(-1, 0, 2)) == -1 and b"parent[2]" in L.ssd_last_error()
+    assert call(parent=(-1, 1)) == -1
+    assert call(parent=(-1,) + (0,) * 64) == -1                  # N = 65
+    assert call(d=None) == -1 and b"draft" in L.ssd_last_error()
+    assert call(tok=None) == -1 and call(ur=None) == -1 and call(out=None) == -1
+    assert call(tb=-2) == -1
+    assert call(ws=None, wsz=0) == -3 and call(wsz=64) == -3
+    assert S.ssd_verify_tree_workspace_size(2, 3, 100, S.SSD_BF16) > 0
+    assert S.ssd_verify_tree_workspace_size(2, 65, 100, S.SSD_BF16) == 0
+    with pytest.raises(S.SsdError):
+        S.ssd_tree_rounds([-1, 0, 5])

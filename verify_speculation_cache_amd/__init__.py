@@ -18,17 +18,17 @@ __all__ = ["SSD_F32", "SSD_BF16", "SsdError", "lib", "ssd_fanout", "ssd_verify",
            "ssd_speedup", "ssd_cache_stats", "Sigma",
            "ssd_verify_workspace_size", "ssd_residual_workspace_size",
            "ssd_build_cache_workspace_size", "ssd_draft_sample_workspace_size",
-           "ssd_verify_greedy_workspace_size", "EXPORTS",
-           "library_path"]
+           "ssd_verify_greedy_workspace_size", "ssd_verify_tree", "ssd_verify_tree_workspace_size",
+           "ssd_tree_rounds", "EXPORTS", "library_path"]
 
 SSD_F32, SSD_BF16 = 0, 1
-SSD_MAX_K, SSD_MAX_F = 64, 64
+SSD_MAX_K, SSD_MAX_F, SSD_MAX_TREE = 64, 64, 64
 EXPORTS = ("ssd_last_error", "ssd_fanout", "ssd_verify_workspace_size", "ssd_verify",
            "ssd_residual_workspace_size", "ssd_residual_sample",
            "ssd_build_cache_workspace_size", "ssd_build_cache", "ssd_cache_lookup",
            "ssd_draft_sample_workspace_size", "ssd_draft_sample",
            "ssd_verify_greedy_workspace_size", "ssd_verify_greedy", "ssd_fanout_uniform", "ssd_speedup",
-           "ssd_cache_stats")
+           "ssd_cache_stats", "ssd_tree_rounds", "ssd_verify_tree_workspace_size", "ssd_verify_tree")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -75,6 +75,10 @@ _SIGS = {
                                          _vp]),
     "ssd_draft_sample": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _i32, _i32, _i32, _f32, _vp, _vp, _vp,
                                         _vp, _sz, _vp]),
+    "ssd_tree_rounds": (ctypes.c_int, [_vp, _i32]),
+    "ssd_verify_tree_workspace_size": (_sz, [_i32, _i32, _i32, ctypes.c_int]),
+    "ssd_verify_tree": (ctypes.c_int, [_vp, _i64, _vp, _i64, ctypes.c_int, _i32, _i32, _i32, _f32, _vp,
+                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
 _lib = None
@@ -399,3 +403,58 @@ def ssd_cache_lookup(cache_tokens, F: Sequence[int], accepted, out_tokens, *, ou
 
 def sigma_from_cache(cache: dict, C: float) -> Sigma:
     return Sigma(C, cache["thr"], cache["draft_stats"])
+
+
+def _parent_array(parent: Sequence[int]):
+    N = len(parent)
+    return (ctypes.c_int32 * max(N, 1))(*[int(x) for x in parent]), N
+
+
+def ssd_tree_rounds(parent: Sequence[int]) -> int:
+    """Round kernels ssd_verify_tree launches for this topology."""
+    arr, N = _parent_array(parent)
+    return _check(lib().ssd_tree_rounds(arr, N))
+
+
+def ssd_verify_tree_workspace_size(B, N, V, dtype) -> int:
+    return int(lib().ssd_verify_tree_workspace_size(B, N, V, dtype))
+
+
+def ssd_verify_tree(target, draft, parent: Sequence[int], tokens, u_acc, u_res, tau: float, *,
+                    out: Optional[dict] = None, stream=None) -> dict:
+    """Token-tree verification. target/draft [B, N, V] (one row per node),
+    parent: host list of N ints (parent[0] = -1), tokens [B, N] int32,
+    u_acc [B, N] and u_res [B] float32. Returns accepted [B], out_tokens
+    [B, N] and out_nodes [B, N]."""
+    torch = _torch()
+    arr, N = _parent_array(parent)
+    if tokens.dim() != 2 or tokens.shape[1] != N:
+        raise ValueError("tokens must be [B, N] with N = len(parent)")
+    B = int(tokens.shape[0])
+    V = int(target.shape[2])
+    dt = _dtype_code(target)
+    if target.shape[0] != B or target.shape[1] != N:
+        raise ValueError("target must be [B, N, V]")
+    tp, tb = _logits(target, "target", N)
+    dp, db = None, 0
+    if draft is not None:
+        if _dtype_code(draft) != dt:
+            raise ValueError("target and draft dtypes differ")
+        if draft.shape[0] != B or draft.shape[1] != N:
+            raise ValueError("draft must be [B, N, V]")
+        dp, db = _logits(draft, "draft", N, V)
+    kp = _dev(tokens, torch.int32, (B, N), "tokens")
+    ua = _dev(u_acc, torch.float32, (B, N), "u_acc")
+    ur = _dev(u_res, torch.float32, (B,), "u_res")
+    if out is None:
+        out = {"accepted": torch.empty(B, dtype=torch.int32, device=target.device),
+               "out_tokens": torch.empty((B, N), dtype=torch.int32, device=target.device),
+               "out_nodes": torch.empty((B, N), dtype=torch.int32, device=target.device)}
+    nodes = out.get("out_nodes")
+    ws, wsz = _workspace(ssd_verify_tree_workspace_size(B, N, V, dt), target.device, ("tree", B, N, V, dt), stream)
+    _check(lib().ssd_verify_tree(tp, tb, dp, db, dt, B, N, V, float(tau), arr, kp, ua, ur,
+                                 _dev(out["accepted"], torch.int32, (B,), "accepted"),
+                                 _dev(out["out_tokens"], torch.int32, (B, N), "out_tokens"),
+                                 None if nodes is None else _dev(nodes, torch.int32, (B, N), "out_nodes"),
+                                 ws, wsz, _stream(stream)))
+    return out

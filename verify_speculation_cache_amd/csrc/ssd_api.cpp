@@ -86,6 +86,58 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// Token-tree topology from a host parent array: children lists in index
+// order, the statistics rows (targets of all nodes, then drafts of inner
+// nodes) and the number of rounds a walk can need.
+struct TreeTopo {
+  int N = 0, NR = 0, rounds = 0;
+  int8_t first_child[SSD_MAX_TREE], next_sib[SSD_MAX_TREE], parent[SSD_MAX_TREE];
+  int8_t drow[SSD_MAX_TREE], rnode[SSD_MAX_TREE];
+};
+
+int tree_topology(const int32_t* parent, int32_t N, TreeTopo& t) {
+  if (N < 1 || N > SSD_MAX_TREE) return fail(SSD_EINVAL, "N=%d outside [1, %d]", N, SSD_MAX_TREE);
+  if (parent == nullptr) return fail(SSD_EINVAL, "parent is NULL");
+  if (parent[0] != -1) return fail(SSD_EINVAL, "parent[0]=%d, the root's must be -1", parent[0]);
+  for (int n = 1; n < N; ++n)
+    if (parent[n] < 0 || parent[n] >= n)
+      return fail(SSD_EINVAL, "parent[%d]=%d outside [0, %d)", n, parent[n], n);
+  t.N = N;
+  int nch[SSD_MAX_TREE] = {0};
+  for (int n = 0; n < N; ++n) {
+    t.first_child[n] = -1;
+    t.next_sib[n] = -1;
+    t.parent[n] = int8_t(parent[n]);
+    t.drow[n] = -1;
+    t.rnode[n] = 0;
+  }
+  for (int n = N - 1; n >= 1; --n) {   // prepend in reverse: lists end up in index order
+    const int p = parent[n];
+    t.next_sib[n] = t.first_child[p];
+    t.first_child[p] = int8_t(n);
+    nch[p] += 1;
+  }
+  int inner = 0;
+  for (int n = 0; n < N; ++n)
+    if (nch[n] > 0) {
+      t.drow[n] = int8_t(N + inner);
+      t.rnode[inner] = int8_t(n);
+      ++inner;
+    }
+  t.NR = N + inner;
+  // A walk ending at node n made one pass per rejected sibling before each
+  // kept node on its path (the siblings with smaller index) and then
+  // max(children, 1) passes at n (every child rejected, or the bonus draw at
+  // a leaf); the largest such count over n is the number of rounds.
+  int extra[SSD_MAX_TREE], seen[SSD_MAX_TREE] = {0};
+  t.rounds = 0;
+  for (int n = 0; n < N; ++n) {
+    extra[n] = n == 0 ? 0 : extra[parent[n]] + seen[parent[n]]++;
+    t.rounds = std::max(t.rounds, extra[n] + std::max(nch[n], 1));
+  }
+  return SSD_OK;
+}
+
 }  // namespace
 
 using namespace ssd;
@@ -491,6 +543,78 @@ SSD_API int ssd_cache_lookup(const int32_t* cache_tokens, const int32_t* F, int3
   a.hit = hit;
   a.slot = slot;
   return hip_status(launch_lookup(a, as_stream(hip_stream)), "lookup launch");
+}
+
+SSD_API int ssd_tree_rounds(const int32_t* parent, int32_t N) {
+  TreeTopo t;
+  const int st = tree_topology(parent, N, t);
+  return st != SSD_OK ? st : t.rounds;
+}
+
+SSD_API size_t ssd_verify_tree_workspace_size(int32_t B, int32_t N, int32_t V, int dtype) {
+  if (B < 1 || B >= (1 << 24) || N < 1 || N > SSD_MAX_TREE || V < 1 || !dtype_ok(dtype)) return 0;
+  return TreeWs(B, N, 2 * N - 1, stats_chunks_per_row(V), chunks_per_row(V)).total;
+}
+
+SSD_API int ssd_verify_tree(const void* target_logits, int64_t target_bstride,
+                            const void* draft_logits, int64_t draft_bstride, int dtype,
+                            int32_t B, int32_t N, int32_t V, float tau, const int32_t* parent,
+                            const int32_t* tokens, const float* u_acc, const float* u_res,
+                            int32_t* accepted, int32_t* out_tokens, int32_t* out_nodes,
+                            void* workspace, size_t ws_bytes, void* hip_stream) {
+  int st;
+  if (!dtype_ok(dtype)) return fail(SSD_EDTYPE, "unknown dtype %d", dtype);
+  if (B < 1 || B >= (1 << 24)) return fail(SSD_EINVAL, "B=%d outside [1, 2^24)", B);
+  if (V < 1) return fail(SSD_EINVAL, "V=%d must be >= 1", V);
+  if ((st = check_tau(tau)) != SSD_OK) return st;
+  TreeTopo t;
+  if ((st = tree_topology(parent, N, t)) != SSD_OK) return st;
+  if (!target_logits || !tokens || !u_acc || !u_res || !accepted || !out_tokens)
+    return fail(SSD_EINVAL, "a required pointer is NULL");
+  if (N > 1 && !draft_logits) return fail(SSD_EINVAL, "draft_logits is NULL for a tree with inner nodes");
+  if (target_bstride < 0 || draft_bstride < 0) return fail(SSD_EINVAL, "negative batch stride");
+  const int64_t SS = stats_chunks_per_row(V), S = chunks_per_row(V);
+  // laid out for the largest statistics row count of N nodes, as the size query
+  const TreeWs tw(B, N, 2 * N - 1, SS, S);
+  if ((st = check_ws(workspace, ws_bytes, tw.total)) != SSD_OK) return st;
+  if ((st = check_grid(int64_t(B) * t.NR * SS)) != SSD_OK) return st;
+  if ((st = check_grid(int64_t(B) * S)) != SSD_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  TreeArgs a{};
+  a.target = target_logits;
+  a.tb = target_bstride;
+  a.draft = draft_logits;
+  a.db = draft_bstride;
+  a.B = B;
+  a.N = N;
+  a.V = V;
+  a.NR = t.NR;
+  a.SS = int(SS);
+  a.S = int(S);
+  a.c32 = float(kLog2e / double(tau));
+  std::memcpy(a.first_child, t.first_child, sizeof(a.first_child));
+  std::memcpy(a.next_sib, t.next_sib, sizeof(a.next_sib));
+  std::memcpy(a.parent, t.parent, sizeof(a.parent));
+  std::memcpy(a.drow, t.drow, sizeof(a.drow));
+  std::memcpy(a.rnode, t.rnode, sizeof(a.rnode));
+  a.tokens = tokens;
+  a.u_acc = u_acc;
+  a.u_res = u_res;
+  a.accepted = accepted;
+  a.out_tokens = out_tokens;
+  a.out_nodes = out_nodes;
+  a.part = reinterpret_cast<RowPartial*>(ws + tw.part);
+  a.rstat = reinterpret_cast<RowPartial*>(ws + tw.rstat);
+  a.pq = reinterpret_cast<double*>(ws + tw.pq);
+  a.state = reinterpret_cast<TreeState*>(ws + tw.state);
+  a.cmass = reinterpret_cast<double*>(ws + tw.cmass);
+  a.cnt_stats = reinterpret_cast<uint32_t*>(ws + tw.cnt_stats);
+  a.cnt_round = reinterpret_cast<uint32_t*>(ws + tw.cnt_round);
+  hipStream_t stream = as_stream(hip_stream);
+  if ((st = hip_status(launch_tree_stats(a, dtype, stream), "tree stats launch")) != SSD_OK) return st;
+  for (int r = 0; r < t.rounds; ++r)
+    if ((st = hip_status(launch_tree_round(a, dtype, stream), "tree round launch")) != SSD_OK) return st;
+  return ok();
 }
 
 }  // extern "C"

@@ -551,6 +551,44 @@ __device__ inline void merge_rows_seg(const uint64_t* part, int NR, int S, float
   }
 }
 
+// Statistics of one loaded chunk: the workgroup max m of the raw logits and
+// the sum of exp2((z - pivot_of(m)) * c32) (per-thread float sums, double
+// across threads). Called by every thread; both results are valid in every
+// thread (sm_f: 4 floats, sm_s: 4 doubles of LDS; two barriers).
+template <int DT, int PT>
+__device__ __forceinline__ void chunk_max_sum(const ChunkVecs<DT, true, PT>& cv, float c32, float* sm_f,
+                                              double* sm_s, float& m_out, double& s_out) {
+  constexpr int PV = Dt<DT>::kPerVec;
+  using CV = ChunkVecs<DT, true, PT>;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < CV::NV; ++j) {
+    float v[PV];
+    cv.get(j, v);
+#pragma unroll
+    for (int e = 0; e < PV; ++e) m = fmaxf(m, v[e]);
+  }
+  m = wave_max_u(m);
+  if (lane == 0) sm_f[w] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(sm_f[0], sm_f[1]), fmaxf(sm_f[2], sm_f[3]));
+  const float piv = pivot_of(m);
+  float sum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CV::NV; ++j) {
+    float v[PV];
+    cv.get(j, v);
+#pragma unroll
+    for (int e = 0; e < PV; ++e) sum += __builtin_amdgcn_exp2f((v[e] - piv) * c32);
+  }
+  const double wsum = wave_sum_u(double(sum));
+  if (lane == 0) sm_s[w] = wsum;
+  __syncthreads();
+  m_out = m;
+  s_out = (sm_s[0] + sm_s[1]) + (sm_s[2] + sm_s[3]);
+}
+
 // Count this workgroup in; returns true in every thread of the workgroup that
 // arrives last, which then reads the others' partials with dev_load. All
 // data a workgroup leaves for others is stored by its thread 0 with

@@ -222,6 +222,63 @@ struct SampleWs {
   }
 };
 
+// Token-tree verification. The topology is shared by the batch and fixed
+// on the host (node 0 = root, parent[n] < n); every node has a target row,
+// every node with children a draft row.
+constexpr int kMaxTree = SSD_MAX_TREE;
+
+// Walk state of one batch row between the rounds of a tree verification.
+// The distribution the next child of `node` is tested against is
+// max(0, p - c q) / nc (p itself when c = 0, nc = 1).
+struct alignas(16) TreeState {
+  int32_t node;     // current node
+  int32_t nxt;      // next child of node to test (-1: none left)
+  int32_t depth;    // accepted tokens so far
+  int32_t status;   // 1: a pass over (node, c) is pending; 0: row finished
+  double c, nc;
+};
+
+struct TreeArgs {
+  const void* target;
+  int64_t tb;
+  const void* draft;
+  int64_t db;
+  int B, N, V, NR, SS, S;   // NR statistics rows, SS stats chunks, S residual chunks
+  float c32;                // log2(e) / tau
+  int8_t first_child[kMaxTree];   // -1: leaf
+  int8_t next_sib[kMaxTree];      // -1: last child
+  int8_t parent[kMaxTree];        // -1 for the root
+  int8_t drow[kMaxTree];          // statistics row of the node's draft row (-1: leaf)
+  int8_t rnode[kMaxTree];         // node of statistics row N + j
+  const int32_t* tokens;    // [B, N]
+  const float* u_acc;       // [B, N]
+  const float* u_res;       // [B]
+  int32_t* accepted;        // [B]
+  int32_t* out_tokens;      // [B, N]
+  int32_t* out_nodes;       // [B, N] or nullptr
+  RowPartial* part;         // [B, NR, SS]
+  RowPartial* rstat;        // [B, NR]: merged (pivot, sum) per row
+  double* pq;               // [B, N, 2]: p and q of node n's token under its parent's rows
+  TreeState* state;         // [B]
+  double* cmass;            // [B, S, 2]
+  uint32_t* cnt_stats;      // [B] (kCntStride apart)
+  uint32_t* cnt_round;      // [B] (kCntStride apart)
+};
+
+struct TreeWs {
+  size_t part, rstat, pq, state, cmass, cnt_stats, cnt_round, total;
+  TreeWs(int64_t B, int64_t N, int64_t NR, int64_t SS, int64_t S) {
+    part = 0;
+    rstat = align256(part + sizeof(RowPartial) * B * NR * SS);
+    pq = align256(rstat + sizeof(RowPartial) * B * NR);
+    state = align256(pq + sizeof(double) * 2 * B * N);
+    cmass = align256(state + sizeof(TreeState) * B);
+    cnt_stats = align256(cmass + sizeof(double) * 2 * B * S);
+    cnt_round = align256(cnt_stats + sizeof(uint32_t) * kCntStride * B);
+    total = align256(cnt_round + sizeof(uint32_t) * kCntStride * B);
+  }
+};
+
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_stats(const StatsArgs& a, int dtype, hipStream_t st);
 hipError_t launch_resid(const ResidArgs& a, int dtype, bool sigma, hipStream_t st);
@@ -230,5 +287,7 @@ hipError_t launch_lookup(const LookupArgs& a, hipStream_t st);
 hipError_t launch_sample(const SampleArgs& a, int dtype, hipStream_t st);
 hipError_t launch_greedy(const GreedyArgs& a, int dtype, hipStream_t st);
 hipError_t launch_cache_stats(const CacheStatsArgs& a, hipStream_t st);
+hipError_t launch_tree_stats(const TreeArgs& a, int dtype, hipStream_t st);
+hipError_t launch_tree_round(const TreeArgs& a, int dtype, hipStream_t st);
 
 }  // namespace ssd

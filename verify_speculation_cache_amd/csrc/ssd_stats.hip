@@ -48,7 +48,6 @@ __device__ __forceinline__ bool in_top(float x, int32_t idx, uint32_t tkey, int3
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_stats(StatsArgs a) {
-  constexpr int PV = Dt<DT>::kPerVec;
   __shared__ float sm_f[4];
   __shared__ double sm_s[4];
   __shared__ int sm_last;
@@ -80,33 +79,10 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsArgs a) {
     }
     CV cv;
     cv.load(row, c0, a.V, (reinterpret_cast<uintptr_t>(row) & 15u) == 0, tid);
-    float m = -__builtin_inff();
-#pragma unroll
-    for (int j = 0; j < CV::NV; ++j) {
-      float v[PV];
-      cv.get(j, v);
-#pragma unroll
-      for (int e = 0; e < PV; ++e) m = fmaxf(m, v[e]);
-    }
-    m = wave_max_u(m);
-    if (lane == 0) sm_f[w] = m;
-    __syncthreads();
-    m = fmaxf(fmaxf(sm_f[0], sm_f[1]), fmaxf(sm_f[2], sm_f[3]));
-    const float piv = pivot_of(m);
-    float sum = 0.0f;
-#pragma unroll
-    for (int j = 0; j < CV::NV; ++j) {
-      float v[PV];
-      cv.get(j, v);
-#pragma unroll
-      for (int e = 0; e < PV; ++e) sum += __builtin_amdgcn_exp2f((v[e] - piv) * a.c32);
-    }
-    // per-thread sums in float, double across threads
-    const double wsum = wave_sum_u(double(sum));
-    if (lane == 0) sm_s[w] = wsum;
-    __syncthreads();
+    float m;
+    double sd;
+    chunk_max_sum(cv, a.c32, sm_f, sm_s, m, sd);
     if (tid == 0) {
-      const double sd = (sm_s[0] + sm_s[1]) + (sm_s[2] + sm_s[3]);
       uint64_t* wp = reinterpret_cast<uint64_t*>(a.part + (int64_t(b) * a.NR + r) * a.S + c);
       dev_store(wp, pack2(m, 0.0f));
       dev_store(wp + 1, dbits(sd));

@@ -30,7 +30,8 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["Config", "CONFIGS", "get_config", "make_inputs", "make_uniforms",
-           "f32_to_bf16_bits", "bf16_bits_to_f32", "sha256"]
+           "f32_to_bf16_bits", "bf16_bits_to_f32", "sha256",
+           "TreeConfig", "TREE_CONFIGS", "tree_parent", "make_tree_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -202,3 +203,106 @@ def make_inputs(cfg: Config, tau: Optional[float] = None, draw_tokens: bool = Tr
         "rows": np.asarray(rows, dtype=np.int64),
         "u_acc": np.ascontiguousarray(u_acc[rows]), "u_res": np.ascontiguousarray(u_res[rows]),
     }
+
+
+# ---------------------------------------------------------------------------
+# token trees
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class TreeConfig:
+    """One synthetic token-tree workload: every node at depth d has
+    branching[d] children (node numbering breadth first, so parents come
+    first); target and draft rows as in Config, one of each per node."""
+    name: str
+    seed: int
+    B: int
+    V: int
+    dtype: str
+    branching: tuple
+    target_sd: float
+    zipf_s: float
+    draft_sd: float
+    tau: float
+
+    @property
+    def parent(self) -> list:
+        return tree_parent(self.branching)
+
+    @property
+    def N(self) -> int:
+        return len(self.parent)
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+
+def tree_parent(branching) -> list:
+    """Parent array of the complete tree with the given per-depth branching."""
+    parent = [-1]
+    level = [0]
+    for k in branching:
+        nxt = []
+        for p in level:
+            for _ in range(int(k)):
+                parent.append(p)
+                nxt.append(len(parent) - 1)
+        level = nxt
+    return parent
+
+
+# The tree workload: 32 sequences over a 128256-entry vocabulary (the size of
+# the main verification workload), four candidates for the first token, two
+# continuations of each, then single chains to depth 4 (29 nodes).
+TREE_CONFIGS = {
+    "tree": TreeConfig("tree_B32_b4x2x1x1_V128256_bf16", 5, 32, 128256, "bf16", (4, 2, 1, 1),
+                       2.0, 1.1, 0.5, 0.7),
+}
+
+
+def make_tree_inputs(cfg: TreeConfig, b_rows: Optional[range] = None, u_seed: Optional[int] = None,
+                     parent: Optional[list] = None) -> dict:
+    """Generate one tree workload.
+
+    Returns target, draft [B, N, V] (uint16 bf16 bits or float32), tokens
+    [B, N] int32 (node n >= 1 drawn from softmax(draft row of its parent /
+    tau) with the Gumbel-max trick, siblings independently), u_acc [B, N]
+    and u_res [B] float32, parent and tau. `parent` overrides the topology
+    (any valid parent array); `u_seed` draws independent extra uniforms.
+    """
+    parent = cfg.parent if parent is None else list(parent)
+    N = len(parent)
+    B, V = cfg.B, cfg.V
+    rows = list(range(B) if b_rows is None else b_rows)
+    store = np.uint16 if cfg.dtype == "bf16" else np.float32
+    target = np.empty((len(rows), N, V), dtype=store)
+    draft = np.empty((len(rows), N, V), dtype=store)
+    tokens = np.zeros((len(rows), N), dtype=np.int32)
+    bias = _zipf_bias(V, cfg.zipf_s) if cfg.zipf_s > 0 else None
+    tau = float(np.float32(cfg.tau))
+    for out_i, b in enumerate(rows):
+        st = _row_streams(cfg.seed + 7919, b)
+        t = st["target"].standard_normal((N, V), dtype=np.float32)
+        t *= np.float32(cfg.target_sd)
+        if bias is not None:
+            t += st["perm"].permuted(np.broadcast_to(bias, (N, V)), axis=1)
+        d = st["draft"].standard_normal((N, V), dtype=np.float32)
+        d *= np.float32(cfg.draft_sd)
+        d += t
+        if cfg.dtype == "bf16":
+            target[out_i] = f32_to_bf16_bits(t)
+            draft[out_i] = f32_to_bf16_bits(d)
+            dvals = bf16_bits_to_f32(draft[out_i])
+        else:
+            target[out_i], draft[out_i] = t, d
+            dvals = d
+        if N > 1:
+            x = dvals[np.asarray(parent[1:])].astype(np.float64) / tau
+            tokens[out_i, 1:] = _gumbel_argmax(x, st["gumbel"])
+    key = [cfg.seed, 1000003, 11] + ([] if u_seed is None else [u_seed])
+    ga, gr = (np.random.Generator(np.random.PCG64(k)) for k in np.random.SeedSequence(key).spawn(2))
+    u_acc = ga.random((B, N), dtype=np.float32)
+    u_res = gr.random(B, dtype=np.float32)
+    return {"cfg": cfg, "tau": tau, "parent": parent, "target": target, "draft": draft, "tokens": tokens,
+            "rows": np.asarray(rows, dtype=np.int64),
+            "u_acc": np.ascontiguousarray(u_acc[rows]), "u_res": np.ascontiguousarray(u_res[rows])}
