@@ -37,6 +37,10 @@ def parse():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--workload", choices=["step", "tree"], default="step",
                     help="step: the verification + cache step (default); tree: token-tree verification")
+    ap.add_argument("--report", default=None,
+                    help="per-workload measurement report instead of the bench line: comma-separated "
+                         "workload numbers 1-5 (5 runs at tau 0.5 and 1.0), or 'all'; one JSON line each")
+    ap.add_argument("--calls", type=int, default=120, help="timed calls per workload in --report")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of graph replay")
@@ -56,6 +60,8 @@ def main():
               "kernel on B/N rows)", file=sys.stderr)
         sys.exit(2)
 
+    if args.report:
+        return bench_report(args)
     if args.workload == "tree":
         return bench_tree(args)
 
@@ -250,6 +256,123 @@ def main():
         "gen_s": round(gen_s, 2),
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_report(args):
+    """Per-workload report: the whole C-ABI call timed with HIP events around
+    it (median, p10, p90 over --calls back-to-back calls on rotating input
+    copies, ceil(512 MB / bytes) + 1 of them, so logits come from HBM), plus
+    the same call on one warm copy. Plain workloads time ssd_verify; cache
+    workloads time the step ssd_build_cache -> ssd_verify(sigma) ->
+    ssd_cache_lookup on drafts drawn on the GPU from q_sigma (ssd_draft_sample).
+    Bytes: single-read logits bytes of the call, and the early-exit minimum
+    (target rows 0..a and draft rows 0..min(a, K-1) per sequence; all draft
+    rows 0..K when the cache is built)."""
+    import torch
+    import verify_speculation_cache_amd as S
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    todo = []
+    ids = [1, 2, 3, 4, 5] if args.report == "all" else [int(x) for x in args.report.split(",")]
+    for c in ids:
+        for tau in W.get_config(c).taus:
+            todo.append((c, tau))
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    for c, tau in todo:
+        cfg = W.get_config(c)
+        B, K, V = cfg.B, cfg.K, cfg.V
+        elem = cfg.elem_bytes
+        t0 = time.time()
+        d = W.make_inputs(cfg, tau=tau, draw_tokens=not cfg.has_cache)
+        gen_s = time.time() - t0
+        cache_mode = cfg.has_cache and c != 2      # workload 2 is the plain-verify metric
+        n_draft = K + 1 if cache_mode else K
+        tgt0 = up(d["target"])
+        dft0 = up(d["draft"][:, :n_draft])
+        bytes_call = B * (K + 1 + n_draft) * V * elem
+        ncopy = int(math.ceil((512 << 20) / bytes_call)) + 1
+        tgts = [tgt0] + [tgt0.clone() for _ in range(ncopy - 1)]
+        dfts = [dft0] + [dft0.clone() for _ in range(ncopy - 1)]
+        ua = torch.from_numpy(d["u_acc"]).to(dev)
+        ur = torch.from_numpy(d["u_res"]).to(dev)
+        tau32 = d["tau"]
+        if cache_mode:
+            F = S.ssd_fanout(cfg.n_budget, K, cfg.a_p, cfg.r)
+            caches = [S.ssd_build_cache(dfts[j], tau32, F) for j in range(ncopy)]
+            gdraw = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.seed, 424242])))
+            u_draft = torch.from_numpy(gdraw.random((B, K), dtype=np.float32)).to(dev)
+            toks = S.ssd_draft_sample(dfts[0], u_draft, tau32, S.sigma_from_cache(caches[0], cfg.C))
+            outs = [S.ssd_verify(tgts[j], dfts[j], toks, ua, ur, tau32, S.sigma_from_cache(caches[j], cfg.C))
+                    for j in range(ncopy)]
+            looks = [S.ssd_cache_lookup(caches[j]["cache_tokens"], F, outs[j]["accepted"], outs[j]["out_tokens"])
+                     for j in range(ncopy)]
+
+            def call(j):
+                S.ssd_build_cache(dfts[j], tau32, F, out=caches[j])
+                S.ssd_verify(tgts[j], dfts[j], toks, ua, ur, tau32, S.sigma_from_cache(caches[j], cfg.C),
+                             out=outs[j])
+                S.ssd_cache_lookup(caches[j]["cache_tokens"], F, outs[j]["accepted"], outs[j]["out_tokens"],
+                                   out=looks[j])
+        else:
+            toks = torch.from_numpy(d["tokens"]).to(dev)
+            outs = [S.ssd_verify(tgts[j], dfts[j], toks, ua, ur, tau32) for j in range(ncopy)]
+
+            def call(j):
+                S.ssd_verify(tgts[j], dfts[j], toks, ua, ur, tau32, out=outs[j])
+        torch.cuda.synchronize()
+
+        def timed(n, rotate):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+            for i in range(n):
+                j = i % ncopy if rotate else 0
+                ev[i][0].record()
+                call(j)
+                ev[i][1].record()
+            torch.cuda.synchronize()
+            return sorted(a.elapsed_time(b) for a, b in ev)
+
+        timed(10, True)
+        ts = timed(args.calls, True)
+        warm = timed(max(20, args.calls // 4), False)
+        med, p10, p90 = ts[len(ts) // 2], ts[len(ts) // 10], ts[(9 * len(ts)) // 10]
+        acc = outs[0]["accepted"].cpu().numpy()
+        ok = acc >= 0
+        a = acc[ok]
+        rows_min = np.sum(a + 1) + (B * n_draft if cache_mode else np.sum(np.minimum(a + 1, K)))
+        bytes_min = int(rows_min) * V * elem
+        alpha = [float(np.sum(a > i) / max(1, np.sum(a >= i))) for i in range(K)]
+        line = {
+            "report": "per_workload", "workload": cfg.name, "B": B, "K": K, "V": V, "dtype": cfg.dtype,
+            "tau": tau, "call": ("ssd_build_cache + ssd_verify(sigma) + ssd_cache_lookup" if cache_mode
+                                 else "ssd_verify"),
+            "calls": args.calls, "rotating_copies": ncopy,
+            "t_call_us": {"median": round(med * 1e3, 2), "p10": round(p10 * 1e3, 2), "p90": round(p90 * 1e3, 2)},
+            "warm_single_copy_us": round(warm[len(warm) // 2] * 1e3, 2),
+            "rows_per_s": round(B / (med / 1e3), 1),
+            "bytes_single_read": bytes_call,
+            "eff_gbps": round(bytes_call / (med / 1e3) / 1e9, 1),
+            "pct_peak": round(100 * bytes_call / (med / 1e3) / 1e9 / PEAK_HBM_GBS, 2),
+            "early_exit_min_bytes": bytes_min,
+            "early_exit_min_gbps": round(bytes_min / (med / 1e3) / 1e9, 1),
+            "alpha_empirical": [round(x, 4) for x in alpha],
+            "mean_accepted_plus_1": round(float(np.mean(a + 1)), 4),
+            "flagged_rows": int(np.sum(~ok)),
+            "gen_s": round(gen_s, 1),
+        }
+        if cache_mode:
+            line["hit_rate"] = round(float(looks[0]["hit"].float().mean().item()), 4)
+            line["F"] = F
+            line["C"] = cfg.C
+        print(json.dumps(line), flush=True)
+        del tgts, dfts, tgt0, dft0, outs
+        torch.cuda.empty_cache()
 
 
 def bench_tree(args):
