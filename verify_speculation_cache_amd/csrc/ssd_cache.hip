@@ -12,17 +12,18 @@
 // Order: logit descending, then token index ascending, on order-preserving
 // integer keys (exact, no tolerance).
 //
-// Thresholds. In a wave (2048 entries, 32 per lane), let T0_w be the F-th
-// largest per-lane maximum key. F lanes each hold an entry >= T0_w, so the
-// wave, its chunk and its row all have at least F entries >= T0_w. Hence the
-// F-th largest entry of a chunk is >= T0 = max over its waves of T0_w, and
-// that of a row is >= the max of its chunks' T0: an entry below either bound
-// can never be in the top F.
+// Thresholds. Any key t such that at least F lanes of a chunk hold an entry
+// >= t (their lane maximum) bounds the chunk's F-th largest entry from
+// below, and so the row's: an entry below it can never be in the top F. In a
+// wave (2048 entries, 32 per lane) let T0_w be the F-th largest lane maximum
+// and Q_w the ceil(F/4)-th largest; both max_w T0_w and min_w Q_w are such
+// bounds (the latter through 4 x ceil(F/4) >= F lanes), and the chunk's T0 is
+// the larger of the two.
 //
 // Two launches.
 //  k_cache_chunk, one workgroup per (batch row b, length k, chunk c): 8192
-//  logits in registers; chunk max and T0; entries >= T0 (typically 2-3 F of
-//  8192) are written out unsorted as candidates, and the exp-mass of all
+//  logits in registers; chunk max and T0; entries >= T0 (about F of 8192 for
+//  the synthetic logits) are written out unsorted as candidates, and the exp-mass of all
 //  other entries is summed. If ties push the candidates past kCandCap the
 //  chunk is only flagged.
 //  k_cache_merge, one workgroup per row (b, k): re-reads flagged chunks and
@@ -507,7 +508,7 @@ __global__ __launch_bounds__(kThreads) void k_cache_chunk(CacheArgs a) {
   constexpr int PV = Dt<DT>::kPerVec;
   constexpr int NV = kPerThread / PV;
   __shared__ float sm_wmax[4];
-  __shared__ uint32_t sm_wthr[4];
+  __shared__ uint32_t sm_wthr[4], sm_wthq[4];
   __shared__ int sm_wcnt[4];
   __shared__ double sm_ws[4];
   __shared__ uint64_t sm_list[4][kCandCap];   // per-wave candidate staging
@@ -548,25 +549,38 @@ __global__ __launch_bounds__(kThreads) void k_cache_chunk(CacheArgs a) {
   for (int j = 1; j < NV; ++j) lm = fmaxf(lm, vm[j]);
   const float c32 = a.c32;
 
-  // ---- per-wave max and threshold T0_w; chunk max and T0 ----
+  // ---- per-wave max and thresholds; chunk max and T0 ----
+  // A key t with at least F lanes whose maximum is >= t bounds the chunk's
+  // top F from below. Two such bounds, the larger taken: the F-th largest
+  // lane maximum of one wave (max over waves), and the smallest over waves of
+  // each wave's ceil(F/4)-th largest lane maximum (4 waves x ceil(F/4) >= F
+  // lanes). The second is far tighter for large F (about F candidates rather
+  // than several times F).
   {
     const float wm = wave_max_u(lm);
-    uint32_t t = 0;
+    uint32_t t = 0, tq = 0;
     if (F > 0) {
+      const int Fq = (F + 3) >> 2;
       const uint32_t kl = local_of<DT>(tid, 0) < nvalid ? key_of<DT>(lm) : 0u;
       for (int bit = Dt<DT>::kKeyBits - 1; bit >= 0; --bit) {
         const uint32_t cand = t | (1u << bit);
         if (__popcll(__ballot(kl >= cand)) >= F) t = cand;
       }
+      for (int bit = Dt<DT>::kKeyBits - 1; bit >= 0; --bit) {
+        const uint32_t cand = tq | (1u << bit);
+        if (__popcll(__ballot(kl >= cand)) >= Fq) tq = cand;
+      }
     }
     if (lane == 0) {
       sm_wmax[w] = wm;
       sm_wthr[w] = t;
+      sm_wthq[w] = tq;
     }
   }
   __syncthreads();
   const float mc = fmaxf(fmaxf(sm_wmax[0], sm_wmax[1]), fmaxf(sm_wmax[2], sm_wmax[3]));
-  const uint32_t t0 = max(max(sm_wthr[0], sm_wthr[1]), max(sm_wthr[2], sm_wthr[3]));
+  const uint32_t t0 = max(max(max(sm_wthr[0], sm_wthr[1]), max(sm_wthr[2], sm_wthr[3])),
+                          min(min(sm_wthq[0], sm_wthq[1]), min(sm_wthq[2], sm_wthq[3])));
   const float piv = pivot_of(mc);
   float f0 = __builtin_nanf("");   // F == 0: compares false, nothing is a candidate
   if (F > 0) f0 = (t0 <= key_of<DT>(-__builtin_inff())) ? -__builtin_inff() : value_of_key<DT>(t0);
