@@ -48,7 +48,6 @@ struct PickLds {
   double scan[4];
   int pick[4];
   int best[4];
-  uint4 run[NROW][kPerThread / Dt<DT>::kPerVec];   // the crossing thread's entries
   double base;
   int lastpos;
   int tok;
@@ -57,15 +56,17 @@ struct PickLds {
 // Token pick inside chunk [c0, c0 + 8192) whose running mass starts at
 // `pre`: every thread owns 32 consecutive tokens of NROW rows (raw vectors in
 // cv, contiguous layout); value(x, idx) is the mass of token idx from its
-// NROW logits x. Thread totals are scanned in double; the crossing thread
-// hands its run to wave 0 through LDS for a parallel rescan. If rounding
-// keeps the running mass at or below `target` through a run, the run's last
-// token with mass is taken (the chunk's, if no thread crosses). Called by
-// every thread of the workgroup; returns the token (-1: no mass).
+// NROW logits x. Thread totals are scanned in double; wave 0 then re-reads
+// the crossing thread's 32 tokens of every row (from cache: the workgroup
+// has just loaded them) for a parallel rescan, so no thread keeps its
+// vectors live across the scan. If rounding keeps the running mass at or
+// below `target` through a run, the run's last token with mass is taken (the
+// chunk's, if no thread crosses). Called by every thread of the workgroup;
+// returns the token (-1: no mass).
 template <int DT, int NROW, class ValueFn>
-__device__ __forceinline__ int chunk_pick(const ChunkVecs<DT, false> (&cv)[NROW], int64_t c0, double pre,
-                                          double target, ValueFn value, PickLds<DT, NROW>& L) {
-  using T = typename Dt<DT>::T;
+__device__ __forceinline__ int chunk_pick(const ChunkVecs<DT, false> (&cv)[NROW],
+                                          const typename Dt<DT>::T* const (&rows)[NROW], int64_t V, int64_t c0,
+                                          double pre, double target, ValueFn value, PickLds<DT, NROW>& L) {
   constexpr int PV = Dt<DT>::kPerVec;
   constexpr int NV = kPerThread / PV;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -86,6 +87,10 @@ __device__ __forceinline__ int chunk_pick(const ChunkVecs<DT, false> (&cv)[NROW]
       tot += double(v);
       if (v > 0.0f) lastpos = j * PV + e;
     }
+    // one vector at a time: keeps the unpacked values of later vectors out
+    // of registers, so this tail of the kernel needs no more of them than
+    // the streaming part
+    __builtin_amdgcn_sched_barrier(0);
   }
   // exclusive scan of thread totals (thread order = token order)
   const double incl_w = wave_incl_scan_d(tot, lane);
@@ -101,10 +106,6 @@ __device__ __forceinline__ int chunk_pick(const ChunkVecs<DT, false> (&cv)[NROW]
   const int first = min(min(L.pick[0], L.pick[1]), min(L.pick[2], L.pick[3]));
   if (first != 0x7FFFFFFF) {
     if (tid == first) {
-#pragma unroll
-      for (int r = 0; r < NROW; ++r)
-#pragma unroll
-        for (int q = 0; q < NV; ++q) L.run[r][q] = cv[r].raw[q];
       L.base = base;
       L.lastpos = lastpos;
     }
@@ -114,7 +115,7 @@ __device__ __forceinline__ int chunk_pick(const ChunkVecs<DT, false> (&cv)[NROW]
       const int f0 = int(c0) + first * kPerThread;
       float x[NROW];
 #pragma unroll
-      for (int r = 0; r < NROW; ++r) x[r] = Dt<DT>::to_f(reinterpret_cast<const T*>(&L.run[r][0])[q]);
+      for (int r = 0; r < NROW; ++r) x[r] = f0 + q < V ? Dt<DT>::to_f(rows[r][f0 + q]) : -__builtin_inff();
       const float v = value(x, f0 + q);
       const double cum = L.base + wave_incl_scan_d(lane < 32 ? double(v) : 0.0, lane);
       const uint64_t cr = __ballot(lane < 32 && cum > target);
