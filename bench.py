@@ -35,8 +35,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2)
-    ap.add_argument("--workload", choices=["step", "tree"], default="step",
-                    help="step: the verification + cache step (default); tree: token-tree verification")
+    ap.add_argument("--workload", choices=["step", "tree", "greedy", "sample"], default="step",
+                    help="step: the verification + cache step (default); tree: token-tree verification; "
+                         "greedy: greedy verification; sample: sigma-aware draft sampling")
     ap.add_argument("--report", default=None,
                     help="per-workload measurement report instead of the bench line: comma-separated "
                          "workload numbers 1-5 (5 runs at tau 0.5 and 1.0), or 'all'; one JSON line each")
@@ -64,6 +65,8 @@ def main():
         return bench_report(args)
     if args.workload == "tree":
         return bench_tree(args)
+    if args.workload in ("greedy", "sample"):
+        return bench_rows(args)
 
     import torch
     import verify_speculation_cache_amd as S
@@ -375,6 +378,143 @@ def bench_report(args):
         torch.cuda.empty_cache()
 
 
+def _graph_time(step, ncopy, args):
+    """Capture step(j) for every rotating copy j as a HIP graph (after one
+    eager warm-up of the per-shape workspaces on the capture stream), replay
+    args.warmup untimed then args.steps timed, HIP events around the loop.
+    Returns ms per step."""
+    import torch
+    stream = torch.cuda.Stream()
+    graphs = []
+    if not args.eager:
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            for j in range(ncopy):
+                step(j)
+        torch.cuda.synchronize()
+        for j in range(ncopy):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                step(j)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(n, offset=0):
+        for i in range(n):
+            j = (offset + i) % ncopy
+            if graphs:
+                graphs[j].replay()
+            else:
+                step(j)
+
+    run(args.warmup)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run(args.steps, args.warmup)
+    e1.record()
+    torch.cuda.synchronize()
+    if args.profile_loop:
+        for i in range(args.profile_loop):
+            step(i % ncopy)
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / args.steps
+
+
+def bench_rows(args):
+    """Greedy verification or sigma-aware draft sampling on the main workload's
+    shape (B=64, K=5, V=128256, bf16, tau=0.7): one step = one library call.
+    greedy: ssd_verify_greedy on target rows 0..K (drafted tokens from the
+    workload); sample: ssd_draft_sample on draft rows 0..K-1 with sigma_{F,C}
+    from ssd_build_cache (budget 64, a_p 0.8, r 1, C 0.5), built once before
+    timing. Bytes: each row the call reads, once."""
+    import torch
+    import verify_speculation_cache_amd as S
+    import workloads as W
+
+    cfg = W.get_config(2)
+    B, K, V, tau = cfg.B, cfg.K, cfg.V, cfg.taus[0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    d = W.make_inputs(cfg, tau=tau)
+    gen_s = time.time() - t0
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    greedy = args.workload == "greedy"
+    src = d["target"] if greedy else d["draft"][:, :K + 1]
+    x0 = up(src)
+    rows_read = K + 1 if greedy else K
+    bytes_call = B * rows_read * V * 2
+    ncopy = int(math.ceil(MALL_BYTES / bytes_call)) + 1
+    xs = [x0] + [x0.clone() for _ in range(ncopy - 1)]
+    toks = torch.from_numpy(d["tokens"]).to(dev)
+    if greedy:
+        outs = [S.ssd_verify_greedy(xs[j], toks) for j in range(ncopy)]
+
+        def step(j):
+            S.ssd_verify_greedy(xs[j], toks, out=outs[j])
+    else:
+        F = S.ssd_fanout(cfg.n_budget, K, cfg.a_p, cfg.r)
+        sig = [S.sigma_from_cache(S.ssd_build_cache(xs[j], tau, F), cfg.C) for j in range(ncopy)]
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.seed, 424242])))
+        u_np = g.random((B, K), dtype=np.float32)
+        u = torch.from_numpy(u_np).to(dev)
+        outs = [S.ssd_draft_sample(xs[j], u, tau, sig[j]) for j in range(ncopy)]
+
+        def step(j):
+            S.ssd_draft_sample(xs[j], u, tau, sig[j], out=outs[j])
+    torch.cuda.synchronize()
+    ref = [(o["out_tokens"] if greedy else o).clone() for o in outs]
+    ms_step = _graph_time(step, ncopy, args)
+    for j, o in enumerate(outs):
+        assert torch.equal(o["out_tokens"] if greedy else o, ref[j])
+    gbps = bytes_call / (ms_step / 1e3) / 1e9
+    cpu = None
+    if not args.no_cpu:
+        import oracle as O
+        t0 = time.time()
+        n = 0
+        while n < B and (time.time() - t0) < args.cpu_seconds:
+            sl = slice(n, n + 1)
+            if greedy:
+                O.verify_greedy(d["target"][sl], d["tokens"][sl])
+            else:
+                O.draft_sample(d["draft"][sl], d["tau"], u_np[sl], F, cfg.C)
+            n += 1
+        dt = time.time() - t0
+        cpu = {"value": round(n / dt, 3), "unit": "rows/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {n} of {B} batch rows of the same call, float64 NumPy, {dt:.1f} s"
+                         + ("" if greedy else " (the oracle takes each row's top-F for sigma itself)")}
+    name = "ssd_verify_greedy" if greedy else "ssd_draft_sample"
+    kern = "k_greedy<1>" if greedy else "k_sample<1, true>"
+    line = {
+        "metric": ("greedy-verified rows/sec" if greedy else "sigma-drafted rows/sec") + ", B=64 K=5 V=128256 bf16",
+        "value": round(B / (ms_step / 1e3), 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded Gaussian + Zipf-rank logits, draft = target + noise)",
+        "config": {"workload": name, "B": B, "K": K, "V": V, "logits": cfg.dtype, "tau": tau,
+                   "rotating_copies": ncopy, "graph_replay": not args.eager},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": f"{name} ({kern}, one launch)", "bytes_per_launch": bytes_call,
+                     "avg_launch_ms": round(ms_step, 5)},
+        "cpu_baseline": cpu,
+        "gen_s": round(gen_s, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def bench_tree(args):
     """Token-tree verification on its workload: B=32 sequences, a 29-node
     tree (4 first-token candidates, 2 continuations each, then chains to
@@ -415,43 +555,9 @@ def bench_tree(args):
     def step(j):
         S.ssd_verify_tree(tgts[j], dfts[j], parent, toks, ua, ur, cfg.tau, out=outs[j])
 
-    stream = torch.cuda.Stream()
-    graphs = []
-    if not args.eager:
-        stream.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(stream):
-            for j in range(ncopy):
-                step(j)
-        torch.cuda.synchronize()
-        for j in range(ncopy):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                step(j)
-            graphs.append(g)
-        torch.cuda.synchronize()
-
-    def run(n, offset=0):
-        for i in range(n):
-            j = (offset + i) % ncopy
-            if graphs:
-                graphs[j].replay()
-            else:
-                step(j)
-
-    run(args.warmup)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    run(args.steps, args.warmup)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step = _graph_time(step, ncopy, args)
     for j, o in enumerate(outs):
         assert torch.equal(o["accepted"], ref[j][0]) and torch.equal(o["out_tokens"], ref[j][1])
-    if args.profile_loop:
-        for i in range(args.profile_loop):
-            step(i % ncopy)
-        torch.cuda.synchronize()
     acc = outs[0]["accepted"].cpu().numpy()
     gbps = bytes_single / (ms_step / 1e3) / 1e9
     cpu = None

@@ -11,7 +11,8 @@
 //
 // The draw is by inverse CDF in token-index order: the smallest v whose
 // running mass exceeds u * Z. One workgroup per (batch row b, position i,
-// 8192-chunk c) sums the chunk's weighted mass against the chunk's own max;
+// pair of 8192-chunks) sums each chunk's weighted mass against the chunk's
+// own max;
 // the last workgroup of row (b, i) rescales the chunk masses to the row max,
 // finds the crossing chunk and picks the token inside it. A row without mass
 // (all logits -inf) draws -1.
@@ -48,9 +49,9 @@ template <int DT, bool SIG>
 __global__ __launch_bounds__(kThreads) void k_sample(SampleArgs a) {
   using T = typename Dt<DT>::T;
   constexpr int PV = Dt<DT>::kPerVec;
-  constexpr int NV = kPerThread / PV;
-  __shared__ float sm_f[4];
-  __shared__ double sm_s[4];
+  constexpr int NV2 = kStatsPerThread / PV;
+  __shared__ float sm_f[8];
+  __shared__ double sm_s[8];
   __shared__ int sm_last;
   __shared__ int sm_c;
   __shared__ double sm_pre, sm_target;
@@ -58,54 +59,73 @@ __global__ __launch_bounds__(kThreads) void k_sample(SampleArgs a) {
   __shared__ PickLds<DT, 1> sm_pk;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t rowid = blockIdx.x / a.S;
-  const int c = int(blockIdx.x - rowid * a.S);
+  const int S2 = (a.S + 1) / 2;   // workgroups per row, two 8192-chunks each
+  const int64_t rowid = blockIdx.x / S2;
+  const int c2 = int(blockIdx.x - rowid * S2);
   const int b = int(rowid / a.K);
   const int i = int(rowid - int64_t(b) * a.K);
   const T* row = static_cast<const T*>(a.draft) + int64_t(b) * a.db + int64_t(i) * a.V;
   const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
   const SigmaTest sg = sigma_test<DT, SIG>(a, b, i);
 
-  // ---------------- phase A: chunk max and weighted chunk mass ----------------
+  // ---------------- phase A: max and weighted mass of two 8192-chunks ----------------
+  // A workgroup reads 16384 entries (64 per thread, strided: vectors j <
+  // NV/2 lie in the first 8192, the others in the second) and writes one
+  // partial per 8192-chunk, so the draw below keeps 8192-entry chunks.
   {
-    const int64_t c0 = int64_t(c) * kChunk;
-    ChunkVecs<DT, true> cv;
+    constexpr int NVH = NV2 / 2;
+    const int64_t c0 = int64_t(c2) * kStatsChunk;
+    ChunkVecs<DT, true, kStatsPerThread> cv;
     cv.load(row, c0, a.V, aligned, tid);
-    float m = -__builtin_inff();
+    float m[2] = {-__builtin_inff(), -__builtin_inff()};
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
+    for (int j = 0; j < NV2; ++j) {
       float v[PV];
       cv.get(j, v);
 #pragma unroll
-      for (int e = 0; e < PV; ++e) m = fmaxf(m, v[e]);
+      for (int e = 0; e < PV; ++e) m[j / NVH] = fmaxf(m[j / NVH], v[e]);
     }
-    m = wave_max_u(m);
-    if (lane == 0) sm_f[w] = m;
+    m[0] = wave_max_u(m[0]);
+    m[1] = wave_max_u(m[1]);
+    if (lane == 0) {
+      sm_f[w] = m[0];
+      sm_f[4 + w] = m[1];
+    }
     __syncthreads();
-    m = fmaxf(fmaxf(sm_f[0], sm_f[1]), fmaxf(sm_f[2], sm_f[3]));
-    const float pc = pivot_of(m);
-    float sum = 0.0f;
+    m[0] = fmaxf(fmaxf(sm_f[0], sm_f[1]), fmaxf(sm_f[2], sm_f[3]));
+    m[1] = fmaxf(fmaxf(sm_f[4], sm_f[5]), fmaxf(sm_f[6], sm_f[7]));
+    const float pc[2] = {pivot_of(m[0]), pivot_of(m[1])};
+    float sum[2] = {0.0f, 0.0f};
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
+    for (int j = 0; j < NV2; ++j) {
       float v[PV];
       cv.get(j, v);
-      const int i0 = int(c0) + ChunkVecs<DT, true>::local(tid, j);
+      const int i0 = int(c0) + ChunkVecs<DT, true, kStatsPerThread>::local(tid, j);
 #pragma unroll
       for (int e = 0; e < PV; ++e) {
-        const float ex = __builtin_amdgcn_exp2f((v[e] - pc) * a.c32);
-        sum += SIG ? sg.weight(v[e], i0 + e) * ex : ex;
+        const float ex = __builtin_amdgcn_exp2f((v[e] - pc[j / NVH]) * a.c32);
+        sum[j / NVH] += SIG ? sg.weight(v[e], i0 + e) * ex : ex;
       }
     }
-    const double ws = wave_sum_u(double(sum));
-    if (lane == 0) sm_s[w] = ws;
+    const double ws0 = wave_sum_u(double(sum[0]));
+    const double ws1 = wave_sum_u(double(sum[1]));
+    if (lane == 0) {
+      sm_s[w] = ws0;
+      sm_s[4 + w] = ws1;
+    }
     __syncthreads();
     if (tid == 0) {
-      uint64_t* wp = reinterpret_cast<uint64_t*>(a.part + rowid * a.S + c);
-      dev_store(wp, pack2(m, 0.0f));
+      const int cc = 2 * c2;
+      uint64_t* wp = reinterpret_cast<uint64_t*>(a.part + rowid * a.S + cc);
+      dev_store(wp, pack2(m[0], 0.0f));
       dev_store(wp + 1, dbits((sm_s[0] + sm_s[1]) + (sm_s[2] + sm_s[3])));
+      if (cc + 1 < a.S) {
+        dev_store(wp + 2, pack2(m[1], 0.0f));
+        dev_store(wp + 3, dbits((sm_s[4] + sm_s[5]) + (sm_s[6] + sm_s[7])));
+      }
     }
   }
-  if (!arrive_last(&a.cnt[rowid * kCntStride], uint32_t(a.S), &sm_last)) return;
+  if (!arrive_last(&a.cnt[rowid * kCntStride], uint32_t(S2), &sm_last)) return;
 
   // ---------------- phase B: last workgroup of row (b, i) ----------------
   if (w == 0) {
@@ -166,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void k_sample(SampleArgs a) {
 }
 
 hipError_t launch_sample(const SampleArgs& a, int dtype, hipStream_t st) {
-  const unsigned grid = unsigned(int64_t(a.B) * a.K * a.S);
+  const unsigned grid = unsigned(int64_t(a.B) * a.K * ((a.S + 1) / 2));
   const bool sig = a.thr != nullptr;
   if (dtype == SSD_BF16) {
     if (sig) hipLaunchKernelGGL((k_sample<1, true>), dim3(grid), dim3(kThreads), 0, st, a);
