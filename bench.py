@@ -1,8 +1,10 @@
 """Throughput of the speculative verification + SAGUARO cache path on one GPU.
 
-One step = one pass of the whole path over one batch:
-  ssd_fanout (host)  ->  ssd_build_cache (draft rows 0..K)  ->
-  ssd_verify with sigma_{F,C}  ->  ssd_cache_lookup.
+One step = one pass of the whole path over one batch: ssd_fanout (host),
+then ssd_verify_round (the cache build on draft rows 0..K, verification
+against sigma_{F,C}, the cache lookup: three launches). --separate runs the
+same step as ssd_build_cache -> ssd_verify (sigma) -> ssd_cache_lookup (five
+launches); both give bit-identical outputs, which the bench checks.
 Default workload: B=64 sequences, K=5 drafted tokens, V=128256, bf16 logits,
 tau=0.7, cache budget 64 split with a_p=0.8, r=1, C=0.5.
 
@@ -45,6 +47,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of graph replay")
+    ap.add_argument("--separate", action="store_true",
+                    help="run the step as three calls (ssd_build_cache, ssd_verify, ssd_cache_lookup) instead of "
+                         "the fused ssd_verify_round")
     ap.add_argument("--profile-loop", type=int, default=0,
                     help="after the bench, run this many extra eager steps (for profilers)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -116,7 +121,27 @@ def main():
         outs.append((cache, res, look))
     torch.cuda.synchronize()
 
+    rounds = [S.ssd_verify_round(tgts[j], dfts[j], F, C, toks, ua, ur, tau) for j in range(ncopy)]
+    torch.cuda.synchronize()
+    # the fused round builds the same cache bit for bit; its verification sums
+    # rows over other chunk partials, so an outcome may differ from the three
+    # calls' only where a decision is within rounding of its threshold
+    round_rows_differ = 0
+    for j in range(ncopy):
+        cache, res, look = outs[j]
+        for k, v in (("cache_tokens", cache["cache_tokens"]), ("draft_stats", cache["draft_stats"]),
+                     ("thr", cache["thr"])):
+            assert torch.equal(rounds[j][k], v), k
+        same = ((rounds[j]["accepted"] == res["accepted"]) & (rounds[j]["out_tokens"] == res["out_tokens"]).all(1)
+                & (rounds[j]["hit"] == look["hit"]))
+        round_rows_differ += int((~same).sum().item())
+    sep_ref = [(o[1]["accepted"].clone(), o[1]["out_tokens"].clone(), o[2]["hit"].clone()) for o in outs]
+    round_ref = [(r["accepted"].clone(), r["out_tokens"].clone(), r["hit"].clone()) for r in rounds]
+
     def step(j):
+        if not args.separate:
+            S.ssd_verify_round(tgts[j], dfts[j], F, C, toks, ua, ur, tau, out=rounds[j])
+            return
         cache, res, look = outs[j]
         S.ssd_build_cache(dfts[j], tau, F, out=cache)
         S.ssd_verify(tgts[j], dfts[j], toks, ua, ur, tau, S.sigma_from_cache(cache, C), out=res)
@@ -157,7 +182,14 @@ def main():
     ms_step = e0.elapsed_time(e1) / args.steps
 
     # replays must reproduce the eager outputs
-    ref = [(o[1]["accepted"].clone(), o[1]["out_tokens"].clone(), o[2]["hit"].clone()) for o in outs]
+    for j in range(ncopy):
+        if args.separate:
+            got = (outs[j][1]["accepted"], outs[j][1]["out_tokens"], outs[j][2]["hit"])
+            want = sep_ref[j]
+        else:
+            got = (rounds[j]["accepted"], rounds[j]["out_tokens"], rounds[j]["hit"])
+            want = round_ref[j]
+        assert all(torch.equal(x, y) for x, y in zip(got, want))
 
     # per-entry-point durations (eager, events on the launching stream)
     def time_call(fn, n=60):
@@ -192,8 +224,8 @@ def main():
     t_plain = time_call(call_plain)
     t_lookup = time_call(call_lookup)
     for j, o in enumerate(outs):
-        assert torch.equal(o[1]["accepted"], ref[j][0]) and torch.equal(o[1]["out_tokens"], ref[j][1])
-        assert torch.equal(o[2]["hit"], ref[j][2])
+        assert torch.equal(o[1]["accepted"], sep_ref[j][0]) and torch.equal(o[1]["out_tokens"], sep_ref[j][1])
+        assert torch.equal(o[2]["hit"], sep_ref[j][2])
 
     if args.profile_loop:
         for i in range(args.profile_loop):
@@ -201,8 +233,8 @@ def main():
             call_plain(i % ncopy)
         torch.cuda.synchronize()
 
-    acc = outs[0][1]["accepted"].cpu().numpy()
-    hit = outs[0][2]["hit"].cpu().numpy()
+    acc = (outs[0][1] if args.separate else rounds[0])["accepted"].cpu().numpy()
+    hit = (outs[0][2] if args.separate else rounds[0])["hit"].cpu().numpy()
 
     # single-read algorithmic bytes
     elem = 2 if cfg.dtype == "bf16" else 4
@@ -213,13 +245,21 @@ def main():
     s_step = ms_step / 1e3
     gbps = step_bytes / s_step / 1e9
 
-    # dominant library call of the step: the cache build (chunk pass + per-row merge)
-    dom_ms = t_build
-    dom_gbps = bytes_build / (dom_ms / 1e3) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(dom_gbps / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
-                "kernel": "ssd_build_cache (k_cache_chunk + k_cache_merge, bf16)", "bytes_per_launch": bytes_build,
-                "avg_launch_ms": round(dom_ms, 5)}
+    if args.separate:
+        # dominant library call of the three-call step: the cache build (chunk pass + per-row merge)
+        dom_ms = t_build
+        dom_gbps = bytes_build / (dom_ms / 1e3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(dom_gbps / PEAK_HBM_GBS, 4), "traffic": measured_traffic(HBM_BYTES_PROFILE),
+                    "kernel": "ssd_build_cache (k_cache_chunk + k_cache_merge, bf16)",
+                    "bytes_per_launch": bytes_build, "avg_launch_ms": round(dom_ms, 5)}
+    else:
+        # the fused round is the step: its three launches read each logit once
+        # (target rows 0..K, draft rows 0..K) plus the residual rows again
+        roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbps / PEAK_HBM_GBS, 4), "traffic": measured_traffic(ROUND_BYTES_PROFILE),
+                    "kernel": "ssd_verify_round (k_round_chunks + k_round_merge + k_resid, bf16)",
+                    "bytes_per_launch": step_bytes, "avg_launch_ms": round(ms_step, 5)}
 
     cpu = None
     if not args.no_cpu:
@@ -238,7 +278,8 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded Gaussian + Zipf-rank logits, draft = target + noise)",
-        "config": {"workload": "ssd_step_fanout_buildcache_verify_sigma_lookup", "B": B, "K": K, "V": V,
+        "config": {"workload": ("ssd_step_fanout_buildcache_verify_sigma_lookup" if args.separate
+                                else "ssd_step_fanout_verify_round"), "B": B, "K": K, "V": V,
                    "logits": cfg.dtype, "tau": tau, "cache": {"budget": cfg.n_budget, "a_p": cfg.a_p,
                                                                 "r": cfg.r, "C": C, "F": F},
                    "rotating_copies": ncopy, "graph_replay": not args.eager},
@@ -253,6 +294,7 @@ def main():
                         "gbps": round(bytes_plain / (t_plain / 1e3) / 1e9, 1),
                         "pct_peak_hbm": round(100 * bytes_plain / (t_plain / 1e3) / 1e9 / PEAK_HBM_GBS, 2)},
         "verify_sigma_gbps": round(bytes_verify_sigma / (t_verify / 1e3) / 1e9, 1),
+        "round_vs_separate_rows_differ": round_rows_differ,
         "mean_accepted_plus_1": round(float(np.mean(acc + 1)), 4),
         "hit_rate": round(float(np.mean(hit)), 4),
         "cpu_baseline": cpu,
@@ -594,6 +636,7 @@ def bench_tree(args):
                      "frac": round(gbps / PEAK_HBM_GBS, 4), "traffic": None,
                      "kernel": "ssd_verify_tree (k_tree_stats + rounds of k_tree_round, bf16)",
                      "bytes_per_launch": bytes_single, "avg_launch_ms": round(ms_step, 5)},
+        "round_vs_separate_rows_differ": round_rows_differ,
         "mean_accepted_plus_1": round(float(np.mean(acc + 1)), 4),
         "cpu_baseline": cpu,
         "gen_s": round(gen_s, 2),
@@ -602,14 +645,15 @@ def bench_tree(args):
 
 
 HBM_BYTES_PROFILE = os.path.join(ROOT, "profiles", "ssd_build_cache_B64_K5_V128256_bf16_hbm_bytes.md")
+ROUND_BYTES_PROFILE = os.path.join(ROOT, "profiles", "ssd_verify_round_B64_K5_V128256_bf16_hbm_bytes.md")
 
 
-def measured_traffic():
-    """HBM bytes per ssd_build_cache call from the committed FETCH_SIZE / WRITE_SIZE
-    counter summary, or None when the kernel sources changed since it was taken."""
+def measured_traffic(profile):
+    """HBM bytes per call from a committed FETCH_SIZE / WRITE_SIZE counter
+    summary, or None when the kernel sources changed since it was taken."""
     import hashlib
     try:
-        text = open(HBM_BYTES_PROFILE).read()
+        text = open(profile).read()
         rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
         h = hashlib.sha256()
         for p in rec["sources"]:

@@ -292,6 +292,38 @@ SSD_API int ssd_build_cache(const void* draft_logits, int64_t draft_bstride, int
                             int32_t* cache_tokens, ssd_rowkey* thr, double* draft_stats,
                             void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* Bytes of workspace ssd_verify_round needs. */
+SSD_API size_t ssd_verify_round_workspace_size(int32_t B, int32_t K, int32_t V, int dtype);
+
+/* One verification round with the speculation cache ([SSD-notes] framework
+ * and key designs 1-2; [SD-notes] The Algorithm, step 3): the cache of
+ * ssd_build_cache on draft rows 0..K, verification of the drafted tokens
+ * against q = sigma_{F_i,C}(draft row i / tau) as ssd_verify with that
+ * sigma, and the hit of the realised outcome as ssd_cache_lookup. The cache
+ * outputs are bit-identical to ssd_build_cache's; the row sums of the
+ * verification add 8192-entry chunk partials (ssd_verify: 16384), so an
+ * outcome can differ from the three calls' only where a decision lies within
+ * rounding of its threshold. Three launches instead of five: the cache's and
+ * the row statistics' chunk passes share one, the accept scan runs in the
+ * last cache merge of each batch row, the lookup in the residual draw's last
+ * workgroup.
+ *   target_logits device [B, K+1, V]; draft_logits device [B, >=K+1, V]
+ *   F host int32 [K+1] (0 <= F_k <= min(V, 64)); C in [0, 1]
+ *   draft_tokens device int32 [B, K] (drawn from q_sigma, e.g. by
+ *   ssd_draft_sample); u_acc device float [B, K]; u_res device float [B]
+ * Outputs (device): cache_tokens int32 [B, sum F], thr ssd_rowkey [B, K+1],
+ *   draft_stats double [B, K+1, 3] (as ssd_build_cache); accepted int32 [B],
+ *   out_tokens int32 [B, K+1] (as ssd_verify); hit uint8 [B], slot int32 [B]
+ *   or NULL (as ssd_cache_lookup).
+ * Three kernel launches on hip_stream. */
+SSD_API int ssd_verify_round(const void* target_logits, int64_t target_bstride,
+                             const void* draft_logits, int64_t draft_bstride, int dtype,
+                             int32_t B, int32_t K, int32_t V, float tau, const int32_t* F, float C,
+                             const int32_t* draft_tokens, const float* u_acc, const float* u_res,
+                             int32_t* cache_tokens, ssd_rowkey* thr, double* draft_stats,
+                             int32_t* accepted, int32_t* out_tokens, uint8_t* hit, int32_t* slot,
+                             void* workspace, size_t ws_bytes, void* hip_stream);
+
 /* Cache hit of the realised outcome ([SSD-notes] framework: the round's
  * outcome (k, t*) hits iff it is among the prepared keys): hit[b] = 1 iff
  * t* = out_tokens[b, a] lies in segment a of cache_tokens row b, with

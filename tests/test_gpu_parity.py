@@ -513,3 +513,78 @@ def test_uniform_fanout_cache_hits(S):
     assert F == O.fanout_uniform(cfg.n_budget, cfg.K)
     d = W.make_inputs(cfg, b_rows=range(0, 32, 4))
     _cache_case(S, d, F, cfg.C, label="cfg3-uniform")
+
+
+# ---------------------------------------------------------------------------
+# the fused verification round: bit-identical to the separate calls
+# ---------------------------------------------------------------------------
+def _round_vs_separate(S, d, F, C, label):
+    tgt, dft = to_dev(d["target"], torch), to_dev(d["draft"], torch)
+    toks, ua, ur = ivec(d["tokens"], torch), fvec(d["u_acc"], torch), fvec(d["u_res"], torch)
+    cache = S.ssd_build_cache(dft, d["tau"], F)
+    sep = S.ssd_verify(tgt, dft, toks, ua, ur, d["tau"], S.sigma_from_cache(cache, C))
+    look = S.ssd_cache_lookup(cache["cache_tokens"], F, sep["accepted"], sep["out_tokens"])
+    rnd = S.ssd_verify_round(tgt, dft, F, C, toks, ua, ur, d["tau"])
+    again = S.ssd_verify_round(tgt, dft, F, C, toks, ua, ur, d["tau"])   # workspace reused
+    torch.cuda.synchronize()
+    # the cache is built by the same code: identical
+    for k in ("cache_tokens", "thr", "draft_stats"):
+        assert torch.equal(rnd[k], cache[k]), (label, k)
+    for k in rnd:
+        assert torch.equal(again[k], rnd[k]), (label, k, "second call")
+    # verification sums rows over 8192-entry chunk partials (ssd_verify uses
+    # 16384): an outcome may differ only where the oracle's deciding margin
+    # is below EXCUSE
+    same = ((rnd["accepted"] == sep["accepted"]) & (rnd["out_tokens"] == sep["out_tokens"]).all(1)
+            & (rnd["hit"] == look["hit"]) & (rnd["slot"] == look["slot"])).cpu().numpy()
+    bad = [int(b) for b in np.flatnonzero(~same)]
+    if bad:
+        K = d["tokens"].shape[1]
+        F_sig = {"F": list(F), "C": C}
+        vref = O.verify(d["target"][bad], d["draft"][bad], d["tokens"][bad], d["u_acc"][bad], d["u_res"][bad],
+                        d["tau"], F_sig)
+        for j, b in enumerate(bad):
+            m = np.nanmin(np.concatenate([vref["acc_margin"][j], [vref["res_margin"][j]]]))
+            assert m < EXCUSE, (label, b, m)
+        log(f"  {label}: rows {bad} differ from the separate calls within rounding")
+    return rnd
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V,K,B,F,mask", [(20000, 4, 6, [3, 2, 5, 1, 4], 0.0), (16385, 2, 3, [0, 7, 64], 0.0),
+                                          (300, 5, 4, [64, 1, 0, 2, 3, 5], 0.3), (8192, 3, 5, [10, 9, 8, 11], 0.0),
+                                          (1, 1, 3, [1, 1], 0.0), (40000, 6, 7, [1] * 7, 0.05)])
+def test_verify_round_matches_separate_calls(S, dtype, V, K, B, F, mask):
+    log(f"[gpu] verify round V={V} K={K} B={B} F={F} {dtype} mask={mask}")
+    d = _random_case(V * 7 + K + B, B, K, V, dtype, 0.8, mask_frac=mask, Kd=K + 1)
+    if B >= 3:
+        d["tokens"][B - 1, K - 1] = V + 2                # a flagged row
+    rnd = _round_vs_separate(S, d, F, 0.4, f"round V={V}")
+    acc = rnd["accepted"].cpu().numpy()
+    if B >= 3:
+        assert acc[B - 1] == -1 and rnd["hit"].cpu().numpy()[B - 1] == 0
+
+
+def test_verify_round_cfg3_against_oracle(S):
+    cfg = W.get_config(3)
+    log(f"[gpu] verify round {cfg.name}")
+    d = W.make_inputs(cfg)
+    F = S.ssd_fanout(cfg.n_budget, cfg.K, cfg.a_p, cfg.r)
+    rnd = _round_vs_separate(S, d, F, cfg.C, cfg.name)
+    rows = list(range(cfg.B))
+    ref = O.build_cache(d["draft"], d["tau"], F, cfg.C)
+    _check_cache(rnd, ref, F, rows, cfg.name + "-round")
+    vref = O.verify(d["target"], d["draft"], d["tokens"], d["u_acc"], d["u_res"], d["tau"], {"F": F, "C": cfg.C})
+    compare_verify(vref, rnd, cfg.K, rows=rows, check_lse=False, label=cfg.name + "-round")
+    acc_g, out_g = rnd["accepted"].cpu().numpy(), rnd["out_tokens"].cpu().numpy()
+    hit_own, slot_own = O.cache_lookup(ref["cache_tokens"], F, acc_g, out_g)
+    assert np.array_equal(rnd["hit"].cpu().numpy(), hit_own)
+    assert np.array_equal(rnd["slot"].cpu().numpy(), slot_own)
+
+
+def test_verify_round_cfg5(S):
+    cfg = W.get_config(5)
+    log(f"[gpu] verify round {cfg.name}")
+    d = W.make_inputs(cfg, tau=1.0)
+    F = S.ssd_fanout(cfg.n_budget, cfg.K, cfg.a_p, cfg.r)
+    _round_vs_separate(S, d, F, cfg.C, cfg.name)

@@ -252,3 +252,26 @@ def test_verify_tree_argument_checks():
     assert S.ssd_verify_tree_workspace_size(2, 65, 100, S.SSD_BF16) == 0
     with pytest.raises(S.SsdError):
         S.ssd_tree_rounds([-1, 0, 5])
+
+
+def test_verify_round_argument_checks():
+    L = S.lib()
+
+    def call(F=(3, 2, 1), **kw):
+        a = dict(t=FAKE, tb=0, d=FAKE, db=0, dtype=S.SSD_BF16, B=2, K=2, V=100, tau=1.0, C=0.5, tok=FAKE, ua=FAKE,
+                 ur=FAKE, ct=FAKE, thr=FAKE, ds=FAKE, acc=FAKE, out=FAKE, hit=FAKE, slot=None, ws=FAKE, wsz=1 << 30)
+        a.update(kw)
+        Fa = (ctypes.c_int32 * len(F))(*F)
+        return L.ssd_verify_round(a["t"], a["tb"], a["d"], a["db"], a["dtype"], a["B"], a["K"], a["V"], a["tau"],
+                                  Fa, a["C"], a["tok"], a["ua"], a["ur"], a["ct"], a["thr"], a["ds"], a["acc"],
+                                  a["out"], a["hit"], a["slot"], a["ws"], a["wsz"], None)
+
+    assert call(dtype=4) == -2
+    assert call(C=1.5) == -1 and call(C=float("nan")) == -1
+    assert call(tau=-1.0) == -1
+    assert call(F=(3, 2, 65)) == -1 and b"F[2]" in L.ssd_last_error()
+    assert call(F=(3, -1, 1)) == -1
+    assert call(hit=None) == -1 and call(thr=None) == -1 and call(ct=None) == -1
+    assert call(tb=-1) == -1
+    assert call(ws=None, wsz=0) == -3 and call(wsz=128) == -3
+    assert S.ssd_verify_round_workspace_size(2, 2, 100, S.SSD_BF16) > S.ssd_build_cache_workspace_size(2, 2, 100, S.SSD_BF16)

@@ -19,7 +19,8 @@ __all__ = ["SSD_F32", "SSD_BF16", "SsdError", "lib", "ssd_fanout", "ssd_verify",
            "ssd_verify_workspace_size", "ssd_residual_workspace_size",
            "ssd_build_cache_workspace_size", "ssd_draft_sample_workspace_size",
            "ssd_verify_greedy_workspace_size", "ssd_verify_tree", "ssd_verify_tree_workspace_size",
-           "ssd_tree_rounds", "EXPORTS", "library_path"]
+           "ssd_tree_rounds", "ssd_verify_round", "ssd_verify_round_workspace_size", "EXPORTS",
+           "library_path"]
 
 SSD_F32, SSD_BF16 = 0, 1
 SSD_MAX_K, SSD_MAX_F, SSD_MAX_TREE = 64, 64, 64
@@ -28,7 +29,8 @@ EXPORTS = ("ssd_last_error", "ssd_fanout", "ssd_verify_workspace_size", "ssd_ver
            "ssd_build_cache_workspace_size", "ssd_build_cache", "ssd_cache_lookup",
            "ssd_draft_sample_workspace_size", "ssd_draft_sample",
            "ssd_verify_greedy_workspace_size", "ssd_verify_greedy", "ssd_fanout_uniform", "ssd_speedup",
-           "ssd_cache_stats", "ssd_tree_rounds", "ssd_verify_tree_workspace_size", "ssd_verify_tree")
+           "ssd_cache_stats", "ssd_tree_rounds", "ssd_verify_tree_workspace_size", "ssd_verify_tree",
+           "ssd_verify_round_workspace_size", "ssd_verify_round")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -76,6 +78,9 @@ _SIGS = {
     "ssd_draft_sample": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _i32, _i32, _i32, _f32, _vp, _vp, _vp,
                                         _vp, _sz, _vp]),
     "ssd_tree_rounds": (ctypes.c_int, [_vp, _i32]),
+    "ssd_verify_round_workspace_size": (_sz, [_i32, _i32, _i32, ctypes.c_int]),
+    "ssd_verify_round": (ctypes.c_int, [_vp, _i64, _vp, _i64, ctypes.c_int, _i32, _i32, _i32, _f32, _vp, _f32,
+                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ssd_verify_tree_workspace_size": (_sz, [_i32, _i32, _i32, ctypes.c_int]),
     "ssd_verify_tree": (ctypes.c_int, [_vp, _i64, _vp, _i64, ctypes.c_int, _i32, _i32, _i32, _f32, _vp,
                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -457,4 +462,53 @@ def ssd_verify_tree(target, draft, parent: Sequence[int], tokens, u_acc, u_res, 
                                  _dev(out["out_tokens"], torch.int32, (B, N), "out_tokens"),
                                  None if nodes is None else _dev(nodes, torch.int32, (B, N), "out_nodes"),
                                  ws, wsz, _stream(stream)))
+    return out
+
+
+def ssd_verify_round_workspace_size(B, K, V, dtype) -> int:
+    return int(lib().ssd_verify_round_workspace_size(B, K, V, dtype))
+
+
+def ssd_verify_round(target, draft, F: Sequence[int], C: float, draft_tokens, u_acc, u_res, tau: float, *,
+                     out: Optional[dict] = None, stream=None) -> dict:
+    """One verification round with the speculation cache: cache build on
+    draft rows 0..K, sigma verification, and the hit of the outcome, in three
+    launches. Returns the outputs of ssd_build_cache, ssd_verify and
+    ssd_cache_lookup in one dict."""
+    torch = _torch()
+    B, K = int(draft_tokens.shape[0]), int(draft_tokens.shape[1])
+    V = int(target.shape[2])
+    dt = _dtype_code(target)
+    if _dtype_code(draft) != dt:
+        raise ValueError("target and draft dtypes differ")
+    if target.shape[0] != B or draft.shape[0] != B:
+        raise ValueError("batch sizes differ")
+    if len(F) != K + 1:
+        raise ValueError("F needs K+1 entries")
+    tp, tb = _logits(target, "target", K + 1)
+    dp, db = _logits(draft, "draft", K + 1, V)
+    Fa = (ctypes.c_int32 * (K + 1))(*[int(f) for f in F])
+    sumF = int(sum(F))
+    dev = target.device
+    if out is None:
+        out = {"cache_tokens": torch.empty((B, sumF), dtype=torch.int32, device=dev),
+               "thr": torch.empty((B, K + 1, 2), dtype=torch.int32, device=dev),
+               "draft_stats": torch.empty((B, K + 1, 3), dtype=torch.float64, device=dev),
+               "accepted": torch.empty(B, dtype=torch.int32, device=dev),
+               "out_tokens": torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+               "hit": torch.empty(B, dtype=torch.uint8, device=dev),
+               "slot": torch.empty(B, dtype=torch.int32, device=dev)}
+    ws, wsz = _workspace(ssd_verify_round_workspace_size(B, K, V, dt), dev, ("round", B, K, V, dt), stream)
+    _check(lib().ssd_verify_round(
+        tp, tb, dp, db, dt, B, K, V, float(tau), Fa, float(C),
+        _dev(draft_tokens, torch.int32, (B, K), "draft_tokens"), _dev(u_acc, torch.float32, (B, K), "u_acc"),
+        _dev(u_res, torch.float32, (B,), "u_res"),
+        _dev(out["cache_tokens"], torch.int32, (B, sumF), "cache_tokens") if sumF > 0 else None,
+        _dev(out["thr"], torch.int32, (B, K + 1, 2), "thr"),
+        _dev(out["draft_stats"], torch.float64, (B, K + 1, 3), "draft_stats"),
+        _dev(out["accepted"], torch.int32, (B,), "accepted"),
+        _dev(out["out_tokens"], torch.int32, (B, K + 1), "out_tokens"),
+        _dev(out["hit"], torch.uint8, (B,), "hit"),
+        _dev(out["slot"], torch.int32, (B,), "slot") if out.get("slot") is not None else None,
+        ws, wsz, _stream(stream)))
     return out

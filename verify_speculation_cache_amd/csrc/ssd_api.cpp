@@ -86,6 +86,96 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// Argument blocks shared by the separate entry points and the fused round.
+using namespace ssd;
+
+CacheArgs cache_args(const void* draft, int64_t db, int32_t B, int32_t K, int32_t V, float tau, const int32_t* F,
+                     int sumF, int32_t* cache_tokens, ssd_rowkey* thr, double* dstats, char* ws, const CacheWs& cw) {
+  CacheArgs a{};
+  a.draft = draft;
+  a.db = db;
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.S = int(chunks_per_row(V));
+  a.sumF = sumF;
+  a.c64 = kLog2e / double(tau);
+  a.c32 = float(a.c64);
+  int acc = 0;
+  for (int k = 0; k <= K; ++k) {
+    a.F[k] = F[k];
+    a.off[k] = acc;
+    acc += F[k];
+  }
+  a.off[K + 1] = acc;
+  a.cache_tokens = cache_tokens;
+  a.thr = thr;
+  a.dstats = dstats;
+  a.part = reinterpret_cast<CachePartial*>(ws + cw.part);
+  a.cand = reinterpret_cast<Cand*>(ws + cw.cand);
+  a.cnt = reinterpret_cast<uint32_t*>(ws + cw.cnt);
+  return a;
+}
+
+StatsArgs verify_stats_args(const void* target, int64_t tb, const void* draft, int64_t db, int32_t B, int32_t K,
+                            int32_t V, float tau, const int32_t* tokens, const float* u_acc, const ssd_sigma* sigma,
+                            int32_t* accepted, int32_t* out_tokens, float* probs, float* row_lse, char* ws,
+                            const StatsWs& sw) {
+  const bool sig = sigma != nullptr;
+  StatsArgs a{};
+  a.target = target;
+  a.tb = tb;
+  a.draft = draft;
+  a.db = db;
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.S = int(stats_chunks_per_row(V));
+  a.NR = sig ? K + 1 : 2 * K + 1;
+  a.mode = sig ? kModeVerifySigma : kModeVerify;
+  a.c64 = kLog2e / double(tau);
+  a.c32 = float(a.c64);
+  a.inv_tau = 1.0 / double(tau);
+  a.tokens = tokens;
+  a.u_acc = u_acc;
+  a.use_sigma = sig ? 1 : 0;
+  a.C = sig ? sigma->C : 1.0f;
+  a.thr = sig ? sigma->thr : nullptr;
+  a.dstats = sig ? sigma->draft_stats : nullptr;
+  a.accepted = accepted;
+  a.out_tokens = out_tokens;
+  a.probs = probs;
+  a.row_lse = row_lse;
+  a.part = reinterpret_cast<RowPartial*>(ws + sw.part);
+  a.cnt = reinterpret_cast<uint32_t*>(ws + sw.cnt);
+  a.info = reinterpret_cast<RowInfo*>(ws + sw.info);
+  a.zg = reinterpret_cast<uint64_t*>(ws + sw.zg);
+  return a;
+}
+
+ResidArgs verify_resid_args(const StatsArgs& a, const float* u_res, float* resid_mass, char* ws_r,
+                            const ResidWs& rw) {
+  ResidArgs r{};
+  r.target = a.target;
+  r.tb = a.tb;
+  r.draft = a.draft;
+  r.db = a.db;
+  r.B = a.B;
+  r.K = a.K;
+  r.V = a.V;
+  r.S = int(chunks_per_row(a.V));
+  r.c32 = a.c32;
+  r.u = u_res;
+  r.info = a.info;
+  r.cmass = reinterpret_cast<double*>(ws_r + rw.cmass);
+  r.cnt = reinterpret_cast<uint32_t*>(ws_r + rw.cnt);
+  r.tok_out = a.out_tokens;
+  r.tok_stride = a.K + 1;
+  r.tok_at_a = 1;
+  r.mass_out = resid_mass;
+  return r;
+}
+
 // Token-tree topology from a host parent array: children lists in index
 // order, the statistics rows (targets of all nodes, then drafts of inner
 // nodes) and the number of rounds a walk can need.
@@ -274,56 +364,11 @@ SSD_API int ssd_verify(const void* target_logits, int64_t target_bstride,
   if ((st = check_grid(int64_t(B) * NR * SS)) != SSD_OK) return st;
   if ((st = check_grid(int64_t(B) * S)) != SSD_OK) return st;
   char* ws = static_cast<char*>(workspace);
-
-  StatsArgs a{};
-  a.target = target_logits;
-  a.tb = target_bstride;
-  a.draft = draft_logits;
-  a.db = draft_bstride;
-  a.B = B;
-  a.K = K;
-  a.V = V;
-  a.S = int(SS);
-  a.NR = NR;
-  a.mode = sig ? kModeVerifySigma : kModeVerify;
-  a.c64 = kLog2e / double(tau);
-  a.c32 = float(a.c64);
-  a.inv_tau = 1.0 / double(tau);
-  a.tokens = draft_tokens;
-  a.u_acc = u_acc;
-  a.use_sigma = sig ? 1 : 0;
-  a.C = sig ? sigma->C : 1.0f;
-  a.thr = sig ? sigma->thr : nullptr;
-  a.dstats = sig ? sigma->draft_stats : nullptr;
-  a.accepted = accepted;
-  a.out_tokens = out_tokens;
-  a.probs = probs;
-  a.row_lse = row_lse;
-  a.part = reinterpret_cast<RowPartial*>(ws + sw.part);
-  a.cnt = reinterpret_cast<uint32_t*>(ws + sw.cnt);
-  a.info = reinterpret_cast<RowInfo*>(ws + sw.info);
-  a.zg = reinterpret_cast<uint64_t*>(ws + sw.zg);
+  const StatsArgs a = verify_stats_args(target_logits, target_bstride, draft_logits, draft_bstride, B, K, V, tau,
+                                        draft_tokens, u_acc, sigma, accepted, out_tokens, probs, row_lse, ws, sw);
   hipStream_t stream = as_stream(hip_stream);
   if ((st = hip_status(launch_stats(a, dtype, stream), "stats launch")) != SSD_OK) return st;
-
-  ResidArgs r{};
-  r.target = target_logits;
-  r.tb = target_bstride;
-  r.draft = draft_logits;
-  r.db = draft_bstride;
-  r.B = B;
-  r.K = K;
-  r.V = V;
-  r.S = int(S);
-  r.c32 = a.c32;
-  r.u = u_res;
-  r.info = a.info;
-  r.cmass = reinterpret_cast<double*>(ws + sw.total + rw.cmass);
-  r.cnt = reinterpret_cast<uint32_t*>(ws + sw.total + rw.cnt);
-  r.tok_out = out_tokens;
-  r.tok_stride = K + 1;
-  r.tok_at_a = 1;
-  r.mass_out = resid_mass;
+  const ResidArgs r = verify_resid_args(a, u_res, resid_mass, ws + sw.total, rw);
   return hip_status(launch_resid(r, dtype, sig, stream), "residual launch");
 }
 
@@ -491,29 +536,8 @@ SSD_API int ssd_build_cache(const void* draft_logits, int64_t draft_bstride, int
   if ((st = check_ws(workspace, ws_bytes, cw.total)) != SSD_OK) return st;
   if ((st = check_grid(int64_t(B) * (K + 1) * S)) != SSD_OK) return st;
   char* ws = static_cast<char*>(workspace);
-  CacheArgs a{};
-  a.draft = draft_logits;
-  a.db = draft_bstride;
-  a.B = B;
-  a.K = K;
-  a.V = V;
-  a.S = int(S);
-  a.sumF = sumF;
-  a.c64 = kLog2e / double(tau);
-  a.c32 = float(a.c64);
-  int acc = 0;
-  for (int k = 0; k <= K; ++k) {
-    a.F[k] = F[k];
-    a.off[k] = acc;
-    acc += F[k];
-  }
-  a.off[K + 1] = acc;
-  a.cache_tokens = cache_tokens;
-  a.thr = thr;
-  a.dstats = draft_stats;
-  a.part = reinterpret_cast<CachePartial*>(ws + cw.part);
-  a.cand = reinterpret_cast<Cand*>(ws + cw.cand);
-  a.cnt = reinterpret_cast<uint32_t*>(ws + cw.cnt);
+  const CacheArgs a = cache_args(draft_logits, draft_bstride, B, K, V, tau, F, sumF, cache_tokens, thr, draft_stats,
+                                 ws, cw);
   return hip_status(launch_cache(a, dtype, as_stream(hip_stream)), "cache build launch");
 }
 
@@ -615,6 +639,65 @@ SSD_API int ssd_verify_tree(const void* target_logits, int64_t target_bstride,
   for (int r = 0; r < t.rounds; ++r)
     if ((st = hip_status(launch_tree_round(a, dtype, stream), "tree round launch")) != SSD_OK) return st;
   return ok();
+}
+
+SSD_API size_t ssd_verify_round_workspace_size(int32_t B, int32_t K, int32_t V, int dtype) {
+  if (check_shape(B, K, V) != SSD_OK || !dtype_ok(dtype)) return 0;
+  const int64_t S = chunks_per_row(V);
+  return CacheWs(B, K, S).total + StatsWs(B, K + 1, S, K).total + ResidWs(B, S).total +
+         align256(sizeof(uint32_t) * kCntStride * B);
+}
+
+SSD_API int ssd_verify_round(const void* target_logits, int64_t target_bstride,
+                             const void* draft_logits, int64_t draft_bstride, int dtype,
+                             int32_t B, int32_t K, int32_t V, float tau, const int32_t* F, float C,
+                             const int32_t* draft_tokens, const float* u_acc, const float* u_res,
+                             int32_t* cache_tokens, ssd_rowkey* thr, double* draft_stats,
+                             int32_t* accepted, int32_t* out_tokens, uint8_t* hit, int32_t* slot,
+                             void* workspace, size_t ws_bytes, void* hip_stream) {
+  int st;
+  if (!dtype_ok(dtype)) return fail(SSD_EDTYPE, "unknown dtype %d", dtype);
+  if ((st = check_shape(B, K, V)) != SSD_OK) return st;
+  if ((st = check_tau(tau)) != SSD_OK) return st;
+  if (!(C >= 0.0f && C <= 1.0f)) return fail(SSD_EINVAL, "C=%g outside [0, 1]", double(C));
+  int sumF = 0;
+  if ((st = check_fanout_vec(F, K, V, &sumF)) != SSD_OK) return st;
+  if (!target_logits || !draft_logits || !draft_tokens || !u_acc || !u_res || !thr || !draft_stats ||
+      !accepted || !out_tokens || !hit || (sumF > 0 && !cache_tokens))
+    return fail(SSD_EINVAL, "a required pointer is NULL");
+  if (target_bstride < 0 || draft_bstride < 0) return fail(SSD_EINVAL, "negative batch stride");
+  // the statistics chunks of the round are 8192 entries, like the cache's
+  const int64_t S = chunks_per_row(V);
+  const CacheWs cw(B, K, S);
+  const StatsWs sw(B, K + 1, S, K);
+  const ResidWs rw(B, S);
+  const size_t off_s = cw.total, off_r = off_s + sw.total, off_c = off_r + rw.total;
+  if ((st = check_ws(workspace, ws_bytes, off_c + align256(sizeof(uint32_t) * kCntStride * B))) != SSD_OK)
+    return st;
+  if ((st = check_grid(int64_t(B) * (K + 1) * 2 * S)) != SSD_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  RoundArgs a{};
+  a.c = cache_args(draft_logits, draft_bstride, B, K, V, tau, F, sumF, cache_tokens, thr, draft_stats, ws, cw);
+  const ssd_sigma sig{C, thr, draft_stats};
+  a.s = verify_stats_args(target_logits, target_bstride, draft_logits, draft_bstride, B, K, V, tau, draft_tokens,
+                          u_acc, &sig, accepted, out_tokens, nullptr, nullptr, ws + off_s, sw);
+  a.s.S = int(S);
+  a.ncw = uint32_t((K + 1) * S);
+  a.nsw = uint32_t((K + 1) * S);
+  a.cnt = reinterpret_cast<uint32_t*>(ws + off_c);
+  ResidArgs r = verify_resid_args(a.s, u_res, nullptr, ws + off_r, rw);
+  r.cache_tokens = cache_tokens;
+  r.sumF = sumF;
+  for (int k = 0; k <= K; ++k) {
+    r.lk_F[k] = F[k];
+    r.lk_off[k] = a.c.off[k];
+  }
+  r.hit = hit;
+  r.slot = slot;
+  hipStream_t stream = as_stream(hip_stream);
+  if ((st = hip_status(launch_round_chunks(a, dtype, stream), "round chunk launch")) != SSD_OK) return st;
+  if ((st = hip_status(launch_round_merge(a, dtype, stream), "round merge launch")) != SSD_OK) return st;
+  return hip_status(launch_resid(r, dtype, true, stream), "round residual launch");
 }
 
 }  // extern "C"

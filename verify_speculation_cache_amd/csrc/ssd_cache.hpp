@@ -1,0 +1,624 @@
+// Device code of the speculation-cache build (shared by the build's own
+// kernels and the fused verification round).
+//
+// Speculation-cache build (top-F_k per acceptance length, sigma statistics)
+// and the cache-hit lookup.
+//
+// The cache holds, for each acceptance length k, the F_k tokens the draft
+// ranks highest on draft row k: the guessed bonus tokens for outcomes
+// (k, t*) (papernotes.org "Speculative Speculative Decoding", framework and
+// key designs 1-2; the cache picks its tokens by draft logit). sigma_{F,C}
+// then needs, per row, S_top = sum of exp((z - zmax)/tau) over those tokens
+// and S_rest over the others; both are summed directly (no subtraction), so
+// C * S_top + S_rest keeps full relative accuracy for any C.
+//
+// Order: logit descending, then token index ascending, on order-preserving
+// integer keys (exact, no tolerance).
+//
+// Thresholds. Any key t such that at least F lanes of a chunk hold an entry
+// >= t (their lane maximum) bounds the chunk's F-th largest entry from
+// below, and so the row's: an entry below it can never be in the top F. In a
+// wave (2048 entries, 32 per lane) let T0_w be the F-th largest lane maximum
+// and Q_w the ceil(F/4)-th largest; both max_w T0_w and min_w Q_w are such
+// bounds (the latter through 4 x ceil(F/4) >= F lanes), and the chunk's T0 is
+// the larger of the two.
+//
+// Two launches.
+//  k_cache_chunk, one workgroup per (batch row b, length k, chunk c): 8192
+//  logits in registers; chunk max and T0; entries >= T0 (about F of 8192 for
+//  the synthetic logits) are written out unsorted as candidates, and the exp-mass of all
+//  other entries is summed. If ties push the candidates past kCandCap the
+//  chunk is only flagged.
+//  k_cache_merge, one workgroup per row (b, k): re-reads flagged chunks and
+//  keeps exactly their top F (bitwise searches for the F-th key and, among
+//  entries tied at it, for the offset bound); loads every candidate in one
+//  round trip; finds the row's F-th largest key exactly with 8-bit radix
+//  histograms; ranks the candidates at or above it by (key, index); the
+//  first F are the cache tokens.
+#pragma once
+
+#include "ssd_device.hpp"
+
+namespace ssd {
+
+constexpr int kFiltCap = 256;   // filtered candidates ranked in LDS by the merge
+constexpr uint64_t kOverflow = 0xFFFFFFFFull;   // chunk record: candidates not written
+
+__device__ __forceinline__ uint64_t cand_bits(uint32_t key, int32_t idx) {
+  return uint64_t(key) | (uint64_t(uint32_t(idx)) << 32);
+}
+__device__ __forceinline__ uint32_t cand_key(uint64_t w) { return uint32_t(w); }
+__device__ __forceinline__ int32_t cand_idx(uint64_t w) { return int32_t(uint32_t(w >> 32)); }
+
+// Offset of entry q of thread tid inside its chunk (strided layout).
+template <int DT>
+__device__ __forceinline__ int local_of(int tid, int q) {
+  constexpr int PV = Dt<DT>::kPerVec;
+  return ((q / PV) * kThreads + tid) * PV + (q % PV);
+}
+
+// Float threshold equivalent to "key >= k" for logits: keys at or below that
+// of -inf accept every entry, keys above that of +inf accept none.
+template <int DT>
+__device__ __forceinline__ float threshold_value(uint32_t k) {
+  if (k <= key_of<DT>(-__builtin_inff())) return -__builtin_inff();
+  if (k > key_of<DT>(__builtin_inff())) return __builtin_nanf("");
+  return value_of_key<DT>(k);
+}
+
+// exp((z - pivot)/tau) of a candidate, from its key
+template <int DT>
+__device__ __forceinline__ double cand_mass(uint64_t e, float prow, float c32) {
+  return double(__builtin_amdgcn_exp2f((value_of_key<DT>(cand_key(e)) - prow) * c32));
+}
+
+// Entries j*PV .. j*PV+PV-1 of this thread (strided layout), NaN past the end.
+template <int DT>
+__device__ __forceinline__ void load_vec(const typename Dt<DT>::T* row, int64_t c0, int nvalid, int tid,
+                                         int j, float (&v)[Dt<DT>::kPerVec]) {
+  constexpr int PV = Dt<DT>::kPerVec;
+  const typename Dt<DT>::T* base = row + c0;   // uniform; per-entry 32-bit offsets
+  const int loc0 = (j * kThreads + tid) * PV;
+#pragma unroll
+  for (int e = 0; e < PV; ++e) {
+    const int loc = loc0 + e;
+    const float val = Dt<DT>::to_f(base[loc < nvalid ? loc : nvalid - 1]);
+    v[e] = loc < nvalid ? val : __builtin_nanf("");
+  }
+}
+
+// Exact top-F of one chunk when ties overflow the candidate slots: bitwise
+// search for the F-th largest key (counting by float comparison), then the
+// entries tied at it are taken in offset order (vector row j, thread, entry)
+// until F are in. Returns the thread's selection bitmask (bit j*PV + e) and
+// the key of the F-th entry. Every pass re-reads the chunk.
+template <int DT>
+__device__ __forceinline__ uint32_t exact_top_f(const typename Dt<DT>::T* row, int64_t c0, int nvalid, int F,
+                                                int tid, int lane, int w, int* sm_i, int* sm_wcnt,
+                                                uint32_t& key_out) {
+  constexpr int PV = Dt<DT>::kPerVec;
+  constexpr int NV = kPerThread / PV;
+  uint32_t t = 0;
+  for (int bit = Dt<DT>::kKeyBits - 1; bit >= 0; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    const float fv = threshold_value<DT>(cand);
+    int cnt = 0;
+#pragma unroll 1
+    for (int j = 0; j < NV; ++j) {
+      float v[PV];
+      load_vec<DT>(row, c0, nvalid, tid, j, v);
+#pragma unroll
+      for (int e = 0; e < PV; ++e) cnt += v[e] >= fv ? 1 : 0;
+    }
+    if (block_sum_i(cnt, sm_i) >= F) t = cand;
+  }
+  const float ft = threshold_value<DT>(t);
+  uint32_t gmask = 0, tmask = 0;
+#pragma unroll 1
+  for (int j = 0; j < NV; ++j) {
+    float v[PV];
+    load_vec<DT>(row, c0, nvalid, tid, j, v);
+#pragma unroll
+    for (int e = 0; e < PV; ++e) {
+      if (v[e] > ft) gmask |= 1u << (j * PV + e);
+      if (v[e] == ft) tmask |= 1u << (j * PV + e);
+    }
+  }
+  const int need = F - block_sum_i(__popc(gmask), sm_i);
+  uint32_t keep = 0;
+  int before = 0;   // ties in earlier vector rows
+#pragma unroll 1
+  for (int j = 0; j < NV; ++j) {
+    const uint32_t bits = (tmask >> (j * PV)) & ((1u << PV) - 1u);
+    const int cj = __popc(bits);
+    const int inc = wave_incl_scan_i(cj, lane);
+    if (lane == 63) sm_wcnt[w] = inc;
+    __syncthreads();
+    int wb = 0;
+    for (int ww = 0; ww < w; ++ww) wb += sm_wcnt[ww];
+    const int tot = (sm_wcnt[0] + sm_wcnt[1]) + (sm_wcnt[2] + sm_wcnt[3]);
+    __syncthreads();
+    const int first = before + wb + inc - cj;   // rank of this thread's first tie in row j
+#pragma unroll
+    for (int e = 0; e < PV; ++e)
+      if (((bits >> e) & 1u) && first + __popc(bits & ((1u << e) - 1u)) < need) keep |= 1u << (j * PV + e);
+    before += tot;
+  }
+  key_out = t;
+  return gmask | keep;
+}
+
+constexpr int kHold = 16;        // candidate slots each merge thread holds in registers
+constexpr int kCountLds = 256;   // chunk candidate counts kept in LDS by the merge
+
+// The candidate slots of one row, as seen by one merge thread: slot
+// i*256 + tid for i < kHold. When the row has at most 256*kHold slots they
+// are loaded once (one round trip, together with the chunk records) and
+// kept in registers; otherwise every visit streams them again.
+struct RowCands {
+  uint64_t v[kHold];
+  uint32_t ok;   // bit i: slot i holds a written candidate
+};
+
+// f(e) for every written candidate of the row, each visited by one thread.
+template <typename Fn>
+__device__ __forceinline__ void visit(const RowCands& rc, bool held, const uint64_t* pp, const int* cnt_lds,
+                                      const uint64_t* cl, int S, Fn f) {
+  if (held) {
+#pragma unroll
+    for (int i = 0; i < kHold; ++i)
+      if ((rc.ok >> i) & 1u) f(rc.v[i]);
+    return;
+  }
+  const int slots = S * kCandCap;
+  for (int base = 0; base < slots; base += kThreads * kHold) {
+    uint64_t e[kHold];
+    bool ok[kHold];
+#pragma unroll
+    for (int i = 0; i < kHold; ++i) {
+      const int sidx = base + i * kThreads + int(threadIdx.x);
+      ok[i] = false;
+      if (sidx < slots) {
+        const int cc = sidx / kCandCap;
+        const int n = cc < kCountLds ? cnt_lds[cc] : int(uint32_t(pp[cc * 4 + 2]));
+        ok[i] = (sidx - cc * kCandCap) < n;
+      }
+      e[i] = ok[i] ? cl[sidx] : 0ull;
+    }
+#pragma unroll
+    for (int i = 0; i < kHold; ++i)
+      if (ok[i]) f(e[i]);
+  }
+}
+
+// Merge of one row (b, k) by the last workgroup to finish its chunk pass.
+// The row's F-th largest candidate key is found exactly with 8-bit radix
+// passes over LDS histograms; candidates above it are in, those equal to it
+// are ranked with it by (key, index), those below only add to S_rest.
+// The merge of row rowid = b * (K+1) + k. thr and draft_stats are stored
+// by thread 0 with device-scope stores, so a workgroup of the same launch
+// that arrives after this one (arrive_last) may read them.
+template <int DT>
+__device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid) {
+  using T = typename Dt<DT>::T;
+  const int KP = a.K + 1;
+  const int b = int(rowid / KP);
+  const int k = int(rowid - int64_t(b) * KP);
+  const int F = a.F[k];
+  __shared__ uint64_t s_list[kFiltCap];
+  __shared__ double s_exp[kFiltCap];
+  __shared__ int s_hist[256];
+  __shared__ int s_cnt[kCountLds];
+  __shared__ int s_n2;
+  __shared__ float s_mrow;
+  __shared__ double s_srest;
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_need;
+  __shared__ double sm_d2[4];
+  __shared__ int sm_i2[4];
+  __shared__ int sm_wcnt2[4];
+  __shared__ int s_anyovf;
+  __shared__ uint64_t s_thrw;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float c32 = a.c32;
+  uint64_t* pw = reinterpret_cast<uint64_t*>(a.part + rowid * a.S);
+  const uint64_t* pp = pw;
+  uint64_t* clw = reinterpret_cast<uint64_t*>(a.cand + rowid * a.S * kCandCap);
+  const uint64_t* cl = clw;
+  const int slots = a.S * kCandCap;
+  const bool held = slots <= kThreads * kHold;
+
+  // row max and the chunks' non-candidate mass (wave 0, one lane per chunk;
+  // lane-local fold in chunk order, then butterflies); candidate counts to LDS
+  if (w == 0) {
+    float ml = -__builtin_inff();
+    double sl = 0.0;
+    int ovf = 0;
+    for (int cc = lane; cc < a.S; cc += 64) {
+      const uint64_t w0 = pp[cc * 4];
+      const double sc = bits_d(pp[cc * 4 + 1]);
+      const uint64_t w2 = pp[cc * 4 + 2];
+      const int nc = w2 == kOverflow ? 0 : int(uint32_t(w2));
+      ovf |= w2 == kOverflow ? 1 : 0;
+      if (cc < kCountLds) s_cnt[cc] = nc;
+      const float qm = lo_f(w0);
+      const float nm = fmaxf(ml, qm);
+      const float pn = pivot_of(nm);
+      double acc = 0.0;
+      if (sl > 0.0) acc += sl * rescale(pivot_of(ml), pn, c32);
+      if (sc > 0.0) acc += sc * rescale(pivot_of(qm), pn, c32);
+      ml = nm;
+      sl = acc;
+    }
+    const float m = wave_max(ml);
+    const double t = sl > 0.0 ? sl * rescale(pivot_of(ml), pivot_of(m), c32) : 0.0;
+    const double srest = wave_sum(t);
+    const bool anyovf = __ballot(ovf != 0) != 0;
+    if (lane == 0) {
+      s_mrow = m;
+      s_srest = srest;
+      s_n2 = 0;
+      s_prefix = 0;
+      s_need = F;
+      s_anyovf = anyovf ? 1 : 0;
+      s_thrw = cand_bits(0xFFFFFFFFu, -1);
+    }
+  }
+  __syncthreads();
+  const float mrow = s_mrow;
+  const float prow = pivot_of(mrow);
+  double s_unsel = 0.0;
+
+  // chunks whose candidates overflowed (ties): re-read them and keep exactly
+  // their top F; the other entries >= T0 of such a chunk add to S_rest
+  if (s_anyovf) {
+    const T* row = static_cast<const T*>(a.draft) + int64_t(b) * a.db + int64_t(k) * a.V;
+    for (int cc = 0; cc < a.S; ++cc) {
+      if (pp[cc * 4 + 2] != kOverflow) continue;   // uniform
+      const int64_t c0 = int64_t(cc) * kChunk;
+      const int nvalid = int(min(int64_t(kChunk), int64_t(a.V) - c0));
+      uint32_t key_unused;
+      const uint32_t sel = exact_top_f<DT>(row, c0, nvalid, F, tid, lane, w, sm_i2, sm_wcnt2, key_unused);
+      float x[kPerThread];
+      load_strided<DT>(row, c0, a.V, (reinterpret_cast<uintptr_t>(row) & 15u) == 0, tid, x);
+      const float f0 = threshold_value<DT>(uint32_t(pp[cc * 4] >> 32));
+      const int nt = __popc(sel);
+      const int incl = wave_incl_scan_i(nt, lane);
+      if (lane == 63) sm_wcnt2[w] = incl;
+      __syncthreads();
+      int pos = incl - nt;
+      for (int ww = 0; ww < w; ++ww) pos += sm_wcnt2[ww];
+      const int nsel = (sm_wcnt2[0] + sm_wcnt2[1]) + (sm_wcnt2[2] + sm_wcnt2[3]);
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < kPerThread; ++q) {
+        const int loc = local_of<DT>(tid, q);
+        if ((sel >> q) & 1u) {
+          clw[int64_t(cc) * kCandCap + pos] = cand_bits(key_of<DT>(x[q]), int32_t(c0) + loc);
+          ++pos;
+        } else if (loc < nvalid && x[q] >= f0) {
+          s_unsel += double(__builtin_amdgcn_exp2f((x[q] - prow) * c32));
+        }
+      }
+      if (tid == 0) {
+        pw[cc * 4 + 2] = uint64_t(uint32_t(nsel));
+        if (cc < kCountLds) s_cnt[cc] = nsel;
+      }
+      __syncthreads();
+    }
+    __threadfence();
+    __syncthreads();
+  }
+
+  // one round trip: every thread loads its candidate slots (unconditionally;
+  // slots past a chunk's count are ignored below)
+  RowCands rc;
+  rc.ok = 0;
+  if (held) {
+#pragma unroll
+    for (int i = 0; i < kHold; ++i) {
+      const int sidx = i * kThreads + tid;
+      rc.v[i] = sidx < slots ? cl[sidx] : 0ull;
+    }
+  }
+  if (held) {
+#pragma unroll
+    for (int i = 0; i < kHold; ++i) {
+      const int sidx = i * kThreads + tid;
+      const int cc = sidx / kCandCap;
+      if (sidx < slots && (sidx - cc * kCandCap) < s_cnt[cc]) rc.ok |= 1u << i;
+    }
+  }
+  int32_t* ct = a.cache_tokens + int64_t(b) * a.sumF + a.off[k];
+
+  // exact F-th largest candidate key, 8 bits at a time from the top
+  constexpr int KB = Dt<DT>::kKeyBits;
+  if (F > 0) {
+    for (int shift = KB - 8; shift >= 0; shift -= 8) {
+      s_hist[tid] = 0;
+      __syncthreads();
+      const uint32_t prefix = s_prefix;
+      visit(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
+        const uint32_t key = cand_key(e);
+        const uint32_t hi = (shift + 8 < 32) ? (key >> (shift + 8)) : 0u;
+        if (hi == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1);
+      });
+      __syncthreads();
+      if (w == 0) {   // bin holding the need-th largest: suffix counts over 4 bins per lane
+        const int need = s_need;
+        const int h0 = s_hist[4 * lane], h1 = s_hist[4 * lane + 1], h2 = s_hist[4 * lane + 2],
+                  h3 = s_hist[4 * lane + 3];
+        const int lane_tot = h0 + h1 + h2 + h3;
+        int v = lane_tot;   // inclusive suffix scan over lanes 63..0
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int t2 = __shfl_down(v, o);
+          if (lane + o < 64) v += t2;
+        }
+        const int above = v - lane_tot;   // counts in bins of higher lanes
+        int binsel = -1, rem_need = 0;
+        int acc = above;
+        const int hh[4] = {h3, h2, h1, h0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (binsel < 0 && acc + hh[i] >= need && acc < need) {
+            binsel = 4 * lane + 3 - i;
+            rem_need = need - acc;
+          }
+          acc += hh[i];
+        }
+        const uint64_t hitm = __ballot(binsel >= 0);
+        if (hitm) {
+          const int l = __ffsll((unsigned long long)hitm) - 1;
+          if (lane == l) {
+            s_prefix = (prefix << 8) | uint32_t(binsel);
+            s_need = rem_need;
+          }
+        } else if (lane == 0) {   // fewer than F candidates: keep them all
+          s_prefix = 0;
+          s_need = 0;
+        }
+      }
+      __syncthreads();
+      if (s_need == 0) break;
+    }
+  }
+  const bool keep_all = F > 0 && s_need == 0;
+  const uint32_t cut = F == 0 ? 0xFFFFFFFFu : (keep_all ? 0u : s_prefix);   // the F-th key
+
+  // candidates at or above the F-th key go to the ranked list; the others
+  // only add to S_rest
+  visit(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
+    if (F > 0 && cand_key(e) >= cut) {
+      const int slot = atomicAdd(&s_n2, 1);
+      if (slot < kFiltCap) s_list[slot] = e;
+    } else {
+      s_unsel += cand_mass<DT>(e, prow, c32);
+    }
+  });
+  __syncthreads();
+  int n2 = s_n2;
+  __syncthreads();
+
+  if (n2 > kFiltCap) {
+    // more ties at the F-th key than the list holds: the needed ties are the
+    // ones with the smallest indices (bitwise search for the index bound)
+    int c = 0;
+    visit(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) { c += cand_key(e) > cut ? 1 : 0; });
+    const int need = F - block_sum_i(c, sm_i2);
+    int lim = 0;   // largest bound with fewer than `need` ties below it
+    for (int bit = 30; bit >= 0; --bit) {
+      const int cand = lim | (1 << bit);
+      int cnt = 0;
+      visit(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
+        cnt += (cand_key(e) == cut && cand_idx(e) < cand) ? 1 : 0;
+      });
+      if (block_sum_i(cnt, sm_i2) < need) lim = cand;
+    }
+    // ties with index <= lim are exactly `need` of them
+    if (tid == 0) s_n2 = 0;
+    __syncthreads();
+    visit(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
+      if (cand_key(e) < cut) return;   // already counted
+      if (cand_key(e) > cut || cand_idx(e) <= lim) {
+        const int slot = atomicAdd(&s_n2, 1);
+        if (slot < kFiltCap) s_list[slot] = e;
+      } else {
+        s_unsel += cand_mass<DT>(e, prow, c32);
+      }
+    });
+    __syncthreads();
+    n2 = min(s_n2, kFiltCap);   // == F
+    __syncthreads();
+  }
+
+  // exact ranks among the kept candidates; ranks are unique, so nothing
+  // below depends on the order in which the list was filled
+  for (int i = tid; i < n2; i += kThreads) {
+    const uint64_t e = s_list[i];
+    const uint64_t rk = rank_key(cand_key(e), cand_idx(e));
+    int rank = 0;
+    for (int j = 0; j < n2; ++j) {
+      const uint64_t o = s_list[j];
+      rank += rank_key(cand_key(o), cand_idx(o)) > rk ? 1 : 0;
+    }
+    s_exp[rank] = cand_mass<DT>(e, prow, c32);
+    if (rank < F) ct[rank] = cand_idx(e);
+    if (rank == F - 1) s_thrw = e;
+  }
+  const double unsel = block_sum(s_unsel, sm_d2);
+  if (tid == 0) {
+    double s_top = 0.0, s_more = 0.0;
+    for (int r = 0; r < n2; ++r) {
+      if (r < F) s_top += s_exp[r];
+      else s_more += s_exp[r];
+    }
+    // the F-th member (key | index << 32, the ssd_rowkey layout), or the
+    // empty marker when F = 0
+    const uint64_t tw = F == 0 ? cand_bits(0xFFFFFFFFu, -1) : s_thrw;
+    dev_store(reinterpret_cast<uint64_t*>(a.thr + rowid), tw);
+    uint64_t* ds = reinterpret_cast<uint64_t*>(a.dstats + rowid * 3);
+    dev_store(ds, dbits(double(mrow)));
+    dev_store(ds + 1, dbits(s_top));
+    dev_store(ds + 2, dbits(s_srest + unsel + s_more));
+  }
+}
+
+
+// Exp-mass of the entries below f0 (the non-candidates). Entries past the
+// row end read as -inf and add nothing; with f0 = NaN (no candidates) every
+// entry counts.
+template <int DT>
+__device__ __forceinline__ float chunk_rest_mass(const float (&x)[kPerThread], float f0, float piv, float c32) {
+  constexpr int PV = Dt<DT>::kPerVec;
+  float sn = 0.0f;
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const float e = __builtin_amdgcn_exp2f((x[q] - piv) * c32);
+    sn += (x[q] >= f0) ? 0.0f : e;
+    // a vector at a time: keeps the exp temporaries short-lived
+    if (q % PV == PV - 1) __builtin_amdgcn_sched_barrier(0);
+  }
+  return sn;
+}
+
+// Compacts one wave's candidates (entries >= f0; with CHECK also inside the
+// row) into its LDS staging list, in (entry, lane) order; entries past
+// kCandCap are counted but not kept. Returns the wave's count.
+template <int DT, bool CHECK>
+__device__ __forceinline__ uint32_t wave_compact(const float (&x)[kPerThread], float f0, int tid, int nvalid, int c0,
+                                                 uint64_t* wlist) {
+  uint32_t cw = 0;
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int loc = local_of<DT>(tid, q);
+    const bool cand = CHECK ? ((x[q] >= f0) & (loc < nvalid)) : (x[q] >= f0);
+    const uint64_t m = __builtin_amdgcn_ballot_w64(cand);
+    if (m != 0) {   // wave-uniform
+      if (cand) {
+        const uint32_t p = cw + __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+        if (p < uint32_t(kCandCap)) wlist[p] = cand_bits(key_of<DT>(x[q]), c0 + loc);
+      }
+      cw += uint32_t(__popcll(m));
+    }
+  }
+  return cw;
+}
+
+// The chunk pass of one workgroup; blk = (b * (K+1) + k) * S + c.
+template <int DT>
+__device__ __forceinline__ void cache_chunk_wg(const CacheArgs& a, uint32_t blk) {
+  using T = typename Dt<DT>::T;
+  constexpr int PV = Dt<DT>::kPerVec;
+  constexpr int NV = kPerThread / PV;
+  __shared__ float sm_wmax[4];
+  __shared__ uint32_t sm_wthr[4], sm_wthq[4];
+  __shared__ int sm_wcnt[4];
+  __shared__ double sm_ws[4];
+  __shared__ uint64_t sm_list[4][kCandCap];   // per-wave candidate staging
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int KP = a.K + 1;
+  const int per_b = KP * a.S;
+  const int b = blk / per_b;
+  const int rem = blk - b * per_b;
+  const int k = rem / a.S;
+  const int c = rem - k * a.S;
+  const int F = a.F[k];
+  const int64_t rowid = int64_t(b) * KP + k;
+  const T* row = static_cast<const T*>(a.draft) + int64_t(b) * a.db + int64_t(k) * a.V;
+
+  const int64_t c0 = int64_t(c) * kChunk;
+  const int nvalid = int(min(int64_t(kChunk), int64_t(a.V) - c0));
+  float x[kPerThread];
+  float vm[NV];   // per-vector maxima (padding is -inf)
+  {
+    ChunkVecs<DT, true> cv;
+    cv.load(row, c0, a.V, (reinterpret_cast<uintptr_t>(row) & 15u) == 0, tid);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      float v[PV];
+      cv.get(j, v);
+      float m = v[0];
+#pragma unroll
+      for (int e = 0; e < PV; ++e) {
+        x[j * PV + e] = v[e];
+        m = fmaxf(m, v[e]);
+      }
+      vm[j] = m;
+    }
+  }
+  float lm = vm[0];
+#pragma unroll
+  for (int j = 1; j < NV; ++j) lm = fmaxf(lm, vm[j]);
+  const float c32 = a.c32;
+
+  // ---- per-wave max and thresholds; chunk max and T0 ----
+  // A key t with at least F lanes whose maximum is >= t bounds the chunk's
+  // top F from below. Two such bounds, the larger taken: the F-th largest
+  // lane maximum of one wave (max over waves), and the smallest over waves of
+  // each wave's ceil(F/4)-th largest lane maximum (4 waves x ceil(F/4) >= F
+  // lanes). The second is far tighter for large F (about F candidates rather
+  // than several times F).
+  {
+    const float wm = wave_max_u(lm);
+    uint32_t t = 0, tq = 0;
+    if (F > 0) {
+      const int Fq = (F + 3) >> 2;
+      const uint32_t kl = local_of<DT>(tid, 0) < nvalid ? key_of<DT>(lm) : 0u;
+      for (int bit = Dt<DT>::kKeyBits - 1; bit >= 0; --bit) {
+        const uint32_t cand = t | (1u << bit);
+        if (__popcll(__ballot(kl >= cand)) >= F) t = cand;
+      }
+      for (int bit = Dt<DT>::kKeyBits - 1; bit >= 0; --bit) {
+        const uint32_t cand = tq | (1u << bit);
+        if (__popcll(__ballot(kl >= cand)) >= Fq) tq = cand;
+      }
+    }
+    if (lane == 0) {
+      sm_wmax[w] = wm;
+      sm_wthr[w] = t;
+      sm_wthq[w] = tq;
+    }
+  }
+  __syncthreads();
+  const float mc = fmaxf(fmaxf(sm_wmax[0], sm_wmax[1]), fmaxf(sm_wmax[2], sm_wmax[3]));
+  const uint32_t t0 = max(max(max(sm_wthr[0], sm_wthr[1]), max(sm_wthr[2], sm_wthr[3])),
+                          min(min(sm_wthq[0], sm_wthq[1]), min(sm_wthq[2], sm_wthq[3])));
+  const float piv = pivot_of(mc);
+  float f0 = __builtin_nanf("");   // F == 0: compares false, nothing is a candidate
+  if (F > 0) f0 = (t0 <= key_of<DT>(-__builtin_inff())) ? -__builtin_inff() : value_of_key<DT>(t0);
+
+  // ---- candidates (per-wave compaction) and exp-mass of the rest ----
+  uint32_t cw;
+  if (nvalid < kChunk && f0 == -__builtin_inff())   // padding would pass the test
+    cw = wave_compact<DT, true>(x, f0, tid, nvalid, int(c0), sm_list[w]);
+  else
+    cw = wave_compact<DT, false>(x, f0, tid, nvalid, int(c0), sm_list[w]);
+  const float sn = chunk_rest_mass<DT>(x, f0, piv, c32);
+  const double ws = wave_sum_u(double(sn));   // double across threads
+  if (lane == 0) {
+    sm_wcnt[w] = int(cw);
+    sm_ws[w] = ws;
+  }
+  __syncthreads();
+  int woff = 0;
+  for (int ww = 0; ww < w; ++ww) woff += sm_wcnt[ww];
+  const int n = (sm_wcnt[0] + sm_wcnt[1]) + (sm_wcnt[2] + sm_wcnt[3]);
+  const bool overflow = n > kCandCap;   // ties: the merge re-reads this chunk
+
+  // ---- candidates out: each wave copies its list, in order ----
+  if (!overflow) {
+    uint64_t* out = reinterpret_cast<uint64_t*>(a.cand + (rowid * a.S + c) * kCandCap) + woff;
+    for (int i = lane; i < int(cw); i += 64) out[i] = sm_list[w][i];
+  }
+  if (tid == 0) {
+    const double s_rest = (sm_ws[0] + sm_ws[1]) + (sm_ws[2] + sm_ws[3]);
+    uint64_t* wp = reinterpret_cast<uint64_t*>(a.part + rowid * a.S + c);
+    wp[0] = uint64_t(__float_as_uint(mc)) | (uint64_t(t0) << 32);
+    wp[1] = dbits(s_rest);
+    wp[2] = overflow ? kOverflow : uint64_t(uint32_t(n));
+  }
+}
+
+}  // namespace ssd

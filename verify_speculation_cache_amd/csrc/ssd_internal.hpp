@@ -106,6 +106,14 @@ struct ResidArgs {
   int64_t tok_stride;
   int tok_at_a;
   float* mass_out;     // nullable [B]
+  // optional cache lookup of the drawn token (when hit != nullptr): hit[b] =
+  // 1 iff it lies in segment a of cache row b, slot[b] = its position
+  const int32_t* cache_tokens;   // [B, sumF]
+  int sumF;
+  int lk_F[SSD_MAX_K + 1];
+  int lk_off[SSD_MAX_K + 1];
+  uint8_t* hit;
+  int32_t* slot;       // nullable
 };
 
 struct CacheArgs {
@@ -279,6 +287,17 @@ struct TreeWs {
   }
 };
 
+// One verification round with the speculation cache (ssd_verify_round):
+// the cache build's and the row statistics' chunk passes in one launch, the
+// cache merges with the accept scan in a second, the residual draw with the
+// cache lookup in a third.
+struct RoundArgs {
+  CacheArgs c;
+  StatsArgs s;
+  uint32_t ncw, nsw;    // cache and statistics workgroups per batch row
+  uint32_t* cnt;        // [B] (kCntStride apart): merges done per batch row
+};
+
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_stats(const StatsArgs& a, int dtype, hipStream_t st);
 hipError_t launch_resid(const ResidArgs& a, int dtype, bool sigma, hipStream_t st);
@@ -289,5 +308,7 @@ hipError_t launch_greedy(const GreedyArgs& a, int dtype, hipStream_t st);
 hipError_t launch_cache_stats(const CacheStatsArgs& a, hipStream_t st);
 hipError_t launch_tree_stats(const TreeArgs& a, int dtype, hipStream_t st);
 hipError_t launch_tree_round(const TreeArgs& a, int dtype, hipStream_t st);
+hipError_t launch_round_chunks(const RoundArgs& a, int dtype, hipStream_t st);
+hipError_t launch_round_merge(const RoundArgs& a, int dtype, hipStream_t st);
 
 }  // namespace ssd

@@ -85,6 +85,10 @@ __global__ __launch_bounds__(kThreads) void k_resid(ResidArgs a) {
       a.tok_out[int64_t(b) * a.tok_stride] = -1;
       if (a.mass_out) a.mass_out[b] = __builtin_nanf("");
     }
+    if (tid == 0 && a.hit) {
+      a.hit[b] = 0;
+      if (a.slot) a.slot[b] = -1;
+    }
     return;
   }
   // chunk masses, then the first chunk whose running mass exceeds u * Z
@@ -109,6 +113,16 @@ __global__ __launch_bounds__(kThreads) void k_resid(ResidArgs a) {
     tok = resid_pick<DT, SIG>(k, rowT, rowD, cs, sm_pre, sm_target, a.V, sm_pk);
   }
   if (tid == 0) a.tok_out[int64_t(b) * a.tok_stride + (a.tok_at_a ? inf.a : 0)] = tok;
+  if (a.hit && w == 0) {
+    // cache hit of the outcome (a, t*): segment a holds at most 64 tokens
+    const int n = a.lk_F[inf.a];
+    const int32_t ct = lane < n ? a.cache_tokens[int64_t(b) * a.sumF + a.lk_off[inf.a] + lane] : -1;
+    const uint64_t m = __ballot(tok >= 0 && lane < n && ct == tok);
+    if (lane == 0) {
+      a.hit[b] = m != 0 ? 1 : 0;
+      if (a.slot) a.slot[b] = m != 0 ? __ffsll((unsigned long long)m) - 1 : -1;
+    }
+  }
 }
 
 hipError_t launch_resid(const ResidArgs& a, int dtype, bool sigma, hipStream_t st) {
