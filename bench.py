@@ -308,8 +308,8 @@ def bench_report(args):
     it (median, p10, p90 over --calls back-to-back calls on rotating input
     copies, ceil(512 MB / bytes) + 1 of them, so logits come from HBM), plus
     the same call on one warm copy. Plain workloads time ssd_verify; cache
-    workloads time the step ssd_build_cache -> ssd_verify(sigma) ->
-    ssd_cache_lookup on drafts drawn on the GPU from q_sigma (ssd_draft_sample).
+    workloads time ssd_verify_round (cache build, sigma verification, lookup)
+    on drafts drawn on the GPU from q_sigma (ssd_draft_sample).
     Bytes: single-read logits bytes of the call, and the early-exit minimum
     (target rows 0..a and draft rows 0..min(a, K-1) per sequence; all draft
     rows 0..K when the cache is built)."""
@@ -350,21 +350,14 @@ def bench_report(args):
         tau32 = d["tau"]
         if cache_mode:
             F = S.ssd_fanout(cfg.n_budget, K, cfg.a_p, cfg.r)
-            caches = [S.ssd_build_cache(dfts[j], tau32, F) for j in range(ncopy)]
+            cache0 = S.ssd_build_cache(dfts[0], tau32, F)   # sigma for the drafts
             gdraw = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.seed, 424242])))
             u_draft = torch.from_numpy(gdraw.random((B, K), dtype=np.float32)).to(dev)
-            toks = S.ssd_draft_sample(dfts[0], u_draft, tau32, S.sigma_from_cache(caches[0], cfg.C))
-            outs = [S.ssd_verify(tgts[j], dfts[j], toks, ua, ur, tau32, S.sigma_from_cache(caches[j], cfg.C))
-                    for j in range(ncopy)]
-            looks = [S.ssd_cache_lookup(caches[j]["cache_tokens"], F, outs[j]["accepted"], outs[j]["out_tokens"])
-                     for j in range(ncopy)]
+            toks = S.ssd_draft_sample(dfts[0], u_draft, tau32, S.sigma_from_cache(cache0, cfg.C))
+            outs = [S.ssd_verify_round(tgts[j], dfts[j], F, cfg.C, toks, ua, ur, tau32) for j in range(ncopy)]
 
             def call(j):
-                S.ssd_build_cache(dfts[j], tau32, F, out=caches[j])
-                S.ssd_verify(tgts[j], dfts[j], toks, ua, ur, tau32, S.sigma_from_cache(caches[j], cfg.C),
-                             out=outs[j])
-                S.ssd_cache_lookup(caches[j]["cache_tokens"], F, outs[j]["accepted"], outs[j]["out_tokens"],
-                                   out=looks[j])
+                S.ssd_verify_round(tgts[j], dfts[j], F, cfg.C, toks, ua, ur, tau32, out=outs[j])
         else:
             toks = torch.from_numpy(d["tokens"]).to(dev)
             outs = [S.ssd_verify(tgts[j], dfts[j], toks, ua, ur, tau32) for j in range(ncopy)]
@@ -395,7 +388,7 @@ def bench_report(args):
         alpha = [float(np.sum(a > i) / max(1, np.sum(a >= i))) for i in range(K)]
         line = {
             "report": "per_workload", "workload": cfg.name, "B": B, "K": K, "V": V, "dtype": cfg.dtype,
-            "tau": tau, "call": ("ssd_build_cache + ssd_verify(sigma) + ssd_cache_lookup" if cache_mode
+            "tau": tau, "call": ("ssd_verify_round (cache build, sigma verification, lookup)" if cache_mode
                                  else "ssd_verify"),
             "calls": args.calls, "rotating_copies": ncopy,
             "t_call_us": {"median": round(med * 1e3, 2), "p10": round(p10 * 1e3, 2), "p90": round(p90 * 1e3, 2)},
@@ -412,7 +405,7 @@ def bench_report(args):
             "gen_s": round(gen_s, 1),
         }
         if cache_mode:
-            line["hit_rate"] = round(float(looks[0]["hit"].float().mean().item()), 4)
+            line["hit_rate"] = round(float(outs[0]["hit"].float().mean().item()), 4)
             line["F"] = F
             line["C"] = cfg.C
         print(json.dumps(line), flush=True)
