@@ -29,8 +29,9 @@
  *   memory outside the caller's buffers. One workspace must not be used by
  *   two calls that may run at the same time.
  * Streams.  Calls enqueue kernels on `hip_stream` (a hipStream_t; NULL = the
- *   default stream) and return without synchronising. Only ssd_fanout runs on
- *   the host. Graph capture is supported (no memset or allocation inside).
+ *   default stream) and return without synchronising. ssd_fanout,
+ *   ssd_fanout_uniform, ssd_speedup and ssd_tree_rounds run on the host only.
+ *   Graph capture is supported (no memset or allocation inside).
  * Errors.  Functions return SSD_OK (0) or a negative status; arguments are
  *   checked on the host before anything is enqueued, and ssd_last_error()
  *   gives a message for the calling thread's last failure. A drafted token
