@@ -588,3 +588,18 @@ def test_verify_round_cfg5(S):
     d = W.make_inputs(cfg, tau=1.0)
     F = S.ssd_fanout(cfg.n_budget, cfg.K, cfg.a_p, cfg.r)
     _round_vs_separate(S, d, F, cfg.C, cfg.name)
+
+
+def test_verify_round_extremes(S):
+    # K = 64 with 65 cache segments (F_k up to 64), and a fully masked row
+    log("[gpu] verify round K=64")
+    K = 64
+    d = _random_case(5, 3, K, 3000, "bf16", 1.0, draft_sd=0.05, Kd=K + 1)
+    F = [(k * 7) % 65 for k in range(K + 1)]
+    _round_vs_separate(S, d, F, 0.5, "round K64")
+    log("[gpu] verify round masked rows, tau extremes")
+    for tau in (0.05, 5.0):
+        d = _random_case(6, 4, 3, 5000, "f32", tau, Kd=4)
+        d["target"][1] = -np.inf                      # a row without mass: empty p
+        d["draft"][2, 0] = -np.inf                    # a draft row without mass
+        _round_vs_separate(S, d, [4, 0, 64, 3], 0.0, f"round tau{tau}")

@@ -180,3 +180,15 @@ def test_tree_first_token_follows_p(S):
     first = got["out_tokens"].cpu().numpy()[:, 0]
     hist = np.bincount(first, minlength=V)
     assert scipy.stats.chisquare(hist, p0 * B).pvalue > 1e-4, (hist / B, p0)
+
+
+def test_tree_tiny_vocabularies(S):
+    # V = 1 (every token 0, everything kept) and V = 2 with ties, 64-node chain
+    for V, parent in ((1, W.tree_parent((2, 2))), (2, W.tree_parent((3, 1))), (3, [-1] + list(range(63)))):
+        log(f"[gpu] tree tiny V={V} N={len(parent)}")
+        cfg = _cfg(5, V, "f32", tau=1.0, draft_sd=0.3, seed=V)
+        d = W.make_tree_inputs(cfg, parent=parent)
+        got, ref = _run(S, d, label=f"tiny V={V}", max_excused=0)
+        if V == 1:
+            depth = max(O.tree_depth(parent))
+            assert np.all(got["accepted"].cpu().numpy() == depth)
