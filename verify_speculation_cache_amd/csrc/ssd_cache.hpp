@@ -582,9 +582,20 @@ __device__ __forceinline__ void cache_chunk_wg(const CacheArgs& a, uint32_t blk)
     }
   }
   __syncthreads();
-  const float mc = fmaxf(fmaxf(sm_wmax[0], sm_wmax[1]), fmaxf(sm_wmax[2], sm_wmax[3]));
-  const uint32_t t0 = max(max(max(sm_wthr[0], sm_wthr[1]), max(sm_wthr[2], sm_wthr[3])),
-                          min(min(sm_wthq[0], sm_wthq[1]), min(sm_wthq[2], sm_wthq[3])));
+  // lane i < 4 reads wave i's values; the combination happens on scalars
+  // (one register each instead of a copy of all twelve per thread)
+  float mc;
+  uint32_t t0;
+  {
+    const int li = lane & 3;
+    const float vm = sm_wmax[li];
+    const uint32_t vt = sm_wthr[li], vq = sm_wthq[li];
+    auto rlf = [](float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
+    auto rlu = [](uint32_t v, int l) { return uint32_t(__builtin_amdgcn_readlane(int(v), l)); };
+    mc = fmaxf(fmaxf(rlf(vm, 0), rlf(vm, 1)), fmaxf(rlf(vm, 2), rlf(vm, 3)));
+    t0 = max(max(max(rlu(vt, 0), rlu(vt, 1)), max(rlu(vt, 2), rlu(vt, 3))),
+             min(min(rlu(vq, 0), rlu(vq, 1)), min(rlu(vq, 2), rlu(vq, 3))));
+  }
   const float piv = pivot_of(mc);
   float f0 = __builtin_nanf("");   // F == 0: compares false, nothing is a candidate
   if (F > 0) f0 = (t0 <= key_of<DT>(-__builtin_inff())) ? -__builtin_inff() : value_of_key<DT>(t0);
