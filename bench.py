@@ -629,7 +629,6 @@ def bench_tree(args):
                      "frac": round(gbps / PEAK_HBM_GBS, 4), "traffic": None,
                      "kernel": "ssd_verify_tree (k_tree_stats + rounds of k_tree_round, bf16)",
                      "bytes_per_launch": bytes_single, "avg_launch_ms": round(ms_step, 5)},
-        "round_vs_separate_rows_differ": round_rows_differ,
         "mean_accepted_plus_1": round(float(np.mean(acc + 1)), 4),
         "cpu_baseline": cpu,
         "gen_s": round(gen_s, 2),
