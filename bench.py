@@ -78,7 +78,7 @@ def main():
     import workloads as W
 
     cfg = W.get_config(args.config)
-    if not cfg.has_cache:   # the cache build reads draft row K: use cfg3's cache parameters
+    if not cfg.has_cache:   # the cache build reads draft row K and needs cache parameters
         raise SystemExit("bench workload needs cache parameters (use --config 2, 3 or 5)")
     B, K, V = cfg.B, cfg.K, cfg.V
     tau = cfg.taus[0]

@@ -294,7 +294,7 @@ def test_cache_lookup_direct(S, K, F):
 # ---------------------------------------------------------------------------
 # the five workloads at full size
 # ---------------------------------------------------------------------------
-def test_cfg1(S):
+def test_workload_B1_K4_V32000_f32(S):
     cfg = W.get_config(1)
     log(f"[gpu] {cfg.name}")
     d = W.make_inputs(cfg)
@@ -310,36 +310,36 @@ def test_cfg1(S):
     torch.cuda.synchronize()
     ref = O.verify(np.broadcast_to(d["target"], (n,) + d["target"].shape[1:]),
                    np.broadcast_to(d["draft"], (n,) + d["draft"].shape[1:]), toks, ua, ur, d["tau"])
-    compare_verify(ref, got, cfg.K, label="cfg1-broadcast")
+    compare_verify(ref, got, cfg.K, label="B1-broadcast")
 
 
-def test_cfg2(S):
+def test_workload_B64_K5_V128256(S):
     cfg = W.get_config(2)
     log(f"[gpu] {cfg.name}")
     d = W.make_inputs(cfg)
     _run_verify(S, d, label=cfg.name)
 
 
-def test_cfg2_cache(S):
+def test_cache_build_B64_K5_V128256(S):
     cfg = W.get_config(2)
     log(f"[gpu] {cfg.name} cache build")
     d = W.make_inputs(cfg)
     F = S.ssd_fanout(cfg.n_budget, cfg.K, cfg.a_p, cfg.r)
-    _cache_case(S, d, F, cfg.C, rows=range(0, 64, 4), label="cfg2-cache")
+    _cache_case(S, d, F, cfg.C, rows=range(0, 64, 4), label="B64-cache")
 
 
-def test_cfg3(S):
+def test_workload_B32_K7_cache(S):
     cfg = W.get_config(3)
     log(f"[gpu] {cfg.name}")
     d = W.make_inputs(cfg)
     F = S.ssd_fanout(cfg.n_budget, cfg.K, cfg.a_p, cfg.r)
     assert F == [10, 9, 8, 8, 7, 6, 5, 11]
     _, _, hits = _cache_case(S, d, F, cfg.C, label=cfg.name)
-    log(f"[gpu] cfg3 hit rate {hits.mean():.3f}")
+    log(f"[gpu] B=32 cache hit rate {hits.mean():.3f}")
     _run_verify(S, d, label=cfg.name + "-plain")
 
 
-def test_cfg4(S):
+def test_workload_B512_K4_V151936(S):
     cfg = W.get_config(4)
     log(f"[gpu] {cfg.name}")
     d = W.make_inputs(cfg)
@@ -348,15 +348,15 @@ def test_cfg4(S):
 
 
 @pytest.mark.parametrize("tau", [0.5, 1.0])
-def test_cfg5(S, tau):
+def test_workload_B256_K8_cache(S, tau):
     cfg = W.get_config(5)
     log(f"[gpu] {cfg.name} tau={tau}")
     d = W.make_inputs(cfg, tau=tau)
     F = S.ssd_fanout(cfg.n_budget, cfg.K, cfg.a_p, cfg.r)
     assert F == [29, 23, 18, 15, 11, 9, 7, 6, 10]
     rows = list(range(0, 256, 29))
-    _, _, hits = _cache_case(S, d, F, cfg.C, rows=rows, label=f"cfg5-{tau}")
-    log(f"[gpu] cfg5 tau={tau} hit rate {hits.mean():.3f}")
+    _, _, hits = _cache_case(S, d, F, cfg.C, rows=rows, label=f"B256-{tau}")
+    log(f"[gpu] B=256 tau={tau} hit rate {hits.mean():.3f}")
 
 
 # ---------------------------------------------------------------------------
@@ -402,7 +402,7 @@ def test_draft_sample_masked_rows(S):
 
 @pytest.mark.slow
 @pytest.mark.parametrize("tau", [0.5, 1.0])
-def test_cfg5_expected_tokens_and_hits(S, tau):
+def test_B256_K8_expected_tokens_and_hits(S, tau):
     """Config 5's statistical checks: the empirical mean of (accepted + 1)
     and the empirical cache-hit rate over many uniform draws (drafts sampled
     on the GPU from q_sigma, verified against q_sigma) fall within 4 standard
@@ -410,7 +410,7 @@ def test_cfg5_expected_tokens_and_hits(S, tau):
     computed by the oracle; the closed form with the mean alpha is printed."""
     cfg = W.get_config(5)
     nb, reps, rounds = 32, 32, 16            # 32 rows x 32 copies x 16 rounds = 16384 samples
-    log(f"[gpu] cfg5 statistics tau={tau}: {nb} rows x {reps * rounds} draws")
+    log(f"[gpu] B=256 statistics tau={tau}: {nb} rows x {reps * rounds} draws")
     d = W.make_inputs(cfg, tau=tau, draw_tokens=False, b_rows=range(nb))
     F = S.ssd_fanout(cfg.n_budget, cfg.K, cfg.a_p, cfg.r)
     K, tau32 = cfg.K, d["tau"]
@@ -438,7 +438,7 @@ def test_cfg5_expected_tokens_and_hits(S, tau):
     assert lens.min() >= 1
     se_t = lens.std(ddof=1) / math.sqrt(lens.size)
     se_h = math.sqrt(max(p_hit * (1 - p_hit), 1e-12) / hits.size)
-    log(f"[gpu] cfg5 tau={tau}: mean tokens {lens.mean():.4f} vs exact {e_tok:.4f} (4 SE {4 * se_t:.4f}); "
+    log(f"[gpu] B=256 tau={tau}: mean tokens {lens.mean():.4f} vs exact {e_tok:.4f} (4 SE {4 * se_t:.4f}); "
         f"closed form with mean alpha {abar:.4f}: {closed:.4f}; hit rate {hits.mean():.4f} vs exact "
         f"{p_hit:.4f} (4 SE {4 * se_h:.4f})")
     assert abs(lens.mean() - e_tok) <= 4 * se_t
@@ -478,9 +478,9 @@ def test_verify_greedy(S, dtype, V, K, B, ties):
     assert np.array_equal(got["out_tokens"].cpu().numpy(), ref["out_tokens"])
 
 
-def test_verify_greedy_cfg2(S):
+def test_verify_greedy_B64_K5(S):
     cfg = W.get_config(2)
-    log("[gpu] greedy cfg2")
+    log("[gpu] greedy B=64 K=5")
     d = W.make_inputs(cfg, draw_tokens=False)
     g = np.array([[O.argmax_token(d["target"][b, i]) for i in range(cfg.K)] for b in range(cfg.B)],
                  dtype=np.int32)
@@ -506,13 +506,13 @@ def test_cache_stats(S, B, K):
 
 
 def test_uniform_fanout_cache_hits(S):
-    # the uniform shape drives the same cache build and lookup (cfg3 rows)
+    # the uniform shape drives the same cache build and lookup (B=32 cache workload)
     cfg = W.get_config(3)
-    log("[gpu] uniform fan-out cache on cfg3 rows")
+    log("[gpu] uniform fan-out cache on the B=32 cache workload")
     F = S.ssd_fanout_uniform(cfg.n_budget, cfg.K)
     assert F == O.fanout_uniform(cfg.n_budget, cfg.K)
     d = W.make_inputs(cfg, b_rows=range(0, 32, 4))
-    _cache_case(S, d, F, cfg.C, label="cfg3-uniform")
+    _cache_case(S, d, F, cfg.C, label="B32-uniform")
 
 
 # ---------------------------------------------------------------------------
@@ -565,7 +565,7 @@ def test_verify_round_matches_separate_calls(S, dtype, V, K, B, F, mask):
         assert acc[B - 1] == -1 and rnd["hit"].cpu().numpy()[B - 1] == 0
 
 
-def test_verify_round_cfg3_against_oracle(S):
+def test_verify_round_B32_K7_against_oracle(S):
     cfg = W.get_config(3)
     log(f"[gpu] verify round {cfg.name}")
     d = W.make_inputs(cfg)
@@ -582,7 +582,7 @@ def test_verify_round_cfg3_against_oracle(S):
     assert np.array_equal(rnd["slot"].cpu().numpy(), slot_own)
 
 
-def test_verify_round_cfg5(S):
+def test_verify_round_B256_K8(S):
     cfg = W.get_config(5)
     log(f"[gpu] verify round {cfg.name}")
     d = W.make_inputs(cfg, tau=1.0)

@@ -76,20 +76,21 @@ class Config:
         return self.B * rows * self.V * self.elem_bytes
 
 
-# The five workloads. Seeds of cfg3/cfg5 and cfg3's temperature are readings
-# (seed = workload number - 1; cfg3 shares cfg2's generator and temperature).
-# cfg2 stores K+1 draft rows so the cache build can be measured on its shape
-# (draft rows 0..K) with cfg3's cache parameters.
+# The five workloads, keyed 1..5. The seeds of the two cache workloads and
+# the B=32 one's temperature are readings (seed = key - 1; the B=32 cache
+# workload shares the B=64 workload's generator and temperature). The B=64
+# workload stores K+1 draft rows so the cache build can be measured on its
+# shape (draft rows 0..K) with the B=32 workload's cache parameters.
 CONFIGS = {
-    1: Config("cfg1_B1_K4_V32000_f32", 0, 1, 4, 32000, "f32", 3.0, 0.0, 1.0,
+    1: Config("verify_B1_K4_V32000_f32", 0, 1, 4, 32000, "f32", 3.0, 0.0, 1.0,
               (1.0,), 4),
-    2: Config("cfg2_B64_K5_V128256_bf16", 1, 64, 5, 128256, "bf16", 2.0, 1.1,
+    2: Config("verify_B64_K5_V128256_bf16", 1, 64, 5, 128256, "bf16", 2.0, 1.1,
               0.5, (0.7,), 6, 64, 0.8, 1.0, 0.5),
-    3: Config("cfg3_B32_K7_V128256_bf16_cache", 2, 32, 7, 128256, "bf16", 2.0,
+    3: Config("cache_B32_K7_V128256_bf16", 2, 32, 7, 128256, "bf16", 2.0,
               1.1, 0.8, (0.7,), 8, 64, 0.8, 1.0, 0.5),
-    4: Config("cfg4_B512_K4_V151936_bf16", 3, 512, 4, 151936, "bf16", 4.0, 1.3,
+    4: Config("verify_B512_K4_V151936_bf16", 3, 512, 4, 151936, "bf16", 4.0, 1.3,
               1.0, (1.0,), 4),
-    5: Config("cfg5_B256_K8_V256000_bf16_cache", 4, 256, 8, 256000, "bf16", 3.0,
+    5: Config("cache_B256_K8_V256000_bf16", 4, 256, 8, 256000, "bf16", 3.0,
               1.1, 0.6, (0.5, 1.0), 9, 128, 0.7, 0.5, 0.3),
 }
 
