@@ -231,11 +231,18 @@ struct ChunkVecs {
       if (l + PV <= lim) raw[j] = *reinterpret_cast<const uint4*>(base + uint32_t(l));
     }
   }
+  // The vectors partition the chunk into PV-entry blocks, so at most one of
+  // them (block lim / PV, when lim is not a multiple of PV) straddles the
+  // end: one thread gathers it, one vector's worth of registers.
   __device__ void patch_tail(const typename Dt<DT>::T* __restrict__ row, int64_t c0, int lim, int tid) {
+    const int vi = lim / PV;
+    const int owner = STRIDED ? vi % kThreads : vi / NV;
+    if (lim % PV != 0 && tid == owner) {
+      const int js = STRIDED ? vi / kThreads : vi % NV;
+      const uint4 g = gather_vec<DT>(row + c0, vi * PV, lim);
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int l = local(tid, j);
-      if (l < lim && l + PV > lim) raw[j] = gather_vec<DT>(row + c0, l, lim);
+      for (int j = 0; j < NV; ++j)
+        if (j == js) raw[j] = g;
     }
   }
   // unaligned row: per-entry reads, one vector at a time (rare path)

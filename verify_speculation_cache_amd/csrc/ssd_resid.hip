@@ -9,8 +9,9 @@
 //
 // Masses are in target units (ssd_resid.hpp) with rho = s_t / s_d.
 //
-// Phase A (all workgroups): one workgroup per (batch row, chunk) sums r and
-// e_t over its chunk (per-thread float sums, double across threads).
+// Phase A (all workgroups): one workgroup per (batch row, pair of chunks)
+// sums r and e_t over each chunk (per-thread float sums, double across
+// threads).
 // Phase B (last workgroup of the batch row): walks the chunk masses in order
 // to find the chunk holding u*Z, re-reads that chunk with each thread owning
 // 32 consecutive tokens, scans thread totals in double and picks the token.
@@ -24,15 +25,16 @@ namespace ssd {
 template <int DT, bool SIG>
 __global__ __launch_bounds__(kThreads) void k_resid(ResidArgs a) {
   using T = typename Dt<DT>::T;
-  __shared__ double sm_pair[8];
+  __shared__ double sm_pair[16];
   __shared__ int sm_last;
   __shared__ double sm_pre, sm_target;
   __shared__ int sm_c, sm_useres;
   __shared__ PickLds<DT, 2> sm_pk;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int b = blockIdx.x / a.S;
-  const int c = blockIdx.x - b * a.S;
+  const int S2 = (a.S + 1) / 2;   // workgroups per batch row, two 8192-chunks each
+  const int b = blockIdx.x / S2;
+  const int c2 = blockIdx.x - b * S2;
   RowInfo inf = a.info[b];
   // Only trust a row index the stats kernel could have written: anything
   // else (a workspace that was not zero-filled for this shape) is treated
@@ -68,16 +70,21 @@ __global__ __launch_bounds__(kThreads) void k_resid(ResidArgs a) {
 
   // ---------------- phase A: chunk masses ----------------
   if (inf.a >= 0) {
-    double R, P;
-    resid_chunk_masses<DT, SIG>(k, rowT, rowD, int64_t(c) * kChunk, a.V, sm_pair, R, P);
+    double R[2], P[2];
+    resid_chunk_masses2<DT, SIG>(k, rowT, rowD, int64_t(c2) * kStatsChunk, a.V, sm_pair, R, P);
     if (tid == 0) {
+      const int c = 2 * c2;
       uint64_t* wp = reinterpret_cast<uint64_t*>(a.cmass + (int64_t(b) * a.S + c) * 2);
-      dev_store(wp, dbits(R));
-      dev_store(wp + 1, dbits(P));
+      dev_store(wp, dbits(R[0]));
+      dev_store(wp + 1, dbits(P[0]));
+      if (c + 1 < a.S) {
+        dev_store(wp + 2, dbits(R[1]));
+        dev_store(wp + 3, dbits(P[1]));
+      }
     }
   }
 
-  if (!arrive_last(&a.cnt[int64_t(b) * kCntStride], uint32_t(a.S), &sm_last)) return;
+  if (!arrive_last(&a.cnt[int64_t(b) * kCntStride], uint32_t(S2), &sm_last)) return;
 
   // ---------------- phase B: last workgroup of batch row b ----------------
   if (inf.a < 0) {
@@ -126,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void k_resid(ResidArgs a) {
 }
 
 hipError_t launch_resid(const ResidArgs& a, int dtype, bool sigma, hipStream_t st) {
-  const unsigned grid = unsigned(int64_t(a.B) * a.S);
+  const unsigned grid = unsigned(int64_t(a.B) * ((a.S + 1) / 2));
   if (dtype == SSD_BF16) {
     if (sigma) hipLaunchKernelGGL((k_resid<1, true>), dim3(grid), dim3(kThreads), 0, st, a);
     else hipLaunchKernelGGL((k_resid<1, false>), dim3(grid), dim3(kThreads), 0, st, a);

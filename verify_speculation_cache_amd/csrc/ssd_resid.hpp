@@ -94,6 +94,52 @@ __device__ __forceinline__ void resid_chunk_masses(const ResidConsts& k, const t
   P = (sm_pair[4] + sm_pair[5]) + (sm_pair[6] + sm_pair[7]);
 }
 
+// Phase A over two consecutive 8192-chunks at once (a 16384-entry span at
+// c0, 64 entries per thread, strided: vectors j < NV/2 lie in the first
+// chunk): the masses of each chunk, so the draw keeps 8192-entry chunks while
+// a workgroup moves twice the bytes per round trip. R[h], P[h] for half h are
+// returned in every thread (sm: 16 doubles of LDS; one barrier).
+template <int DT, bool SIG>
+__device__ __forceinline__ void resid_chunk_masses2(const ResidConsts& k, const typename Dt<DT>::T* rowT,
+                                                    const typename Dt<DT>::T* rowD, int64_t c0, int V,
+                                                    double* sm, double (&R)[2], double (&P)[2]) {
+  constexpr int PV = Dt<DT>::kPerVec;
+  using CV = ChunkVecs<DT, true, kStatsPerThread>;
+  constexpr int NVH = CV::NV / 2;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  CV vt, vd;
+  load_pair(vt, rowT, vd, rowD, c0, V, tid);
+  float rs[2] = {0.0f, 0.0f}, ts[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < CV::NV; ++j) {
+    float xt[PV], xd[PV];
+    vt.get(j, xt);
+    vd.get(j, xd);
+    const int i0 = int(c0) + CV::local(tid, j);
+#pragma unroll
+    for (int e = 0; e < PV; ++e) {
+      ts[j / NVH] += target_elem(k, xt[e]);
+      rs[j / NVH] += resid_elem<SIG>(k, xt[e], xd[e], i0 + e);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // one vector pair at a time
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const double Rw = wave_sum(double(rs[h]));
+    const double Pw = wave_sum(double(ts[h]));
+    if (lane == 0) {
+      sm[8 * h + w] = Rw;
+      sm[8 * h + 4 + w] = Pw;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    R[h] = (sm[8 * h] + sm[8 * h + 1]) + (sm[8 * h + 2] + sm[8 * h + 3]);
+    P[h] = (sm[8 * h + 4] + sm[8 * h + 5]) + (sm[8 * h + 6] + sm[8 * h + 7]);
+  }
+}
+
 // Phase B, first level (wave 0): from per-chunk (residual, target) masses at
 // cmw[2*cc], cmw[2*cc+1] (one lane per chunk, one round trip for S <= 64),
 // the totals Z_res and Z_tgt, and the chunk holding target = u * Z of the
