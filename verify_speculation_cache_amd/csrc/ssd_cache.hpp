@@ -31,9 +31,10 @@
 //  chunk is only flagged.
 //  k_cache_merge, one workgroup per row (b, k): re-reads flagged chunks and
 //  keeps exactly their top F (bitwise searches for the F-th key and, among
-//  entries tied at it, for the offset bound); loads every candidate in one
-//  round trip; finds the row's F-th largest key exactly with 8-bit radix
-//  histograms; ranks the candidates at or above it by (key, index); the
+//  entries tied at it, for the offset bound); loads every candidate and the
+//  chunk records in one round trip; ranks the candidates at or above the
+//  largest chunk T0 by (key, index) (when too many remain, after finding
+//  the row's F-th largest key exactly with 8-bit radix histograms); the
 //  first F are the cache tokens.
 #pragma once
 
@@ -150,15 +151,31 @@ __device__ __forceinline__ uint32_t exact_top_f(const typename Dt<DT>::T* row, i
 
 constexpr int kHold = 16;        // candidate slots each merge thread holds in registers
 constexpr int kCountLds = 256;   // chunk candidate counts kept in LDS by the merge
+constexpr int kHeldChunks = 32;  // rows of at most this many chunks keep their candidates in registers
 
-// The candidate slots of one row, as seen by one merge thread: slot
-// i*256 + tid for i < kHold. When the row has at most 256*kHold slots they
-// are loaded once (one round trip, together with the chunk records) and
-// kept in registers; otherwise every visit streams them again.
+// The candidate slots of one row, as seen by one merge thread. Rows of at
+// most kHeldChunks chunks are held in registers, chunk-major: with G the
+// chunk count rounded up to a power of two and P = 256 / G, thread tid
+// serves chunk tid / P at positions tid % P + P * i, i < kHold, which
+// covers every slot of the chunk. A thread's valid slots are a prefix of
+// its i, a chunk's candidates spread over its P threads, and one wave load
+// instruction reads 64 / P runs of P consecutive slots. They are loaded
+// once, in the round trip of the chunk records. Longer rows stream their
+// slots on every visit.
 struct RowCands {
   uint64_t v[kHold];
   uint32_t ok;   // bit i: slot i holds a written candidate
 };
+
+struct HeldMap {
+  int chunk, pos, step;   // this thread's chunk, first position, position step
+};
+__device__ __forceinline__ HeldMap held_map(int S, int tid) {
+  int lg = 0;
+  while ((1 << lg) < S && lg < 8) ++lg;
+  const int P = kThreads >> lg;
+  return HeldMap{tid / P, tid % P, P};
+}
 
 // f(e) for every written candidate of the row, each visited by one thread.
 template <typename Fn>
@@ -191,13 +208,46 @@ __device__ __forceinline__ void visit(const RowCands& rc, bool held, const uint6
   }
 }
 
-// Merge of one row (b, k) by the last workgroup to finish its chunk pass.
-// The row's F-th largest candidate key is found exactly with 8-bit radix
-// passes over LDS histograms; candidates above it are in, those equal to it
-// are ranked with it by (key, index), those below only add to S_rest.
-// The merge of row rowid = b * (K+1) + k. thr and draft_stats are stored
-// by thread 0 with device-scope stores, so a workgroup of the same launch
-// that arrives after this one (arrive_last) may read them.
+// Every thread's held slots, loaded unconditionally (slots past a chunk's
+// count are masked out later; the chunk and position are clamped into the
+// row's slots, so there is no branch around the loads).
+__device__ __forceinline__ void load_held(RowCands& rc, const uint64_t* cl, const HeldMap& hm, int S) {
+  const uint64_t* base = cl + min(hm.chunk, S - 1) * kCandCap;
+#pragma unroll
+  for (int i = 0; i < kHold; ++i) rc.v[i] = base[min(hm.pos + hm.step * i, kCandCap - 1)];
+}
+
+// Appends e to the LDS list when keep holds: one LDS atomic per wave (the
+// lowest selected lane reserves the wave's slots), entries past kFiltCap
+// are counted but not stored. Called by the active lanes of a wave together.
+__device__ __forceinline__ void wave_append(uint64_t e, bool keep, int lane, int* n, uint64_t* list) {
+  const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
+  if (m == 0) return;   // uniform over the active lanes
+  const int leader = __builtin_ctzll(m);
+  int base = 0;
+  if (lane == leader) base = atomicAdd(n, __popcll(m));
+  base = __builtin_amdgcn_readlane(base, leader);
+  if (keep) {
+    const int slot = base + int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
+    if (slot < kFiltCap) list[slot] = e;
+  }
+}
+
+// The merge of row rowid = b * (K+1) + k.
+//
+// Every chunk's T0 bounds the row's F-th largest key from below (the chunk
+// holds at least F entries at or above it), and so does the F-th largest of
+// the chunk maxima when F <= S (they are F distinct entries of the row).
+// The larger of the largest T0 and that maximum, Tmax, is the bound used:
+// the row's top F are among the candidates at or above Tmax, and every
+// candidate below it only adds to S_rest. Those at or above Tmax (from F to
+// a few times F on the synthetic rows) are ranked directly by (key,
+// index). Only when more than kFiltCap of them remain is the row's F-th
+// largest key found exactly first (8-bit radix passes over LDS histograms),
+// and then the candidates tied at it by a bitwise search over the index.
+// thr and draft_stats are stored by thread 0 with device-scope stores, so a
+// workgroup of the same launch that arrives after this one (arrive_last) may
+// read them.
 template <int DT>
 __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid) {
   using T = typename Dt<DT>::T;
@@ -212,7 +262,7 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
   __shared__ int s_n2;
   __shared__ float s_mrow;
   __shared__ double s_srest;
-  __shared__ uint32_t s_prefix;
+  __shared__ uint32_t s_prefix, s_tmax;
   __shared__ int s_need;
   __shared__ double sm_d2[4];
   __shared__ int sm_i2[4];
@@ -225,22 +275,39 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
   const uint64_t* pp = pw;
   uint64_t* clw = reinterpret_cast<uint64_t*>(a.cand + rowid * a.S * kCandCap);
   const uint64_t* cl = clw;
-  const int slots = a.S * kCandCap;
-  const bool held = slots <= kThreads * kHold;
+  const bool held = a.S <= kHeldChunks;
+  const HeldMap hm = held_map(a.S, tid);
 
-  // row max and the chunks' non-candidate mass (wave 0, one lane per chunk;
-  // lane-local fold in chunk order, then butterflies); candidate counts to LDS
+  // The chunk records (wave 0, one lane per chunk) are requested first and
+  // every thread's candidate slots right after, so both arrive in one round
+  // trip and wave 0 folds the records while the candidates are in flight.
+  // Both are issued without branches (indices clamped into the row) so that
+  // the fold waits only for the records.
+  // Lane l < S of wave 0 holds chunk l's record; every thread also reads
+  // the candidate count of the chunk it holds.
+  const bool rec = w == 0 && lane < a.S;
+  const int rl = min(lane, a.S - 1);
+  const uint64_t r0 = pp[rl * 4], r1 = pp[rl * 4 + 1], r2 = pp[rl * 4 + 2];
+  const uint64_t own_cnt = pp[min(hm.chunk, a.S - 1) * 4 + 2];
+  __builtin_amdgcn_sched_barrier(0);
+  RowCands rc;
+  rc.ok = 0;
+  load_held(rc, cl, hm, a.S);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // row max, the chunks' non-candidate mass (lane-local fold in chunk order,
+  // then butterflies), Tmax; candidate counts to LDS
   if (w == 0) {
     float ml = -__builtin_inff();
     double sl = 0.0;
     int ovf = 0;
-    for (int cc = lane; cc < a.S; cc += 64) {
-      const uint64_t w0 = pp[cc * 4];
-      const double sc = bits_d(pp[cc * 4 + 1]);
-      const uint64_t w2 = pp[cc * 4 + 2];
+    uint32_t tmax = 0;
+    auto fold = [&](int cc, uint64_t w0, uint64_t w1, uint64_t w2) {
+      const double sc = bits_d(w1);
       const int nc = w2 == kOverflow ? 0 : int(uint32_t(w2));
       ovf |= w2 == kOverflow ? 1 : 0;
       if (cc < kCountLds) s_cnt[cc] = nc;
+      tmax = max(tmax, uint32_t(w0 >> 32));
       const float qm = lo_f(w0);
       const float nm = fmaxf(ml, qm);
       const float pn = pivot_of(nm);
@@ -249,10 +316,25 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
       if (sc > 0.0) acc += sc * rescale(pivot_of(qm), pn, c32);
       ml = nm;
       sl = acc;
-    }
+    };
+    if (rec) fold(lane, r0, r1, r2);
+    for (int cc = lane + 64; cc < a.S; cc += 64) fold(cc, pp[cc * 4], pp[cc * 4 + 1], pp[cc * 4 + 2]);
     const float m = wave_max(ml);
     const double t = sl > 0.0 ? sl * rescale(pivot_of(ml), pivot_of(m), c32) : 0.0;
     const double srest = wave_sum(t);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) tmax = max(tmax, uint32_t(__shfl_xor(int(tmax), o)));
+    // the F-th largest chunk maximum (the F largest are F distinct entries
+    // of the row), by a bitwise search over the lanes' chunk-max keys
+    if (F > 0 && F <= a.S && a.S <= 64) {
+      const uint32_t km = rec ? key_of<DT>(lo_f(r0)) : 0u;
+      uint32_t mf = 0;
+      for (int bit = Dt<DT>::kKeyBits - 1; bit >= 0; --bit) {
+        const uint32_t cand = mf | (1u << bit);
+        if (__popcll(__ballot(km >= cand)) >= F) mf = cand;
+      }
+      tmax = max(tmax, mf);
+    }
     const bool anyovf = __ballot(ovf != 0) != 0;
     if (lane == 0) {
       s_mrow = m;
@@ -260,6 +342,7 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
       s_n2 = 0;
       s_prefix = 0;
       s_need = F;
+      s_tmax = tmax;
       s_anyovf = anyovf ? 1 : 0;
       s_thrw = cand_bits(0xFFFFFFFFu, -1);
     }
@@ -308,32 +391,36 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
     }
     __threadfence();
     __syncthreads();
+    load_held(rc, cl, hm, a.S);   // the rewritten lists
   }
 
-  // one round trip: every thread loads its candidate slots (unconditionally;
-  // slots past a chunk's count are ignored below)
-  RowCands rc;
-  rc.ok = 0;
   if (held) {
+    // this thread's chunk count: from its own record, or from LDS where an
+    // overflowed chunk was rewritten
+    int nc = hm.chunk < a.S ? (own_cnt == kOverflow ? 0 : int(uint32_t(own_cnt))) : 0;
+    if (s_anyovf && hm.chunk < a.S) nc = s_cnt[hm.chunk];
 #pragma unroll
-    for (int i = 0; i < kHold; ++i) {
-      const int sidx = i * kThreads + tid;
-      rc.v[i] = sidx < slots ? cl[sidx] : 0ull;
-    }
-  }
-  if (held) {
-#pragma unroll
-    for (int i = 0; i < kHold; ++i) {
-      const int sidx = i * kThreads + tid;
-      const int cc = sidx / kCandCap;
-      if (sidx < slots && (sidx - cc * kCandCap) < s_cnt[cc]) rc.ok |= 1u << i;
-    }
+    for (int i = 0; i < kHold; ++i)
+      if (hm.pos + hm.step * i < nc) rc.ok |= 1u << i;
   }
   int32_t* ct = a.cache_tokens + int64_t(b) * a.sumF + a.off[k];
 
-  // exact F-th largest candidate key, 8 bits at a time from the top
-  constexpr int KB = Dt<DT>::kKeyBits;
-  if (F > 0) {
+  // candidates at or above Tmax go to the ranked list; the others only add
+  // to S_rest
+  const uint32_t tcut = s_tmax;
+  visit(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
+    const bool keep = F > 0 && cand_key(e) >= tcut;
+    wave_append(e, keep, lane, &s_n2, s_list);
+    if (!keep) s_unsel += cand_mass<DT>(e, prow, c32);
+  });
+  __syncthreads();
+  int n2 = __builtin_amdgcn_readfirstlane(s_n2);   // uniform
+  __syncthreads();
+
+  if (n2 > kFiltCap) {
+    // too many at or above Tmax: the row's F-th largest key, exactly, 8 bits
+    // at a time from the top (it is >= Tmax, so only those are re-sorted)
+    constexpr int KB = Dt<DT>::kKeyBits;
     for (int shift = KB - 8; shift >= 0; shift -= 8) {
       s_hist[tid] = 0;
       __syncthreads();
@@ -382,85 +469,102 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
       __syncthreads();
       if (s_need == 0) break;
     }
-  }
-  const bool keep_all = F > 0 && s_need == 0;
-  const uint32_t cut = F == 0 ? 0xFFFFFFFFu : (keep_all ? 0u : s_prefix);   // the F-th key
-
-  // candidates at or above the F-th key go to the ranked list; the others
-  // only add to S_rest
-  visit(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
-    if (F > 0 && cand_key(e) >= cut) {
-      const int slot = atomicAdd(&s_n2, 1);
-      if (slot < kFiltCap) s_list[slot] = e;
-    } else {
-      s_unsel += cand_mass<DT>(e, prow, c32);
-    }
-  });
-  __syncthreads();
-  int n2 = s_n2;
-  __syncthreads();
-
-  if (n2 > kFiltCap) {
-    // more ties at the F-th key than the list holds: the needed ties are the
-    // ones with the smallest indices (bitwise search for the index bound)
-    int c = 0;
-    visit(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) { c += cand_key(e) > cut ? 1 : 0; });
-    const int need = F - block_sum_i(c, sm_i2);
-    int lim = 0;   // largest bound with fewer than `need` ties below it
-    for (int bit = 30; bit >= 0; --bit) {
-      const int cand = lim | (1 << bit);
-      int cnt = 0;
-      visit(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
-        cnt += (cand_key(e) == cut && cand_idx(e) < cand) ? 1 : 0;
-      });
-      if (block_sum_i(cnt, sm_i2) < need) lim = cand;
-    }
-    // ties with index <= lim are exactly `need` of them
+    const uint32_t cut = s_need == 0 && s_prefix == 0 ? tcut : s_prefix;   // the F-th key
     if (tid == 0) s_n2 = 0;
     __syncthreads();
     visit(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
-      if (cand_key(e) < cut) return;   // already counted
-      if (cand_key(e) > cut || cand_idx(e) <= lim) {
-        const int slot = atomicAdd(&s_n2, 1);
-        if (slot < kFiltCap) s_list[slot] = e;
-      } else {
-        s_unsel += cand_mass<DT>(e, prow, c32);
-      }
+      if (cand_key(e) < tcut) return;   // already counted
+      const bool keep = cand_key(e) >= cut;
+      wave_append(e, keep, lane, &s_n2, s_list);
+      if (!keep) s_unsel += cand_mass<DT>(e, prow, c32);
     });
     __syncthreads();
-    n2 = min(s_n2, kFiltCap);   // == F
+    n2 = s_n2;
     __syncthreads();
+
+    if (n2 > kFiltCap) {
+      // more ties at the F-th key than the list holds: the needed ties are
+      // the ones with the smallest indices (bitwise search for the index bound)
+      int c = 0;
+      visit(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) { c += cand_key(e) > cut ? 1 : 0; });
+      const int need = F - block_sum_i(c, sm_i2);
+      int lim = 0;   // largest bound with fewer than `need` ties below it
+      for (int bit = 30; bit >= 0; --bit) {
+        const int cand = lim | (1 << bit);
+        int cnt = 0;
+        visit(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
+          cnt += (cand_key(e) == cut && cand_idx(e) < cand) ? 1 : 0;
+        });
+        if (block_sum_i(cnt, sm_i2) < need) lim = cand;
+      }
+      // ties with index <= lim are exactly `need` of them
+      if (tid == 0) s_n2 = 0;
+      __syncthreads();
+      visit(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
+        if (cand_key(e) < cut) return;   // already counted
+        const bool keep = cand_key(e) > cut || cand_idx(e) <= lim;
+        wave_append(e, keep, lane, &s_n2, s_list);
+        if (!keep) s_unsel += cand_mass<DT>(e, prow, c32);
+      });
+      __syncthreads();
+      n2 = min(s_n2, kFiltCap);   // == F
+      __syncthreads();
+    }
   }
 
   // exact ranks among the kept candidates; ranks are unique, so nothing
   // below depends on the order in which the list was filled
-  for (int i = tid; i < n2; i += kThreads) {
-    const uint64_t e = s_list[i];
-    const uint64_t rk = rank_key(cand_key(e), cand_idx(e));
-    int rank = 0;
-    for (int j = 0; j < n2; ++j) {
-      const uint64_t o = s_list[j];
-      rank += rank_key(cand_key(o), cand_idx(o)) > rk ? 1 : 0;
-    }
+  auto place = [&](uint64_t e, int rank) {
     s_exp[rank] = cand_mass<DT>(e, prow, c32);
     if (rank < F) ct[rank] = cand_idx(e);
     if (rank == F - 1) s_thrw = e;
-  }
-  const double unsel = block_sum(s_unsel, sm_d2);
-  if (tid == 0) {
-    double s_top = 0.0, s_more = 0.0;
-    for (int r = 0; r < n2; ++r) {
-      if (r < F) s_top += s_exp[r];
-      else s_more += s_exp[r];
+  };
+  if (n2 <= 64) {
+    // one wave, entry i in lane i, the others read with readlane
+    if (w == 0) {
+      const uint64_t e = lane < n2 ? s_list[lane] : 0ull;
+      const uint64_t rk = rank_key(cand_key(e), cand_idx(e));
+      int rank = 0;
+      for (int j = 0; j < n2; ++j) {
+        const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(rk)), j));
+        const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(rk >> 32)), j));
+        rank += ((uint64_t(hi) << 32) | lo) > rk ? 1 : 0;
+      }
+      if (lane < n2) place(e, rank);
     }
-    // the F-th member (key | index << 32, the ssd_rowkey layout), or the
-    // empty marker when F = 0
-    const uint64_t tw = F == 0 ? cand_bits(0xFFFFFFFFu, -1) : s_thrw;
-    dev_store(reinterpret_cast<uint64_t*>(a.thr + rowid), tw);
-    uint64_t* ds = reinterpret_cast<uint64_t*>(a.dstats + rowid * 3);
-    dev_store(ds, dbits(double(mrow)));
-    dev_store(ds + 1, dbits(s_top));
-    dev_store(ds + 2, dbits(s_srest + unsel + s_more));
+  } else {
+    for (int i = tid; i < n2; i += kThreads) {
+      const uint64_t e = s_list[i];
+      const uint64_t rk = rank_key(cand_key(e), cand_idx(e));
+      int rank = 0;
+      for (int j = 0; j < n2; ++j) {
+        const uint64_t o = s_list[j];
+        rank += rank_key(cand_key(o), cand_idx(o)) > rk ? 1 : 0;
+      }
+      place(e, rank);
+    }
+  }
+  const double unsel = block_sum(s_unsel, sm_d2);   // its barriers also publish s_exp
+  if (w == 0) {
+    // S_top over ranks < F, the ranked rest into S_rest (lane-strided, then
+    // butterflies)
+    double top = 0.0, more = 0.0;
+    for (int r = lane; r < n2; r += 64) {
+      if (r < F) top += s_exp[r];
+      else more += s_exp[r];
+    }
+    top = wave_sum_u(top);
+    more = wave_sum_u(more);
+    if (lane == 0) {
+      // the F-th member (key | index << 32, the ssd_rowkey layout), or the
+      // empty marker when F = 0
+      const uint64_t tw = F == 0 ? cand_bits(0xFFFFFFFFu, -1) : s_thrw;
+      dev_store(reinterpret_cast<uint64_t*>(a.thr + rowid), tw);
+      uint64_t* ds = reinterpret_cast<uint64_t*>(a.dstats + rowid * 3);
+      dev_store(ds, dbits(double(mrow)));
+      dev_store(ds + 1, dbits(top));
+      dev_store(ds + 2, dbits(s_srest + unsel + more));
+    }
   }
 }
 

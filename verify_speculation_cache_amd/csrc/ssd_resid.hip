@@ -98,6 +98,13 @@ __global__ __launch_bounds__(kThreads) void k_resid(ResidArgs a) {
     }
     return;
   }
+  // the cache segment of length a (at most 64 tokens, lane i holds slot i),
+  // requested first so that its round trip overlaps those of the draw
+  int32_t seg_tok = -1;
+  if (a.hit && w == 0) {
+    const int n = a.lk_F[inf.a];
+    seg_tok = lane < n ? a.cache_tokens[int64_t(b) * a.sumF + a.lk_off[inf.a] + lane] : -1;
+  }
   // chunk masses, then the first chunk whose running mass exceeds u * Z
   if (w == 0) {
     double zres, ztgt, target, pre;
@@ -121,10 +128,8 @@ __global__ __launch_bounds__(kThreads) void k_resid(ResidArgs a) {
   }
   if (tid == 0) a.tok_out[int64_t(b) * a.tok_stride + (a.tok_at_a ? inf.a : 0)] = tok;
   if (a.hit && w == 0) {
-    // cache hit of the outcome (a, t*): segment a holds at most 64 tokens
-    const int n = a.lk_F[inf.a];
-    const int32_t ct = lane < n ? a.cache_tokens[int64_t(b) * a.sumF + a.lk_off[inf.a] + lane] : -1;
-    const uint64_t m = __ballot(tok >= 0 && lane < n && ct == tok);
+    // cache hit of the outcome (a, t*)
+    const uint64_t m = __ballot(tok >= 0 && seg_tok == tok);
     if (lane == 0) {
       a.hit[b] = m != 0 ? 1 : 0;
       if (a.slot) a.slot[b] = m != 0 ? __ffsll((unsigned long long)m) - 1 : -1;

@@ -117,7 +117,6 @@ template <int DT>
 __device__ __forceinline__ void stats_epilogue(const StatsArgs& a, int b) {
   __shared__ float e_piv[kMaxRows];
   __shared__ double e_s[kMaxRows];
-  __shared__ int sm_a;
   const int tid = threadIdx.x;
   const int K = a.K;
   // per drafted position (wave 0, lane i < K): inputs of the accept test,
@@ -177,7 +176,9 @@ __device__ __forceinline__ void stats_epilogue(const StatsArgs& a, int b) {
     return;
   }
 
-  // verify: wave 0, lane i handles drafted position i (K <= 64)
+  // verify: wave 0, lane i handles drafted position i (K <= 64); the same
+  // wave then leaves the RowInfo, taking the sigma statistics of the row to
+  // sample from out of the lane that loaded them
   if (tid < 64) {
     const int i = tid;
     bool bad = false, acc = true;
@@ -202,19 +203,45 @@ __device__ __forceinline__ void stats_epilogue(const StatsArgs& a, int b) {
     }
     const uint64_t badm = __ballot(i < K && bad);
     const uint64_t rej = __ballot(i < K && !acc);
-    const int av = badm ? -1 : (rej ? (__ffsll((unsigned long long)rej) - 1) : K);
+    const int av = badm ? -1 : (rej ? (__ffsll((unsigned long long)rej) - 1) : K);   // wave-uniform
     if (i < K && a.probs != nullptr) {
       a.probs[(int64_t(b) * K + i) * 2 + 0] = float(pd);
       a.probs[(int64_t(b) * K + i) * 2 + 1] = float(qd);
     }
-    for (int ii = i; ii <= K; ii += 64) {
-      int32_t o = -1;
-      if (av >= 0 && ii < av) o = a.tokens[int64_t(b) * K + ii];
-      a.out_tokens[int64_t(b) * (K + 1) + ii] = o;
+    // positions 0..K: the kept drafts (lane ii < av <= K holds d_ii), then -1
+    for (int ii = i; ii <= K; ii += 64) a.out_tokens[int64_t(b) * (K + 1) + ii] = (av >= 0 && ii < av) ? d : -1;
+
+    RowInfo inf{};
+    inf.a = av;
+    inf.C = 1.0f;
+    inf.thr_key = 0xFFFFFFFFu;
+    inf.thr_idx = -1;
+    if (av >= 0) {
+      inf.bonus = (av == K) ? 1 : 0;
+      inf.piv_t = e_piv[av];
+      inf.s_t = e_s[av];
+      if (!inf.bonus) {
+        if (a.use_sigma) {   // av < K <= 64: lane av holds draft row av's statistics
+          auto rl_d = [av](double v) {
+            const uint64_t u = dbits(v);
+            const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u)), av));
+            const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u >> 32)), av));
+            return bits_d(uint64_t(lo) | (uint64_t(hi) << 32));
+          };
+          inf.piv_d = pivot_of(float(rl_d(sp0)));
+          inf.s_d = double(a.C) * rl_d(sp1) + rl_d(sp2);
+          inf.thr_key = uint32_t(__builtin_amdgcn_readlane(int(tk.key), av));
+          inf.thr_idx = __builtin_amdgcn_readlane(tk.idx, av);
+          inf.C = a.C;
+        } else {
+          inf.piv_d = e_piv[K + 1 + av];
+          inf.s_d = e_s[K + 1 + av];
+        }
+      }
     }
     if (i == 0) {
       a.accepted[b] = av;
-      sm_a = av;
+      a.info[b] = inf;
     }
   }
   if (a.row_lse != nullptr) {
@@ -232,36 +259,6 @@ __device__ __forceinline__ void stats_epilogue(const StatsArgs& a, int b) {
       }
       a.row_lse[int64_t(b) * (2 * K + 1) + rr] = float(l);
     }
-  }
-  __syncthreads();
-  if (tid == 0) {
-    const int av = sm_a;
-    RowInfo inf{};
-    inf.a = av;
-    inf.C = 1.0f;
-    inf.thr_key = 0xFFFFFFFFu;
-    inf.thr_idx = -1;
-    if (av >= 0) {
-      inf.bonus = (av == K) ? 1 : 0;
-      inf.piv_t = e_piv[av];
-      inf.s_t = e_s[av];
-      if (!inf.bonus) {
-        if (a.use_sigma) {
-          double z0, st1, st2;
-          ssd_rowkey tk;
-          load_sigma(a, b, av, z0, st1, st2, tk);
-          inf.piv_d = pivot_of(float(z0));
-          inf.s_d = double(a.C) * st1 + st2;
-          inf.thr_key = tk.key;
-          inf.thr_idx = tk.idx;
-          inf.C = a.C;
-        } else {
-          inf.piv_d = e_piv[K + 1 + av];
-          inf.s_d = e_s[K + 1 + av];
-        }
-      }
-    }
-    a.info[b] = inf;
   }
 }
 
