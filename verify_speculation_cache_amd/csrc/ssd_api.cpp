@@ -644,8 +644,7 @@ SSD_API int ssd_verify_tree(const void* target_logits, int64_t target_bstride,
 SSD_API size_t ssd_verify_round_workspace_size(int32_t B, int32_t K, int32_t V, int dtype) {
   if (check_shape(B, K, V) != SSD_OK || !dtype_ok(dtype)) return 0;
   const int64_t S = chunks_per_row(V);
-  return CacheWs(B, K, S).total + StatsWs(B, K + 1, S, K).total + ResidWs(B, S).total +
-         align256(sizeof(uint32_t) * kCntStride * B);
+  return CacheWs(B, K, S).total + StatsWs(B, K + 1, S, K).total + ResidWs(B, S).total;
 }
 
 SSD_API int ssd_verify_round(const void* target_logits, int64_t target_bstride,
@@ -671,9 +670,8 @@ SSD_API int ssd_verify_round(const void* target_logits, int64_t target_bstride,
   const CacheWs cw(B, K, S);
   const StatsWs sw(B, K + 1, S, K);
   const ResidWs rw(B, S);
-  const size_t off_s = cw.total, off_r = off_s + sw.total, off_c = off_r + rw.total;
-  if ((st = check_ws(workspace, ws_bytes, off_c + align256(sizeof(uint32_t) * kCntStride * B))) != SSD_OK)
-    return st;
+  const size_t off_s = cw.total, off_r = off_s + sw.total;
+  if ((st = check_ws(workspace, ws_bytes, off_r + rw.total)) != SSD_OK) return st;
   if ((st = check_grid(int64_t(B) * (K + 1) * 2 * S)) != SSD_OK) return st;
   char* ws = static_cast<char*>(workspace);
   RoundArgs a{};
@@ -684,8 +682,10 @@ SSD_API int ssd_verify_round(const void* target_logits, int64_t target_bstride,
   a.s.S = int(S);
   a.ncw = uint32_t((K + 1) * S);
   a.nsw = uint32_t((K + 1) * S);
-  a.cnt = reinterpret_cast<uint32_t*>(ws + off_c);
-  ResidArgs r = verify_resid_args(a.s, u_res, nullptr, ws + off_r, rw);
+  RoundResidArgs rr{};
+  rr.s = a.s;
+  ResidArgs& r = rr.r;
+  r = verify_resid_args(a.s, u_res, nullptr, ws + off_r, rw);
   r.cache_tokens = cache_tokens;
   r.sumF = sumF;
   for (int k = 0; k <= K; ++k) {
@@ -696,8 +696,8 @@ SSD_API int ssd_verify_round(const void* target_logits, int64_t target_bstride,
   r.slot = slot;
   hipStream_t stream = as_stream(hip_stream);
   if ((st = hip_status(launch_round_chunks(a, dtype, stream), "round chunk launch")) != SSD_OK) return st;
-  if ((st = hip_status(launch_round_merge(a, dtype, stream), "round merge launch")) != SSD_OK) return st;
-  return hip_status(launch_resid(r, dtype, true, stream), "round residual launch");
+  if ((st = hip_status(launch_cache_merge(a.c, dtype, stream), "round merge launch")) != SSD_OK) return st;
+  return hip_status(launch_round_resid(rr, dtype, stream), "round residual launch");
 }
 
 }  // extern "C"

@@ -18,10 +18,11 @@
 // Thresholds. Any key t such that at least F lanes of a chunk hold an entry
 // >= t (their lane maximum) bounds the chunk's F-th largest entry from
 // below, and so the row's: an entry below it can never be in the top F. In a
-// wave (2048 entries, 32 per lane) let T0_w be the F-th largest lane maximum
-// and Q_w the ceil(F/4)-th largest; both max_w T0_w and min_w Q_w are such
-// bounds (the latter through 4 x ceil(F/4) >= F lanes), and the chunk's T0 is
-// the larger of the two.
+// wave (2048 entries, 32 per lane) let Q_w be the ceil(F/4)-th largest lane
+// maximum; min_w Q_w is such a bound (4 x ceil(F/4) >= F lanes) and is the
+// chunk's T0. (The F-th largest lane maximum of one wave, max over waves, is
+// another; on the synthetic rows it kept 3 % fewer candidates, and its
+// bitwise search cost more than that saved.)
 //
 // Two launches.
 //  k_cache_chunk, one workgroup per (batch row b, length k, chunk c): 8192
@@ -569,16 +570,17 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
 }
 
 
-// Exp-mass of the entries below f0 (the non-candidates). Entries past the
-// row end read as -inf and add nothing; with f0 = NaN (no candidates) every
+// Scaled exp-mass (scaled_mass) of the entries below f0 (the
+// non-candidates); the caller applies the chunk's fix. Entries past the row
+// end read as -inf and add nothing; with f0 = NaN (no candidates) every
 // entry counts.
 template <int DT>
-__device__ __forceinline__ float chunk_rest_mass(const float (&x)[kPerThread], float f0, float piv, float c32) {
+__device__ __forceinline__ float chunk_rest_mass(const float (&x)[kPerThread], float f0, float P, float c32) {
   constexpr int PV = Dt<DT>::kPerVec;
   float sn = 0.0f;
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
-    const float e = __builtin_amdgcn_exp2f((x[q] - piv) * c32);
+    const float e = scaled_mass(x[q], c32, P);
     sn += (x[q] >= f0) ? 0.0f : e;
     // a vector at a time: keeps the exp temporaries short-lived
     if (q % PV == PV - 1) __builtin_amdgcn_sched_barrier(0);
@@ -616,7 +618,7 @@ __device__ __forceinline__ void cache_chunk_wg(const CacheArgs& a, uint32_t blk)
   constexpr int PV = Dt<DT>::kPerVec;
   constexpr int NV = kPerThread / PV;
   __shared__ float sm_wmax[4];
-  __shared__ uint32_t sm_wthr[4], sm_wthq[4];
+  __shared__ uint32_t sm_wthq[4];
   __shared__ int sm_wcnt[4];
   __shared__ double sm_ws[4];
   __shared__ uint64_t sm_list[4][kCandCap];   // per-wave candidate staging
@@ -657,23 +659,17 @@ __device__ __forceinline__ void cache_chunk_wg(const CacheArgs& a, uint32_t blk)
   for (int j = 1; j < NV; ++j) lm = fmaxf(lm, vm[j]);
   const float c32 = a.c32;
 
-  // ---- per-wave max and thresholds; chunk max and T0 ----
+  // ---- per-wave max and threshold; chunk max and T0 ----
   // A key t with at least F lanes whose maximum is >= t bounds the chunk's
-  // top F from below. Two such bounds, the larger taken: the F-th largest
-  // lane maximum of one wave (max over waves), and the smallest over waves of
-  // each wave's ceil(F/4)-th largest lane maximum (4 waves x ceil(F/4) >= F
-  // lanes). The second is far tighter for large F (about F candidates rather
-  // than several times F).
+  // top F from below. Each wave finds its ceil(F/4)-th largest lane maximum
+  // (bitwise search over the lanes' keys); the smallest over the four waves
+  // is such a bound (4 x ceil(F/4) >= F lanes). It is the chunk's T0.
   {
     const float wm = wave_max_u(lm);
-    uint32_t t = 0, tq = 0;
+    uint32_t tq = 0;
     if (F > 0) {
       const int Fq = (F + 3) >> 2;
       const uint32_t kl = local_of<DT>(tid, 0) < nvalid ? key_of<DT>(lm) : 0u;
-      for (int bit = Dt<DT>::kKeyBits - 1; bit >= 0; --bit) {
-        const uint32_t cand = t | (1u << bit);
-        if (__popcll(__ballot(kl >= cand)) >= F) t = cand;
-      }
       for (int bit = Dt<DT>::kKeyBits - 1; bit >= 0; --bit) {
         const uint32_t cand = tq | (1u << bit);
         if (__popcll(__ballot(kl >= cand)) >= Fq) tq = cand;
@@ -681,26 +677,24 @@ __device__ __forceinline__ void cache_chunk_wg(const CacheArgs& a, uint32_t blk)
     }
     if (lane == 0) {
       sm_wmax[w] = wm;
-      sm_wthr[w] = t;
       sm_wthq[w] = tq;
     }
   }
   __syncthreads();
   // lane i < 4 reads wave i's values; the combination happens on scalars
-  // (one register each instead of a copy of all twelve per thread)
+  // (one register each instead of a copy of all eight per thread)
   float mc;
   uint32_t t0;
   {
     const int li = lane & 3;
     const float vm = sm_wmax[li];
-    const uint32_t vt = sm_wthr[li], vq = sm_wthq[li];
+    const uint32_t vq = sm_wthq[li];
     auto rlf = [](float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
     auto rlu = [](uint32_t v, int l) { return uint32_t(__builtin_amdgcn_readlane(int(v), l)); };
     mc = fmaxf(fmaxf(rlf(vm, 0), rlf(vm, 1)), fmaxf(rlf(vm, 2), rlf(vm, 3)));
-    t0 = max(max(max(rlu(vt, 0), rlu(vt, 1)), max(rlu(vt, 2), rlu(vt, 3))),
-             min(min(rlu(vq, 0), rlu(vq, 1)), min(rlu(vq, 2), rlu(vq, 3))));
+    t0 = min(min(rlu(vq, 0), rlu(vq, 1)), min(rlu(vq, 2), rlu(vq, 3)));
   }
-  const float piv = pivot_of(mc);
+  const ScaledPivot sp = scaled_pivot(pivot_of(mc), c32);
   float f0 = __builtin_nanf("");   // F == 0: compares false, nothing is a candidate
   if (F > 0) f0 = (t0 <= key_of<DT>(-__builtin_inff())) ? -__builtin_inff() : value_of_key<DT>(t0);
 
@@ -710,7 +704,7 @@ __device__ __forceinline__ void cache_chunk_wg(const CacheArgs& a, uint32_t blk)
     cw = wave_compact<DT, true>(x, f0, tid, nvalid, int(c0), sm_list[w]);
   else
     cw = wave_compact<DT, false>(x, f0, tid, nvalid, int(c0), sm_list[w]);
-  const float sn = chunk_rest_mass<DT>(x, f0, piv, c32);
+  const float sn = chunk_rest_mass<DT>(x, f0, sp.P, c32);
   const double ws = wave_sum_u(double(sn));   // double across threads
   if (lane == 0) {
     sm_wcnt[w] = int(cw);
@@ -728,7 +722,7 @@ __device__ __forceinline__ void cache_chunk_wg(const CacheArgs& a, uint32_t blk)
     for (int i = lane; i < int(cw); i += 64) out[i] = sm_list[w][i];
   }
   if (tid == 0) {
-    const double s_rest = (sm_ws[0] + sm_ws[1]) + (sm_ws[2] + sm_ws[3]);
+    const double s_rest = ((sm_ws[0] + sm_ws[1]) + (sm_ws[2] + sm_ws[3])) * double(sp.fix);
     uint64_t* wp = reinterpret_cast<uint64_t*>(a.part + rowid * a.S + c);
     wp[0] = uint64_t(__float_as_uint(mc)) | (uint64_t(t0) << 32);
     wp[1] = dbits(s_rest);

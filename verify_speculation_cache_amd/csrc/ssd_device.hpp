@@ -558,10 +558,31 @@ __device__ inline void merge_rows_seg(const uint64_t* part, int NR, int S, float
   }
 }
 
+// exp2((z - piv) * c32) up to a factor common to a whole chunk, in one
+// fused multiply-add: with P = piv * c32 rounded to float, the argument
+// z * c32 - P is formed with a single rounding. Since the chunk's masses all
+// share P, their sum is the sum of exp2((z - piv) * c32) times
+// exp2(piv * c32 - P); scaled_mass_fix returns the inverse of that factor,
+// from the product's rounding error, which the fused multiply-add gives
+// exactly. Callers multiply their chunk total by it once.
+struct ScaledPivot {
+  float P;     // piv * c32, rounded
+  float fix;   // exp2(P - piv * c32)
+};
+__device__ __forceinline__ ScaledPivot scaled_pivot(float piv, float c32) {
+  const float P = piv * c32;
+  const float err = __builtin_fmaf(piv, c32, -P);   // piv * c32 - P, exact
+  return ScaledPivot{P, __builtin_amdgcn_exp2f(-err)};
+}
+__device__ __forceinline__ float scaled_mass(float z, float c32, float P) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(z, c32, -P));
+}
+
 // Statistics of one loaded chunk: the workgroup max m of the raw logits and
-// the sum of exp2((z - pivot_of(m)) * c32) (per-thread float sums, double
-// across threads). Called by every thread; both results are valid in every
-// thread (sm_f: 4 floats, sm_s: 4 doubles of LDS; two barriers).
+// the sum of exp2((z - pivot_of(m)) * c32) (per-thread float sums of
+// scaled_mass, double across threads, then the chunk's fix). Called by every
+// thread; both results are valid in every thread (sm_f: 4 floats, sm_s: 4
+// doubles of LDS; two barriers).
 template <int DT, int PT>
 __device__ __forceinline__ void chunk_max_sum(const ChunkVecs<DT, true, PT>& cv, float c32, float* sm_f,
                                               double* sm_s, float& m_out, double& s_out) {
@@ -580,20 +601,20 @@ __device__ __forceinline__ void chunk_max_sum(const ChunkVecs<DT, true, PT>& cv,
   if (lane == 0) sm_f[w] = m;
   __syncthreads();
   m = fmaxf(fmaxf(sm_f[0], sm_f[1]), fmaxf(sm_f[2], sm_f[3]));
-  const float piv = pivot_of(m);
+  const ScaledPivot sp = scaled_pivot(pivot_of(m), c32);
   float sum = 0.0f;
 #pragma unroll
   for (int j = 0; j < CV::NV; ++j) {
     float v[PV];
     cv.get(j, v);
 #pragma unroll
-    for (int e = 0; e < PV; ++e) sum += __builtin_amdgcn_exp2f((v[e] - piv) * c32);
+    for (int e = 0; e < PV; ++e) sum += scaled_mass(v[e], c32, sp.P);
   }
   const double wsum = wave_sum_u(double(sum));
   if (lane == 0) sm_s[w] = wsum;
   __syncthreads();
   m_out = m;
-  s_out = (sm_s[0] + sm_s[1]) + (sm_s[2] + sm_s[3]);
+  s_out = ((sm_s[0] + sm_s[1]) + (sm_s[2] + sm_s[3])) * double(sp.fix);
 }
 
 // Count this workgroup in; returns true in every thread of the workgroup that

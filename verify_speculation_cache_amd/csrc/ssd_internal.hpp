@@ -295,7 +295,10 @@ struct RoundArgs {
   CacheArgs c;
   StatsArgs s;
   uint32_t ncw, nsw;    // cache and statistics workgroups per batch row
-  uint32_t* cnt;        // [B] (kCntStride apart): merges done per batch row
+};
+struct RoundResidArgs {
+  ResidArgs r;
+  StatsArgs s;          // the accept scan's inputs (partials, sigma statistics)
 };
 
 // Launchers (return the hipError_t of the launch).
@@ -309,6 +312,7 @@ hipError_t launch_cache_stats(const CacheStatsArgs& a, hipStream_t st);
 hipError_t launch_tree_stats(const TreeArgs& a, int dtype, hipStream_t st);
 hipError_t launch_tree_round(const TreeArgs& a, int dtype, hipStream_t st);
 hipError_t launch_round_chunks(const RoundArgs& a, int dtype, hipStream_t st);
-hipError_t launch_round_merge(const RoundArgs& a, int dtype, hipStream_t st);
+hipError_t launch_cache_merge(const CacheArgs& a, int dtype, hipStream_t st);
+hipError_t launch_round_resid(const RoundResidArgs& a, int dtype, hipStream_t st);
 
 }  // namespace ssd

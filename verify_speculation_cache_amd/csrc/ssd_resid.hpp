@@ -9,6 +9,14 @@
 // keeps double-precision scaling. With every rho zero (set_plain) the mass
 // is e_t itself: fma(-0, e_d, e_t) = e_t, so no select is needed and the
 // per-entry code stays branch-free.
+//
+// Per entry the exponentials are taken in scaled form (scaled_mass: one
+// fused multiply-add for the argument): e_t = fix_t * e'_t and e_d = fix_d *
+// e'_d with row constants fix_t, fix_d, so r = fix_t * max(0, e'_t - rho' *
+// e'_d) with rho' = rho_w * fix_d / fix_t. The per-entry values are r / fix_t
+// (and e_t / fix_t); chunk masses are returned in target units (times
+// fix_t), and the in-chunk pick compares running sums of the per-entry
+// values against targets divided by fix_t.
 #pragma once
 
 #include "ssd_cdf.hpp"
@@ -16,20 +24,38 @@
 namespace ssd {
 
 struct ResidConsts {
-  float piv_t, piv_d, c32;
+  float Pt, Pd, c32;   // scaled pivots of the target and draft rows, log2(e)/tau
+  float fix_t;         // e_t = fix_t * (per-entry target value)
+  double dratio;       // fix_d / fix_t
   float rho_hi, rho_lo, rhoC_hi, rhoC_lo;
   float thr_val;     // sigma threshold as a logit value (key order = value order)
   int32_t thr_idx;
 };
 
-// Mass = e_t (bonus draw, or a residual without mass).
-__device__ __forceinline__ void set_plain(ResidConsts& k) {
-  k.rho_hi = k.rho_lo = k.rhoC_hi = k.rhoC_lo = 0.0f;
-}
-
 __device__ __forceinline__ void split2(double v, float& hi, float& lo) {
   hi = float(v);
   lo = float(v - double(hi));
+}
+
+// Row constants from the target and draft rows' pivots (raw logit units).
+__device__ __forceinline__ void set_rows(ResidConsts& k, float piv_t, float piv_d, float c32) {
+  const ScaledPivot st = scaled_pivot(piv_t, c32), sd = scaled_pivot(piv_d, c32);
+  k.c32 = c32;
+  k.Pt = st.P;
+  k.Pd = sd.P;
+  k.fix_t = st.fix;
+  k.dratio = double(sd.fix) / double(st.fix);
+}
+
+// The residual's weights: rho for non-members, rho * C for sigma members.
+__device__ __forceinline__ void set_rho(ResidConsts& k, double rho, double C) {
+  split2(rho * k.dratio, k.rho_hi, k.rho_lo);
+  split2(rho * C * k.dratio, k.rhoC_hi, k.rhoC_lo);
+}
+
+// Mass = e_t (bonus draw, or a residual without mass).
+__device__ __forceinline__ void set_plain(ResidConsts& k) {
+  k.rho_hi = k.rho_lo = k.rhoC_hi = k.rhoC_lo = 0.0f;
 }
 
 // Residual mass of one entry in target units (e_t when plain).
@@ -38,8 +64,8 @@ __device__ __forceinline__ void split2(double v, float& hi, float& lo) {
 // with -0 and +0 equal in both.
 template <bool SIG>
 __device__ __forceinline__ float resid_elem(const ResidConsts& k, float xt, float xd, int idx) {
-  const float et = __builtin_amdgcn_exp2f((xt - k.piv_t) * k.c32);
-  const float ed = __builtin_amdgcn_exp2f((xd - k.piv_d) * k.c32);
+  const float et = scaled_mass(xt, k.c32, k.Pt);
+  const float ed = scaled_mass(xd, k.c32, k.Pd);
   float hi = k.rho_hi, lo = k.rho_lo;
   if constexpr (SIG) {
     // bitwise, not short-circuit: keeps the test branch-free
@@ -53,7 +79,7 @@ __device__ __forceinline__ float resid_elem(const ResidConsts& k, float xt, floa
 }
 
 __device__ __forceinline__ float target_elem(const ResidConsts& k, float xt) {
-  return __builtin_amdgcn_exp2f((xt - k.piv_t) * k.c32);
+  return scaled_mass(xt, k.c32, k.Pt);
 }
 
 // Phase A: residual mass and target mass of the 8192-entry chunk at c0
@@ -90,8 +116,8 @@ __device__ __forceinline__ void resid_chunk_masses(const ResidConsts& k, const t
     sm_pair[4 + w] = Pw;
   }
   __syncthreads();
-  R = (sm_pair[0] + sm_pair[1]) + (sm_pair[2] + sm_pair[3]);
-  P = (sm_pair[4] + sm_pair[5]) + (sm_pair[6] + sm_pair[7]);
+  R = ((sm_pair[0] + sm_pair[1]) + (sm_pair[2] + sm_pair[3])) * double(k.fix_t);
+  P = ((sm_pair[4] + sm_pair[5]) + (sm_pair[6] + sm_pair[7])) * double(k.fix_t);
 }
 
 // Phase A over two consecutive 8192-chunks at once (a 16384-entry span at
@@ -135,8 +161,8 @@ __device__ __forceinline__ void resid_chunk_masses2(const ResidConsts& k, const 
   __syncthreads();
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    R[h] = (sm[8 * h] + sm[8 * h + 1]) + (sm[8 * h + 2] + sm[8 * h + 3]);
-    P[h] = (sm[8 * h + 4] + sm[8 * h + 5]) + (sm[8 * h + 6] + sm[8 * h + 7]);
+    R[h] = ((sm[8 * h] + sm[8 * h + 1]) + (sm[8 * h + 2] + sm[8 * h + 3])) * double(k.fix_t);
+    P[h] = ((sm[8 * h + 4] + sm[8 * h + 5]) + (sm[8 * h + 6] + sm[8 * h + 7])) * double(k.fix_t);
   }
 }
 
@@ -179,7 +205,8 @@ __device__ __forceinline__ void resid_find_chunk(const uint64_t* cmw, int S, flo
 }
 
 // Phase B, second level (every thread): re-read chunk cs of both rows and
-// pick the token whose running mass crosses target.
+// pick the token whose running mass crosses target (pre and target in
+// target units; the per-entry values are those units divided by fix_t).
 template <int DT, bool SIG>
 __device__ __forceinline__ int resid_pick(const ResidConsts& k, const typename Dt<DT>::T* rowT,
                                           const typename Dt<DT>::T* rowD, int cs, double pre, double target,
@@ -189,8 +216,120 @@ __device__ __forceinline__ int resid_pick(const ResidConsts& k, const typename D
   ChunkVecs<DT, false> cv[2];
   load_pair(cv[0], rowT, cv[1], rowD, c0, V, threadIdx.x);
   const typename Dt<DT>::T* const rows[2] = {rowT, rowD};
-  return chunk_pick<DT, 2>(cv, rows, V, c0, pre, target,
+  const double inv = 1.0 / double(k.fix_t);
+  return chunk_pick<DT, 2>(cv, rows, V, c0, pre * inv, target * inv,
                            [&](const float (&x)[2], int idx) { return resid_elem<SIG>(k, x[0], x[1], idx); }, pk);
+}
+
+// The residual / bonus draw of batch row b by one of its (S+1)/2 workgroups
+// (c2: its chunk pair), given the row's RowInfo as written by the accept
+// scan. Every thread calls it.
+template <int DT, bool SIG>
+__device__ __forceinline__ void resid_row_wg(const ResidArgs& a, RowInfo inf, int b, int c2) {
+  using T = typename Dt<DT>::T;
+  __shared__ double sm_pair[16];
+  __shared__ int sm_last;
+  __shared__ double sm_pre, sm_target;
+  __shared__ int sm_c, sm_useres;
+  __shared__ PickLds<DT, 2> sm_pk;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int S2 = (a.S + 1) / 2;   // workgroups per batch row, two 8192-chunks each
+  // Only trust a row index the stats kernel could have written: anything
+  // else (a workspace that was not zero-filled for this shape) is treated
+  // as a flagged row, so stale state can never address outside the inputs.
+  if (inf.a < -1 || inf.a > a.K) inf.a = -1;
+  if (inf.a == a.K || a.draft == nullptr) inf.bonus = 1;
+
+  // A bonus row has no draft: it reads the target row twice with rho = 0,
+  // so both rows take the same load and arithmetic path.
+  ResidConsts k{};
+  const T* rowT = nullptr;
+  const T* rowD = nullptr;
+  if (inf.a >= 0) {
+    rowT = static_cast<const T*>(a.target) + int64_t(b) * a.tb + int64_t(inf.a) * a.V;
+    k.thr_val = value_of_key<DT>(inf.thr_key);
+    k.thr_idx = inf.thr_idx;
+    if (inf.bonus) {
+      rowD = rowT;
+      set_rows(k, inf.piv_t, inf.piv_t, a.c32);
+      set_plain(k);
+    } else {
+      rowD = static_cast<const T*>(a.draft) + int64_t(b) * a.db + int64_t(inf.a) * a.V;
+      set_rows(k, inf.piv_t, inf.piv_d, a.c32);
+      set_rho(k, inf.s_d > 0.0 ? inf.s_t / inf.s_d : 0.0, double(inf.C));
+    }
+  }
+  // sigma thresholds that admit no entry (key above that of +inf)
+  if (SIG && inf.thr_key > key_of<DT>(__builtin_inff())) k.thr_val = __builtin_nanf("");
+
+  // ---------------- phase A: chunk masses ----------------
+  if (inf.a >= 0) {
+    double R[2], P[2];
+    resid_chunk_masses2<DT, SIG>(k, rowT, rowD, int64_t(c2) * kStatsChunk, a.V, sm_pair, R, P);
+    if (tid == 0) {
+      const int c = 2 * c2;
+      uint64_t* wp = reinterpret_cast<uint64_t*>(a.cmass + (int64_t(b) * a.S + c) * 2);
+      dev_store(wp, dbits(R[0]));
+      dev_store(wp + 1, dbits(P[0]));
+      if (c + 1 < a.S) {
+        dev_store(wp + 2, dbits(R[1]));
+        dev_store(wp + 3, dbits(P[1]));
+      }
+    }
+  }
+
+  if (!arrive_last(&a.cnt[int64_t(b) * kCntStride], uint32_t(S2), &sm_last)) return;
+
+  // ---------------- phase B: last workgroup of batch row b ----------------
+  if (inf.a < 0) {
+    if (tid == 0 && !a.tok_at_a) {
+      a.tok_out[int64_t(b) * a.tok_stride] = -1;
+      if (a.mass_out) a.mass_out[b] = __builtin_nanf("");
+    }
+    if (tid == 0 && a.hit) {
+      a.hit[b] = 0;
+      if (a.slot) a.slot[b] = -1;
+    }
+    return;
+  }
+  // the cache segment of length a (at most 64 tokens, lane i holds slot i),
+  // requested first so that its round trip overlaps those of the draw
+  int32_t seg_tok = -1;
+  if (a.hit && w == 0) {
+    const int n = a.lk_F[inf.a];
+    seg_tok = lane < n ? a.cache_tokens[int64_t(b) * a.sumF + a.lk_off[inf.a] + lane] : -1;
+  }
+  // chunk masses, then the first chunk whose running mass exceeds u * Z
+  if (w == 0) {
+    double zres, ztgt, target, pre;
+    int useres, cs;
+    resid_find_chunk(reinterpret_cast<const uint64_t*>(a.cmass + int64_t(b) * a.S * 2), a.S, a.u[b], lane, zres,
+                     ztgt, useres, target, cs, pre);
+    if (lane == 0) {
+      sm_c = cs;
+      sm_pre = pre;
+      sm_target = target;
+      sm_useres = useres;
+      if (a.mass_out) a.mass_out[b] = useres ? float(zres / inf.s_t) : 0.0f;
+    }
+  }
+  __syncthreads();
+  const int cs = sm_c;
+  int tok = -1;
+  if (cs >= 0) {
+    if (!sm_useres) set_plain(k);
+    tok = resid_pick<DT, SIG>(k, rowT, rowD, cs, sm_pre, sm_target, a.V, sm_pk);
+  }
+  if (tid == 0) a.tok_out[int64_t(b) * a.tok_stride + (a.tok_at_a ? inf.a : 0)] = tok;
+  if (a.hit && w == 0) {
+    // cache hit of the outcome (a, t*)
+    const uint64_t m = __ballot(tok >= 0 && seg_tok == tok);
+    if (lane == 0) {
+      a.hit[b] = m != 0 ? 1 : 0;
+      if (a.slot) a.slot[b] = m != 0 ? __ffsll((unsigned long long)m) - 1 : -1;
+    }
+  }
 }
 
 }  // namespace ssd

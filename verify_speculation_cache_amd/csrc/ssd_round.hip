@@ -6,22 +6,26 @@
 // the realised outcome is looked up in the cache.
 //
 // The separate entry points need five launches (cache chunk pass, cache
-// merge, row statistics, residual, lookup). Here:
+// merge, row statistics, residual, lookup). Here three:
 //  k_round_chunks  the cache chunk pass over draft rows 0..K and the row
 //                  statistics' chunk pass over target rows 0..K in one grid
 //                  (they read different rows and depend on nothing), so the
 //                  two streams share one launch and one tail;
-//  k_round_merge   the cache merge of every (b, k); the last merge of batch
-//                  row b to finish runs that row's accept scan, which needs
-//                  the sigma statistics of all K+1 merges;
-//  k_resid         the residual / bonus draw, whose last workgroup per row
-//                  also looks the outcome up in the cache.
+//  k_cache_merge   the cache merge of every (b, k), as in the cache build;
+//  k_round_resid   every workgroup of batch row b first runs the row's accept
+//                  scan itself (it needs the sigma statistics of all K+1
+//                  merges and the target rows' chunk partials, a few KiB),
+//                  then its share of the residual / bonus draw; the last
+//                  workgroup per row also looks the outcome up in the cache.
+//                  Repeating the small scan in each of the row's workgroups
+//                  costs less than a cross-workgroup hand-off of its result.
 // The arithmetic is that of the separate entry points: the cache is
 // bit-identical to ssd_build_cache's; the row statistics here sum 8192-entry
 // chunk partials (ssd_verify's pass sums 16384-entry ones, a register budget
 // this launch cannot afford next to the cache pass), so accept decisions and
 // draws agree with ssd_verify's except at rounding-level ties.
 #include "ssd_cache.hpp"
+#include "ssd_resid.hpp"
 #include "ssd_stats.hpp"
 
 namespace ssd {
@@ -39,13 +43,16 @@ __global__ __launch_bounds__(kThreads) void k_round_chunks(RoundArgs a) {
 }
 
 template <int DT>
-__global__ __launch_bounds__(kThreads) void k_round_merge(RoundArgs a) {
-  __shared__ int sm_last;
-  const int64_t rowid = blockIdx.x;   // b * (K+1) + k
-  cache_merge_wg<DT>(a.c, rowid);
-  const int b = int(rowid / (a.c.K + 1));
-  if (!arrive_last(&a.cnt[int64_t(b) * kCntStride], uint32_t(a.c.K + 1), &sm_last)) return;
-  stats_epilogue<DT>(a.s, b);
+__global__ __launch_bounds__(kThreads) void k_round_resid(RoundResidArgs a) {
+  __shared__ float e_piv[kMaxRows];
+  __shared__ double e_s[kMaxRows];
+  __shared__ RowInfo sm_inf;
+  const int S2 = (a.r.S + 1) / 2;
+  const int b = blockIdx.x / S2;
+  const int c2 = blockIdx.x - b * S2;
+  // the row's first workgroup also stores accepted[b] and out_tokens
+  const RowInfo inf = accept_scan<DT, true>(a.s, b, c2 == 0, e_piv, e_s, &sm_inf);
+  resid_row_wg<DT, true>(a.r, inf, b, c2);
 }
 
 hipError_t launch_round_chunks(const RoundArgs& a, int dtype, hipStream_t st) {
@@ -55,10 +62,10 @@ hipError_t launch_round_chunks(const RoundArgs& a, int dtype, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_round_merge(const RoundArgs& a, int dtype, hipStream_t st) {
-  const unsigned grid = unsigned(int64_t(a.c.B) * (a.c.K + 1));
-  if (dtype == SSD_BF16) hipLaunchKernelGGL(k_round_merge<1>, dim3(grid), dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL(k_round_merge<0>, dim3(grid), dim3(kThreads), 0, st, a);
+hipError_t launch_round_resid(const RoundResidArgs& a, int dtype, hipStream_t st) {
+  const unsigned grid = unsigned(int64_t(a.r.B) * ((a.r.S + 1) / 2));
+  if (dtype == SSD_BF16) hipLaunchKernelGGL(k_round_resid<1>, dim3(grid), dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL(k_round_resid<0>, dim3(grid), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -110,13 +110,29 @@ __device__ __forceinline__ void stats_chunk_wg(const StatsArgs& a, uint32_t blk)
   }
 }
 
-// Epilogue of batch row b (run by the last workgroup to finish its chunks):
-// merge the row partials and run the accept scan (verify) or record the row
-// to sample from (rows mode); leaves a RowInfo for the residual kernel.
-template <int DT>
-__device__ __forceinline__ void stats_epilogue(const StatsArgs& a, int b) {
-  __shared__ float e_piv[kMaxRows];
-  __shared__ double e_s[kMaxRows];
+// Row max pivots and sums of the a.NR logit rows of batch row b, merged
+// from their chunk partials (loaded with device-scope loads: the partials
+// may come from other workgroups of the same launch). Called by every
+// thread; the results are in e_piv / e_s after the caller's barrier.
+__device__ __forceinline__ void merge_row_partials(const StatsArgs& a, int b, float* e_piv, double* e_s) {
+  const uint64_t* pb = reinterpret_cast<const uint64_t*>(a.part) + int64_t(b) * a.NR * a.S * 2;
+  if (a.S <= 64) merge_rows_seg(pb, a.NR, a.S, a.c32, e_piv, e_s);
+  else merge_rows<2>(pb, a.NR, a.S, a.c32, e_piv, e_s, nullptr);
+}
+
+// The accept scan of batch row b (verify mode): merges the target rows'
+// partials, takes p and q at the drafted tokens, keeps d iff u*q(d) < p(d)
+// up to the first rejection, and fills the RowInfo of the row to sample
+// from (wave 0, lane i for drafted position i; the sigma statistics of the
+// sampled row come out of the lane that loaded them). With `write`, wave 0
+// also stores accepted[b], out_tokens and probs. Called by every thread;
+// the RowInfo is returned in every thread (through *sm_inf, one barrier)
+// when BCAST, else only in wave 0. BCAST is for a caller that draws in the
+// same launch: out_tokens at the accepted length is then not written here
+// (the draw stores it). e_piv / e_s stay valid for the caller.
+template <int DT, bool BCAST>
+__device__ __forceinline__ RowInfo accept_scan(const StatsArgs& a, int b, bool write, float* e_piv, double* e_s,
+                                               RowInfo* sm_inf) {
   const int tid = threadIdx.x;
   const int K = a.K;
   // per drafted position (wave 0, lane i < K): inputs of the accept test,
@@ -125,7 +141,7 @@ __device__ __forceinline__ void stats_epilogue(const StatsArgs& a, int b) {
   float ua = 0.0f, zt = 0.0f, zd = 0.0f;
   double sp0 = 0.0, sp1 = 0.0, sp2 = 0.0;
   ssd_rowkey tk{0xFFFFFFFFu, -1};
-  if (a.mode != kModeRows && tid < K) {
+  if (tid < K) {
     const int i = tid;
     d = a.tokens[int64_t(b) * K + i];
     ua = a.u_acc[int64_t(b) * K + i];
@@ -134,14 +150,112 @@ __device__ __forceinline__ void stats_epilogue(const StatsArgs& a, int b) {
     zd = __uint_as_float(uint32_t(g >> 32));
     if (a.use_sigma) load_sigma(a, b, i, sp0, sp1, sp2, tk);
   }
-  {
-    const uint64_t* pb = reinterpret_cast<const uint64_t*>(a.part) + int64_t(b) * a.NR * a.S * 2;
-    if (a.S <= 64) merge_rows_seg(pb, a.NR, a.S, a.c32, e_piv, e_s);
-    else merge_rows<2>(pb, a.NR, a.S, a.c32, e_piv, e_s, nullptr);
-  }
+  merge_row_partials(a, b, e_piv, e_s);
   __syncthreads();
 
+  RowInfo inf{};
+  if (tid < 64) {
+    const int i = tid;
+    bool bad = false, acc = true;
+    double pd = 0.0, qd = 0.0;
+    if (i < K) {
+      bad = (d < 0 || d >= a.V);
+      if (!bad) {
+        const double st = e_s[i];
+        pd = st > 0.0 ? exp2(double(zt - e_piv[i]) * double(a.c32)) / st : 0.0;
+        double pivd, sdn, wgt = 1.0;
+        if (a.use_sigma) {
+          pivd = double(pivot_of(float(sp0)));
+          sdn = double(a.C) * sp1 + sp2;
+          if (in_top<DT>(zd, d, tk.key, tk.idx)) wgt = double(a.C);
+        } else {
+          pivd = double(e_piv[K + 1 + i]);
+          sdn = e_s[K + 1 + i];
+        }
+        qd = sdn > 0.0 ? wgt * exp2(double(zd - float(pivd)) * double(a.c32)) / sdn : 0.0;
+        acc = double(ua) * qd < pd;
+      }
+    }
+    const uint64_t badm = __ballot(i < K && bad);
+    const uint64_t rej = __ballot(i < K && !acc);
+    const int av = badm ? -1 : (rej ? (__ffsll((unsigned long long)rej) - 1) : K);   // wave-uniform
+    if (write) {
+      if (i < K && a.probs != nullptr) {
+        a.probs[(int64_t(b) * K + i) * 2 + 0] = float(pd);
+        a.probs[(int64_t(b) * K + i) * 2 + 1] = float(qd);
+      }
+      // positions 0..K: the kept drafts (lane ii < av <= K holds d_ii), then
+      // -1; position av is left to the draw when BCAST (the draw runs in the
+      // same launch and stores the token there)
+      for (int ii = i; ii <= K; ii += 64)
+        if (!BCAST || ii != av) a.out_tokens[int64_t(b) * (K + 1) + ii] = (av >= 0 && ii < av) ? d : -1;
+      if (i == 0) a.accepted[b] = av;
+    }
+
+    inf.a = av;
+    inf.C = 1.0f;
+    inf.thr_key = 0xFFFFFFFFu;
+    inf.thr_idx = -1;
+    if (av >= 0) {
+      inf.bonus = (av == K) ? 1 : 0;
+      inf.piv_t = e_piv[av];
+      inf.s_t = e_s[av];
+      if (!inf.bonus) {
+        if (a.use_sigma) {   // av < K <= 64: lane av holds draft row av's statistics
+          auto rl_d = [av](double v) {
+            const uint64_t u = dbits(v);
+            const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u)), av));
+            const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u >> 32)), av));
+            return bits_d(uint64_t(lo) | (uint64_t(hi) << 32));
+          };
+          inf.piv_d = pivot_of(float(rl_d(sp0)));
+          inf.s_d = double(a.C) * rl_d(sp1) + rl_d(sp2);
+          inf.thr_key = uint32_t(__builtin_amdgcn_readlane(int(tk.key), av));
+          inf.thr_idx = __builtin_amdgcn_readlane(tk.idx, av);
+          inf.C = a.C;
+        } else {
+          inf.piv_d = e_piv[K + 1 + av];
+          inf.s_d = e_s[K + 1 + av];
+        }
+      }
+    }
+    if (BCAST && i == 0) *sm_inf = inf;
+  }
+  if (BCAST) {
+    __syncthreads();
+    // the same in every lane: kept in scalar registers
+    auto u32 = [](const void* p) { return uint32_t(__builtin_amdgcn_readfirstlane(*static_cast<const int*>(p))); };
+    auto f32 = [&](const float* p) { return __uint_as_float(u32(p)); };
+    auto f64 = [&](const double* p) {
+      const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+      return bits_d(uint64_t(u32(q)) | (uint64_t(u32(q + 1)) << 32));
+    };
+    inf.a = int32_t(u32(&sm_inf->a));
+    inf.bonus = int32_t(u32(&sm_inf->bonus));
+    inf.piv_t = f32(&sm_inf->piv_t);
+    inf.piv_d = f32(&sm_inf->piv_d);
+    inf.s_t = f64(&sm_inf->s_t);
+    inf.s_d = f64(&sm_inf->s_d);
+    inf.thr_key = u32(&sm_inf->thr_key);
+    inf.thr_idx = int32_t(u32(&sm_inf->thr_idx));
+    inf.C = f32(&sm_inf->C);
+  }
+  return inf;
+}
+
+// Epilogue of batch row b (run by the last workgroup to finish its chunks):
+// the accept scan (verify) or the record of the row to sample from (rows
+// mode); leaves a RowInfo for the residual kernel.
+template <int DT>
+__device__ __forceinline__ void stats_epilogue(const StatsArgs& a, int b) {
+  __shared__ float e_piv[kMaxRows];
+  __shared__ double e_s[kMaxRows];
+  const int tid = threadIdx.x;
+  const int K = a.K;
+
   if (a.mode == kModeRows) {
+    merge_row_partials(a, b, e_piv, e_s);
+    __syncthreads();
     if (tid == 0) {
       RowInfo inf{};
       const int j = a.rows_in[b];
@@ -176,74 +290,8 @@ __device__ __forceinline__ void stats_epilogue(const StatsArgs& a, int b) {
     return;
   }
 
-  // verify: wave 0, lane i handles drafted position i (K <= 64); the same
-  // wave then leaves the RowInfo, taking the sigma statistics of the row to
-  // sample from out of the lane that loaded them
-  if (tid < 64) {
-    const int i = tid;
-    bool bad = false, acc = true;
-    double pd = 0.0, qd = 0.0;
-    if (i < K) {
-      bad = (d < 0 || d >= a.V);
-      if (!bad) {
-        const double st = e_s[i];
-        pd = st > 0.0 ? exp2(double(zt - e_piv[i]) * double(a.c32)) / st : 0.0;
-        double pivd, sdn, wgt = 1.0;
-        if (a.use_sigma) {
-          pivd = double(pivot_of(float(sp0)));
-          sdn = double(a.C) * sp1 + sp2;
-          if (in_top<DT>(zd, d, tk.key, tk.idx)) wgt = double(a.C);
-        } else {
-          pivd = double(e_piv[K + 1 + i]);
-          sdn = e_s[K + 1 + i];
-        }
-        qd = sdn > 0.0 ? wgt * exp2(double(zd - float(pivd)) * double(a.c32)) / sdn : 0.0;
-        acc = double(ua) * qd < pd;
-      }
-    }
-    const uint64_t badm = __ballot(i < K && bad);
-    const uint64_t rej = __ballot(i < K && !acc);
-    const int av = badm ? -1 : (rej ? (__ffsll((unsigned long long)rej) - 1) : K);   // wave-uniform
-    if (i < K && a.probs != nullptr) {
-      a.probs[(int64_t(b) * K + i) * 2 + 0] = float(pd);
-      a.probs[(int64_t(b) * K + i) * 2 + 1] = float(qd);
-    }
-    // positions 0..K: the kept drafts (lane ii < av <= K holds d_ii), then -1
-    for (int ii = i; ii <= K; ii += 64) a.out_tokens[int64_t(b) * (K + 1) + ii] = (av >= 0 && ii < av) ? d : -1;
-
-    RowInfo inf{};
-    inf.a = av;
-    inf.C = 1.0f;
-    inf.thr_key = 0xFFFFFFFFu;
-    inf.thr_idx = -1;
-    if (av >= 0) {
-      inf.bonus = (av == K) ? 1 : 0;
-      inf.piv_t = e_piv[av];
-      inf.s_t = e_s[av];
-      if (!inf.bonus) {
-        if (a.use_sigma) {   // av < K <= 64: lane av holds draft row av's statistics
-          auto rl_d = [av](double v) {
-            const uint64_t u = dbits(v);
-            const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u)), av));
-            const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u >> 32)), av));
-            return bits_d(uint64_t(lo) | (uint64_t(hi) << 32));
-          };
-          inf.piv_d = pivot_of(float(rl_d(sp0)));
-          inf.s_d = double(a.C) * rl_d(sp1) + rl_d(sp2);
-          inf.thr_key = uint32_t(__builtin_amdgcn_readlane(int(tk.key), av));
-          inf.thr_idx = __builtin_amdgcn_readlane(tk.idx, av);
-          inf.C = a.C;
-        } else {
-          inf.piv_d = e_piv[K + 1 + av];
-          inf.s_d = e_s[K + 1 + av];
-        }
-      }
-    }
-    if (i == 0) {
-      a.accepted[b] = av;
-      a.info[b] = inf;
-    }
-  }
+  const RowInfo inf = accept_scan<DT, false>(a, b, true, e_piv, e_s, nullptr);
+  if (tid == 0) a.info[b] = inf;
   if (a.row_lse != nullptr) {
     for (int rr = tid; rr < 2 * K + 1; rr += kThreads) {
       double l;

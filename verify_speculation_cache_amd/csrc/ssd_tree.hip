@@ -193,15 +193,14 @@ __global__ __launch_bounds__(kThreads) void k_tree_round(TreeArgs a) {
   const T* rowT = tree_row<DT>(a, b, node);
   const T* rowD = rowT;
   ResidConsts k{};
-  k.piv_t = rt.m;
-  k.piv_d = rt.m;
-  k.c32 = a.c32;
+  set_rows(k, rt.m, rt.m, a.c32);
+  set_plain(k);
   const int dr = a.drow[node];
   if (st.c > 0.0 && dr >= 0) {
     const RowPartial rd = a.rstat[int64_t(b) * a.NR + dr];
     rowD = tree_row<DT>(a, b, dr);
-    k.piv_d = rd.m;
-    split2(rd.s > 0.0 ? st.c * rt.s / rd.s : 0.0, k.rho_hi, k.rho_lo);
+    set_rows(k, rt.m, rd.m, a.c32);
+    set_rho(k, rd.s > 0.0 ? st.c * rt.s / rd.s : 0.0, 1.0);
   }
 
   // ---------------- phase A: chunk masses ----------------
