@@ -258,7 +258,7 @@ def main():
         # (target rows 0..K, draft rows 0..K) plus the residual rows again
         roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(gbps / PEAK_HBM_GBS, 4), "traffic": measured_traffic(ROUND_BYTES_PROFILE),
-                    "kernel": "ssd_verify_round (k_round_chunks + k_round_merge + k_resid, bf16)",
+                    "kernel": "ssd_verify_round (k_round_chunks + k_cache_merge + k_round_resid, bf16)",
                     "bytes_per_launch": step_bytes, "avg_launch_ms": round(ms_step, 5)}
 
     cpu = None

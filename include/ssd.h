@@ -305,9 +305,9 @@ SSD_API size_t ssd_verify_round_workspace_size(int32_t B, int32_t K, int32_t V, 
  * verification add 8192-entry chunk partials (ssd_verify: 16384), so an
  * outcome can differ from the three calls' only where a decision lies within
  * rounding of its threshold. Three launches instead of five: the cache's and
- * the row statistics' chunk passes share one, the accept scan runs in the
- * last cache merge of each batch row, the lookup in the residual draw's last
- * workgroup.
+ * the row statistics' chunk passes share one, the cache merge follows, and
+ * each residual workgroup runs its batch row's accept scan before its share
+ * of the draw (the lookup in the draw's last workgroup).
  *   target_logits device [B, K+1, V]; draft_logits device [B, >=K+1, V]
  *   F host int32 [K+1] (0 <= F_k <= min(V, 64)); C in [0, 1]
  *   draft_tokens device int32 [B, K] (drawn from q_sigma, e.g. by
