@@ -664,13 +664,21 @@ __device__ __forceinline__ void cache_chunk_wg(const CacheArgs& a, uint32_t blk)
   // top F from below. Each wave finds its ceil(F/4)-th largest lane maximum
   // (bitwise search over the lanes' keys); the smallest over the four waves
   // is such a bound (4 x ceil(F/4) >= F lanes). It is the chunk's T0.
+  // Every lane's key lies between the wave's smallest key and the key of
+  // its maximum, so all keys share those two keys' common leading bits, and
+  // the full search would set exactly those: it starts from that prefix and
+  // tests only the bits below it (same result, typically half the steps;
+  // lanes past the row end have key 0, which leaves no common prefix).
   {
     const float wm = wave_max_u(lm);
     uint32_t tq = 0;
     if (F > 0) {
       const int Fq = (F + 3) >> 2;
       const uint32_t kl = local_of<DT>(tid, 0) < nvalid ? key_of<DT>(lm) : 0u;
-      for (int bit = Dt<DT>::kKeyBits - 1; bit >= 0; --bit) {
+      const uint32_t diff = wave_min_u32(kl) ^ key_of<DT>(wm);
+      const int h = diff == 0 ? 0 : 32 - __clz(diff);   // bits below h may differ
+      tq = h >= 32 ? 0u : (key_of<DT>(wm) >> h) << h;
+      for (int bit = h - 1; bit >= 0; --bit) {
         const uint32_t cand = tq | (1u << bit);
         if (__popcll(__ballot(kl >= cand)) >= Fq) tq = cand;
       }

@@ -348,6 +348,19 @@ __device__ __forceinline__ float wave_max_u(float v) {
   v = fmaxf(v, movf<kBcast31, 0xC>(v, v));
   return lane63f(v);
 }
+// wave min of an unsigned int, uniform result
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  using namespace dpp;
+  auto mn = [](uint32_t a, uint32_t b) { return a < b ? a : b; };
+  const int id = -1;   // 0xFFFFFFFF: identity of min for rows a row_mask leaves out
+  v = mn(v, uint32_t(mov<kXor1>(id, int(v))));
+  v = mn(v, uint32_t(mov<kXor2>(id, int(v))));
+  v = mn(v, uint32_t(mov<kHalfMirror>(id, int(v))));
+  v = mn(v, uint32_t(mov<kMirror>(id, int(v))));
+  v = mn(v, uint32_t(mov<kBcast15, 0xA>(id, int(v))));
+  v = mn(v, uint32_t(mov<kBcast31, 0xC>(id, int(v))));
+  return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
+}
 // wave sum of a float, uniform result (fixed order: deterministic)
 __device__ __forceinline__ float wave_sum_uf(float v) {
   using namespace dpp;
