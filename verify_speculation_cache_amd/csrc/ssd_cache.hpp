@@ -323,8 +323,7 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
     const float m = wave_max(ml);
     const double t = sl > 0.0 ? sl * rescale(pivot_of(ml), pivot_of(m), c32) : 0.0;
     const double srest = wave_sum(t);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) tmax = max(tmax, uint32_t(__shfl_xor(int(tmax), o)));
+    tmax = wave_max_u32(tmax);
     // the F-th largest chunk maximum (the F largest are F distinct entries
     // of the row), by a bitwise search over the lanes' chunk-max keys
     if (F > 0 && F <= a.S && a.S <= 64) {

@@ -22,20 +22,19 @@ __device__ __forceinline__ void chunk_crossing(MassFn mass, int S, double target
     const int cc = g + lane;
     const double mc = mass(cc, g);
     const double incl = wave_incl_scan_d(mc, lane);
-    const double prev = __shfl_up(incl, 1);   // all lanes shuffle (lane 0 reads itself)
-    const double excl = base + (lane > 0 ? prev : 0.0);
+    const double excl = base + wave_shift_up1_d(incl);
     const uint64_t crossing = __ballot(cc < S && base + incl > target);
     const uint64_t pos = __ballot(cc < S && mc > 0.0);
     if (crossing) {
       const int l = __ffsll((unsigned long long)crossing) - 1;
       cs = g + l;
-      pre = __shfl(excl, l);
+      pre = lane_d(excl, l);
     } else if (pos) {
       const int l = 63 - __clzll((long long)pos);
       lastpos = g + l;
-      lastpre = __shfl(excl, l);
+      lastpre = lane_d(excl, l);
     }
-    base += __shfl(incl, 63);
+    base += lane_d(incl, 63);
   }
   if (cs < 0) {
     cs = lastpos;

@@ -312,6 +312,7 @@ constexpr int kHalfMirror = 0x141;
 constexpr int kMirror = 0x140;
 constexpr int kBcast15 = 0x142;
 constexpr int kBcast31 = 0x143;
+constexpr int kWaveShr1 = 0x138;   // wave_shr:1 (across rows)
 constexpr int shr(int n) { return 0x110 + n; }
 template <int CTRL, int ROWS = 0xF>
 __device__ __forceinline__ int mov(int old, int v) {
@@ -395,38 +396,55 @@ __device__ __forceinline__ int wave_scan_i(int v) {
   return v;
 }
 
-// ---- wave64 reductions (butterflies: every lane ends with the same bits) ----
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
+// ---- wave64 reductions and scans (DPP lane moves; call with the whole wave
+// active). Reductions return the same value in every lane. ----
+__device__ __forceinline__ float wave_max(float v) { return wave_max_u(v); }
+__device__ __forceinline__ double wave_sum(double v) { return wave_sum_u(v); }
 __device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  using namespace dpp;
+  v += mov<kXor1>(0, v);
+  v += mov<kXor2>(0, v);
+  v += mov<kHalfMirror>(0, v);
+  v += mov<kMirror>(0, v);
+  v += mov<kBcast15, 0xA>(0, v);
+  v += mov<kBcast31, 0xC>(0, v);
+  return __builtin_amdgcn_readlane(v, 63);
 }
-// inclusive prefix sum over lanes 0..63
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  using namespace dpp;
+  auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  v = mx(v, uint32_t(mov<kXor1>(0, int(v))));
+  v = mx(v, uint32_t(mov<kXor2>(0, int(v))));
+  v = mx(v, uint32_t(mov<kHalfMirror>(0, int(v))));
+  v = mx(v, uint32_t(mov<kMirror>(0, int(v))));
+  v = mx(v, uint32_t(mov<kBcast15, 0xA>(0, int(v))));
+  v = mx(v, uint32_t(mov<kBcast31, 0xC>(0, int(v))));
+  return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
+}
+// inclusive prefix sum over lanes 0..63 (lane is unused; kept for callers)
 __device__ __forceinline__ int wave_incl_scan_i(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
-  return v;
+  (void)lane;
+  return wave_scan_i(v);
 }
 __device__ __forceinline__ double wave_incl_scan_d(double v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
+  using namespace dpp;
+  (void)lane;
+  v += movd<shr(1)>(v);
+  v += movd<shr(2)>(v);
+  v += movd<shr(4)>(v);
+  v += movd<shr(8)>(v);
+  v += movd<kBcast15, 0xA>(v);
+  v += movd<kBcast31, 0xC>(v);
   return v;
+}
+// the value of lane lane - 1 (0 in lane 0)
+__device__ __forceinline__ double wave_shift_up1_d(double v) { return dpp::movd<dpp::kWaveShr1>(v); }
+// lane l's value (l the same in every lane)
+__device__ __forceinline__ double lane_d(double v, int l) {
+  const uint64_t b = uint64_t(__double_as_longlong(v));
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(b)), l));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(b >> 32)), l));
+  return __longlong_as_double(int64_t((uint64_t(hi) << 32) | lo));
 }
 
 // ---- workgroup (4 waves) reductions; all threads must call ----
@@ -542,6 +560,31 @@ __device__ void merge_rows(const uint64_t* part, int NR, int S, float c32, float
 // merge_rows for S <= 64 chunks per row, all partials in one round trip:
 // each row gets a segment of G lanes (G = S rounded up to a power of two),
 // one lane per chunk; segmented butterflies give the row max and the
+
+// All-reduce over aligned segments of G lanes (G a power of two <= 64): the
+// in-row DPP steps (quad swaps, half-row mirror, row mirror) reduce segments
+// of up to 16 lanes; wider ones add one or two shuffles across rows.
+__device__ __forceinline__ float seg_max(float v, int G) {
+  using namespace dpp;
+  if (G >= 2) v = fmaxf(v, movf<kXor1>(v, v));
+  if (G >= 4) v = fmaxf(v, movf<kXor2>(v, v));
+  if (G >= 8) v = fmaxf(v, movf<kHalfMirror>(v, v));
+  if (G >= 16) v = fmaxf(v, movf<kMirror>(v, v));
+  if (G >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+  if (G >= 64) v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ double seg_sum(double v, int G) {
+  using namespace dpp;
+  if (G >= 2) v += movd<kXor1>(v);
+  if (G >= 4) v += movd<kXor2>(v);
+  if (G >= 8) v += movd<kHalfMirror>(v);
+  if (G >= 16) v += movd<kMirror>(v);
+  if (G >= 32) v += __shfl_xor(v, 16);
+  if (G >= 64) v += __shfl_xor(v, 32);
+  return v;
+}
+
 // rescaled sum (fixed order, deterministic).
 __device__ inline void merge_rows_seg(const uint64_t* part, int NR, int S, float c32, float* piv_out,
                                       double* s_out) {
@@ -559,11 +602,9 @@ __device__ inline void merge_rows_seg(const uint64_t* part, int NR, int S, float
       m = lo_f(dev_load(p));
       s = bits_d(dev_load(p + 1));
     }
-    float mr = m;
-    for (int o = 1; o < G; o <<= 1) mr = fmaxf(mr, __shfl_xor(mr, o));
+    const float mr = seg_max(m, G);
     const float pr = pivot_of(mr);
-    double t = s > 0.0 ? s * rescale(pivot_of(m), pr, c32) : 0.0;
-    for (int o = 1; o < G; o <<= 1) t += __shfl_xor(t, o);
+    const double t = seg_sum(s > 0.0 ? s * rescale(pivot_of(m), pr, c32) : 0.0, G);
     if (cl == 0 && r < NR) {
       piv_out[r] = pr;
       s_out[r] = t;

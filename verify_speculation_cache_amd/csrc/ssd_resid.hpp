@@ -185,8 +185,8 @@ __device__ __forceinline__ void resid_find_chunk(const uint64_t* cmw, int S, flo
       r0 = r;
       t0 = t;
     }
-    zres += __shfl(wave_incl_scan_d(r, lane), 63);
-    ztgt += __shfl(wave_incl_scan_d(t, lane), 63);
+    zres += lane_d(wave_incl_scan_d(r, lane), 63);
+    ztgt += lane_d(wave_incl_scan_d(t, lane), 63);
   }
   useres = zres > 0.0 ? 1 : 0;
   const double tot = useres ? zres : ztgt;

@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void k_sample(SampleArgs a) {
       return sc > 0.0 ? sc * rescale(pivot_of(mc), P, a.c32) : 0.0;
     };
     double Z = 0.0;
-    for (int g = 0; g < a.S; g += 64) Z += __shfl(wave_incl_scan_d(mass(g + lane, g), lane), 63);
+    for (int g = 0; g < a.S; g += 64) Z += lane_d(wave_incl_scan_d(mass(g + lane, g), lane), 63);
     const double target = double(a.u[rowid]) * Z;
     int cs = -1;
     double pre = 0.0;

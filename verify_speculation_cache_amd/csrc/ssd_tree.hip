@@ -234,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_round(TreeArgs a) {
       for (int g = 0; g < a.S; g += 64) {
         const int cc = g + lane;
         const double r = cc < a.S ? bits_d(dev_load(cmw + cc * 2)) : 0.0;
-        zres += __shfl(wave_incl_scan_d(r, lane), 63);
+        zres += lane_d(wave_incl_scan_d(r, lane), 63);
       }
       sP[n] = P;
       sQ[n] = Q;
