@@ -633,10 +633,12 @@ __device__ __forceinline__ float scaled_mass(float z, float c32, float P) {
 }
 
 // Statistics of one loaded chunk: the workgroup max m of the raw logits and
-// the sum of exp2((z - pivot_of(m)) * c32) (per-thread float sums of
-// scaled_mass, double across threads, then the chunk's fix). Called by every
-// thread; both results are valid in every thread (sm_f: 4 floats, sm_s: 4
-// doubles of LDS; two barriers).
+// the sum of exp2((z - pivot_of(m)) * c32). Each wave sums scaled_mass
+// against its own maximum (per-thread float sums, double across lanes, then
+// the wave's fix), so no barrier separates the max from the sum; one
+// barrier then combines the four waves, rescaling each wave's sum to the
+// chunk max. Called by every thread; both results are valid in every thread
+// (sm_f: 4 floats, sm_s: 4 doubles of LDS).
 template <int DT, int PT>
 __device__ __forceinline__ void chunk_max_sum(const ChunkVecs<DT, true, PT>& cv, float c32, float* sm_f,
                                               double* sm_s, float& m_out, double& s_out) {
@@ -652,9 +654,6 @@ __device__ __forceinline__ void chunk_max_sum(const ChunkVecs<DT, true, PT>& cv,
     for (int e = 0; e < PV; ++e) m = fmaxf(m, v[e]);
   }
   m = wave_max_u(m);
-  if (lane == 0) sm_f[w] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(sm_f[0], sm_f[1]), fmaxf(sm_f[2], sm_f[3]));
   const ScaledPivot sp = scaled_pivot(pivot_of(m), c32);
   float sum = 0.0f;
 #pragma unroll
@@ -664,11 +663,19 @@ __device__ __forceinline__ void chunk_max_sum(const ChunkVecs<DT, true, PT>& cv,
 #pragma unroll
     for (int e = 0; e < PV; ++e) sum += scaled_mass(v[e], c32, sp.P);
   }
-  const double wsum = wave_sum_u(double(sum));
-  if (lane == 0) sm_s[w] = wsum;
+  const double wsum = wave_sum_u(double(sum)) * double(sp.fix);
+  if (lane == 0) {
+    sm_f[w] = m;
+    sm_s[w] = wsum;
+  }
   __syncthreads();
-  m_out = m;
-  s_out = ((sm_s[0] + sm_s[1]) + (sm_s[2] + sm_s[3])) * double(sp.fix);
+  const float M = fmaxf(fmaxf(sm_f[0], sm_f[1]), fmaxf(sm_f[2], sm_f[3]));
+  const float pM = pivot_of(M);
+  double t[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t[i] = sm_s[i] > 0.0 ? sm_s[i] * rescale(pivot_of(sm_f[i]), pM, c32) : 0.0;
+  m_out = M;
+  s_out = (t[0] + t[1]) + (t[2] + t[3]);
 }
 
 // Count this workgroup in; returns true in every thread of the workgroup that
