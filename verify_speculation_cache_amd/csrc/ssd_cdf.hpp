@@ -50,22 +50,22 @@ struct PickLds {
   double base;
   int lastpos;
   int tok;
+  float vals[kPerThread];   // the crossing thread's masses, token order
 };
 
 // Token pick inside chunk [c0, c0 + 8192) whose running mass starts at
 // `pre`: every thread owns 32 consecutive tokens of NROW rows (raw vectors in
 // cv, contiguous layout); value(x, idx) is the mass of token idx from its
-// NROW logits x. Thread totals are scanned in double; wave 0 then re-reads
-// the crossing thread's 32 tokens of every row (from cache: the workgroup
-// has just loaded them) for a parallel rescan, so no thread keeps its
-// vectors live across the scan. If rounding keeps the running mass at or
-// below `target` through a run, the run's last token with mass is taken (the
-// chunk's, if no thread crosses). Called by every thread of the workgroup;
-// returns the token (-1: no mass).
+// NROW logits x. Thread totals are scanned in double; the crossing thread
+// then recomputes its 32 masses from the vectors it still holds and hands
+// them to wave 0 through LDS for a parallel rescan (no second memory round
+// trip; the same values as in the totals, bit for bit). If rounding keeps
+// the running mass at or below `target` through a run, the run's last token
+// with mass is taken (the chunk's, if no thread crosses). Called by every
+// thread of the workgroup; returns the token (-1: no mass).
 template <int DT, int NROW, class ValueFn>
-__device__ __forceinline__ int chunk_pick(const ChunkVecs<DT, false> (&cv)[NROW],
-                                          const typename Dt<DT>::T* const (&rows)[NROW], int64_t V, int64_t c0,
-                                          double pre, double target, ValueFn value, PickLds<DT, NROW>& L) {
+__device__ __forceinline__ int chunk_pick(const ChunkVecs<DT, false> (&cv)[NROW], int64_t c0, double pre,
+                                          double target, ValueFn value, PickLds<DT, NROW>& L) {
   constexpr int PV = Dt<DT>::kPerVec;
   constexpr int NV = kPerThread / PV;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -107,15 +107,25 @@ __device__ __forceinline__ int chunk_pick(const ChunkVecs<DT, false> (&cv)[NROW]
     if (tid == first) {
       L.base = base;
       L.lastpos = lastpos;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        float xv[NROW][PV];
+#pragma unroll
+        for (int r = 0; r < NROW; ++r) cv[r].get(j, xv[r]);
+#pragma unroll
+        for (int e = 0; e < PV; ++e) {
+          float x[NROW];
+#pragma unroll
+          for (int r = 0; r < NROW; ++r) x[r] = xv[r][e];
+          L.vals[j * PV + e] = value(x, i0 + j * PV + e);
+        }
+      }
     }
     __syncthreads();
     if (w == 0) {
       const int q = lane & 31;
       const int f0 = int(c0) + first * kPerThread;
-      float x[NROW];
-#pragma unroll
-      for (int r = 0; r < NROW; ++r) x[r] = f0 + q < V ? Dt<DT>::to_f(rows[r][f0 + q]) : -__builtin_inff();
-      const float v = value(x, f0 + q);
+      const float v = L.vals[q];
       const double cum = L.base + wave_incl_scan_d(lane < 32 ? double(v) : 0.0, lane);
       const uint64_t cr = __ballot(lane < 32 && cum > target);
       if (lane == 0) L.tok = f0 + (cr ? __ffsll((unsigned long long)cr) - 1 : L.lastpos);

@@ -215,9 +215,8 @@ __device__ __forceinline__ int resid_pick(const ResidConsts& k, const typename D
   // each thread owns 32 consecutive tokens of the chunk
   ChunkVecs<DT, false> cv[2];
   load_pair(cv[0], rowT, cv[1], rowD, c0, V, threadIdx.x);
-  const typename Dt<DT>::T* const rows[2] = {rowT, rowD};
   const double inv = 1.0 / double(k.fix_t);
-  return chunk_pick<DT, 2>(cv, rows, V, c0, pre * inv, target * inv,
+  return chunk_pick<DT, 2>(cv, c0, pre * inv, target * inv,
                            [&](const float (&x)[2], int idx) { return resid_elem<SIG>(k, x[0], x[1], idx); }, pk);
 }
 

@@ -174,8 +174,7 @@ __global__ __launch_bounds__(kThreads) void k_sample(SampleArgs a) {
     const float P = sm_piv, c32 = a.c32;
     ChunkVecs<DT, false> cv[1];
     cv[0].load(row, c0, a.V, aligned, tid);
-    const T* const rows[1] = {row};
-    tok = chunk_pick<DT, 1>(cv, rows, a.V, c0, sm_pre, sm_target,
+    tok = chunk_pick<DT, 1>(cv, c0, sm_pre, sm_target,
                             [&](const float (&x)[1], int idx) {
                               const float ex = __builtin_amdgcn_exp2f((x[0] - P) * c32);
                               return SIG ? sg.weight(x[0], idx) * ex : ex;
