@@ -155,7 +155,9 @@ SSD_API size_t ssd_verify_workspace_size(int32_t B, int32_t K, int32_t V, int dt
  *               1 for a bonus, 0 when the residual was empty)
  *   row_lse     float [B, 2K+1] or NULL: log-sum-exp of x over target rows
  *               0..K, then draft rows 0..K-1 (sigma form when sigma given)
- * Launches two kernels on hip_stream. */
+ * Launches two kernels on hip_stream: the row statistics' chunk pass, then
+ * one in which every workgroup of a batch row runs the row's accept scan
+ * before its share of the draw. */
 SSD_API int ssd_verify(const void* target_logits, int64_t target_bstride,
                        const void* draft_logits, int64_t draft_bstride, int dtype,
                        int32_t B, int32_t K, int32_t V, float tau,

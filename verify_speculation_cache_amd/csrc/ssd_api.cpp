@@ -367,9 +367,11 @@ SSD_API int ssd_verify(const void* target_logits, int64_t target_bstride,
   const StatsArgs a = verify_stats_args(target_logits, target_bstride, draft_logits, draft_bstride, B, K, V, tau,
                                         draft_tokens, u_acc, sigma, accepted, out_tokens, probs, row_lse, ws, sw);
   hipStream_t stream = as_stream(hip_stream);
-  if ((st = hip_status(launch_stats(a, dtype, stream), "stats launch")) != SSD_OK) return st;
-  const ResidArgs r = verify_resid_args(a, u_res, resid_mass, ws + sw.total, rw);
-  return hip_status(launch_resid(r, dtype, sig, stream), "residual launch");
+  // two launches: the statistics chunk pass, then per batch row the accept
+  // scan (repeated in each of the row's residual workgroups) and the draw
+  if ((st = hip_status(launch_stats_chunks(a, dtype, stream), "stats launch")) != SSD_OK) return st;
+  const RoundResidArgs rr{verify_resid_args(a, u_res, resid_mass, ws + sw.total, rw), a};
+  return hip_status(launch_round_resid(rr, dtype, sig, stream), "residual launch");
 }
 
 SSD_API int ssd_residual_sample(const void* target_logits, int64_t target_bstride,
@@ -697,7 +699,7 @@ SSD_API int ssd_verify_round(const void* target_logits, int64_t target_bstride,
   hipStream_t stream = as_stream(hip_stream);
   if ((st = hip_status(launch_round_chunks(a, dtype, stream), "round chunk launch")) != SSD_OK) return st;
   if ((st = hip_status(launch_cache_merge(a.c, dtype, stream), "round merge launch")) != SSD_OK) return st;
-  return hip_status(launch_round_resid(rr, dtype, stream), "round residual launch");
+  return hip_status(launch_round_resid(rr, dtype, true, stream), "round residual launch");
 }
 
 }  // extern "C"

@@ -42,7 +42,9 @@ __global__ __launch_bounds__(kThreads) void k_round_chunks(RoundArgs a) {
   else stats_chunk_wg<DT, kPerThread>(a.s, b * a.nsw + (rem - a.ncw));
 }
 
-template <int DT>
+// Also the second launch of ssd_verify (after its statistics chunk pass),
+// with SIG as the caller's sigma switch and no lookup.
+template <int DT, bool SIG>
 __global__ __launch_bounds__(kThreads) void k_round_resid(RoundResidArgs a) {
   __shared__ float e_piv[kMaxRows];
   __shared__ double e_s[kMaxRows];
@@ -50,9 +52,11 @@ __global__ __launch_bounds__(kThreads) void k_round_resid(RoundResidArgs a) {
   const int S2 = (a.r.S + 1) / 2;
   const int b = blockIdx.x / S2;
   const int c2 = blockIdx.x - b * S2;
-  // the row's first workgroup also stores accepted[b] and out_tokens
+  // the row's first workgroup also stores accepted[b], out_tokens, probs and
+  // the optional row log-normalisers
   const RowInfo inf = accept_scan<DT, true>(a.s, b, c2 == 0, e_piv, e_s, &sm_inf);
-  resid_row_wg<DT, true>(a.r, inf, b, c2);
+  if (c2 == 0) write_row_lse(a.s, b, e_piv, e_s);
+  resid_row_wg<DT, SIG>(a.r, inf, b, c2);
 }
 
 hipError_t launch_round_chunks(const RoundArgs& a, int dtype, hipStream_t st) {
@@ -62,10 +66,15 @@ hipError_t launch_round_chunks(const RoundArgs& a, int dtype, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_round_resid(const RoundResidArgs& a, int dtype, hipStream_t st) {
+hipError_t launch_round_resid(const RoundResidArgs& a, int dtype, bool sigma, hipStream_t st) {
   const unsigned grid = unsigned(int64_t(a.r.B) * ((a.r.S + 1) / 2));
-  if (dtype == SSD_BF16) hipLaunchKernelGGL(k_round_resid<1>, dim3(grid), dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL(k_round_resid<0>, dim3(grid), dim3(kThreads), 0, st, a);
+  if (dtype == SSD_BF16) {
+    if (sigma) hipLaunchKernelGGL((k_round_resid<1, true>), dim3(grid), dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((k_round_resid<1, false>), dim3(grid), dim3(kThreads), 0, st, a);
+  } else {
+    if (sigma) hipLaunchKernelGGL((k_round_resid<0, true>), dim3(grid), dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((k_round_resid<0, false>), dim3(grid), dim3(kThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 

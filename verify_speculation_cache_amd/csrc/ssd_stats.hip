@@ -1,4 +1,4 @@
-// Row statistics and the accept scan: the kernel and its launcher; the
+// Row statistics and the accept scan: the kernels and their launchers; the
 // device code is in ssd_stats.hpp.
 #include "ssd_stats.hpp"
 
@@ -11,6 +11,22 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsArgs a) {
   const int b = blockIdx.x / (a.NR * a.S);
   if (!arrive_last(&a.cnt[int64_t(b) * kCntStride], uint32_t(a.NR * a.S), &sm_last)) return;
   stats_epilogue<DT>(a, b);
+}
+
+// The chunk pass alone: partials and gathered logits for a consumer in a
+// later launch that merges them itself (the verify path's residual kernel).
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_stats_chunks(StatsArgs a) {
+  stats_chunk_wg<DT>(a, blockIdx.x);
+}
+
+hipError_t launch_stats_chunks(const StatsArgs& a, int dtype, hipStream_t st) {
+  const int64_t grid = int64_t(a.B) * a.NR * a.S;
+  if (dtype == SSD_BF16)
+    hipLaunchKernelGGL(k_stats_chunks<1>, dim3(unsigned(grid)), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_stats_chunks<0>, dim3(unsigned(grid)), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_stats(const StatsArgs& a, int dtype, hipStream_t st) {

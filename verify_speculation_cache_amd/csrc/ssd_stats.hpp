@@ -243,6 +243,29 @@ __device__ __forceinline__ RowInfo accept_scan(const StatsArgs& a, int b, bool w
   return inf;
 }
 
+// Optional log-normalisers of batch row b's 2K+1 rows (verify mode), from
+// the merged partials in e_piv / e_s (target rows 0..K, and draft rows
+// without sigma) or the sigma statistics (draft rows with sigma):
+// lse = pivot / tau + ln(sum). Called by every thread after accept_scan.
+__device__ __forceinline__ void write_row_lse(const StatsArgs& a, int b, const float* e_piv, const double* e_s) {
+  if (a.row_lse == nullptr) return;
+  const int K = a.K;
+  for (int rr = threadIdx.x; rr < 2 * K + 1; rr += kThreads) {
+    double l;
+    if (rr <= K || !a.use_sigma) {
+      const double s = e_s[rr];
+      l = s > 0.0 ? double(e_piv[rr]) * a.inv_tau + log(s) : -__builtin_inf();
+    } else {
+      double z0, st1, st2;
+      ssd_rowkey tk;
+      load_sigma(a, b, rr - K - 1, z0, st1, st2, tk);
+      const double s = double(a.C) * st1 + st2;
+      l = s > 0.0 ? double(pivot_of(float(z0))) * a.inv_tau + log(s) : -__builtin_inf();
+    }
+    a.row_lse[int64_t(b) * (2 * K + 1) + rr] = float(l);
+  }
+}
+
 // Epilogue of batch row b (run by the last workgroup to finish its chunks):
 // the accept scan (verify) or the record of the row to sample from (rows
 // mode); leaves a RowInfo for the residual kernel.
@@ -292,22 +315,7 @@ __device__ __forceinline__ void stats_epilogue(const StatsArgs& a, int b) {
 
   const RowInfo inf = accept_scan<DT, false>(a, b, true, e_piv, e_s, nullptr);
   if (tid == 0) a.info[b] = inf;
-  if (a.row_lse != nullptr) {
-    for (int rr = tid; rr < 2 * K + 1; rr += kThreads) {
-      double l;
-      if (rr <= K || !a.use_sigma) {
-        const double s = e_s[rr];
-        l = s > 0.0 ? double(e_piv[rr]) * a.inv_tau + log(s) : -__builtin_inf();
-      } else {
-        double z0, st1, st2;
-        ssd_rowkey tk;
-        load_sigma(a, b, rr - K - 1, z0, st1, st2, tk);
-        const double s = double(a.C) * st1 + st2;
-        l = s > 0.0 ? double(pivot_of(float(z0))) * a.inv_tau + log(s) : -__builtin_inf();
-      }
-      a.row_lse[int64_t(b) * (2 * K + 1) + rr] = float(l);
-    }
-  }
+  write_row_lse(a, b, e_piv, e_s);
 }
 
 }  // namespace ssd
