@@ -524,7 +524,7 @@ def bench_rows(args):
                "sample": f"first {n} of {B} batch rows of the same call, float64 NumPy, {dt:.1f} s"
                          + ("" if greedy else " (the oracle takes each row's top-F for sigma itself)")}
     name = "ssd_verify_greedy" if greedy else "ssd_draft_sample"
-    kern = "k_greedy<1>" if greedy else "k_sample<1, true>"
+    kern = "k_greedy<1>, one launch" if greedy else "k_sample_chunks<1, true> + k_sample_pick<1, true>"
     line = {
         "metric": ("greedy-verified rows/sec" if greedy else "sigma-drafted rows/sec") + ", B=64 K=5 V=128256 bf16",
         "value": round(B / (ms_step / 1e3), 1),
@@ -542,7 +542,7 @@ def bench_rows(args):
                    "rotating_copies": ncopy, "graph_replay": not args.eager},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbps / PEAK_HBM_GBS, 4), "traffic": None,
-                     "kernel": f"{name} ({kern}, one launch)", "bytes_per_launch": bytes_call,
+                     "kernel": f"{name} ({kern})", "bytes_per_launch": bytes_call,
                      "avg_launch_ms": round(ms_step, 5)},
         "cpu_baseline": cpu,
         "gen_s": round(gen_s, 2),

@@ -221,7 +221,8 @@ SSD_API size_t ssd_draft_sample_workspace_size(int32_t B, int32_t K, int32_t V, 
  *                not read)
  *   u            device float [B, K] in [0, 1)
  *   tokens_out   device int32 [B, K]
- * One kernel launch on hip_stream. */
+ * Two kernel launches on hip_stream (chunk masses, then the per-row draw);
+ * the workspace holds only chunk partials, written before they are read. */
 SSD_API int ssd_draft_sample(const void* draft_logits, int64_t draft_bstride, int dtype,
                              int32_t B, int32_t K, int32_t V, float tau, const ssd_sigma* sigma,
                              const float* u, int32_t* tokens_out,

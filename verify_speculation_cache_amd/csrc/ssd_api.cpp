@@ -516,7 +516,6 @@ SSD_API int ssd_draft_sample(const void* draft_logits, int64_t draft_bstride, in
   a.u = u;
   a.tok_out = tokens_out;
   a.part = reinterpret_cast<RowPartial*>(ws + sw.part);
-  a.cnt = reinterpret_cast<uint32_t*>(ws + sw.cnt);
   return hip_status(launch_sample(a, dtype, as_stream(hip_stream)), "sample launch");
 }
 

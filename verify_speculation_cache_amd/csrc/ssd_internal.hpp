@@ -142,7 +142,6 @@ struct SampleArgs {
   const float* u;           // [B, K]
   int32_t* tok_out;         // [B, K]
   RowPartial* part;         // [B*K, S]
-  uint32_t* cnt;            // [B*K] (kCntStride apart)
 };
 
 struct LookupArgs {
@@ -222,11 +221,10 @@ struct GreedyWs {
 };
 
 struct SampleWs {
-  size_t part, cnt, total;
+  size_t part, total;
   SampleWs(int64_t rows, int64_t S) {
     part = 0;
-    cnt = align256(part + sizeof(RowPartial) * rows * S);
-    total = align256(cnt + sizeof(uint32_t) * kCntStride * rows);
+    total = align256(part + sizeof(RowPartial) * rows * S);
   }
 };
 

@@ -10,12 +10,14 @@
 // plain softmax of draft row k at temperature tau.
 //
 // The draw is by inverse CDF in token-index order: the smallest v whose
-// running mass exceeds u * Z. One workgroup per (batch row b, position i,
-// pair of 8192-chunks) sums each chunk's weighted mass against the chunk's
-// own max;
-// the last workgroup of row (b, i) rescales the chunk masses to the row max,
-// finds the crossing chunk and picks the token inside it. A row without mass
-// (all logits -inf) draws -1.
+// running mass exceeds u * Z. Two launches: k_sample_chunks, one workgroup
+// per (batch row b, position i, pair of 8192-chunks), sums each chunk's
+// weighted mass against the chunk's own max; k_sample_pick, one workgroup
+// per (b, i), rescales the chunk masses to the row max, finds the crossing
+// chunk and picks the token inside it. A row without mass (all logits -inf)
+// draws -1. The second launch replaces an arrival count in the first (the
+// last workgroup of a row drawing): that count and the draw's latency kept
+// workgroup slots of the streaming pass busy.
 #include "ssd_cdf.hpp"
 
 namespace ssd {
@@ -46,17 +48,12 @@ __device__ __forceinline__ SigmaTest sigma_test(const SampleArgs& a, int b, int 
 }
 
 template <int DT, bool SIG>
-__global__ __launch_bounds__(kThreads) void k_sample(SampleArgs a) {
+__global__ __launch_bounds__(kThreads) void k_sample_chunks(SampleArgs a) {
   using T = typename Dt<DT>::T;
   constexpr int PV = Dt<DT>::kPerVec;
   constexpr int NV2 = kStatsPerThread / PV;
   __shared__ float sm_f[8];
   __shared__ double sm_s[8];
-  __shared__ int sm_last;
-  __shared__ int sm_c;
-  __shared__ double sm_pre, sm_target;
-  __shared__ float sm_piv;
-  __shared__ PickLds<DT, 1> sm_pk;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int S2 = (a.S + 1) / 2;   // workgroups per row, two 8192-chunks each
@@ -68,8 +65,7 @@ __global__ __launch_bounds__(kThreads) void k_sample(SampleArgs a) {
   const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
   const SigmaTest sg = sigma_test<DT, SIG>(a, b, i);
 
-  // ---------------- phase A: max and weighted mass of two 8192-chunks ----------------
-  // A workgroup reads 16384 entries (64 per thread, strided: vectors j <
+  // max and weighted mass of two 8192-chunks: a workgroup reads 16384 entries (64 per thread, strided: vectors j <
   // NV/2 lie in the first 8192, the others in the second) and writes one
   // partial per 8192-chunk, so the draw below keeps 8192-entry chunks.
   {
@@ -125,9 +121,24 @@ __global__ __launch_bounds__(kThreads) void k_sample(SampleArgs a) {
       }
     }
   }
-  if (!arrive_last(&a.cnt[rowid * kCntStride], uint32_t(S2), &sm_last)) return;
+}
 
-  // ---------------- phase B: last workgroup of row (b, i) ----------------
+// The draw of row (b, i) = blockIdx.x from its chunk partials.
+template <int DT, bool SIG>
+__global__ __launch_bounds__(kThreads) void k_sample_pick(SampleArgs a) {
+  using T = typename Dt<DT>::T;
+  __shared__ int sm_c;
+  __shared__ double sm_pre, sm_target;
+  __shared__ float sm_piv;
+  __shared__ PickLds<DT, 1> sm_pk;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t rowid = blockIdx.x;
+  const int b = int(rowid / a.K);
+  const int i = int(rowid - int64_t(b) * a.K);
+  const T* row = static_cast<const T*>(a.draft) + int64_t(b) * a.db + int64_t(i) * a.V;
+  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+  const SigmaTest sg = sigma_test<DT, SIG>(a, b, i);
   if (w == 0) {
     const uint64_t* pw = reinterpret_cast<const uint64_t*>(a.part + rowid * a.S);
     // chunk partials (the first 64 stay in registers: one round trip for S <= 64)
@@ -184,17 +195,20 @@ __global__ __launch_bounds__(kThreads) void k_sample(SampleArgs a) {
   if (tid == 0) a.tok_out[rowid] = tok;
 }
 
-hipError_t launch_sample(const SampleArgs& a, int dtype, hipStream_t st) {
-  const unsigned grid = unsigned(int64_t(a.B) * a.K * ((a.S + 1) / 2));
-  const bool sig = a.thr != nullptr;
-  if (dtype == SSD_BF16) {
-    if (sig) hipLaunchKernelGGL((k_sample<1, true>), dim3(grid), dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((k_sample<1, false>), dim3(grid), dim3(kThreads), 0, st, a);
-  } else {
-    if (sig) hipLaunchKernelGGL((k_sample<0, true>), dim3(grid), dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((k_sample<0, false>), dim3(grid), dim3(kThreads), 0, st, a);
-  }
+template <int DT, bool SIG>
+static hipError_t launch_sample_t(const SampleArgs& a, hipStream_t st) {
+  const int64_t rows = int64_t(a.B) * a.K;
+  hipLaunchKernelGGL((k_sample_chunks<DT, SIG>), dim3(unsigned(rows * ((a.S + 1) / 2))), dim3(kThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_sample_pick<DT, SIG>), dim3(unsigned(rows)), dim3(kThreads), 0, st, a);
   return hipGetLastError();
+}
+
+hipError_t launch_sample(const SampleArgs& a, int dtype, hipStream_t st) {
+  const bool sig = a.thr != nullptr;
+  if (dtype == SSD_BF16) return sig ? launch_sample_t<1, true>(a, st) : launch_sample_t<1, false>(a, st);
+  return sig ? launch_sample_t<0, true>(a, st) : launch_sample_t<0, false>(a, st);
 }
 
 }  // namespace ssd
