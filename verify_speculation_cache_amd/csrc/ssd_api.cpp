@@ -633,12 +633,13 @@ SSD_API int ssd_verify_tree(const void* target_logits, int64_t target_bstride,
   a.pq = reinterpret_cast<double*>(ws + tw.pq);
   a.state = reinterpret_cast<TreeState*>(ws + tw.state);
   a.cmass = reinterpret_cast<double*>(ws + tw.cmass);
-  a.cnt_stats = reinterpret_cast<uint32_t*>(ws + tw.cnt_stats);
   a.cnt_round = reinterpret_cast<uint32_t*>(ws + tw.cnt_round);
   hipStream_t stream = as_stream(hip_stream);
   if ((st = hip_status(launch_tree_stats(a, dtype, stream), "tree stats launch")) != SSD_OK) return st;
+  // the first round also starts every row's walk (rounds >= 1: the walk
+  // always ends in a draw)
   for (int r = 0; r < t.rounds; ++r)
-    if ((st = hip_status(launch_tree_round(a, dtype, stream), "tree round launch")) != SSD_OK) return st;
+    if ((st = hip_status(launch_tree_round(a, dtype, r == 0, stream), "tree round launch")) != SSD_OK) return st;
   return ok();
 }
 

@@ -267,20 +267,18 @@ struct TreeArgs {
   double* pq;               // [B, N, 2]: p and q of node n's token under its parent's rows
   TreeState* state;         // [B]
   double* cmass;            // [B, S, 2]
-  uint32_t* cnt_stats;      // [B] (kCntStride apart)
   uint32_t* cnt_round;      // [B] (kCntStride apart)
 };
 
 struct TreeWs {
-  size_t part, rstat, pq, state, cmass, cnt_stats, cnt_round, total;
+  size_t part, rstat, pq, state, cmass, cnt_round, total;
   TreeWs(int64_t B, int64_t N, int64_t NR, int64_t SS, int64_t S) {
     part = 0;
     rstat = align256(part + sizeof(RowPartial) * B * NR * SS);
     pq = align256(rstat + sizeof(RowPartial) * B * NR);
     state = align256(pq + sizeof(double) * 2 * B * N);
     cmass = align256(state + sizeof(TreeState) * B);
-    cnt_stats = align256(cmass + sizeof(double) * 2 * B * S);
-    cnt_round = align256(cnt_stats + sizeof(uint32_t) * kCntStride * B);
+    cnt_round = align256(cmass + sizeof(double) * 2 * B * S);
     total = align256(cnt_round + sizeof(uint32_t) * kCntStride * B);
   }
 };
@@ -309,7 +307,7 @@ hipError_t launch_sample(const SampleArgs& a, int dtype, hipStream_t st);
 hipError_t launch_greedy(const GreedyArgs& a, int dtype, hipStream_t st);
 hipError_t launch_cache_stats(const CacheStatsArgs& a, hipStream_t st);
 hipError_t launch_tree_stats(const TreeArgs& a, int dtype, hipStream_t st);
-hipError_t launch_tree_round(const TreeArgs& a, int dtype, hipStream_t st);
+hipError_t launch_tree_round(const TreeArgs& a, int dtype, bool first, hipStream_t st);
 hipError_t launch_round_chunks(const RoundArgs& a, int dtype, hipStream_t st);
 hipError_t launch_cache_merge(const CacheArgs& a, int dtype, hipStream_t st);
 hipError_t launch_round_resid(const RoundResidArgs& a, int dtype, bool sigma, hipStream_t st);

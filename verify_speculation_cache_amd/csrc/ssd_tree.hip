@@ -21,16 +21,20 @@
 // Kernels:
 //  k_tree_stats  one workgroup per (batch row, statistics row, 16384-entry
 //                chunk): chunk max and sum of every target row and every
-//                draft row of an inner node. The last workgroup of a batch
-//                row merges them, gathers p and q at every node's token and
-//                walks until the walk needs a pass.
+//                draft row of an inner node.
 //  k_tree_round  one workgroup per (batch row, 8192-entry chunk): the
 //                residual mass max(0, e_t - c rho e_d) and the target mass of
 //                the pending node over the chunk; the last workgroup of the
 //                batch row either takes N(c) and walks on, or (no child left)
 //                picks the token and writes the row's outputs. Rows without a
 //                pending pass exit at once. The host launches as many rounds
-//                as the topology can need.
+//                as the topology can need. In the first round every
+//                workgroup of a batch row starts by merging the row's
+//                statistics partials, gathering p and q at every node's token
+//                and walking until the walk needs a pass (the row's first
+//                workgroup stores what later rounds read); repeating that in
+//                each workgroup costs less than an arrival count and a
+//                last-workgroup tail in the statistics pass.
 #include "ssd_resid.hpp"
 
 namespace ssd {
@@ -70,38 +74,39 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) void k_tree_stats(TreeArgs a) {
   __shared__ float sm_f[4];
   __shared__ double sm_s[4];
-  __shared__ int sm_last;
-  __shared__ float e_piv[kMaxRows];
-  __shared__ double e_s[kMaxRows];
-  __shared__ double sP[kMaxTree], sQ[kMaxTree];
-  __shared__ float sU[kMaxTree];
-  __shared__ int sm_bad;
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int per_b = a.NR * a.SS;
   const int b = blockIdx.x / per_b;
   const int rem = blockIdx.x - b * per_b;
   const int r = rem / a.SS;
   const int c = rem - r * a.SS;
 
-  {
-    const typename Dt<DT>::T* row = tree_row<DT>(a, b, r);
-    ChunkVecs<DT, true, kStatsPerThread> cv;
-    const int64_t c0 = int64_t(c) * kStatsChunk;
-    cv.load(row, c0, a.V, (reinterpret_cast<uintptr_t>(row) & 15u) == 0, tid);
-    float m;
-    double sd;
-    chunk_max_sum(cv, a.c32, sm_f, sm_s, m, sd);
-    if (tid == 0) {
-      uint64_t* wp = reinterpret_cast<uint64_t*>(a.part + (int64_t(b) * a.NR + r) * a.SS + c);
-      dev_store(wp, pack2(m, 0.0f));
-      dev_store(wp + 1, dbits(sd));
-    }
+  const typename Dt<DT>::T* row = tree_row<DT>(a, b, r);
+  ChunkVecs<DT, true, kStatsPerThread> cv;
+  const int64_t c0 = int64_t(c) * kStatsChunk;
+  cv.load(row, c0, a.V, (reinterpret_cast<uintptr_t>(row) & 15u) == 0, tid);
+  float m;
+  double sd;
+  chunk_max_sum(cv, a.c32, sm_f, sm_s, m, sd);
+  if (tid == 0) {
+    uint64_t* wp = reinterpret_cast<uint64_t*>(a.part + (int64_t(b) * a.NR + r) * a.SS + c);
+    dev_store(wp, pack2(m, 0.0f));
+    dev_store(wp + 1, dbits(sd));
   }
+}
 
-  if (!arrive_last(&a.cnt_stats[int64_t(b) * kCntStride], uint32_t(per_b), &sm_last)) return;
-
-  // ---------------- epilogue: last workgroup of batch row b ----------------
+// Start of batch row b's walk (every thread of a first-round workgroup):
+// merges the row's statistics partials into e_piv / e_s, puts p and q of
+// every node's token under its parent's rows and the node uniforms into
+// sP / sQ / sU, and walks from the root until a pass is needed; the state
+// comes back in *sm_st. With `writer` (one workgroup per row) it also stores
+// the merged statistics and p, q for later rounds, and the outputs of a
+// flagged row (a token outside [0, V)). Returns false for a flagged row.
+template <int DT>
+__device__ __forceinline__ bool tree_start(const TreeArgs& a, int b, bool writer, float* e_piv, double* e_s,
+                                           double* sP, double* sQ, float* sU, TreeState* sm_st, int* sm_bad) {
+  const int tid = threadIdx.x;
   const int N = a.N;
   int32_t x = 0;
   float u = 0.0f;
@@ -115,11 +120,13 @@ __global__ __launch_bounds__(kThreads) void k_tree_stats(TreeArgs a) {
     else merge_rows<2>(pb, a.NR, a.SS, a.c32, e_piv, e_s, nullptr);
   }
   __syncthreads();
-  for (int rr = tid; rr < a.NR; rr += kThreads) {
-    RowPartial rp{};
-    rp.m = e_piv[rr];
-    rp.s = e_s[rr];
-    a.rstat[int64_t(b) * a.NR + rr] = rp;
+  if (writer) {
+    for (int rr = tid; rr < a.NR; rr += kThreads) {
+      RowPartial rp{};
+      rp.m = e_piv[rr];
+      rp.s = e_s[rr];
+      a.rstat[int64_t(b) * a.NR + rr] = rp;
+    }
   }
   if (tid < 64) {
     // p and q of node n's token under its parent's rows (lane n, n >= 1)
@@ -134,27 +141,31 @@ __global__ __launch_bounds__(kThreads) void k_tree_stats(TreeArgs a) {
       const double st = e_s[pn], sd = e_s[dr];
       P = st > 0.0 ? exp2(double(zt - e_piv[pn]) * double(a.c32)) / st : 0.0;
       Q = sd > 0.0 ? exp2(double(zd - e_piv[dr]) * double(a.c32)) / sd : 0.0;
-      a.pq[(int64_t(b) * N + n) * 2 + 0] = P;
-      a.pq[(int64_t(b) * N + n) * 2 + 1] = Q;
+      if (writer) {
+        a.pq[(int64_t(b) * N + n) * 2 + 0] = P;
+        a.pq[(int64_t(b) * N + n) * 2 + 1] = Q;
+      }
     }
     sP[n] = P;
     sQ[n] = Q;
     sU[n] = u;
     const uint64_t badm = __ballot(bad);
-    if (n == 0) sm_bad = badm != 0 ? 1 : 0;
+    if (n == 0) *sm_bad = badm != 0 ? 1 : 0;
   }
   __syncthreads();
-  if (sm_bad) {   // a token outside [0, V): the row is flagged
-    for (int i = tid; i < N; i += kThreads) {
-      a.out_tokens[int64_t(b) * N + i] = -1;
-      if (a.out_nodes) a.out_nodes[int64_t(b) * N + i] = -1;
+  if (*sm_bad) {   // a token outside [0, V): the row is flagged
+    if (writer) {
+      for (int i = tid; i < N; i += kThreads) {
+        a.out_tokens[int64_t(b) * N + i] = -1;
+        if (a.out_nodes) a.out_nodes[int64_t(b) * N + i] = -1;
+      }
+      if (tid == 0) {
+        a.accepted[b] = -1;
+        TreeState st{};
+        a.state[b] = st;   // status 0: no pass
+      }
     }
-    if (tid == 0) {
-      a.accepted[b] = -1;
-      TreeState st{};
-      a.state[b] = st;   // status 0: no pass
-    }
-    return;
+    return false;
   }
   if (tid == 0) {
     TreeState st{};
@@ -164,11 +175,13 @@ __global__ __launch_bounds__(kThreads) void k_tree_stats(TreeArgs a) {
     st.c = 0.0;
     st.nc = 1.0;
     tree_walk(a, st, sP, sQ, sU);
-    a.state[b] = st;
+    *sm_st = st;
   }
+  __syncthreads();
+  return true;
 }
 
-template <int DT>
+template <int DT, bool FIRST>
 __global__ __launch_bounds__(kThreads) void k_tree_round(TreeArgs a) {
   using T = typename Dt<DT>::T;
   __shared__ double sm_pair[8];
@@ -179,17 +192,37 @@ __global__ __launch_bounds__(kThreads) void k_tree_round(TreeArgs a) {
   __shared__ double sP[kMaxTree], sQ[kMaxTree];
   __shared__ float sU[kMaxTree];
   __shared__ int path[kMaxTree];
+  __shared__ float e_piv[FIRST ? kMaxRows : 1];
+  __shared__ double e_s[FIRST ? kMaxRows : 1];
+  __shared__ TreeState sm_st;
+  __shared__ int sm_bad;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = blockIdx.x / a.S;
   const int c = blockIdx.x - b * a.S;
-  TreeState st = a.state[b];
+  TreeState st;
+  if (FIRST) {
+    if (!tree_start<DT>(a, b, c == 0, e_piv, e_s, sP, sQ, sU, &sm_st, &sm_bad)) return;
+    st = sm_st;
+  } else {
+    st = a.state[b];
+  }
   // Only a state the walk could have written is trusted; anything else (a
   // workspace not zero-filled for this shape) ends the row's rounds.
   if (st.status != 1 || st.node < 0 || st.node >= a.N || st.nxt >= a.N || st.depth < 0 || st.depth >= a.N)
     return;
   const int node = st.node;
-  const RowPartial rt = a.rstat[int64_t(b) * a.NR + node];
+  // merged statistics of a row: in LDS in the first round, else as stored
+  auto rstat = [&](int r) {
+    if (FIRST) {
+      RowPartial rp{};
+      rp.m = e_piv[r];
+      rp.s = e_s[r];
+      return rp;
+    }
+    return a.rstat[int64_t(b) * a.NR + r];
+  };
+  const RowPartial rt = rstat(node);
   const T* rowT = tree_row<DT>(a, b, node);
   const T* rowD = rowT;
   ResidConsts k{};
@@ -197,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_round(TreeArgs a) {
   set_plain(k);
   const int dr = a.drow[node];
   if (st.c > 0.0 && dr >= 0) {
-    const RowPartial rd = a.rstat[int64_t(b) * a.NR + dr];
+    const RowPartial rd = rstat(dr);
     rowD = tree_row<DT>(a, b, dr);
     set_rows(k, rt.m, rd.m, a.c32);
     set_rho(k, rd.s > 0.0 ? st.c * rt.s / rd.s : 0.0, 1.0);
@@ -223,9 +256,10 @@ __global__ __launch_bounds__(kThreads) void k_tree_round(TreeArgs a) {
     __shared__ double sm_z;
     if (w == 0) {
       const int n = lane;
+      // p, q and u of every node (already in LDS in the first round)
       double P = 0.0, Q = 0.0;
       float u = 0.0f;
-      if (n >= 1 && n < N) {
+      if (!FIRST && n >= 1 && n < N) {
         P = a.pq[(int64_t(b) * N + n) * 2 + 0];
         Q = a.pq[(int64_t(b) * N + n) * 2 + 1];
         u = a.u_acc[int64_t(b) * N + n];
@@ -236,9 +270,11 @@ __global__ __launch_bounds__(kThreads) void k_tree_round(TreeArgs a) {
         const double r = cc < a.S ? bits_d(dev_load(cmw + cc * 2)) : 0.0;
         zres += lane_d(wave_incl_scan_d(r, lane), 63);
       }
-      sP[n] = P;
-      sQ[n] = Q;
-      sU[n] = u;
+      if (!FIRST) {
+        sP[n] = P;
+        sQ[n] = Q;
+        sU[n] = u;
+      }
       if (lane == 0) sm_z = zres;
     }
     __syncthreads();
@@ -304,10 +340,15 @@ hipError_t launch_tree_stats(const TreeArgs& a, int dtype, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_tree_round(const TreeArgs& a, int dtype, hipStream_t st) {
+hipError_t launch_tree_round(const TreeArgs& a, int dtype, bool first, hipStream_t st) {
   const unsigned grid = unsigned(int64_t(a.B) * a.S);
-  if (dtype == SSD_BF16) hipLaunchKernelGGL(k_tree_round<1>, dim3(grid), dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL(k_tree_round<0>, dim3(grid), dim3(kThreads), 0, st, a);
+  if (dtype == SSD_BF16) {
+    if (first) hipLaunchKernelGGL((k_tree_round<1, true>), dim3(grid), dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((k_tree_round<1, false>), dim3(grid), dim3(kThreads), 0, st, a);
+  } else {
+    if (first) hipLaunchKernelGGL((k_tree_round<0, true>), dim3(grid), dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((k_tree_round<0, false>), dim3(grid), dim3(kThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 
