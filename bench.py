@@ -8,8 +8,12 @@ launches); both give bit-identical outputs, which the bench checks.
 Default workload: B=64 sequences, K=5 drafted tokens, V=128256, bf16 logits,
 tau=0.7, cache budget 64 split with a_p=0.8, r=1, C=0.5.
 
-Inputs are resident in HBM before timing; NCOPY rotating copies (more than
-the 256 MB Infinity Cache holds) make each step read its logits from HBM.
+Inputs are resident in HBM before timing; ceil(512 MB / bytes) + 1
+rotating copies (more than the 256 MB Infinity Cache holds) make each step
+read its logits from HBM. The drafted tokens of the step are drawn on the GPU
+from q_sigma (ssd_draft_sample) before timing, as the SAGUARO draft phase
+does, so the acceptance and hit rates are those of the process the cache is
+built for.
 Each copy's step is captured once in a HIP graph and replayed. Timing uses
 HIP events on the stream the library launches on.
 
@@ -28,7 +32,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E peak, GB/s
-MALL_BYTES = 256 << 20
+ROTATE_BYTES = 512 << 20   # twice the 256 MB Infinity Cache
+
+
+def n_copies(nbytes):
+    """Rotating input copies so that consecutive steps never find their
+    logits in the 256 MB Infinity Cache: ceil(512 MB / bytes) + 1."""
+    return int(math.ceil(ROTATE_BYTES / nbytes)) + 1
 
 
 def parse():
@@ -104,14 +114,20 @@ def main():
 
     tgt0, dft0 = up(d["target"]), up(d["draft"][:, :K + 1])
     step_bytes = tgt0.numel() * tgt0.element_size() + dft0.numel() * dft0.element_size()
-    ncopy = int(math.ceil(MALL_BYTES / step_bytes)) + 1
+    ncopy = n_copies(step_bytes)
     tgts = [tgt0] + [tgt0.clone() for _ in range(ncopy - 1)]
     dfts = [dft0] + [dft0.clone() for _ in range(ncopy - 1)]
-    toks = torch.from_numpy(d["tokens"]).to(dev)
     ua = torch.from_numpy(d["u_acc"]).to(dev)
     ur = torch.from_numpy(d["u_res"]).to(dev)
     F = S.ssd_fanout(cfg.n_budget, K, cfg.a_p, cfg.r)
     C = cfg.C
+    # the draft phase: d_{i+1} ~ sigma_{F_i,C}(draft row i / tau), on the GPU
+    u_draft_np = W.make_draft_uniforms(cfg, tau)
+    cache_d = S.ssd_build_cache(dfts[0], tau, F)
+    toks = S.ssd_draft_sample(dfts[0], torch.from_numpy(u_draft_np).to(dev), tau, S.sigma_from_cache(cache_d, C))
+    toks_plain = torch.from_numpy(d["tokens"]).to(dev)   # softmax drafts for plain verification
+    torch.cuda.synchronize()
+    toks_np = toks.cpu().numpy()
 
     outs = []
     for j in range(ncopy):
@@ -209,13 +225,13 @@ def main():
         S.ssd_verify(tgts[j], dfts[j], toks, ua, ur, tau, S.sigma_from_cache(outs[j][0], C), out=outs[j][1])
 
     def call_plain(j):
-        S.ssd_verify(tgts[j], dfts[j], toks, ua, ur, tau, out=plain_out[j])
+        S.ssd_verify(tgts[j], dfts[j], toks_plain, ua, ur, tau, out=plain_out[j])
 
     def call_lookup(j):
         cache, res, look = outs[j]
         S.ssd_cache_lookup(cache["cache_tokens"], F, res["accepted"], res["out_tokens"], out=look)
 
-    plain_out = [S.ssd_verify(tgts[j], dfts[j], toks, ua, ur, tau) for j in range(ncopy)]
+    plain_out = [S.ssd_verify(tgts[j], dfts[j], toks_plain, ua, ur, tau) for j in range(ncopy)]
     torch.cuda.synchronize()
     for _ in range(2):
         time_call(call_build, 10), time_call(call_verify, 10), time_call(call_plain, 10)
@@ -261,9 +277,15 @@ def main():
                     "kernel": "ssd_verify_round (k_round_chunks + k_cache_merge + k_round_resid, bf16)",
                     "bytes_per_launch": step_bytes, "avg_launch_ms": round(ms_step, 5)}
 
-    cpu = None
+    cpu, check = None, None
     if not args.no_cpu:
-        cpu = cpu_baseline(cfg, d, F, C, tau, args.cpu_seconds)
+        src = outs[0] if args.separate else None
+        gpu = {"accepted": (src[1] if src else rounds[0])["accepted"].cpu().numpy(),
+               "out_tokens": (src[1] if src else rounds[0])["out_tokens"].cpu().numpy(),
+               "hit": (src[2] if src else rounds[0])["hit"].cpu().numpy(),
+               "cache_tokens": (src[0] if src else rounds[0])["cache_tokens"].cpu().numpy(),
+               "tokens": toks_np}
+        cpu, check = cpu_baseline(args.config, tau, F, C, gpu, u_draft_np, args.cpu_seconds)
 
     line = {
         "metric": "verified rows/sec + logits HBM GB/s (% of peak), B=64 K=5 V=128256 bf16",
@@ -277,7 +299,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.dtype,
-        "data": "synthetic (seeded Gaussian + Zipf-rank logits, draft = target + noise)",
+        "data": "synthetic (seeded Gaussian + Zipf-rank logits, draft = target + noise, drafts drawn on the GPU "
+                "from q_sigma)",
         "config": {"workload": ("ssd_step_fanout_buildcache_verify_sigma_lookup" if args.separate
                                 else "ssd_step_fanout_verify_round"), "B": B, "K": K, "V": V,
                    "logits": cfg.dtype, "tau": tau, "cache": {"budget": cfg.n_budget, "a_p": cfg.a_p,
@@ -295,12 +318,16 @@ def main():
                         "pct_peak_hbm": round(100 * bytes_plain / (t_plain / 1e3) / 1e9 / PEAK_HBM_GBS, 2)},
         "verify_sigma_gbps": round(bytes_verify_sigma / (t_verify / 1e3) / 1e9, 1),
         "round_vs_separate_rows_differ": round_rows_differ,
+        "oracle_check": check,
         "mean_accepted_plus_1": round(float(np.mean(acc + 1)), 4),
         "hit_rate": round(float(np.mean(hit)), 4),
         "cpu_baseline": cpu,
         "gen_s": round(gen_s, 2),
     }
     print(json.dumps(line), flush=True)
+    if check is not None and check["rows_differ"] > 0:
+        print(f"oracle parity FAILED on rows {check['differ_rows']}", file=sys.stderr)
+        sys.exit(1)
 
 
 def bench_report(args):
@@ -342,7 +369,7 @@ def bench_report(args):
         tgt0 = up(d["target"])
         dft0 = up(d["draft"][:, :n_draft])
         bytes_call = B * (K + 1 + n_draft) * V * elem
-        ncopy = int(math.ceil((512 << 20) / bytes_call)) + 1
+        ncopy = n_copies(bytes_call)
         tgts = [tgt0] + [tgt0.clone() for _ in range(ncopy - 1)]
         dfts = [dft0] + [dft0.clone() for _ in range(ncopy - 1)]
         ua = torch.from_numpy(d["u_acc"]).to(dev)
@@ -351,8 +378,7 @@ def bench_report(args):
         if cache_mode:
             F = S.ssd_fanout(cfg.n_budget, K, cfg.a_p, cfg.r)
             cache0 = S.ssd_build_cache(dfts[0], tau32, F)   # sigma for the drafts
-            gdraw = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.seed, 424242])))
-            u_draft = torch.from_numpy(gdraw.random((B, K), dtype=np.float32)).to(dev)
+            u_draft = torch.from_numpy(W.make_draft_uniforms(cfg, tau)).to(dev)
             toks = S.ssd_draft_sample(dfts[0], u_draft, tau32, S.sigma_from_cache(cache0, cfg.C))
             outs = [S.ssd_verify_round(tgts[j], dfts[j], F, cfg.C, toks, ua, ur, tau32) for j in range(ncopy)]
 
@@ -483,7 +509,7 @@ def bench_rows(args):
     x0 = up(src)
     rows_read = K + 1 if greedy else K
     bytes_call = B * rows_read * V * 2
-    ncopy = int(math.ceil(MALL_BYTES / bytes_call)) + 1
+    ncopy = n_copies(bytes_call)
     xs = [x0] + [x0.clone() for _ in range(ncopy - 1)]
     toks = torch.from_numpy(d["tokens"]).to(dev)
     if greedy:
@@ -494,8 +520,7 @@ def bench_rows(args):
     else:
         F = S.ssd_fanout(cfg.n_budget, K, cfg.a_p, cfg.r)
         sig = [S.sigma_from_cache(S.ssd_build_cache(xs[j], tau, F), cfg.C) for j in range(ncopy)]
-        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.seed, 424242])))
-        u_np = g.random((B, K), dtype=np.float32)
+        u_np = W.make_draft_uniforms(cfg, tau)
         u = torch.from_numpy(u_np).to(dev)
         outs = [S.ssd_draft_sample(xs[j], u, tau, sig[j]) for j in range(ncopy)]
 
@@ -522,7 +547,8 @@ def bench_rows(args):
         dt = time.time() - t0
         cpu = {"value": round(n / dt, 3), "unit": "rows/s", "cores": 1, "kind": "oracle",
                "sample": f"first {n} of {B} batch rows of the same call, float64 NumPy, {dt:.1f} s"
-                         + ("" if greedy else " (the oracle takes each row's top-F for sigma itself)")}
+                         + ("" if greedy else " (the oracle takes each row's top-F for sigma itself)"),
+               "cpu_model": _cpu_model()}
     name = "ssd_verify_greedy" if greedy else "ssd_draft_sample"
     kern = "k_greedy<1>, one launch" if greedy else "k_sample_chunks<1, true> + k_sample_pick<1, true>"
     line = {
@@ -577,7 +603,7 @@ def bench_tree(args):
     dft0 = up(d["draft"])
     row_bytes = V * 2
     bytes_single = B * (N + inner) * row_bytes       # every statistics row once
-    ncopy = int(math.ceil(MALL_BYTES / bytes_single)) + 1
+    ncopy = n_copies(bytes_single)
     tgts = [tgt0] + [tgt0.clone() for _ in range(ncopy - 1)]
     dfts = [dft0] + [dft0.clone() for _ in range(ncopy - 1)]
     toks = torch.from_numpy(d["tokens"]).to(dev)
@@ -655,22 +681,125 @@ def measured_traffic(profile):
     return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["source_sha256"] else None
 
 
-def cpu_baseline(cfg, d, F, C, tau, budget_s):
-    """The float64 oracle on the host, same workload, single thread, bounded sample."""
+def _cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_inputs(cid, tau, b):
+    import workloads as W
+    return W.make_inputs(W.get_config(cid), tau=tau, draw_tokens=False, b_rows=[b])
+
+
+def _oracle_step_row(d, K, F, C, b, toks_row, u_row):
+    """The oracle on batch row b of the step: its sigma draws with the GPU's
+    uniforms (a parity check of the draft phase, untimed), then, timed, the
+    cache build, the sigma verification of the GPU's drafted tokens and the
+    lookup. Returns its outputs and the seconds the step took."""
     import oracle as O
+    dtoks, dmarg = O.draft_sample(d["draft"][:, :K], d["tau"], u_row[None, :], F, C)
+    t1 = time.time()
+    cache = O.build_cache(d["draft"][:, :K + 1], d["tau"], F, C)
+    ref = O.verify(d["target"], d["draft"], toks_row[None, :], d["u_acc"], d["u_res"], d["tau"], {"F": F, "C": C})
+    hit, _ = O.cache_lookup(cache["cache_tokens"], F, ref["accepted"], ref["out_tokens"])
+    return {"b": b, "accepted": int(ref["accepted"][0]), "out_tokens": ref["out_tokens"][0],
+            "acc_margin": ref["acc_margin"][0], "res_margin": float(ref["res_margin"][0]),
+            "cache_tokens": cache["cache_tokens"][0], "hit": int(hit[0]),
+            "draft_tokens": dtoks[0], "draft_margin": dmarg[0], "oracle_s": time.time() - t1}
+
+
+def _oracle_worker(jobs, barrier, queue):
+    """One host process of the fan-out: generate its rows' inputs, wait for
+    every process, then run the oracle on them and report."""
+    for v in ("OMP_NUM_THREADS", "MKL_NUM_THREADS", "OPENBLAS_NUM_THREADS"):
+        os.environ[v] = "1"
+    inputs = [_oracle_inputs(j[0], j[1], j[4]) for j in jobs]
+    barrier.wait()
+    out = []
+    for d, (cid, tau, F, C, b, toks_row, u_row, K) in zip(inputs, jobs):
+        out.append(_oracle_step_row(d, K, F, C, b, toks_row, u_row))
+    queue.put(out)
+
+
+def _check_rows(rows, gpu, F):
+    """GPU outputs of the step against the oracle rows: cache tokens exact;
+    drafted tokens equal the oracle's draws unless that draw's margin is
+    below 1e-6; accepted length and emitted tokens equal unless the oracle's
+    margin at the first differing decision is below 1e-6; the hit bit of the
+    GPU's own outcome equals the oracle lookup of that outcome."""
+    import oracle as O
+    differ, excused = [], []
+    for r in rows:
+        b = r["b"]
+        ok = np.array_equal(gpu["cache_tokens"][b], r["cache_tokens"])
+        dt_ok = np.all((gpu["tokens"][b] == r["draft_tokens"]) | (r["draft_margin"] < 1e-6))
+        a_g, out_g = int(gpu["accepted"][b]), gpu["out_tokens"][b]
+        same = a_g == r["accepted"] and np.array_equal(out_g, r["out_tokens"])
+        if not same:
+            if a_g != r["accepted"]:
+                m = r["acc_margin"][min(a_g, r["accepted"])] if min(a_g, r["accepted"]) >= 0 else math.inf
+            else:
+                m = r["res_margin"]
+            if m < 1e-6:
+                excused.append(b)
+            else:
+                ok = False
+        h_own, _ = O.cache_lookup(r["cache_tokens"][None, :], F, np.array([a_g]), out_g[None, :])
+        ok = ok and dt_ok and int(h_own[0]) == int(gpu["hit"][b])
+        if not ok:
+            differ.append(b)
+    return {"rows": len(rows), "rows_differ": len(differ), "differ_rows": differ, "excused_rows": excused}
+
+
+def cpu_baseline(cid, tau, F, C, gpu, u_draft, budget_s):
+    """The float64 oracle on the host over the same step (drafted tokens as
+    the GPU drew them): (i) one process, rows in order for at most budget_s
+    of oracle time; (ii) the same per-row function over every batch row,
+    fanned out over all host cores the process may use (rows are
+    independent; each process generates its rows' inputs first, then all
+    start together and the wall time of the oracle phase is taken). The rows
+    of (ii) are checked against the GPU's outputs. Returns (baseline, check)."""
+    import multiprocessing as mp
+    import queue as qmod
+    import workloads as W
+    cfg = W.get_config(cid)
+    B, K = cfg.B, cfg.K
+    jobs = [(cid, tau, list(F), C, b, gpu["tokens"][b], u_draft[b], K) for b in range(B)]
+    single, dt1 = [], 0.0
+    while len(single) < B and dt1 < budget_s:
+        j = jobs[len(single)]
+        single.append(_oracle_step_row(_oracle_inputs(cid, tau, j[4]), K, j[2], j[3], j[4], j[5], j[6]))
+        dt1 += single[-1]["oracle_s"]
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    ctx = mp.get_context("spawn")
+    barrier, q = ctx.Barrier(cores + 1), ctx.Queue()
+    procs = [ctx.Process(target=_oracle_worker, args=(jobs[i::cores], barrier, q)) for i in range(cores)]
+    for p in procs:
+        p.start()
+    barrier.wait(timeout=600)
     t0 = time.time()
-    n = 0
-    while n < cfg.B and (time.time() - t0) < budget_s:
-        b = slice(n, n + 1)
-        cache = O.build_cache(d["draft"][b], tau, F, C)
-        ref = O.verify(d["target"][b], d["draft"][b], d["tokens"][b], d["u_acc"][b], d["u_res"][b],
-                       tau, {"F": F, "C": C})
-        O.cache_lookup(cache["cache_tokens"], F, ref["accepted"], ref["out_tokens"])
-        n += 1
-    dt = time.time() - t0
-    return {"value": round(n / dt, 3), "unit": "verified rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} of {cfg.B} batch rows of the same step (fan-out, cache build, "
-                      f"sigma verify, lookup), float64 NumPy, {dt:.1f} s"}
+    rows = []
+    for _ in range(cores):
+        try:
+            rows += q.get(timeout=600)
+        except qmod.Empty:
+            break
+    dtn = time.time() - t0
+    for p in procs:
+        p.join(timeout=60)
+    rows.sort(key=lambda r: r["b"])
+    base = {"value": round(len(rows) / dtn, 3), "unit": "verified rows/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(),
+            "sample": f"all {len(rows)} of {B} batch rows of the same step (cache build, sigma verify, lookup), "
+                      f"float64 NumPy, the per-row oracle fanned out over {cores} processes, {dtn:.1f} s wall",
+            "single_thread": {"value": round(len(single) / dt1, 3), "unit": "verified rows/s", "cores": 1,
+                              "sample": f"first {len(single)} of {B} rows, {dt1:.1f} s"}}
+    return base, _check_rows(rows, gpu, F)
 
 
 if __name__ == "__main__":

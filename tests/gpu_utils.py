@@ -32,6 +32,49 @@ def fvec(a, torch, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
 
 
+def divergence_margin(ref, j, a_g, out_g):
+    """The oracle's margin at the first decision where a GPU outcome (a_g,
+    out_g) of row j departs from the oracle's, or None when the two cannot be
+    reconciled by a near-tie (a flagged row on one side only).
+
+    The emitted tokens before position a are the drafted ones on both sides,
+    so the first differing decision is the accept test at min(a_ref, a_gpu)
+    when the accepted lengths differ, else the final draw."""
+    a_r = int(ref["accepted"][j])
+    a_g = int(a_g)
+    if a_r != a_g:
+        if a_r < 0 or a_g < 0:
+            return None
+        return float(ref["acc_margin"][j][min(a_r, a_g)])
+    if a_r < 0:
+        return None
+    return float(ref["res_margin"][j])
+
+
+def tree_divergence_margin(ref, j, a_g, nodes_g):
+    """The oracle's margin at the first decision where a GPU token-tree walk
+    (its kept-path nodes) departs from the oracle's walk of row j, or None
+    for a flag mismatch. Both walks test the children of a node in index
+    order, so at the first depth where the kept nodes differ, the earliest
+    differing decision is the test of the smaller of the two children (a
+    walk that stopped there tested, and rejected, every child); with equal
+    paths only the final draw can differ."""
+    a_r = int(ref["accepted"][j])
+    if (a_r < 0) != (int(a_g) < 0):
+        return None
+    if a_r < 0:
+        return None
+    nr, ng = ref["out_nodes"][j], nodes_g
+    for depth in range(1, len(nr)):
+        xr, xg = int(nr[depth]), int(ng[depth])
+        if xr == xg:
+            if xr < 0:
+                break
+            continue
+        return float(ref["acc_margin"][j][min(x for x in (xr, xg) if x >= 0)])
+    return float(ref["res_margin"][j])
+
+
 def compare_verify(ref, got, K, rows=None, check_lse=True, label=""):
     """Compare GPU verify outputs with the oracle's on the listed batch rows.
 
@@ -55,12 +98,8 @@ def compare_verify(ref, got, K, rows=None, check_lse=True, label=""):
         if a_r == a_g and np.array_equal(out_r, out_g[b]):
             pass
         else:
-            if a_r != a_g:
-                lo = min(a_r, a_g) if a_r >= 0 and a_g >= 0 else -1
-                assert lo >= 0, f"{label} row {b}: flagged mismatch {a_r} vs {a_g}"
-                m = ref["acc_margin"][j][lo]
-            else:
-                m = ref["res_margin"][j]
+            m = divergence_margin(ref, j, a_g, out_g[b])
+            assert m is not None, f"{label} row {b}: flagged mismatch {a_r} vs {a_g}"
             assert m < EXCUSE, (f"{label} row {b}: accepted {a_r} vs {a_g}, out {out_r} vs "
                                 f"{out_g[b]}, margin {m}")
             excused.append(b)
@@ -86,3 +125,65 @@ def compare_verify(ref, got, K, rows=None, check_lse=True, label=""):
     if excused:
         log(f"[{label}] excused rows (margin < {EXCUSE}): {excused}")
     return len(excused)
+
+
+def compare_cache(cache, ref, F, rows, label):
+    """Cache tokens and threshold indices bit-exact; zmax exact; S_top and
+    S_rest as masses of the row: each within 1e-5 of the row's total mass
+    S_top + S_rest (probability units, the bar of the row log-sum-exp; a
+    component many orders below the total, e.g. the tail at a low
+    temperature, carries the fp32 exponent error of its far-from-max
+    entries and is not held to 1e-5 of itself)."""
+    ct = cache["cache_tokens"].cpu().numpy()
+    thr = cache["thr"].cpu().numpy()
+    st = cache["draft_stats"].cpu().numpy()
+    sumF = sum(F)
+    for j, b in enumerate(rows):
+        assert np.array_equal(ct[b, :sumF], ref["cache_tokens"][j]), f"{label} row {b} cache tokens"
+        assert np.array_equal(thr[b, :, 1], ref["thr_idx"][j]), f"{label} row {b} thr"
+        for k in range(len(F)):
+            zr, tr, rr = ref["stats"][j, k]
+            zg, tg, rg = st[b, k]
+            tot = abs(tr) + abs(rr)
+            assert zg == zr or (np.isinf(zg) and np.isinf(zr)), f"{label} zmax"
+            assert abs(tg - tr) <= 1e-5 * tot + 1e-300, f"{label} row {b} k {k} S_top {tg} vs {tr}"
+            assert abs(rg - rr) <= 1e-5 * tot + 1e-300, f"{label} row {b} k {k} S_rest {rg} vs {rr}"
+
+
+def compare_hits(hit_g, slot_g, ref_cache_tokens, F, acc_g, out_g, ref, label):
+    """hit/slot of the GPU's own outcome equal the oracle lookup of that
+    outcome in the oracle's cache; on rows whose outcome equals the oracle's,
+    they equal the oracle's hit/slot."""
+    import oracle as O
+    h_own, s_own = O.cache_lookup(ref_cache_tokens, F, acc_g, out_g)
+    assert np.array_equal(hit_g, h_own), f"{label}: hit of the GPU outcome"
+    assert np.array_equal(slot_g.astype(np.int64), s_own), f"{label}: slot of the GPU outcome"
+    same = (acc_g == ref["accepted"]) & np.all(out_g == ref["out_tokens"], axis=1)
+    if "hit" in ref:
+        assert np.array_equal(hit_g[same], ref["hit"][same]), f"{label}: hit"
+    return int((~same).sum())
+
+
+def load_golden(name):
+    """Expected outputs stored by tests/golden/make_golden.py (oracle only)."""
+    import importlib.util
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "make_golden.py")
+    spec = importlib.util.spec_from_file_location("make_golden", path)
+    mg = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mg)
+    return mg, mg.load(name)
+
+
+def golden_inputs(name):
+    """The golden case's inputs regenerated from the seeded generator, with
+    every row's digest checked against the stored one; the drafted tokens are
+    the stored ones (drawn by the oracle from q_sigma for cache cases)."""
+    import workloads as W
+    mg, g = load_golden(name)
+    cfg, tau, sigma, F, C = mg.case_params(name)
+    d = W.make_inputs(cfg, tau=tau, draw_tokens=not sigma)
+    for b in range(cfg.B):
+        assert mg.row_digest(d["target"][b], d["draft"][b]) == g["row_digest"][b], f"{name}: input row {b} changed"
+    d["tokens"] = np.ascontiguousarray(g["tokens"].astype(np.int32))
+    return cfg, d, g

@@ -12,7 +12,7 @@ import pytest
 
 import oracle as O
 import workloads as W
-from gpu_utils import EXCUSE, fvec, ivec, log, to_dev
+from gpu_utils import EXCUSE, fvec, ivec, log, to_dev, tree_divergence_margin
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -45,8 +45,8 @@ def _run(S, d, rows=None, label="", max_excused=1):
                 and np.array_equal(nodes[b], ref["out_nodes"][j]))
         if same:
             continue
-        m = np.nanmin(np.concatenate([ref["acc_margin"][j], [ref["res_margin"][j]]]))
-        assert m < EXCUSE, (f"{label} row {b}: accepted {acc[b]} vs {ref['accepted'][j]}, out {out[b]} vs "
+        m = tree_divergence_margin(ref, j, acc[b], nodes[b])
+        assert m is not None and m < EXCUSE, (f"{label} row {b}: accepted {acc[b]} vs {ref['accepted'][j]}, out {out[b]} vs "
                             f"{ref['out_tokens'][j]}, nodes {nodes[b]} vs {ref['out_nodes'][j]}, margin {m}")
         excused.append(b)
     if excused:

@@ -29,7 +29,7 @@ from typing import Optional
 
 import numpy as np
 
-__all__ = ["Config", "CONFIGS", "get_config", "make_inputs", "make_uniforms",
+__all__ = ["Config", "CONFIGS", "get_config", "make_inputs", "make_uniforms", "make_draft_uniforms",
            "f32_to_bf16_bits", "bf16_bits_to_f32", "sha256",
            "TreeConfig", "TREE_CONFIGS", "tree_parent", "make_tree_inputs"]
 
@@ -154,6 +154,17 @@ def make_uniforms(cfg: Config, u_seed: Optional[int] = None):
     u_acc = ga.random((cfg.B, cfg.K), dtype=np.float32)
     u_res = gr.random(cfg.B, dtype=np.float32)
     return u_acc, u_res
+
+
+def make_draft_uniforms(cfg: Config, tau: Optional[float] = None) -> np.ndarray:
+    """Uniforms u [B, K] (fp32 in [0, 1)) for drawing the drafted tokens by
+    inverse CDF, one stream per (workload, temperature), independent of the
+    accept and resample uniforms. Used where the drafts must come from the
+    sigma-reshaped draft distribution (the cache workloads); the draw itself
+    is the sampler's business, not this module's."""
+    tau = float(np.float32(cfg.taus[0] if tau is None else tau))
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.seed, 424242, int(round(tau * 1000))])))
+    return g.random((cfg.B, cfg.K), dtype=np.float32)
 
 
 def make_inputs(cfg: Config, tau: Optional[float] = None, draw_tokens: bool = True,
