@@ -167,6 +167,31 @@ SSD_API int ssd_verify(const void* target_logits, int64_t target_bstride,
                        float* resid_mass, float* row_lse,
                        void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* ssd_verify without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc). The workspace is a file-scope device array of
+ * ssd_noalloc_scratch_bytes() bytes (SSD_NOALLOC_SCRATCH_BYTES, 16 MiB), one
+ * copy per GPU the library runs on, held until the process ends; its
+ * address on the current device is looked up on the first call on that
+ * device. Every call clears the part it uses with a fill kernel before the
+ * kernels of ssd_verify run (no memset, no allocation, so it can be
+ * captured), so what an earlier call left there never matters. Arguments,
+ * outputs and errors are those of ssd_verify; a shape whose workspace
+ * (ssd_verify_workspace_size) exceeds the array returns SSD_EINVAL with a
+ * message. All calls on one GPU share the array: calls that may overlap in
+ * time on one GPU (other streams, other threads) race and give wrong
+ * results. Launches the fill kernel, then ssd_verify's two kernels, on
+ * hip_stream (the current device's). */
+#define SSD_NOALLOC_SCRATCH_BYTES (16u << 20)
+SSD_API size_t ssd_noalloc_scratch_bytes(void);
+SSD_API int ssd_verify_noalloc(const void* target_logits, int64_t target_bstride,
+                               const void* draft_logits, int64_t draft_bstride, int dtype,
+                               int32_t B, int32_t K, int32_t V, float tau,
+                               const int32_t* draft_tokens, const float* u_acc, const float* u_res,
+                               const ssd_sigma* sigma,
+                               int32_t* accepted, int32_t* out_tokens, float* probs,
+                               float* resid_mass, float* row_lse, void* hip_stream);
+
 /* Bytes of workspace ssd_residual_sample needs. */
 SSD_API size_t ssd_residual_workspace_size(int32_t B, int32_t K, int32_t V, int dtype);
 

@@ -19,7 +19,8 @@ __all__ = ["SSD_F32", "SSD_BF16", "SsdError", "lib", "ssd_fanout", "ssd_verify",
            "ssd_verify_workspace_size", "ssd_residual_workspace_size",
            "ssd_build_cache_workspace_size", "ssd_draft_sample_workspace_size",
            "ssd_verify_greedy_workspace_size", "ssd_verify_tree", "ssd_verify_tree_workspace_size",
-           "ssd_tree_rounds", "ssd_verify_round", "ssd_verify_round_workspace_size", "EXPORTS",
+           "ssd_tree_rounds", "ssd_verify_round", "ssd_verify_round_workspace_size", "ssd_verify_noalloc",
+           "ssd_noalloc_scratch_bytes", "EXPORTS",
            "library_path"]
 
 SSD_F32, SSD_BF16 = 0, 1
@@ -30,7 +31,8 @@ EXPORTS = ("ssd_last_error", "ssd_fanout", "ssd_verify_workspace_size", "ssd_ver
            "ssd_draft_sample_workspace_size", "ssd_draft_sample",
            "ssd_verify_greedy_workspace_size", "ssd_verify_greedy", "ssd_fanout_uniform", "ssd_speedup",
            "ssd_cache_stats", "ssd_tree_rounds", "ssd_verify_tree_workspace_size", "ssd_verify_tree",
-           "ssd_verify_round_workspace_size", "ssd_verify_round")
+           "ssd_verify_round_workspace_size", "ssd_verify_round", "ssd_noalloc_scratch_bytes",
+           "ssd_verify_noalloc")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -63,6 +65,9 @@ _SIGS = {
     "ssd_build_cache_workspace_size": (_sz, [_i32, _i32, _i32, ctypes.c_int]),
     "ssd_verify": (ctypes.c_int, [_vp, _i64, _vp, _i64, ctypes.c_int, _i32, _i32, _i32, _f32,
                                   _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ssd_noalloc_scratch_bytes": (_sz, []),
+    "ssd_verify_noalloc": (ctypes.c_int, [_vp, _i64, _vp, _i64, ctypes.c_int, _i32, _i32, _i32, _f32,
+                                          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "ssd_residual_sample": (ctypes.c_int, [_vp, _i64, _vp, _i64, ctypes.c_int, _i32, _i32, _i32,
                                            _f32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ssd_build_cache": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _i32, _i32, _i32, _f32, _vp,
@@ -243,6 +248,39 @@ def ssd_verify(target, draft, draft_tokens, u_acc, u_res, tau: float, sigma: Opt
                             ptr(out["accepted"]), ptr(out["out_tokens"]), ptr(out.get("probs")),
                             ptr(out.get("resid_mass")), ptr(out.get("row_lse")),
                             ws, wsz, _stream(stream)))
+    return out
+
+
+def ssd_noalloc_scratch_bytes() -> int:
+    return int(lib().ssd_noalloc_scratch_bytes())
+
+
+def ssd_verify_noalloc(target, draft, draft_tokens, u_acc, u_res, tau: float, sigma: Optional[Sigma] = None,
+                       *, out: dict, stream=None) -> dict:
+    """ssd_verify through the entry point that allocates nothing (its workspace
+    is the library's per-GPU device array). `out` holds caller-allocated
+    outputs as for ssd_verify (accepted, out_tokens; probs, resid_mass,
+    row_lse may be None); no device memory is allocated here either."""
+    torch = _torch()
+    B, K = int(draft_tokens.shape[0]), int(draft_tokens.shape[1])
+    V = int(target.shape[2])
+    dt = _dtype_code(target)
+    if _dtype_code(draft) != dt:
+        raise TypeError("target and draft dtypes differ")
+    tp, tb = _logits(target, "target", K + 1)
+    dp, db = _logits(draft, "draft", K, V)
+    if target.shape[0] != B or draft.shape[0] != B:
+        raise ValueError("target/draft batch size differs from draft_tokens")
+    tok = _dev(draft_tokens, torch.int32, (B, K), "draft_tokens")
+    ua = _dev(u_acc, torch.float32, (B, K), "u_acc")
+    ur = _dev(u_res, torch.float32, (B,), "u_res")
+    _dev(out["accepted"], torch.int32, (B,), "accepted")
+    _dev(out["out_tokens"], torch.int32, (B, K + 1), "out_tokens")
+    sig = ctypes.byref(sigma._c()) if sigma is not None else None
+    ptr = lambda t: None if t is None else t.data_ptr()
+    _check(lib().ssd_verify_noalloc(tp, tb, dp, db, dt, B, K, V, float(tau), tok, ua, ur, sig,
+                                    ptr(out["accepted"]), ptr(out["out_tokens"]), ptr(out.get("probs")),
+                                    ptr(out.get("resid_mass")), ptr(out.get("row_lse")), _stream(stream)))
     return out
 
 

@@ -29,7 +29,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-ffp-contract=of
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 SOURCES = ["ssd_stats.hip", "ssd_resid.hip", "ssd_cache.hip", "ssd_sample.hip", "ssd_greedy.hip", "ssd_tree.hip",
-           "ssd_round.hip", "ssd_api.cpp"]
+           "ssd_round.hip", "ssd_noalloc.hip", "ssd_api.cpp"]
 
 
 def _compile(src: str, obj: str):

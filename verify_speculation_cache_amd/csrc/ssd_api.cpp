@@ -234,6 +234,9 @@ using namespace ssd;
 
 extern "C" {
 
+// Status message setter for entry points defined in other source files.
+int ssd_internal_fail(int code, const char* msg) { return fail(code, "%s", msg); }
+
 SSD_API const char* ssd_last_error(void) { return g_err.c_str(); }
 
 SSD_API int ssd_fanout(int32_t n_budget, int32_t K, double a_p, double r, int32_t* F_out) {
