@@ -199,10 +199,16 @@ SSD_API size_t ssd_residual_workspace_size(int32_t B, int32_t K, int32_t V, int 
  * Derivation of Acceptance Criterion): from max(0, p - q)/Z when row[b] < K
  * and draft_logits is given (q optionally sigma-reshaped), otherwise from p
  * of that target row (the bonus form). Same inverse-CDF convention and
- * fallbacks as ssd_verify.
+ * fallbacks as ssd_verify. The rows' log-normalisers are recomputed from the
+ * logits (one statistics pass over the row pair) rather than taken from the
+ * caller: an fp32 log-normaliser carries about |lse| * 2^-24 of relative
+ * error into every probability, more than the draws tolerate.
  *   target_logits device [B, K+1, V]; draft_logits device [B, >=K, V] or NULL
  *   row device int32 [B]; u device float [B]
- *   token_out device int32 [B]; mass_out device float [B] or NULL (Z). */
+ *   token_out device int32 [B]; mass_out device float [B] or NULL (Z).
+ * Two kernel launches on hip_stream: the statistics chunk pass over each
+ * batch row's pair of rows, then the draw (every workgroup of a batch row
+ * merges the pair's partials itself). */
 SSD_API int ssd_residual_sample(const void* target_logits, int64_t target_bstride,
                                 const void* draft_logits, int64_t draft_bstride, int dtype,
                                 int32_t B, int32_t K, int32_t V, float tau,

@@ -426,9 +426,13 @@ SSD_API int ssd_residual_sample(const void* target_logits, int64_t target_bstrid
   a.info = reinterpret_cast<RowInfo*>(ws + sw.info);
   a.zg = reinterpret_cast<uint64_t*>(ws + sw.zg);
   hipStream_t stream = as_stream(hip_stream);
-  if ((st = hip_status(launch_stats(a, dtype, stream), "stats launch")) != SSD_OK) return st;
+  // two launches: the statistics chunk pass over each batch row's pair of
+  // rows, then the draw, every workgroup of which merges its row's partials
+  if ((st = hip_status(launch_stats_chunks(a, dtype, stream), "stats launch")) != SSD_OK) return st;
 
-  ResidArgs r{};
+  RoundResidArgs rr{};
+  rr.s = a;
+  ResidArgs& r = rr.r;
   r.target = target_logits;
   r.tb = target_bstride;
   r.draft = draft_logits;
@@ -446,7 +450,7 @@ SSD_API int ssd_residual_sample(const void* target_logits, int64_t target_bstrid
   r.tok_stride = 1;
   r.tok_at_a = 0;
   r.mass_out = mass_out;
-  return hip_status(launch_resid(r, dtype, sig, stream), "residual launch");
+  return hip_status(launch_rows_resid(rr, dtype, sig, stream), "residual launch");
 }
 
 SSD_API size_t ssd_verify_greedy_workspace_size(int32_t B, int32_t K, int32_t V, int dtype) {

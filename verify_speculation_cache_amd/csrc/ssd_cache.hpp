@@ -179,7 +179,7 @@ __device__ __forceinline__ HeldMap held_map(int S, int tid) {
 }
 
 // f(e) for every written candidate of the row, each visited by one thread.
-template <typename Fn>
+template <bool COH, typename Fn>
 __device__ __forceinline__ void visit(const RowCands& rc, bool held, const uint64_t* pp, const int* cnt_lds,
                                       const uint64_t* cl, int S, Fn f) {
   if (held) {
@@ -198,10 +198,10 @@ __device__ __forceinline__ void visit(const RowCands& rc, bool held, const uint6
       ok[i] = false;
       if (sidx < slots) {
         const int cc = sidx / kCandCap;
-        const int n = cc < kCountLds ? cnt_lds[cc] : int(uint32_t(pp[cc * 4 + 2]));
+        const int n = cc < kCountLds ? cnt_lds[cc] : int(uint32_t(ld64<COH>(pp + cc * 4 + 2)));
         ok[i] = (sidx - cc * kCandCap) < n;
       }
-      e[i] = ok[i] ? cl[sidx] : 0ull;
+      e[i] = ok[i] ? ld64<COH>(cl + sidx) : 0ull;
     }
 #pragma unroll
     for (int i = 0; i < kHold; ++i)
@@ -212,10 +212,11 @@ __device__ __forceinline__ void visit(const RowCands& rc, bool held, const uint6
 // Every thread's held slots, loaded unconditionally (slots past a chunk's
 // count are masked out later; the chunk and position are clamped into the
 // row's slots, so there is no branch around the loads).
+template <bool COH>
 __device__ __forceinline__ void load_held(RowCands& rc, const uint64_t* cl, const HeldMap& hm, int S) {
   const uint64_t* base = cl + min(hm.chunk, S - 1) * kCandCap;
 #pragma unroll
-  for (int i = 0; i < kHold; ++i) rc.v[i] = base[min(hm.pos + hm.step * i, kCandCap - 1)];
+  for (int i = 0; i < kHold; ++i) rc.v[i] = ld64<COH>(base + min(hm.pos + hm.step * i, kCandCap - 1));
 }
 
 // Appends e to the LDS list when keep holds: one LDS atomic per wave (the
@@ -248,8 +249,10 @@ __device__ __forceinline__ void wave_append(uint64_t e, bool keep, int lane, int
 // and then the candidates tied at it by a bitwise search over the index.
 // thr and draft_stats are stored by thread 0 with device-scope stores, so a
 // workgroup of the same launch that arrives after this one (arrive_last) may
-// read them.
-template <int DT>
+// read them. COH: the chunk records and candidates were written by other
+// workgroups of the same launch, so they are read (and rewritten) with
+// device-scope accesses, and so are the cache tokens written.
+template <int DT, bool COH = false>
 __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid) {
   using T = typename Dt<DT>::T;
   const int KP = a.K + 1;
@@ -288,12 +291,12 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
   // the candidate count of the chunk it holds.
   const bool rec = w == 0 && lane < a.S;
   const int rl = min(lane, a.S - 1);
-  const uint64_t r0 = pp[rl * 4], r1 = pp[rl * 4 + 1], r2 = pp[rl * 4 + 2];
-  const uint64_t own_cnt = pp[min(hm.chunk, a.S - 1) * 4 + 2];
+  const uint64_t r0 = ld64<COH>(pp + rl * 4), r1 = ld64<COH>(pp + rl * 4 + 1), r2 = ld64<COH>(pp + rl * 4 + 2);
+  const uint64_t own_cnt = ld64<COH>(pp + min(hm.chunk, a.S - 1) * 4 + 2);
   __builtin_amdgcn_sched_barrier(0);
   RowCands rc;
   rc.ok = 0;
-  load_held(rc, cl, hm, a.S);
+  load_held<COH>(rc, cl, hm, a.S);
   __builtin_amdgcn_sched_barrier(0);
 
   // row max, the chunks' non-candidate mass (lane-local fold in chunk order,
@@ -319,7 +322,8 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
       sl = acc;
     };
     if (rec) fold(lane, r0, r1, r2);
-    for (int cc = lane + 64; cc < a.S; cc += 64) fold(cc, pp[cc * 4], pp[cc * 4 + 1], pp[cc * 4 + 2]);
+    for (int cc = lane + 64; cc < a.S; cc += 64)
+      fold(cc, ld64<COH>(pp + cc * 4), ld64<COH>(pp + cc * 4 + 1), ld64<COH>(pp + cc * 4 + 2));
     const float m = wave_max(ml);
     const double t = sl > 0.0 ? sl * rescale(pivot_of(ml), pivot_of(m), c32) : 0.0;
     const double srest = wave_sum(t);
@@ -357,14 +361,14 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
   if (s_anyovf) {
     const T* row = static_cast<const T*>(a.draft) + int64_t(b) * a.db + int64_t(k) * a.V;
     for (int cc = 0; cc < a.S; ++cc) {
-      if (pp[cc * 4 + 2] != kOverflow) continue;   // uniform
+      if (ld64<COH>(pp + cc * 4 + 2) != kOverflow) continue;   // uniform
       const int64_t c0 = int64_t(cc) * kChunk;
       const int nvalid = int(min(int64_t(kChunk), int64_t(a.V) - c0));
       uint32_t key_unused;
       const uint32_t sel = exact_top_f<DT>(row, c0, nvalid, F, tid, lane, w, sm_i2, sm_wcnt2, key_unused);
       float x[kPerThread];
       load_strided<DT>(row, c0, a.V, (reinterpret_cast<uintptr_t>(row) & 15u) == 0, tid, x);
-      const float f0 = threshold_value<DT>(uint32_t(pp[cc * 4] >> 32));
+      const float f0 = threshold_value<DT>(uint32_t(ld64<COH>(pp + cc * 4) >> 32));
       const int nt = __popc(sel);
       const int incl = wave_incl_scan_i(nt, lane);
       if (lane == 63) sm_wcnt2[w] = incl;
@@ -377,21 +381,21 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
       for (int q = 0; q < kPerThread; ++q) {
         const int loc = local_of<DT>(tid, q);
         if ((sel >> q) & 1u) {
-          clw[int64_t(cc) * kCandCap + pos] = cand_bits(key_of<DT>(x[q]), int32_t(c0) + loc);
+          st64<COH>(clw + int64_t(cc) * kCandCap + pos, cand_bits(key_of<DT>(x[q]), int32_t(c0) + loc));
           ++pos;
         } else if (loc < nvalid && x[q] >= f0) {
           s_unsel += double(__builtin_amdgcn_exp2f((x[q] - prow) * c32));
         }
       }
       if (tid == 0) {
-        pw[cc * 4 + 2] = uint64_t(uint32_t(nsel));
+        st64<COH>(pw + cc * 4 + 2, uint64_t(uint32_t(nsel)));
         if (cc < kCountLds) s_cnt[cc] = nsel;
       }
       __syncthreads();
     }
     __threadfence();
     __syncthreads();
-    load_held(rc, cl, hm, a.S);   // the rewritten lists
+    load_held<COH>(rc, cl, hm, a.S);   // the rewritten lists
   }
 
   if (held) {
@@ -408,7 +412,7 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
   // candidates at or above Tmax go to the ranked list; the others only add
   // to S_rest
   const uint32_t tcut = s_tmax;
-  visit(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
+  visit<COH>(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
     const bool keep = F > 0 && cand_key(e) >= tcut;
     wave_append(e, keep, lane, &s_n2, s_list);
     if (!keep) s_unsel += cand_mass<DT>(e, prow, c32);
@@ -425,7 +429,7 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
       s_hist[tid] = 0;
       __syncthreads();
       const uint32_t prefix = s_prefix;
-      visit(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
+      visit<COH>(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
         const uint32_t key = cand_key(e);
         const uint32_t hi = (shift + 8 < 32) ? (key >> (shift + 8)) : 0u;
         if (hi == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1);
@@ -472,7 +476,7 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
     const uint32_t cut = s_need == 0 && s_prefix == 0 ? tcut : s_prefix;   // the F-th key
     if (tid == 0) s_n2 = 0;
     __syncthreads();
-    visit(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
+    visit<COH>(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
       if (cand_key(e) < tcut) return;   // already counted
       const bool keep = cand_key(e) >= cut;
       wave_append(e, keep, lane, &s_n2, s_list);
@@ -486,13 +490,13 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
       // more ties at the F-th key than the list holds: the needed ties are
       // the ones with the smallest indices (bitwise search for the index bound)
       int c = 0;
-      visit(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) { c += cand_key(e) > cut ? 1 : 0; });
+      visit<COH>(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) { c += cand_key(e) > cut ? 1 : 0; });
       const int need = F - block_sum_i(c, sm_i2);
       int lim = 0;   // largest bound with fewer than `need` ties below it
       for (int bit = 30; bit >= 0; --bit) {
         const int cand = lim | (1 << bit);
         int cnt = 0;
-        visit(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
+        visit<COH>(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
           cnt += (cand_key(e) == cut && cand_idx(e) < cand) ? 1 : 0;
         });
         if (block_sum_i(cnt, sm_i2) < need) lim = cand;
@@ -500,7 +504,7 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
       // ties with index <= lim are exactly `need` of them
       if (tid == 0) s_n2 = 0;
       __syncthreads();
-      visit(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
+      visit<COH>(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
         if (cand_key(e) < cut) return;   // already counted
         const bool keep = cand_key(e) > cut || cand_idx(e) <= lim;
         wave_append(e, keep, lane, &s_n2, s_list);
@@ -516,7 +520,7 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
   // below depends on the order in which the list was filled
   auto place = [&](uint64_t e, int rank) {
     s_exp[rank] = cand_mass<DT>(e, prow, c32);
-    if (rank < F) ct[rank] = cand_idx(e);
+    if (rank < F) st32<COH>(ct + rank, cand_idx(e));
     if (rank == F - 1) s_thrw = e;
   };
   if (n2 <= 64) {
@@ -610,8 +614,10 @@ __device__ __forceinline__ uint32_t wave_compact(const float (&x)[kPerThread], f
   return cw;
 }
 
-// The chunk pass of one workgroup; blk = (b * (K+1) + k) * S + c.
-template <int DT>
+// The chunk pass of one workgroup; blk = (b * (K+1) + k) * S + c. COH: the
+// record and candidates are read by a merge in the same launch, so they are
+// stored with device-scope stores.
+template <int DT, bool COH = false>
 __device__ __forceinline__ void cache_chunk_wg(const CacheArgs& a, uint32_t blk) {
   using T = typename Dt<DT>::T;
   constexpr int PV = Dt<DT>::kPerVec;
@@ -726,14 +732,14 @@ __device__ __forceinline__ void cache_chunk_wg(const CacheArgs& a, uint32_t blk)
   // ---- candidates out: each wave copies its list, in order ----
   if (!overflow) {
     uint64_t* out = reinterpret_cast<uint64_t*>(a.cand + (rowid * a.S + c) * kCandCap) + woff;
-    for (int i = lane; i < int(cw); i += 64) out[i] = sm_list[w][i];
+    for (int i = lane; i < int(cw); i += 64) st64<COH>(out + i, sm_list[w][i]);
   }
   if (tid == 0) {
     const double s_rest = ((sm_ws[0] + sm_ws[1]) + (sm_ws[2] + sm_ws[3])) * double(sp.fix);
     uint64_t* wp = reinterpret_cast<uint64_t*>(a.part + rowid * a.S + c);
-    wp[0] = uint64_t(__float_as_uint(mc)) | (uint64_t(t0) << 32);
-    wp[1] = dbits(s_rest);
-    wp[2] = overflow ? kOverflow : uint64_t(uint32_t(n));
+    st64<COH>(wp, uint64_t(__float_as_uint(mc)) | (uint64_t(t0) << 32));
+    st64<COH>(wp + 1, dbits(s_rest));
+    st64<COH>(wp + 2, overflow ? kOverflow : uint64_t(uint32_t(n)));
   }
 }
 

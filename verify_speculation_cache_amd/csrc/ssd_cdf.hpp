@@ -42,7 +42,7 @@ __device__ __forceinline__ void chunk_crossing(MassFn mass, int S, double target
   }
 }
 
-template <int DT, int NROW>
+template <int DT, int NROW, int PT = kPerThread>
 struct PickLds {
   double scan[4];
   int pick[4];
@@ -50,26 +50,27 @@ struct PickLds {
   double base;
   int lastpos;
   int tok;
-  float vals[kPerThread];   // the crossing thread's masses, token order
+  float vals[PT];   // the crossing thread's masses, token order
 };
 
-// Token pick inside chunk [c0, c0 + 8192) whose running mass starts at
-// `pre`: every thread owns 32 consecutive tokens of NROW rows (raw vectors in
-// cv, contiguous layout); value(x, idx) is the mass of token idx from its
-// NROW logits x. Thread totals are scanned in double; the crossing thread
-// then recomputes its 32 masses from the vectors it still holds and hands
-// them to wave 0 through LDS for a parallel rescan (no second memory round
-// trip; the same values as in the totals, bit for bit). If rounding keeps
+// Token pick inside chunk [c0, c0 + 256 PT) whose running mass starts at
+// `pre`: every thread owns PT (32 or 64) consecutive tokens of NROW rows (raw
+// vectors in cv, contiguous layout); value(x, idx) is the mass of token idx
+// from its NROW logits x. Thread totals are scanned in double; the crossing
+// thread then recomputes its PT masses from the vectors it still holds and
+// hands them to wave 0 through LDS for a parallel rescan (no second memory
+// round trip; the same values as in the totals, bit for bit). If rounding keeps
 // the running mass at or below `target` through a run, the run's last token
 // with mass is taken (the chunk's, if no thread crosses). Called by every
 // thread of the workgroup; returns the token (-1: no mass).
-template <int DT, int NROW, class ValueFn>
-__device__ __forceinline__ int chunk_pick(const ChunkVecs<DT, false> (&cv)[NROW], int64_t c0, double pre,
-                                          double target, ValueFn value, PickLds<DT, NROW>& L) {
+template <int DT, int NROW, int PT, class ValueFn>
+__device__ __forceinline__ int chunk_pick(const ChunkVecs<DT, false, PT> (&cv)[NROW], int64_t c0, double pre,
+                                          double target, ValueFn value, PickLds<DT, NROW, PT>& L) {
+  static_assert(PT <= 64, "the rescan holds one token per lane");
   constexpr int PV = Dt<DT>::kPerVec;
-  constexpr int NV = kPerThread / PV;
+  constexpr int NV = PT / PV;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int i0 = int(c0) + tid * kPerThread;
+  const int i0 = int(c0) + tid * PT;
   double tot = 0.0;
   int lastpos = -1;
 #pragma unroll
@@ -123,11 +124,11 @@ __device__ __forceinline__ int chunk_pick(const ChunkVecs<DT, false> (&cv)[NROW]
     }
     __syncthreads();
     if (w == 0) {
-      const int q = lane & 31;
-      const int f0 = int(c0) + first * kPerThread;
+      const int q = lane & (PT - 1);
+      const int f0 = int(c0) + first * PT;
       const float v = L.vals[q];
-      const double cum = L.base + wave_incl_scan_d(lane < 32 ? double(v) : 0.0, lane);
-      const uint64_t cr = __ballot(lane < 32 && cum > target);
+      const double cum = L.base + wave_incl_scan_d(lane < PT ? double(v) : 0.0, lane);
+      const uint64_t cr = __ballot(lane < PT && cum > target);
       if (lane == 0) L.tok = f0 + (cr ? __ffsll((unsigned long long)cr) - 1 : L.lastpos);
     }
   } else {

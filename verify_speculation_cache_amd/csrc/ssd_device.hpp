@@ -485,6 +485,30 @@ __device__ __forceinline__ void dev_store(uint64_t* p, uint64_t v) {
 __device__ __forceinline__ uint64_t dev_load(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void dev_store32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t dev_load32(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Loads and stores of data exchanged between workgroups of one launch
+// (COH: device-scope, as dev_load / dev_store) or only across launches
+// (plain: kernel boundaries make them visible).
+template <bool COH>
+__device__ __forceinline__ uint64_t ld64(const uint64_t* p) {
+  if constexpr (COH) return dev_load(p);
+  else return *p;
+}
+template <bool COH>
+__device__ __forceinline__ void st64(uint64_t* p, uint64_t v) {
+  if constexpr (COH) dev_store(p, v);
+  else *p = v;
+}
+template <bool COH>
+__device__ __forceinline__ void st32(int32_t* p, int32_t v) {
+  if constexpr (COH) dev_store32(reinterpret_cast<uint32_t*>(p), uint32_t(v));
+  else *p = v;
+}
 __device__ __forceinline__ uint64_t pack2(float a, float b) {
   return uint64_t(__float_as_uint(a)) | (uint64_t(__float_as_uint(b)) << 32);
 }

@@ -298,9 +298,7 @@ struct RoundResidArgs {
 };
 
 // Launchers (return the hipError_t of the launch).
-hipError_t launch_stats(const StatsArgs& a, int dtype, hipStream_t st);
 hipError_t launch_stats_chunks(const StatsArgs& a, int dtype, hipStream_t st);
-hipError_t launch_resid(const ResidArgs& a, int dtype, bool sigma, hipStream_t st);
 hipError_t launch_cache(const CacheArgs& a, int dtype, hipStream_t st);
 hipError_t launch_lookup(const LookupArgs& a, hipStream_t st);
 hipError_t launch_sample(const SampleArgs& a, int dtype, hipStream_t st);
@@ -311,5 +309,6 @@ hipError_t launch_tree_round(const TreeArgs& a, int dtype, bool first, hipStream
 hipError_t launch_round_chunks(const RoundArgs& a, int dtype, hipStream_t st);
 hipError_t launch_cache_merge(const CacheArgs& a, int dtype, hipStream_t st);
 hipError_t launch_round_resid(const RoundResidArgs& a, int dtype, bool sigma, hipStream_t st);
+hipError_t launch_rows_resid(const RoundResidArgs& a, int dtype, bool sigma, hipStream_t st);
 
 }  // namespace ssd

@@ -19,24 +19,33 @@
 // that chunk with positive mass is taken. With no residual mass at all the
 // draw uses p (e_t) instead; with no mass in p either the token is -1.
 #include "ssd_resid.hpp"
+#include "ssd_stats.hpp"
 
 namespace ssd {
 
+// ssd_residual_sample's draw, after the statistics chunk pass over the row
+// pair of each batch row (rows mode): every workgroup of batch row b merges
+// the pair's partials itself (a few hundred bytes) before its share of the
+// draw, so no workgroup of the chunk pass waits on a counter.
 template <int DT, bool SIG>
-__global__ __launch_bounds__(kThreads) void k_resid(ResidArgs a) {
-  const int S2 = (a.S + 1) / 2;
+__global__ __launch_bounds__(kThreads) void k_rows_resid(RoundResidArgs a) {
+  __shared__ float e_piv[2];
+  __shared__ double e_s[2];
+  __shared__ RowInfo sm_inf;
+  const int S2 = (a.r.S + 1) / 2;
   const int b = blockIdx.x / S2;
-  resid_row_wg<DT, SIG>(a, a.info[b], b, blockIdx.x - b * S2);
+  const RowInfo inf = rows_mode_info(a.s, b, e_piv, e_s, &sm_inf);
+  resid_row_wg<DT, SIG>(a.r, inf, b, blockIdx.x - b * S2);
 }
 
-hipError_t launch_resid(const ResidArgs& a, int dtype, bool sigma, hipStream_t st) {
-  const unsigned grid = unsigned(int64_t(a.B) * ((a.S + 1) / 2));
+hipError_t launch_rows_resid(const RoundResidArgs& a, int dtype, bool sigma, hipStream_t st) {
+  const unsigned grid = unsigned(int64_t(a.r.B) * ((a.r.S + 1) / 2));
   if (dtype == SSD_BF16) {
-    if (sigma) hipLaunchKernelGGL((k_resid<1, true>), dim3(grid), dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((k_resid<1, false>), dim3(grid), dim3(kThreads), 0, st, a);
+    if (sigma) hipLaunchKernelGGL((k_rows_resid<1, true>), dim3(grid), dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((k_rows_resid<1, false>), dim3(grid), dim3(kThreads), 0, st, a);
   } else {
-    if (sigma) hipLaunchKernelGGL((k_resid<0, true>), dim3(grid), dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((k_resid<0, false>), dim3(grid), dim3(kThreads), 0, st, a);
+    if (sigma) hipLaunchKernelGGL((k_rows_resid<0, true>), dim3(grid), dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((k_rows_resid<0, false>), dim3(grid), dim3(kThreads), 0, st, a);
   }
   return hipGetLastError();
 }

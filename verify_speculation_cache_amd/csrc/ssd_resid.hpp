@@ -220,31 +220,21 @@ __device__ __forceinline__ int resid_pick(const ResidConsts& k, const typename D
                            [&](const float (&x)[2], int idx) { return resid_elem<SIG>(k, x[0], x[1], idx); }, pk);
 }
 
-// The residual / bonus draw of batch row b by one of its (S+1)/2 workgroups
-// (c2: its chunk pair), given the row's RowInfo as written by the accept
-// scan. Every thread calls it.
+// Row pointers and constants of the draw of batch row b described by inf
+// (validated: a row index the accept scan could not have written is taken
+// as a flagged row, so stale state can never address outside the inputs).
 template <int DT, bool SIG>
-__device__ __forceinline__ void resid_row_wg(const ResidArgs& a, RowInfo inf, int b, int c2) {
+__device__ __forceinline__ void resid_setup(const ResidArgs& a, RowInfo& inf, int b, ResidConsts& k,
+                                            const typename Dt<DT>::T*& rowT, const typename Dt<DT>::T*& rowD) {
   using T = typename Dt<DT>::T;
-  __shared__ double sm_pair[16];
-  __shared__ int sm_last;
-  __shared__ double sm_pre, sm_target;
-  __shared__ int sm_c, sm_useres;
-  __shared__ PickLds<DT, 2> sm_pk;
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int S2 = (a.S + 1) / 2;   // workgroups per batch row, two 8192-chunks each
-  // Only trust a row index the stats kernel could have written: anything
-  // else (a workspace that was not zero-filled for this shape) is treated
-  // as a flagged row, so stale state can never address outside the inputs.
   if (inf.a < -1 || inf.a > a.K) inf.a = -1;
   if (inf.a == a.K || a.draft == nullptr) inf.bonus = 1;
 
   // A bonus row has no draft: it reads the target row twice with rho = 0,
   // so both rows take the same load and arithmetic path.
-  ResidConsts k{};
-  const T* rowT = nullptr;
-  const T* rowD = nullptr;
+  k = ResidConsts{};
+  rowT = nullptr;
+  rowD = nullptr;
   if (inf.a >= 0) {
     rowT = static_cast<const T*>(a.target) + int64_t(b) * a.tb + int64_t(inf.a) * a.V;
     k.thr_val = value_of_key<DT>(inf.thr_key);
@@ -261,8 +251,20 @@ __device__ __forceinline__ void resid_row_wg(const ResidArgs& a, RowInfo inf, in
   }
   // sigma thresholds that admit no entry (key above that of +inf)
   if (SIG && inf.thr_key > key_of<DT>(__builtin_inff())) k.thr_val = __builtin_nanf("");
+}
 
-  // ---------------- phase A: chunk masses ----------------
+// Phase A of the draw of batch row b by its workgroup c2 (chunk pair c2):
+// the residual and target masses of the two 8192-chunks, left in a.cmass by
+// thread 0 with device-scope stores. Every thread calls it.
+template <int DT, bool SIG>
+__device__ __forceinline__ void resid_phase_a(const ResidArgs& a, RowInfo inf, int b, int c2) {
+  using T = typename Dt<DT>::T;
+  __shared__ double sm_pair[16];
+  const int tid = threadIdx.x;
+  ResidConsts k;
+  const T* rowT;
+  const T* rowD;
+  resid_setup<DT, SIG>(a, inf, b, k, rowT, rowD);
   if (inf.a >= 0) {
     double R[2], P[2];
     resid_chunk_masses2<DT, SIG>(k, rowT, rowD, int64_t(c2) * kStatsChunk, a.V, sm_pair, R, P);
@@ -277,10 +279,43 @@ __device__ __forceinline__ void resid_row_wg(const ResidArgs& a, RowInfo inf, in
       }
     }
   }
+}
 
-  if (!arrive_last(&a.cnt[int64_t(b) * kCntStride], uint32_t(S2), &sm_last)) return;
+// Phase A for the single 8192-chunk c of batch row b (half the registers of
+// the chunk-pair form).
+template <int DT, bool SIG>
+__device__ __forceinline__ void resid_phase_a1(const ResidArgs& a, RowInfo inf, int b, int c) {
+  using T = typename Dt<DT>::T;
+  __shared__ double sm_pair[8];
+  ResidConsts k;
+  const T* rowT;
+  const T* rowD;
+  resid_setup<DT, SIG>(a, inf, b, k, rowT, rowD);
+  if (inf.a >= 0) {
+    double R, P;
+    resid_chunk_masses<DT, SIG>(k, rowT, rowD, int64_t(c) * kChunk, a.V, sm_pair, R, P);
+    if (threadIdx.x == 0) {
+      uint64_t* wp = reinterpret_cast<uint64_t*>(a.cmass + (int64_t(b) * a.S + c) * 2);
+      dev_store(wp, dbits(R));
+      dev_store(wp + 1, dbits(P));
+    }
+  }
+}
 
-  // ---------------- phase B: last workgroup of batch row b ----------------
+// Phase B of the draw of batch row b, once every chunk mass of the row is in
+// a.cmass: the chunk holding u * Z, then the token inside it (and the cache
+// hit when a lookup is attached). Every thread calls it.
+template <int DT, bool SIG>
+__device__ __forceinline__ void resid_phase_b(const ResidArgs& a, RowInfo inf, int b) {
+  using T = typename Dt<DT>::T;
+  __shared__ double sm_pre, sm_target;
+  __shared__ int sm_c, sm_useres;
+  __shared__ PickLds<DT, 2> sm_pk;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  ResidConsts k;
+  const T* rowT;
+  const T* rowD;
+  resid_setup<DT, SIG>(a, inf, b, k, rowT, rowD);
   if (inf.a < 0) {
     if (tid == 0 && !a.tok_at_a) {
       a.tok_out[int64_t(b) * a.tok_stride] = -1;
@@ -297,7 +332,10 @@ __device__ __forceinline__ void resid_row_wg(const ResidArgs& a, RowInfo inf, in
   int32_t seg_tok = -1;
   if (a.hit && w == 0) {
     const int n = a.lk_F[inf.a];
-    seg_tok = lane < n ? a.cache_tokens[int64_t(b) * a.sumF + a.lk_off[inf.a] + lane] : -1;
+    // device-scope: the cache may come from another workgroup of this launch
+    seg_tok = lane < n ? int32_t(dev_load32(reinterpret_cast<const uint32_t*>(a.cache_tokens) +
+                                            int64_t(b) * a.sumF + a.lk_off[inf.a] + lane))
+                       : -1;
   }
   // chunk masses, then the first chunk whose running mass exceeds u * Z
   if (w == 0) {
@@ -329,6 +367,19 @@ __device__ __forceinline__ void resid_row_wg(const ResidArgs& a, RowInfo inf, in
       if (a.slot) a.slot[b] = m != 0 ? __ffsll((unsigned long long)m) - 1 : -1;
     }
   }
+}
+
+// The residual / bonus draw of batch row b by one of its (S+1)/2 workgroups
+// (c2: its chunk pair), given the row's RowInfo as written by the accept
+// scan: phase A, then phase B in the workgroup that arrives last. Every
+// thread calls it; returns true in the workgroup that finished the row.
+template <int DT, bool SIG>
+__device__ __forceinline__ bool resid_row_wg(const ResidArgs& a, RowInfo inf, int b, int c2) {
+  __shared__ int sm_last;
+  resid_phase_a<DT, SIG>(a, inf, b, c2);
+  if (!arrive_last(&a.cnt[int64_t(b) * kCntStride], uint32_t((a.S + 1) / 2), &sm_last)) return false;
+  resid_phase_b<DT, SIG>(a, inf, b);
+  return true;
 }
 
 }  // namespace ssd

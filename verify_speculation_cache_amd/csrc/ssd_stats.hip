@@ -1,20 +1,11 @@
-// Row statistics and the accept scan: the kernels and their launchers; the
-// device code is in ssd_stats.hpp.
+// The row-statistics chunk pass: kernel and launcher; the device code is in
+// ssd_stats.hpp.
 #include "ssd_stats.hpp"
 
 namespace ssd {
 
-template <int DT>
-__global__ __launch_bounds__(kThreads) void k_stats(StatsArgs a) {
-  __shared__ int sm_last;
-  stats_chunk_wg<DT>(a, blockIdx.x);
-  const int b = blockIdx.x / (a.NR * a.S);
-  if (!arrive_last(&a.cnt[int64_t(b) * kCntStride], uint32_t(a.NR * a.S), &sm_last)) return;
-  stats_epilogue<DT>(a, b);
-}
-
-// The chunk pass alone: partials and gathered logits for a consumer in a
-// later launch that merges them itself (the verify path's residual kernel).
+// The chunk pass: partials and gathered logits for a consumer in a later
+// launch that merges them itself (the residual kernels).
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_stats_chunks(StatsArgs a) {
   stats_chunk_wg<DT>(a, blockIdx.x);
@@ -26,15 +17,6 @@ hipError_t launch_stats_chunks(const StatsArgs& a, int dtype, hipStream_t st) {
     hipLaunchKernelGGL(k_stats_chunks<1>, dim3(unsigned(grid)), dim3(kThreads), 0, st, a);
   else
     hipLaunchKernelGGL(k_stats_chunks<0>, dim3(unsigned(grid)), dim3(kThreads), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_stats(const StatsArgs& a, int dtype, hipStream_t st) {
-  const int64_t grid = int64_t(a.B) * a.NR * a.S;
-  if (dtype == SSD_BF16)
-    hipLaunchKernelGGL(k_stats<1>, dim3(unsigned(grid)), dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(k_stats<0>, dim3(unsigned(grid)), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

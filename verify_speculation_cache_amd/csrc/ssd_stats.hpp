@@ -65,22 +65,16 @@ __device__ __forceinline__ void load_sigma(const StatsArgs& a, int b, int i, dou
   tk.idx = int32_t(uint32_t(t >> 32));
 }
 
-// The chunk pass of one workgroup: blk = (b * NR + r) * S + c, chunks of
-// kThreads * PT entries (a.S of them per row). Partials and gathered logits
-// are left with device-scope stores by thread 0.
+// The chunk pass of one workgroup over chunk c of logit row r of batch row
+// b (chunks of kThreads * PT entries, a.S of them per row). The partial and
+// any gathered logits are left with device-scope stores by thread 0.
 template <int DT, int PT = kStatsPerThread>
-__device__ __forceinline__ void stats_chunk_wg(const StatsArgs& a, uint32_t blk) {
+__device__ __forceinline__ void stats_chunk_at(const StatsArgs& a, int b, int r, int c) {
   constexpr int kSpan = kThreads * PT;
   __shared__ float sm_f[4];
   __shared__ double sm_s[4];
 
   const int tid = threadIdx.x;
-  const int per_b = a.NR * a.S;
-  const int b = blk / per_b;
-  const int rem = blk - b * per_b;
-  const int r = rem / a.S;
-  const int c = rem - r * a.S;
-
   const typename Dt<DT>::T* row = stats_row_ptr<DT>(a, b, r);
   if (row != nullptr) {  // uniform per workgroup
     using CV = ChunkVecs<DT, true, PT>;
@@ -108,6 +102,17 @@ __device__ __forceinline__ void stats_chunk_wg(const StatsArgs& a, uint32_t blk)
       if (owns) dev_store(a.zg + int64_t(b) * a.K + r, pack2(gzt, gzd));
     }
   }
+}
+
+// The same for workgroup blk = (b * NR + r) * S + c of a one-chunk-per-
+// workgroup grid.
+template <int DT, int PT = kStatsPerThread>
+__device__ __forceinline__ void stats_chunk_wg(const StatsArgs& a, uint32_t blk) {
+  const int per_b = a.NR * a.S;
+  const int b = blk / per_b;
+  const int rem = blk - b * per_b;
+  const int r = rem / a.S;
+  stats_chunk_at<DT, PT>(a, b, r, rem - r * a.S);
 }
 
 // Row max pivots and sums of the a.NR logit rows of batch row b, merged
@@ -266,56 +271,49 @@ __device__ __forceinline__ void write_row_lse(const StatsArgs& a, int b, const f
   }
 }
 
-// Epilogue of batch row b (run by the last workgroup to finish its chunks):
-// the accept scan (verify) or the record of the row to sample from (rows
-// mode); leaves a RowInfo for the residual kernel.
-template <int DT>
-__device__ __forceinline__ void stats_epilogue(const StatsArgs& a, int b) {
-  __shared__ float e_piv[kMaxRows];
-  __shared__ double e_s[kMaxRows];
-  const int tid = threadIdx.x;
+// RowInfo of the draw ssd_residual_sample makes for batch row b (rows mode:
+// logit row 0 = target row j = rows_in[b], row 1 = draft row j): merges the
+// two rows' chunk partials (loaded with device-scope loads) and takes the
+// sigma statistics of draft row j when sigma is given. Every thread calls
+// it; the result is returned in every thread (through *sm_inf, one barrier).
+__device__ __forceinline__ RowInfo rows_mode_info(const StatsArgs& a, int b, float* e_piv, double* e_s,
+                                                  RowInfo* sm_inf) {
   const int K = a.K;
-
-  if (a.mode == kModeRows) {
-    merge_row_partials(a, b, e_piv, e_s);
-    __syncthreads();
-    if (tid == 0) {
-      RowInfo inf{};
-      const int j = a.rows_in[b];
-      inf.C = 1.0f;
-      inf.thr_key = 0xFFFFFFFFu;
-      inf.thr_idx = -1;
-      if (j < 0 || j > K) {
-        inf.a = -1;
-      } else {
-        inf.a = j;
-        inf.bonus = (a.use_draft && j < K) ? 0 : 1;
-        inf.piv_t = e_piv[0];
-        inf.s_t = e_s[0];
-        if (!inf.bonus) {
-          if (a.use_sigma) {
-            double z0, st1, st2;
-            ssd_rowkey tk;
-            load_sigma(a, b, j, z0, st1, st2, tk);
-            inf.piv_d = pivot_of(float(z0));
-            inf.s_d = double(a.C) * st1 + st2;
-            inf.thr_key = tk.key;
-            inf.thr_idx = tk.idx;
-            inf.C = a.C;
-          } else {
-            inf.piv_d = e_piv[1];
-            inf.s_d = e_s[1];
-          }
+  merge_row_partials(a, b, e_piv, e_s);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    RowInfo inf{};
+    const int j = a.rows_in[b];
+    inf.C = 1.0f;
+    inf.thr_key = 0xFFFFFFFFu;
+    inf.thr_idx = -1;
+    if (j < 0 || j > K) {
+      inf.a = -1;
+    } else {
+      inf.a = j;
+      inf.bonus = (a.use_draft && j < K) ? 0 : 1;
+      inf.piv_t = e_piv[0];
+      inf.s_t = e_s[0];
+      if (!inf.bonus) {
+        if (a.use_sigma) {
+          double z0, st1, st2;
+          ssd_rowkey tk;
+          load_sigma(a, b, j, z0, st1, st2, tk);
+          inf.piv_d = pivot_of(float(z0));
+          inf.s_d = double(a.C) * st1 + st2;
+          inf.thr_key = tk.key;
+          inf.thr_idx = tk.idx;
+          inf.C = a.C;
+        } else {
+          inf.piv_d = e_piv[1];
+          inf.s_d = e_s[1];
         }
       }
-      a.info[b] = inf;
     }
-    return;
+    *sm_inf = inf;
   }
-
-  const RowInfo inf = accept_scan<DT, false>(a, b, true, e_piv, e_s, nullptr);
-  if (tid == 0) a.info[b] = inf;
-  write_row_lse(a, b, e_piv, e_s);
+  __syncthreads();
+  return *sm_inf;
 }
 
 }  // namespace ssd
