@@ -163,30 +163,11 @@ def main():
         S.ssd_verify(tgts[j], dfts[j], toks, ua, ur, tau, S.sigma_from_cache(cache, C), out=res)
         S.ssd_cache_lookup(cache["cache_tokens"], F, res["accepted"], res["out_tokens"], out=look)
 
-    stream = torch.cuda.Stream()
-    graphs = []
-    if not args.eager:
-        stream.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(stream):
-            for j in range(ncopy):     # warm the per-shape workspaces on this stream
-                step(j)
-        torch.cuda.synchronize()
-        for j in range(ncopy):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                step(j)
-            graphs.append(g)
-        torch.cuda.synchronize()
+    def host_row(j):
+        F_host = S.ssd_fanout(cfg.n_budget, K, cfg.a_p, cfg.r)   # host row of the step
+        assert F_host == F
 
-    def run(n, offset=0):
-        for i in range(n):
-            j = (offset + i) % ncopy
-            F_host = S.ssd_fanout(cfg.n_budget, K, cfg.a_p, cfg.r)   # host row of the step
-            assert F_host == F
-            if graphs:
-                graphs[j].replay()
-            else:
-                step(j)
+    run = _replay_runner(step, ncopy, args, per_step=host_row)
 
     run(args.warmup)
     torch.cuda.synchronize()
@@ -439,35 +420,62 @@ def bench_report(args):
         torch.cuda.empty_cache()
 
 
-def _graph_time(step, ncopy, args):
-    """Capture step(j) for every rotating copy j as a HIP graph (after one
-    eager warm-up of the per-shape workspaces on the capture stream), replay
-    args.warmup untimed then args.steps timed, HIP events around the loop.
-    Returns ms per step."""
+def _replay_runner(step, ncopy, args, per_step=None):
+    """Return run(n, offset) that performs n steps over the rotating copies,
+    copy (offset + i) % ncopy at step i.
+
+    Unless args.eager, the steps run as HIP graph replays: one graph holds a
+    whole cycle step(0) .. step(ncopy - 1), so a launch is paid once per
+    ncopy steps, and one graph per copy serves the steps that do not start
+    or fill a whole cycle. Every step still runs, in order, exactly once.
+    The per-shape workspaces are warmed eagerly on the capture stream first.
+    per_step(j), if given, runs on the host for every step."""
     import torch
-    stream = torch.cuda.Stream()
-    graphs = []
+    whole, single = None, []
     if not args.eager:
+        stream = torch.cuda.Stream()
         stream.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(stream):
             for j in range(ncopy):
                 step(j)
         torch.cuda.synchronize()
+        whole = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(whole, stream=stream):
+            for j in range(ncopy):
+                step(j)
         for j in range(ncopy):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
                 step(j)
-            graphs.append(g)
+            single.append(g)
         torch.cuda.synchronize()
 
     def run(n, offset=0):
-        for i in range(n):
+        i = 0
+        while i < n:
             j = (offset + i) % ncopy
-            if graphs:
-                graphs[j].replay()
-            else:
+            if per_step is not None:
+                per_step(j)
+            if whole is None:
                 step(j)
+                i += 1
+            elif j == 0 and n - i >= ncopy:
+                if per_step is not None:
+                    for jj in range(1, ncopy):
+                        per_step(jj)
+                whole.replay()
+                i += ncopy
+            else:
+                single[j].replay()
+                i += 1
+    return run
 
+
+def _graph_time(step, ncopy, args):
+    """Time args.steps steps (after args.warmup untimed ones) through
+    _replay_runner, HIP events around the loop. Returns ms per step."""
+    import torch
+    run = _replay_runner(step, ncopy, args)
     run(args.warmup)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -410,14 +410,16 @@ def ssd_build_cache(draft, tau: float, F: Sequence[int], *, out: Optional[dict] 
     if len(F) < 2:
         raise ValueError("F needs K+1 >= 2 entries")
     if out is None:
-        out = {"cache_tokens": torch.empty(B, max(sumF, 1), dtype=torch.int32, device=dev),
+        out = {"cache_tokens": torch.empty(B, sumF, dtype=torch.int32, device=dev),
                "thr": torch.empty(B, K + 1, 2, dtype=torch.int32, device=dev),
                "draft_stats": torch.empty(B, K + 1, 3, dtype=torch.float64, device=dev)}
     Fa = (ctypes.c_int32 * (K + 1))(*[int(f) for f in F])
     ws, wsz = _workspace(ssd_build_cache_workspace_size(B, K, V, dt), dev, ("cache", B, K, V, dt), stream)
-    _check(lib().ssd_build_cache(dp, db, dt, B, K, V, float(tau), Fa,
-                                 out["cache_tokens"].data_ptr(), out["thr"].data_ptr(),
-                                 out["draft_stats"].data_ptr(), ws, wsz, _stream(stream)))
+    _check(lib().ssd_build_cache(
+        dp, db, dt, B, K, V, float(tau), Fa,
+        _dev(out["cache_tokens"], torch.int32, (B, sumF), "cache_tokens") if sumF > 0 else None,
+        _dev(out["thr"], torch.int32, (B, K + 1, 2), "thr"),
+        _dev(out["draft_stats"], torch.float64, (B, K + 1, 3), "draft_stats"), ws, wsz, _stream(stream)))
     out["F"] = list(F)
     return out
 
@@ -437,7 +439,7 @@ def ssd_cache_lookup(cache_tokens, F: Sequence[int], accepted, out_tokens, *, ou
         out = {"hit": torch.empty(B, dtype=torch.uint8, device=dev),
                "slot": torch.empty(B, dtype=torch.int32, device=dev)}
     Fa = (ctypes.c_int32 * (K + 1))(*[int(f) for f in F])
-    _check(lib().ssd_cache_lookup(cache_tokens.data_ptr(), Fa, B, K,
+    _check(lib().ssd_cache_lookup(cache_tokens.data_ptr() if sum(F) > 0 else None, Fa, B, K,
                                   _dev(accepted, torch.int32, (B,), "accepted"),
                                   _dev(out_tokens, torch.int32, (B, K + 1), "out_tokens"),
                                   out["hit"].data_ptr(), out["slot"].data_ptr(), _stream(stream)))
