@@ -246,6 +246,33 @@ def test_cache_ties_and_limits(S):
     _cache_case(S, d, [5, 64, 1, 33], 0.2, label="ties-f32")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_cache_masked_full_chunks(S, dtype):
+    """Full 8192-entry chunks whose lanes are mostly or wholly masked: the
+    chunk bound must stay valid with -inf lane maxima (rows with 99 % of
+    the tokens masked, a wholly masked first chunk, a chunk with two finite
+    tokens, and negative-only and positive-only rows)."""
+    log(f"[gpu] cache masked full chunks {dtype}")
+    B, K, V = 6, 3, 3 * 8192 + 77
+    rng = np.random.default_rng(4242)
+    d = _random_case(4243, B, K, V, "f32", 0.9, Kd=K + 1)
+    dr = d["draft"]
+    dr[0][rng.random((K + 1, V)) < 0.99] = -np.inf
+    dr[1, :, :8192] = -np.inf
+    dr[2, :, 8192:16384] = -np.inf
+    dr[2, :, 8192 + 5] = 1.5
+    dr[2, :, 8192 + 4000] = -7.25
+    dr[3] = -np.abs(dr[3]) - 1.0
+    dr[4] = np.abs(dr[4]) + 1.0
+    dr[5][rng.random((K + 1, V)) < 0.5] = -np.inf
+    if dtype == "bf16":
+        d["target"], d["draft"] = W.f32_to_bf16_bits(d["target"]), W.f32_to_bf16_bits(dr)
+    for b in range(B):   # drafts from the masked rows (token 0 for a row without mass)
+        for i in range(K):
+            d["tokens"][b, i] = max(O.sample_draft(d["draft"][b, i], d["tau"], rng.random()), 0)
+    _cache_case(S, d, [64, 13, 1, 0], 0.3, label=f"masked-{dtype}")
+
+
 @pytest.mark.parametrize("K,F", [(64, [5] * 65), (4, [64] * 5), (3, [0, 10, 0, 64]), (1, [1, 0])])
 def test_cache_lookup_direct(S, K, F):
     """Lookup against the oracle on synthetic caches: rows whose cache holds

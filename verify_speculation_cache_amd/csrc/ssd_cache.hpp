@@ -18,10 +18,14 @@
 // Thresholds. Any key t such that at least F lanes of a chunk hold an entry
 // >= t (their lane maximum) bounds the chunk's F-th largest entry from
 // below, and so the row's: an entry below it can never be in the top F. In a
-// wave (2048 entries, 32 per lane) let Q_w be the ceil(F/4)-th largest lane
-// maximum; min_w Q_w is such a bound (4 x ceil(F/4) >= F lanes) and is the
-// chunk's T0. (The F-th largest lane maximum of one wave, max over waves, is
-// another; on the synthetic rows it kept 3 % fewer candidates, and its
+// wave (2048 entries, 32 per lane) let Q_w be any value that at least
+// ceil(F/4) lane maxima reach; min_w Q_w is such a bound (4 x ceil(F/4) >= F
+// lanes) and is the chunk's T0. The tightest Q_w is the ceil(F/4)-th largest
+// lane maximum; a full chunk settles for a few bisection steps towards it
+// (about 21 candidates per chunk on the B=64 K=5 rows against 19 for the
+// exact value, for far fewer serial steps), a partial chunk finds it
+// exactly. (The F-th largest lane maximum of one wave, max over waves, is
+// another bound; on the synthetic rows it kept 3 % fewer candidates, and its
 // bitwise search cost more than that saved.)
 //
 // Two launches.
@@ -614,6 +618,22 @@ __device__ __forceinline__ uint32_t wave_compact(const float (&x)[kPerThread], f
   return cw;
 }
 
+constexpr int kBisectSteps = 5;   // value bisection steps of a full chunk's per-wave bound
+
+// Largest key of the dtype whose value is <= v (v not NaN). For bfloat16
+// the float key's top half is that key when the low half is 0xFFFF (a
+// negative value that is exactly a bfloat16) or the value is positive;
+// otherwise a negative v lies strictly between two bfloat16 values and the
+// next smaller one is one key below.
+template <int DT> __device__ __forceinline__ uint32_t floor_key(float v);
+template <> __device__ __forceinline__ uint32_t floor_key<0>(float v) { return key_of<0>(v); }
+template <> __device__ __forceinline__ uint32_t floor_key<1>(float v) {
+  const uint32_t k32 = key_of<0>(v);
+  uint32_t k = k32 >> 16;
+  if (k32 < 0x80000000u && (k32 & 0xFFFFu) != 0xFFFFu) k -= 1u;
+  return k;
+}
+
 // The chunk pass of one workgroup; blk = (b * (K+1) + k) * S + c. COH: the
 // record and candidates are read by a merge in the same launch, so they are
 // stored with device-scope stores.
@@ -666,18 +686,40 @@ __device__ __forceinline__ void cache_chunk_wg(const CacheArgs& a, uint32_t blk)
 
   // ---- per-wave max and threshold; chunk max and T0 ----
   // A key t with at least F lanes whose maximum is >= t bounds the chunk's
-  // top F from below. Each wave finds its ceil(F/4)-th largest lane maximum
-  // (bitwise search over the lanes' keys); the smallest over the four waves
-  // is such a bound (4 x ceil(F/4) >= F lanes). It is the chunk's T0.
-  // Every lane's key lies between the wave's smallest key and the key of
-  // its maximum, so all keys share those two keys' common leading bits, and
-  // the full search would set exactly those: it starts from that prefix and
-  // tests only the bits below it (same result, typically half the steps;
-  // lanes past the row end have key 0, which leaves no common prefix).
+  // top F from below. Each wave finds a key that ceil(F/4) of its lane
+  // maxima reach; the smallest over the four waves is such a bound (4 x
+  // ceil(F/4) >= F lanes). It is the chunk's T0.
+  // In the exact search every lane's key lies between the wave's smallest
+  // key and the key of its maximum, so all keys share those two keys'
+  // common leading bits, and the full search would set exactly those: it
+  // starts from that prefix and tests only the bits below it (same result,
+  // typically half the steps; lanes past the row end have key 0, which
+  // leaves no common prefix).
   {
     const float wm = wave_max_u(lm);
     uint32_t tq = 0;
-    if (F > 0) {
+    if (F > 0 && nvalid == kChunk) {
+      // Full chunk: five bisection steps on values between the wave's
+      // smallest finite and largest lane maximum. lo starts at a value at
+      // least Fq lanes reach (the smallest finite lane maximum, or -inf when
+      // fewer than Fq lanes have a finite entry) and only ever takes a
+      // midpoint that at least Fq lanes reach, so it stays a valid bound;
+      // its key is rounded down to a logit of the row's dtype. A handful
+      // of steps keeps the candidates within a few of the exact bound's.
+      const int Fq = (F + 3) >> 2;
+      float lo = -wave_max_u(lm > -__builtin_inff() ? -lm : -__builtin_inff()), hi = wm;
+      if (__popcll(__ballot(lm >= lo)) < Fq) lo = -__builtin_inff();
+#pragma unroll
+      for (int it = 0; it < kBisectSteps; ++it) {
+        const float mid = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(0.5f * (lo + hi))));
+        const bool ok = __popcll(__ballot(lm >= mid)) >= Fq;
+        lo = ok ? mid : lo;
+        hi = ok ? hi : mid;
+      }
+      tq = floor_key<DT>(lo);
+    } else if (F > 0) {
+      // Partial chunk (lanes past the row end hold no entry): the exact
+      // ceil(F/4)-th largest lane maximum, by a bitwise search.
       const int Fq = (F + 3) >> 2;
       const uint32_t kl = local_of<DT>(tid, 0) < nvalid ? key_of<DT>(lm) : 0u;
       const uint32_t diff = wave_min_u32(kl) ^ key_of<DT>(wm);
