@@ -163,7 +163,7 @@ ResidArgs verify_resid_args(const StatsArgs& a, const float* u_res, float* resid
   r.B = a.B;
   r.K = a.K;
   r.V = a.V;
-  r.S = int(chunks_per_row(a.V));
+  r.S = int(pick_chunks_per_row(a.V));
   r.c32 = a.c32;
   r.u = u_res;
   r.info = a.info;
@@ -325,14 +325,14 @@ SSD_API int ssd_cache_stats(const int32_t* accepted, const uint8_t* hit, int32_t
 SSD_API size_t ssd_verify_workspace_size(int32_t B, int32_t K, int32_t V, int dtype) {
   if (check_shape(B, K, V) != SSD_OK || !dtype_ok(dtype)) return 0;
   const StatsWs sw(B, 2 * K + 1, stats_chunks_per_row(V), K);
-  const ResidWs rw(B, chunks_per_row(V));
+  const ResidWs rw(B, pick_chunks_per_row(V));
   return sw.total + rw.total;
 }
 
 SSD_API size_t ssd_residual_workspace_size(int32_t B, int32_t K, int32_t V, int dtype) {
   if (check_shape(B, K, V) != SSD_OK || !dtype_ok(dtype)) return 0;
   const StatsWs sw(B, 2, stats_chunks_per_row(V), K);
-  const ResidWs rw(B, chunks_per_row(V));
+  const ResidWs rw(B, pick_chunks_per_row(V));
   return sw.total + rw.total;
 }
 
@@ -357,15 +357,15 @@ SSD_API int ssd_verify(const void* target_logits, int64_t target_bstride,
   if (!target_logits || !draft_logits || !draft_tokens || !u_acc || !u_res || !accepted || !out_tokens)
     return fail(SSD_EINVAL, "a required pointer is NULL");
   if (target_bstride < 0 || draft_bstride < 0) return fail(SSD_EINVAL, "negative batch stride");
-  const int64_t S = chunks_per_row(V);
+  const int64_t SP = pick_chunks_per_row(V);
   const int64_t SS = stats_chunks_per_row(V);
   const bool sig = sigma != nullptr;
   const int NR = sig ? K + 1 : 2 * K + 1;
   const StatsWs sw(B, 2 * K + 1, SS, K);
-  const ResidWs rw(B, S);
+  const ResidWs rw(B, SP);
   if ((st = check_ws(workspace, ws_bytes, sw.total + rw.total)) != SSD_OK) return st;
   if ((st = check_grid(int64_t(B) * NR * SS)) != SSD_OK) return st;
-  if ((st = check_grid(int64_t(B) * S)) != SSD_OK) return st;
+  if ((st = check_grid(int64_t(B) * SS)) != SSD_OK) return st;
   char* ws = static_cast<char*>(workspace);
   const StatsArgs a = verify_stats_args(target_logits, target_bstride, draft_logits, draft_bstride, B, K, V, tau,
                                         draft_tokens, u_acc, sigma, accepted, out_tokens, probs, row_lse, ws, sw);
@@ -391,13 +391,12 @@ SSD_API int ssd_residual_sample(const void* target_logits, int64_t target_bstrid
   if (!target_logits || !row || !u || !token_out) return fail(SSD_EINVAL, "a required pointer is NULL");
   if (sigma && !draft_logits) return fail(SSD_EINVAL, "sigma given without draft logits");
   if (target_bstride < 0 || draft_bstride < 0) return fail(SSD_EINVAL, "negative batch stride");
-  const int64_t S = chunks_per_row(V);
+  const int64_t SP = pick_chunks_per_row(V);
   const int64_t SS = stats_chunks_per_row(V);
   const StatsWs sw(B, 2, SS, K);
-  const ResidWs rw(B, S);
+  const ResidWs rw(B, SP);
   if ((st = check_ws(workspace, ws_bytes, sw.total + rw.total)) != SSD_OK) return st;
   if ((st = check_grid(int64_t(B) * 2 * SS)) != SSD_OK) return st;
-  if ((st = check_grid(int64_t(B) * S)) != SSD_OK) return st;
   char* ws = static_cast<char*>(workspace);
   const bool sig = sigma != nullptr;
 
@@ -440,7 +439,7 @@ SSD_API int ssd_residual_sample(const void* target_logits, int64_t target_bstrid
   r.B = B;
   r.K = K;
   r.V = V;
-  r.S = int(S);
+  r.S = int(SP);
   r.c32 = a.c32;
   r.u = u;
   r.info = a.info;
@@ -653,7 +652,7 @@ SSD_API int ssd_verify_tree(const void* target_logits, int64_t target_bstride,
 SSD_API size_t ssd_verify_round_workspace_size(int32_t B, int32_t K, int32_t V, int dtype) {
   if (check_shape(B, K, V) != SSD_OK || !dtype_ok(dtype)) return 0;
   const int64_t S = chunks_per_row(V);
-  return CacheWs(B, K, S).total + StatsWs(B, K + 1, S, K).total + ResidWs(B, S).total;
+  return CacheWs(B, K, S).total + StatsWs(B, K + 1, S, K).total + ResidWs(B, pick_chunks_per_row(V)).total;
 }
 
 SSD_API int ssd_verify_round(const void* target_logits, int64_t target_bstride,
@@ -678,7 +677,7 @@ SSD_API int ssd_verify_round(const void* target_logits, int64_t target_bstride,
   const int64_t S = chunks_per_row(V);
   const CacheWs cw(B, K, S);
   const StatsWs sw(B, K + 1, S, K);
-  const ResidWs rw(B, S);
+  const ResidWs rw(B, pick_chunks_per_row(V));
   const size_t off_s = cw.total, off_r = off_s + sw.total;
   if ((st = check_ws(workspace, ws_bytes, off_r + rw.total)) != SSD_OK) return st;
   if ((st = check_grid(int64_t(B) * (K + 1) * 2 * S)) != SSD_OK) return st;

@@ -26,6 +26,16 @@ constexpr int kStatsPerThread = 64;
 constexpr int kStatsChunk = kThreads * kStatsPerThread;   // 16384
 inline int64_t stats_chunks_per_row(int64_t V) { return (V + kStatsChunk - 1) / kStatsChunk; }
 
+// The residual / bonus draw keeps its chunk masses per 4096 entries: a
+// workgroup of its first phase covers one 16384-entry statistics span (four
+// such chunks), and the in-chunk pick of the second phase, which runs on
+// one workgroup per row with nothing else on its compute unit, has 16
+// tokens per thread to scan instead of 32.
+constexpr int kPickPerThread = 16;
+constexpr int kPickChunk = kThreads * kPickPerThread;      // 4096
+constexpr int kPicksPerSpan = kStatsChunk / kPickChunk;     // 4
+inline int64_t pick_chunks_per_row(int64_t V) { return (V + kPickChunk - 1) / kPickChunk; }
+
 // Per-(row, chunk) statistics: chunk max of the raw logits and the chunk's
 // sum of exp2((z - pivot) * log2(e)/tau), pivot = chunk max (0 if -inf).
 struct alignas(16) RowPartial {
@@ -100,7 +110,8 @@ struct ResidArgs {
   float c32;
   const float* u;
   const RowInfo* info;
-  double* cmass;       // [B, S, 2]: residual mass, target mass per chunk
+  double* cmass;       // [B, S, 2]: residual mass, target mass per chunk (S chunks of kPickChunk
+                       // for the one-path draw, of kChunk for the token-tree rounds)
   uint32_t* cnt;       // [B] (kCntStride apart)
   int32_t* tok_out;    // token written at tok_out[b * tok_stride + (tok_at_a ? a : 0)]
   int64_t tok_stride;

@@ -9,12 +9,12 @@
 //
 // Masses are in target units (ssd_resid.hpp) with rho = s_t / s_d.
 //
-// Phase A (all workgroups): one workgroup per (batch row, pair of chunks)
-// sums r and e_t over each chunk (per-thread float sums, double across
-// threads).
+// Phase A (all workgroups): one workgroup per (batch row, 16384-entry span)
+// sums r and e_t over each 4096-entry chunk of its span (per-thread float
+// sums, double across threads).
 // Phase B (last workgroup of the batch row): walks the chunk masses in order
 // to find the chunk holding u*Z, re-reads that chunk with each thread owning
-// 32 consecutive tokens, scans thread totals in double and picks the token.
+// 16 consecutive tokens, scans thread totals in double and picks the token.
 // If rounding leaves no crossing inside the chosen chunk the last token of
 // that chunk with positive mass is taken. With no residual mass at all the
 // draw uses p (e_t) instead; with no mass in p either the token is -1.
@@ -32,14 +32,14 @@ __global__ __launch_bounds__(kThreads) void k_rows_resid(RoundResidArgs a) {
   __shared__ float e_piv[2];
   __shared__ double e_s[2];
   __shared__ RowInfo sm_inf;
-  const int S2 = (a.r.S + 1) / 2;
-  const int b = blockIdx.x / S2;
+  const int nw = resid_wgs_per_row(a.r.S);
+  const int b = blockIdx.x / nw;
   const RowInfo inf = rows_mode_info(a.s, b, e_piv, e_s, &sm_inf);
-  resid_row_wg<DT, SIG>(a.r, inf, b, blockIdx.x - b * S2);
+  resid_row_wg<DT, SIG>(a.r, inf, b, blockIdx.x - b * nw);
 }
 
 hipError_t launch_rows_resid(const RoundResidArgs& a, int dtype, bool sigma, hipStream_t st) {
-  const unsigned grid = unsigned(int64_t(a.r.B) * ((a.r.S + 1) / 2));
+  const unsigned grid = unsigned(int64_t(a.r.B) * resid_wgs_per_row(a.r.S));
   if (dtype == SSD_BF16) {
     if (sigma) hipLaunchKernelGGL((k_rows_resid<1, true>), dim3(grid), dim3(kThreads), 0, st, a);
     else hipLaunchKernelGGL((k_rows_resid<1, false>), dim3(grid), dim3(kThreads), 0, st, a);

@@ -120,22 +120,27 @@ __device__ __forceinline__ void resid_chunk_masses(const ResidConsts& k, const t
   P = ((sm_pair[4] + sm_pair[5]) + (sm_pair[6] + sm_pair[7])) * double(k.fix_t);
 }
 
-// Phase A over two consecutive 8192-chunks at once (a 16384-entry span at
-// c0, 64 entries per thread, strided: vectors j < NV/2 lie in the first
-// chunk): the masses of each chunk, so the draw keeps 8192-entry chunks while
-// a workgroup moves twice the bytes per round trip. R[h], P[h] for half h are
-// returned in every thread (sm: 16 doubles of LDS; one barrier).
+// Phase A over one 16384-entry span at c0 (64 entries per thread, strided:
+// vectors j < NV/4 lie in the first 4096 entries, the next NV/4 in the
+// second, and so on): the masses of each of its four 4096-entry pick
+// chunks, so the draw's second phase scans short chunks while a workgroup
+// of the first moves 64 KiB (bf16) per round trip. R[h], P[h] for quarter h
+// are returned in every thread (sm: 32 doubles of LDS; one barrier).
 template <int DT, bool SIG>
-__device__ __forceinline__ void resid_chunk_masses2(const ResidConsts& k, const typename Dt<DT>::T* rowT,
+__device__ __forceinline__ void resid_chunk_masses4(const ResidConsts& k, const typename Dt<DT>::T* rowT,
                                                     const typename Dt<DT>::T* rowD, int64_t c0, int V,
-                                                    double* sm, double (&R)[2], double (&P)[2]) {
+                                                    double* sm, double (&R)[kPicksPerSpan],
+                                                    double (&P)[kPicksPerSpan]) {
   constexpr int PV = Dt<DT>::kPerVec;
   using CV = ChunkVecs<DT, true, kStatsPerThread>;
-  constexpr int NVH = CV::NV / 2;
+  constexpr int NQ = CV::NV / kPicksPerSpan;   // vectors per quarter
+  static_assert(NQ * kPicksPerSpan == CV::NV, "quarters must split the vectors evenly");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   CV vt, vd;
   load_pair(vt, rowT, vd, rowD, c0, V, tid);
-  float rs[2] = {0.0f, 0.0f}, ts[2] = {0.0f, 0.0f};
+  float rs[kPicksPerSpan], ts[kPicksPerSpan];
+#pragma unroll
+  for (int h = 0; h < kPicksPerSpan; ++h) rs[h] = ts[h] = 0.0f;
 #pragma unroll
   for (int j = 0; j < CV::NV; ++j) {
     float xt[PV], xd[PV];
@@ -144,13 +149,13 @@ __device__ __forceinline__ void resid_chunk_masses2(const ResidConsts& k, const 
     const int i0 = int(c0) + CV::local(tid, j);
 #pragma unroll
     for (int e = 0; e < PV; ++e) {
-      ts[j / NVH] += target_elem(k, xt[e]);
-      rs[j / NVH] += resid_elem<SIG>(k, xt[e], xd[e], i0 + e);
+      ts[j / NQ] += target_elem(k, xt[e]);
+      rs[j / NQ] += resid_elem<SIG>(k, xt[e], xd[e], i0 + e);
     }
     __builtin_amdgcn_sched_barrier(0);   // one vector pair at a time
   }
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < kPicksPerSpan; ++h) {
     const double Rw = wave_sum(double(rs[h]));
     const double Pw = wave_sum(double(ts[h]));
     if (lane == 0) {
@@ -160,7 +165,7 @@ __device__ __forceinline__ void resid_chunk_masses2(const ResidConsts& k, const 
   }
   __syncthreads();
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < kPicksPerSpan; ++h) {
     R[h] = ((sm[8 * h] + sm[8 * h + 1]) + (sm[8 * h + 2] + sm[8 * h + 3])) * double(k.fix_t);
     P[h] = ((sm[8 * h + 4] + sm[8 * h + 5]) + (sm[8 * h + 6] + sm[8 * h + 7])) * double(k.fix_t);
   }
@@ -204,16 +209,17 @@ __device__ __forceinline__ void resid_find_chunk(const uint64_t* cmw, int S, flo
   }
 }
 
-// Phase B, second level (every thread): re-read chunk cs of both rows and
-// pick the token whose running mass crosses target (pre and target in
-// target units; the per-entry values are those units divided by fix_t).
-template <int DT, bool SIG>
+// Phase B, second level (every thread): re-read chunk cs (chunks of
+// 256 * PT entries) of both rows and pick the token whose running mass
+// crosses target (pre and target in target units; the per-entry values are
+// those units divided by fix_t).
+template <int DT, bool SIG, int PT = kPerThread>
 __device__ __forceinline__ int resid_pick(const ResidConsts& k, const typename Dt<DT>::T* rowT,
                                           const typename Dt<DT>::T* rowD, int cs, double pre, double target,
-                                          int V, PickLds<DT, 2>& pk) {
-  const int64_t c0 = int64_t(cs) * kChunk;
-  // each thread owns 32 consecutive tokens of the chunk
-  ChunkVecs<DT, false> cv[2];
+                                          int V, PickLds<DT, 2, PT>& pk) {
+  const int64_t c0 = int64_t(cs) * (kThreads * PT);
+  // each thread owns PT consecutive tokens of the chunk
+  ChunkVecs<DT, false, PT> cv[2];
   load_pair(cv[0], rowT, cv[1], rowD, c0, V, threadIdx.x);
   const double inv = 1.0 / double(k.fix_t);
   return chunk_pick<DT, 2>(cv, c0, pre * inv, target * inv,
@@ -253,51 +259,32 @@ __device__ __forceinline__ void resid_setup(const ResidArgs& a, RowInfo& inf, in
   if (SIG && inf.thr_key > key_of<DT>(__builtin_inff())) k.thr_val = __builtin_nanf("");
 }
 
-// Phase A of the draw of batch row b by its workgroup c2 (chunk pair c2):
-// the residual and target masses of the two 8192-chunks, left in a.cmass by
-// thread 0 with device-scope stores. Every thread calls it.
+// Phase A of the draw of batch row b by its workgroup c4 (16384-entry span
+// c4, pick chunks 4 c4 .. 4 c4 + 3): the residual and target masses of
+// those chunks, left in a.cmass by thread 0 with device-scope stores. Every
+// thread calls it.
 template <int DT, bool SIG>
-__device__ __forceinline__ void resid_phase_a(const ResidArgs& a, RowInfo inf, int b, int c2) {
+__device__ __forceinline__ void resid_phase_a(const ResidArgs& a, RowInfo inf, int b, int c4) {
   using T = typename Dt<DT>::T;
-  __shared__ double sm_pair[16];
+  __shared__ double sm_pair[8 * kPicksPerSpan];
   const int tid = threadIdx.x;
   ResidConsts k;
   const T* rowT;
   const T* rowD;
   resid_setup<DT, SIG>(a, inf, b, k, rowT, rowD);
   if (inf.a >= 0) {
-    double R[2], P[2];
-    resid_chunk_masses2<DT, SIG>(k, rowT, rowD, int64_t(c2) * kStatsChunk, a.V, sm_pair, R, P);
+    double R[kPicksPerSpan], P[kPicksPerSpan];
+    resid_chunk_masses4<DT, SIG>(k, rowT, rowD, int64_t(c4) * kStatsChunk, a.V, sm_pair, R, P);
     if (tid == 0) {
-      const int c = 2 * c2;
+      const int c = kPicksPerSpan * c4;
       uint64_t* wp = reinterpret_cast<uint64_t*>(a.cmass + (int64_t(b) * a.S + c) * 2);
-      dev_store(wp, dbits(R[0]));
-      dev_store(wp + 1, dbits(P[0]));
-      if (c + 1 < a.S) {
-        dev_store(wp + 2, dbits(R[1]));
-        dev_store(wp + 3, dbits(P[1]));
+#pragma unroll
+      for (int h = 0; h < kPicksPerSpan; ++h) {
+        if (c + h < a.S) {
+          dev_store(wp + 2 * h, dbits(R[h]));
+          dev_store(wp + 2 * h + 1, dbits(P[h]));
+        }
       }
-    }
-  }
-}
-
-// Phase A for the single 8192-chunk c of batch row b (half the registers of
-// the chunk-pair form).
-template <int DT, bool SIG>
-__device__ __forceinline__ void resid_phase_a1(const ResidArgs& a, RowInfo inf, int b, int c) {
-  using T = typename Dt<DT>::T;
-  __shared__ double sm_pair[8];
-  ResidConsts k;
-  const T* rowT;
-  const T* rowD;
-  resid_setup<DT, SIG>(a, inf, b, k, rowT, rowD);
-  if (inf.a >= 0) {
-    double R, P;
-    resid_chunk_masses<DT, SIG>(k, rowT, rowD, int64_t(c) * kChunk, a.V, sm_pair, R, P);
-    if (threadIdx.x == 0) {
-      uint64_t* wp = reinterpret_cast<uint64_t*>(a.cmass + (int64_t(b) * a.S + c) * 2);
-      dev_store(wp, dbits(R));
-      dev_store(wp + 1, dbits(P));
     }
   }
 }
@@ -310,7 +297,7 @@ __device__ __forceinline__ void resid_phase_b(const ResidArgs& a, RowInfo inf, i
   using T = typename Dt<DT>::T;
   __shared__ double sm_pre, sm_target;
   __shared__ int sm_c, sm_useres;
-  __shared__ PickLds<DT, 2> sm_pk;
+  __shared__ PickLds<DT, 2, kPickPerThread> sm_pk;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   ResidConsts k;
   const T* rowT;
@@ -356,7 +343,7 @@ __device__ __forceinline__ void resid_phase_b(const ResidArgs& a, RowInfo inf, i
   int tok = -1;
   if (cs >= 0) {
     if (!sm_useres) set_plain(k);
-    tok = resid_pick<DT, SIG>(k, rowT, rowD, cs, sm_pre, sm_target, a.V, sm_pk);
+    tok = resid_pick<DT, SIG, kPickPerThread>(k, rowT, rowD, cs, sm_pre, sm_target, a.V, sm_pk);
   }
   if (tid == 0) a.tok_out[int64_t(b) * a.tok_stride + (a.tok_at_a ? inf.a : 0)] = tok;
   if (a.hit && w == 0) {
@@ -369,15 +356,19 @@ __device__ __forceinline__ void resid_phase_b(const ResidArgs& a, RowInfo inf, i
   }
 }
 
-// The residual / bonus draw of batch row b by one of its (S+1)/2 workgroups
-// (c2: its chunk pair), given the row's RowInfo as written by the accept
-// scan: phase A, then phase B in the workgroup that arrives last. Every
-// thread calls it; returns true in the workgroup that finished the row.
+// Workgroups of the draw per batch row (one per 16384-entry span).
+__host__ __device__ __forceinline__ int resid_wgs_per_row(int S) { return (S + kPicksPerSpan - 1) / kPicksPerSpan; }
+
+// The residual / bonus draw of batch row b by one of its resid_wgs_per_row
+// workgroups (c4: its span), given the row's RowInfo as written by the
+// accept scan: phase A, then phase B in the workgroup that arrives last.
+// Every thread calls it; returns true in the workgroup that finished the
+// row.
 template <int DT, bool SIG>
-__device__ __forceinline__ bool resid_row_wg(const ResidArgs& a, RowInfo inf, int b, int c2) {
+__device__ __forceinline__ bool resid_row_wg(const ResidArgs& a, RowInfo inf, int b, int c4) {
   __shared__ int sm_last;
-  resid_phase_a<DT, SIG>(a, inf, b, c2);
-  if (!arrive_last(&a.cnt[int64_t(b) * kCntStride], uint32_t((a.S + 1) / 2), &sm_last)) return false;
+  resid_phase_a<DT, SIG>(a, inf, b, c4);
+  if (!arrive_last(&a.cnt[int64_t(b) * kCntStride], uint32_t(resid_wgs_per_row(a.S)), &sm_last)) return false;
   resid_phase_b<DT, SIG>(a, inf, b);
   return true;
 }

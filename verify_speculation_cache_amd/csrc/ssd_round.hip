@@ -49,14 +49,14 @@ __global__ __launch_bounds__(kThreads) void k_round_resid(RoundResidArgs a) {
   __shared__ float e_piv[kMaxRows];
   __shared__ double e_s[kMaxRows];
   __shared__ RowInfo sm_inf;
-  const int S2 = (a.r.S + 1) / 2;
-  const int b = blockIdx.x / S2;
-  const int c2 = blockIdx.x - b * S2;
+  const int nw = resid_wgs_per_row(a.r.S);
+  const int b = blockIdx.x / nw;
+  const int c4 = blockIdx.x - b * nw;
   // the row's first workgroup also stores accepted[b], out_tokens, probs and
   // the optional row log-normalisers
-  const RowInfo inf = accept_scan<DT, true>(a.s, b, c2 == 0, e_piv, e_s, &sm_inf);
-  if (c2 == 0) write_row_lse(a.s, b, e_piv, e_s);
-  resid_row_wg<DT, SIG>(a.r, inf, b, c2);
+  const RowInfo inf = accept_scan<DT, true>(a.s, b, c4 == 0, e_piv, e_s, &sm_inf);
+  if (c4 == 0) write_row_lse(a.s, b, e_piv, e_s);
+  resid_row_wg<DT, SIG>(a.r, inf, b, c4);
 }
 
 hipError_t launch_round_chunks(const RoundArgs& a, int dtype, hipStream_t st) {
@@ -67,7 +67,7 @@ hipError_t launch_round_chunks(const RoundArgs& a, int dtype, hipStream_t st) {
 }
 
 hipError_t launch_round_resid(const RoundResidArgs& a, int dtype, bool sigma, hipStream_t st) {
-  const unsigned grid = unsigned(int64_t(a.r.B) * ((a.r.S + 1) / 2));
+  const unsigned grid = unsigned(int64_t(a.r.B) * resid_wgs_per_row(a.r.S));
   if (dtype == SSD_BF16) {
     if (sigma) hipLaunchKernelGGL((k_round_resid<1, true>), dim3(grid), dim3(kThreads), 0, st, a);
     else hipLaunchKernelGGL((k_round_resid<1, false>), dim3(grid), dim3(kThreads), 0, st, a);
