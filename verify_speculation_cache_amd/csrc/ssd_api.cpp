@@ -120,7 +120,7 @@ CacheArgs cache_args(const void* draft, int64_t db, int32_t B, int32_t K, int32_
 StatsArgs verify_stats_args(const void* target, int64_t tb, const void* draft, int64_t db, int32_t B, int32_t K,
                             int32_t V, float tau, const int32_t* tokens, const float* u_acc, const ssd_sigma* sigma,
                             int32_t* accepted, int32_t* out_tokens, float* probs, float* row_lse, char* ws,
-                            const StatsWs& sw) {
+                            const StatsWs& sw, int pt) {
   const bool sig = sigma != nullptr;
   StatsArgs a{};
   a.target = target;
@@ -130,7 +130,8 @@ StatsArgs verify_stats_args(const void* target, int64_t tb, const void* draft, i
   a.B = B;
   a.K = K;
   a.V = V;
-  a.S = int(stats_chunks_per_row(V));
+  a.pt = pt;
+  a.S = int(chunks_of(V, pt));
   a.NR = sig ? K + 1 : 2 * K + 1;
   a.mode = sig ? kModeVerifySigma : kModeVerify;
   a.c64 = kLog2e / double(tau);
@@ -164,6 +165,8 @@ ResidArgs verify_resid_args(const StatsArgs& a, const float* u_res, float* resid
   r.K = a.K;
   r.V = a.V;
   r.S = int(pick_chunks_per_row(a.V));
+  // small grids take one pick chunk per first-phase workgroup
+  r.span_pt = a.pt == kSmallPerThread ? kSmallPerThread : kStatsPerThread;
   r.c32 = a.c32;
   r.u = u_res;
   r.info = a.info;
@@ -324,14 +327,14 @@ SSD_API int ssd_cache_stats(const int32_t* accepted, const uint8_t* hit, int32_t
 
 SSD_API size_t ssd_verify_workspace_size(int32_t B, int32_t K, int32_t V, int dtype) {
   if (check_shape(B, K, V) != SSD_OK || !dtype_ok(dtype)) return 0;
-  const StatsWs sw(B, 2 * K + 1, stats_chunks_per_row(V), K);
+  const StatsWs sw(B, 2 * K + 1, chunks_of(V, stats_pt(B, 2 * K + 1, V)), K);
   const ResidWs rw(B, pick_chunks_per_row(V));
   return sw.total + rw.total;
 }
 
 SSD_API size_t ssd_residual_workspace_size(int32_t B, int32_t K, int32_t V, int dtype) {
   if (check_shape(B, K, V) != SSD_OK || !dtype_ok(dtype)) return 0;
-  const StatsWs sw(B, 2, stats_chunks_per_row(V), K);
+  const StatsWs sw(B, 2, chunks_of(V, stats_pt(B, 2, V)), K);
   const ResidWs rw(B, pick_chunks_per_row(V));
   return sw.total + rw.total;
 }
@@ -358,17 +361,18 @@ SSD_API int ssd_verify(const void* target_logits, int64_t target_bstride,
     return fail(SSD_EINVAL, "a required pointer is NULL");
   if (target_bstride < 0 || draft_bstride < 0) return fail(SSD_EINVAL, "negative batch stride");
   const int64_t SP = pick_chunks_per_row(V);
-  const int64_t SS = stats_chunks_per_row(V);
+  const int pt = stats_pt(B, 2 * K + 1, V);
+  const int64_t SS = chunks_of(V, pt);
   const bool sig = sigma != nullptr;
   const int NR = sig ? K + 1 : 2 * K + 1;
   const StatsWs sw(B, 2 * K + 1, SS, K);
   const ResidWs rw(B, SP);
   if ((st = check_ws(workspace, ws_bytes, sw.total + rw.total)) != SSD_OK) return st;
   if ((st = check_grid(int64_t(B) * NR * SS)) != SSD_OK) return st;
-  if ((st = check_grid(int64_t(B) * SS)) != SSD_OK) return st;
   char* ws = static_cast<char*>(workspace);
   const StatsArgs a = verify_stats_args(target_logits, target_bstride, draft_logits, draft_bstride, B, K, V, tau,
-                                        draft_tokens, u_acc, sigma, accepted, out_tokens, probs, row_lse, ws, sw);
+                                        draft_tokens, u_acc, sigma, accepted, out_tokens, probs, row_lse, ws, sw,
+                                        pt);
   hipStream_t stream = as_stream(hip_stream);
   // two launches: the statistics chunk pass, then per batch row the accept
   // scan (repeated in each of the row's residual workgroups) and the draw
@@ -392,7 +396,8 @@ SSD_API int ssd_residual_sample(const void* target_logits, int64_t target_bstrid
   if (sigma && !draft_logits) return fail(SSD_EINVAL, "sigma given without draft logits");
   if (target_bstride < 0 || draft_bstride < 0) return fail(SSD_EINVAL, "negative batch stride");
   const int64_t SP = pick_chunks_per_row(V);
-  const int64_t SS = stats_chunks_per_row(V);
+  const int pt = stats_pt(B, 2, V);
+  const int64_t SS = chunks_of(V, pt);
   const StatsWs sw(B, 2, SS, K);
   const ResidWs rw(B, SP);
   if ((st = check_ws(workspace, ws_bytes, sw.total + rw.total)) != SSD_OK) return st;
@@ -408,6 +413,7 @@ SSD_API int ssd_residual_sample(const void* target_logits, int64_t target_bstrid
   a.B = B;
   a.K = K;
   a.V = V;
+  a.pt = pt;
   a.S = int(SS);
   a.NR = 2;
   a.mode = kModeRows;
@@ -440,6 +446,7 @@ SSD_API int ssd_residual_sample(const void* target_logits, int64_t target_bstrid
   r.K = K;
   r.V = V;
   r.S = int(SP);
+  r.span_pt = pt == kSmallPerThread ? kSmallPerThread : kStatsPerThread;
   r.c32 = a.c32;
   r.u = u;
   r.info = a.info;
@@ -686,7 +693,7 @@ SSD_API int ssd_verify_round(const void* target_logits, int64_t target_bstride,
   a.c = cache_args(draft_logits, draft_bstride, B, K, V, tau, F, sumF, cache_tokens, thr, draft_stats, ws, cw);
   const ssd_sigma sig{C, thr, draft_stats};
   a.s = verify_stats_args(target_logits, target_bstride, draft_logits, draft_bstride, B, K, V, tau, draft_tokens,
-                          u_acc, &sig, accepted, out_tokens, nullptr, nullptr, ws + off_s, sw);
+                          u_acc, &sig, accepted, out_tokens, nullptr, nullptr, ws + off_s, sw, kPerThread);
   a.s.S = int(S);
   a.ncw = uint32_t((K + 1) * S);
   a.nsw = uint32_t((K + 1) * S);

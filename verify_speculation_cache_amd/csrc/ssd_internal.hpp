@@ -28,13 +28,27 @@ inline int64_t stats_chunks_per_row(int64_t V) { return (V + kStatsChunk - 1) / 
 
 // The residual / bonus draw keeps its chunk masses per 4096 entries: a
 // workgroup of its first phase covers one 16384-entry statistics span (four
-// such chunks), and the in-chunk pick of the second phase, which runs on
-// one workgroup per row with nothing else on its compute unit, has 16
-// tokens per thread to scan instead of 32.
+// such chunks; one on small grids), and the in-chunk pick of the second
+// phase, which runs on one workgroup per row with nothing else on its
+// compute unit, has 16 tokens per thread to scan instead of 32.
 constexpr int kPickPerThread = 16;
 constexpr int kPickChunk = kThreads * kPickPerThread;      // 4096
-constexpr int kPicksPerSpan = kStatsChunk / kPickChunk;     // 4
 inline int64_t pick_chunks_per_row(int64_t V) { return (V + kPickChunk - 1) / kPickChunk; }
+
+// Small grids: when a verification's statistics pass would have fewer than
+// kSmallGridWgs workgroups of 16384 entries (about two per compute unit),
+// its statistics chunks and the draw's first-phase spans are 4096 entries
+// instead: four times the workgroups with a quarter of the bytes each,
+// since at that size one workgroup's own loads, not HBM, set the time.
+constexpr int64_t kSmallGridWgs = 512;
+constexpr int kSmallPerThread = kPickPerThread;   // 16: a span of one pick chunk
+inline int stats_pt(int64_t B, int64_t NR, int64_t V) {
+  return B * NR * stats_chunks_per_row(V) < kSmallGridWgs ? kSmallPerThread : kStatsPerThread;
+}
+inline int64_t chunks_of(int64_t V, int pt) {
+  const int64_t span = int64_t(kThreads) * pt;
+  return (V + span - 1) / span;
+}
 
 // Per-(row, chunk) statistics: chunk max of the raw logits and the chunk's
 // sum of exp2((z - pivot) * log2(e)/tau), pivot = chunk max (0 if -inf).
@@ -80,6 +94,7 @@ struct StatsArgs {
   const void* draft;
   int64_t db;
   int B, K, V, S, NR, mode;
+  int pt;           // entries per thread of a statistics chunk (S = chunks of 256 * pt)
   float c32;        // log2(e) / tau
   double c64;       // log2(e) / tau in double
   double inv_tau;   // 1 / tau
@@ -107,6 +122,7 @@ struct ResidArgs {
   const void* draft;
   int64_t db;
   int B, K, V, S;
+  int span_pt;         // entries per thread of a first-phase span: 64 (four pick chunks) or 16 (one)
   float c32;
   const float* u;
   const RowInfo* info;

@@ -27,25 +27,33 @@ namespace ssd {
 // pair of each batch row (rows mode): every workgroup of batch row b merges
 // the pair's partials itself (a few hundred bytes) before its share of the
 // draw, so no workgroup of the chunk pass waits on a counter.
-template <int DT, bool SIG>
+template <int DT, bool SIG, int PT>
 __global__ __launch_bounds__(kThreads) void k_rows_resid(RoundResidArgs a) {
   __shared__ float e_piv[2];
   __shared__ double e_s[2];
   __shared__ RowInfo sm_inf;
-  const int nw = resid_wgs_per_row(a.r.S);
+  const int nw = resid_wgs_per_row(a.r.S, PT);
   const int b = blockIdx.x / nw;
   const RowInfo inf = rows_mode_info(a.s, b, e_piv, e_s, &sm_inf);
-  resid_row_wg<DT, SIG>(a.r, inf, b, blockIdx.x - b * nw);
+  resid_row_wg<DT, SIG, PT>(a.r, inf, b, blockIdx.x - b * nw);
+}
+
+template <int DT, bool SIG>
+static void launch_rows_resid_t(const RoundResidArgs& a, unsigned grid, hipStream_t st) {
+  if (a.r.span_pt == kSmallPerThread)
+    hipLaunchKernelGGL((k_rows_resid<DT, SIG, kSmallPerThread>), dim3(grid), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_rows_resid<DT, SIG, kStatsPerThread>), dim3(grid), dim3(kThreads), 0, st, a);
 }
 
 hipError_t launch_rows_resid(const RoundResidArgs& a, int dtype, bool sigma, hipStream_t st) {
-  const unsigned grid = unsigned(int64_t(a.r.B) * resid_wgs_per_row(a.r.S));
+  const unsigned grid = unsigned(int64_t(a.r.B) * resid_wgs_per_row(a.r.S, a.r.span_pt));
   if (dtype == SSD_BF16) {
-    if (sigma) hipLaunchKernelGGL((k_rows_resid<1, true>), dim3(grid), dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((k_rows_resid<1, false>), dim3(grid), dim3(kThreads), 0, st, a);
+    if (sigma) launch_rows_resid_t<1, true>(a, grid, st);
+    else launch_rows_resid_t<1, false>(a, grid, st);
   } else {
-    if (sigma) hipLaunchKernelGGL((k_rows_resid<0, true>), dim3(grid), dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((k_rows_resid<0, false>), dim3(grid), dim3(kThreads), 0, st, a);
+    if (sigma) launch_rows_resid_t<0, true>(a, grid, st);
+    else launch_rows_resid_t<0, false>(a, grid, st);
   }
   return hipGetLastError();
 }

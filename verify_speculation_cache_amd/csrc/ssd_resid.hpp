@@ -120,27 +120,29 @@ __device__ __forceinline__ void resid_chunk_masses(const ResidConsts& k, const t
   P = ((sm_pair[4] + sm_pair[5]) + (sm_pair[6] + sm_pair[7])) * double(k.fix_t);
 }
 
-// Phase A over one 16384-entry span at c0 (64 entries per thread, strided:
-// vectors j < NV/4 lie in the first 4096 entries, the next NV/4 in the
-// second, and so on): the masses of each of its four 4096-entry pick
-// chunks, so the draw's second phase scans short chunks while a workgroup
-// of the first moves 64 KiB (bf16) per round trip. R[h], P[h] for quarter h
-// are returned in every thread (sm: 32 doubles of LDS; one barrier).
-template <int DT, bool SIG>
-__device__ __forceinline__ void resid_chunk_masses4(const ResidConsts& k, const typename Dt<DT>::T* rowT,
-                                                    const typename Dt<DT>::T* rowD, int64_t c0, int V,
-                                                    double* sm, double (&R)[kPicksPerSpan],
-                                                    double (&P)[kPicksPerSpan]) {
+// Phase A over one span of 256 * PT entries at c0 (PT per thread, strided:
+// the first NV/NQ vectors of every thread lie in the first 4096 entries,
+// the next NV/NQ in the second, and so on): the masses of each of its NQ =
+// PT/16 pick chunks. PT = 64 lets a workgroup move 64 KiB (bf16) per round
+// trip; small grids use PT = 16 (one pick chunk per workgroup). R[h], P[h]
+// for chunk h are returned in every thread (sm: 8 NQ doubles of LDS; one
+// barrier).
+template <int DT, bool SIG, int PT>
+__device__ __forceinline__ void resid_span_masses(const ResidConsts& k, const typename Dt<DT>::T* rowT,
+                                                  const typename Dt<DT>::T* rowD, int64_t c0, int V, double* sm,
+                                                  double (&R)[PT / kPickPerThread],
+                                                  double (&P)[PT / kPickPerThread]) {
   constexpr int PV = Dt<DT>::kPerVec;
-  using CV = ChunkVecs<DT, true, kStatsPerThread>;
-  constexpr int NQ = CV::NV / kPicksPerSpan;   // vectors per quarter
-  static_assert(NQ * kPicksPerSpan == CV::NV, "quarters must split the vectors evenly");
+  constexpr int NQ = PT / kPickPerThread;
+  using CV = ChunkVecs<DT, true, PT>;
+  constexpr int NVQ = CV::NV / NQ;   // vectors per pick chunk
+  static_assert(NVQ * NQ == CV::NV, "pick chunks must split the vectors evenly");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   CV vt, vd;
   load_pair(vt, rowT, vd, rowD, c0, V, tid);
-  float rs[kPicksPerSpan], ts[kPicksPerSpan];
+  float rs[NQ], ts[NQ];
 #pragma unroll
-  for (int h = 0; h < kPicksPerSpan; ++h) rs[h] = ts[h] = 0.0f;
+  for (int h = 0; h < NQ; ++h) rs[h] = ts[h] = 0.0f;
 #pragma unroll
   for (int j = 0; j < CV::NV; ++j) {
     float xt[PV], xd[PV];
@@ -149,13 +151,13 @@ __device__ __forceinline__ void resid_chunk_masses4(const ResidConsts& k, const 
     const int i0 = int(c0) + CV::local(tid, j);
 #pragma unroll
     for (int e = 0; e < PV; ++e) {
-      ts[j / NQ] += target_elem(k, xt[e]);
-      rs[j / NQ] += resid_elem<SIG>(k, xt[e], xd[e], i0 + e);
+      ts[j / NVQ] += target_elem(k, xt[e]);
+      rs[j / NVQ] += resid_elem<SIG>(k, xt[e], xd[e], i0 + e);
     }
     __builtin_amdgcn_sched_barrier(0);   // one vector pair at a time
   }
 #pragma unroll
-  for (int h = 0; h < kPicksPerSpan; ++h) {
+  for (int h = 0; h < NQ; ++h) {
     const double Rw = wave_sum(double(rs[h]));
     const double Pw = wave_sum(double(ts[h]));
     if (lane == 0) {
@@ -165,7 +167,7 @@ __device__ __forceinline__ void resid_chunk_masses4(const ResidConsts& k, const 
   }
   __syncthreads();
 #pragma unroll
-  for (int h = 0; h < kPicksPerSpan; ++h) {
+  for (int h = 0; h < NQ; ++h) {
     R[h] = ((sm[8 * h] + sm[8 * h + 1]) + (sm[8 * h + 2] + sm[8 * h + 3])) * double(k.fix_t);
     P[h] = ((sm[8 * h + 4] + sm[8 * h + 5]) + (sm[8 * h + 6] + sm[8 * h + 7])) * double(k.fix_t);
   }
@@ -259,27 +261,28 @@ __device__ __forceinline__ void resid_setup(const ResidArgs& a, RowInfo& inf, in
   if (SIG && inf.thr_key > key_of<DT>(__builtin_inff())) k.thr_val = __builtin_nanf("");
 }
 
-// Phase A of the draw of batch row b by its workgroup c4 (16384-entry span
-// c4, pick chunks 4 c4 .. 4 c4 + 3): the residual and target masses of
-// those chunks, left in a.cmass by thread 0 with device-scope stores. Every
-// thread calls it.
-template <int DT, bool SIG>
+// Phase A of the draw of batch row b by its workgroup c4 (span c4 of 256 *
+// PT entries: pick chunks NQ c4 .. NQ c4 + NQ - 1): the residual and target
+// masses of those chunks, left in a.cmass by thread 0 with device-scope
+// stores. Every thread calls it.
+template <int DT, bool SIG, int PT>
 __device__ __forceinline__ void resid_phase_a(const ResidArgs& a, RowInfo inf, int b, int c4) {
   using T = typename Dt<DT>::T;
-  __shared__ double sm_pair[8 * kPicksPerSpan];
+  constexpr int NQ = PT / kPickPerThread;
+  __shared__ double sm_pair[8 * NQ];
   const int tid = threadIdx.x;
   ResidConsts k;
   const T* rowT;
   const T* rowD;
   resid_setup<DT, SIG>(a, inf, b, k, rowT, rowD);
   if (inf.a >= 0) {
-    double R[kPicksPerSpan], P[kPicksPerSpan];
-    resid_chunk_masses4<DT, SIG>(k, rowT, rowD, int64_t(c4) * kStatsChunk, a.V, sm_pair, R, P);
+    double R[NQ], P[NQ];
+    resid_span_masses<DT, SIG, PT>(k, rowT, rowD, int64_t(c4) * (kThreads * PT), a.V, sm_pair, R, P);
     if (tid == 0) {
-      const int c = kPicksPerSpan * c4;
+      const int c = NQ * c4;
       uint64_t* wp = reinterpret_cast<uint64_t*>(a.cmass + (int64_t(b) * a.S + c) * 2);
 #pragma unroll
-      for (int h = 0; h < kPicksPerSpan; ++h) {
+      for (int h = 0; h < NQ; ++h) {
         if (c + h < a.S) {
           dev_store(wp + 2 * h, dbits(R[h]));
           dev_store(wp + 2 * h + 1, dbits(P[h]));
@@ -356,19 +359,23 @@ __device__ __forceinline__ void resid_phase_b(const ResidArgs& a, RowInfo inf, i
   }
 }
 
-// Workgroups of the draw per batch row (one per 16384-entry span).
-__host__ __device__ __forceinline__ int resid_wgs_per_row(int S) { return (S + kPicksPerSpan - 1) / kPicksPerSpan; }
+// Workgroups of the draw per batch row (one per span of 256 * span_pt
+// entries, span_pt / 16 pick chunks each).
+__host__ __device__ __forceinline__ int resid_wgs_per_row(int S, int span_pt) {
+  const int nq = span_pt / kPickPerThread;
+  return (S + nq - 1) / nq;
+}
 
 // The residual / bonus draw of batch row b by one of its resid_wgs_per_row
 // workgroups (c4: its span), given the row's RowInfo as written by the
 // accept scan: phase A, then phase B in the workgroup that arrives last.
 // Every thread calls it; returns true in the workgroup that finished the
 // row.
-template <int DT, bool SIG>
+template <int DT, bool SIG, int PT>
 __device__ __forceinline__ bool resid_row_wg(const ResidArgs& a, RowInfo inf, int b, int c4) {
   __shared__ int sm_last;
-  resid_phase_a<DT, SIG>(a, inf, b, c4);
-  if (!arrive_last(&a.cnt[int64_t(b) * kCntStride], uint32_t(resid_wgs_per_row(a.S)), &sm_last)) return false;
+  resid_phase_a<DT, SIG, PT>(a, inf, b, c4);
+  if (!arrive_last(&a.cnt[int64_t(b) * kCntStride], uint32_t(resid_wgs_per_row(a.S, PT)), &sm_last)) return false;
   resid_phase_b<DT, SIG>(a, inf, b);
   return true;
 }

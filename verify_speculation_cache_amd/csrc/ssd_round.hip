@@ -44,19 +44,19 @@ __global__ __launch_bounds__(kThreads) void k_round_chunks(RoundArgs a) {
 
 // Also the second launch of ssd_verify (after its statistics chunk pass),
 // with SIG as the caller's sigma switch and no lookup.
-template <int DT, bool SIG>
+template <int DT, bool SIG, int PT>
 __global__ __launch_bounds__(kThreads) void k_round_resid(RoundResidArgs a) {
   __shared__ float e_piv[kMaxRows];
   __shared__ double e_s[kMaxRows];
   __shared__ RowInfo sm_inf;
-  const int nw = resid_wgs_per_row(a.r.S);
+  const int nw = resid_wgs_per_row(a.r.S, PT);
   const int b = blockIdx.x / nw;
   const int c4 = blockIdx.x - b * nw;
   // the row's first workgroup also stores accepted[b], out_tokens, probs and
   // the optional row log-normalisers
   const RowInfo inf = accept_scan<DT, true>(a.s, b, c4 == 0, e_piv, e_s, &sm_inf);
   if (c4 == 0) write_row_lse(a.s, b, e_piv, e_s);
-  resid_row_wg<DT, SIG>(a.r, inf, b, c4);
+  resid_row_wg<DT, SIG, PT>(a.r, inf, b, c4);
 }
 
 hipError_t launch_round_chunks(const RoundArgs& a, int dtype, hipStream_t st) {
@@ -66,14 +66,22 @@ hipError_t launch_round_chunks(const RoundArgs& a, int dtype, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int DT, bool SIG>
+static void launch_round_resid_t(const RoundResidArgs& a, unsigned grid, hipStream_t st) {
+  if (a.r.span_pt == kSmallPerThread)
+    hipLaunchKernelGGL((k_round_resid<DT, SIG, kSmallPerThread>), dim3(grid), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_round_resid<DT, SIG, kStatsPerThread>), dim3(grid), dim3(kThreads), 0, st, a);
+}
+
 hipError_t launch_round_resid(const RoundResidArgs& a, int dtype, bool sigma, hipStream_t st) {
-  const unsigned grid = unsigned(int64_t(a.r.B) * resid_wgs_per_row(a.r.S));
+  const unsigned grid = unsigned(int64_t(a.r.B) * resid_wgs_per_row(a.r.S, a.r.span_pt));
   if (dtype == SSD_BF16) {
-    if (sigma) hipLaunchKernelGGL((k_round_resid<1, true>), dim3(grid), dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((k_round_resid<1, false>), dim3(grid), dim3(kThreads), 0, st, a);
+    if (sigma) launch_round_resid_t<1, true>(a, grid, st);
+    else launch_round_resid_t<1, false>(a, grid, st);
   } else {
-    if (sigma) hipLaunchKernelGGL((k_round_resid<0, true>), dim3(grid), dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((k_round_resid<0, false>), dim3(grid), dim3(kThreads), 0, st, a);
+    if (sigma) launch_round_resid_t<0, true>(a, grid, st);
+    else launch_round_resid_t<0, false>(a, grid, st);
   }
   return hipGetLastError();
 }

@@ -6,17 +6,22 @@ namespace ssd {
 
 // The chunk pass: partials and gathered logits for a consumer in a later
 // launch that merges them itself (the residual kernels).
-template <int DT>
+// PT entries per thread: 64 (16384-entry chunks), or 16 for small grids.
+template <int DT, int PT>
 __global__ __launch_bounds__(kThreads) void k_stats_chunks(StatsArgs a) {
-  stats_chunk_wg<DT>(a, blockIdx.x);
+  stats_chunk_wg<DT, PT>(a, blockIdx.x);
 }
 
 hipError_t launch_stats_chunks(const StatsArgs& a, int dtype, hipStream_t st) {
-  const int64_t grid = int64_t(a.B) * a.NR * a.S;
-  if (dtype == SSD_BF16)
-    hipLaunchKernelGGL(k_stats_chunks<1>, dim3(unsigned(grid)), dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(k_stats_chunks<0>, dim3(unsigned(grid)), dim3(kThreads), 0, st, a);
+  const dim3 grid(unsigned(int64_t(a.B) * a.NR * a.S));
+  const bool small = a.pt == kSmallPerThread;
+  if (dtype == SSD_BF16) {
+    if (small) hipLaunchKernelGGL((k_stats_chunks<1, kSmallPerThread>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((k_stats_chunks<1, kStatsPerThread>), grid, dim3(kThreads), 0, st, a);
+  } else {
+    if (small) hipLaunchKernelGGL((k_stats_chunks<0, kSmallPerThread>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((k_stats_chunks<0, kStatsPerThread>), grid, dim3(kThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 
