@@ -315,7 +315,9 @@ def bench_report(args):
     """Per-workload report: the whole C-ABI call timed with HIP events around
     it (median, p10, p90 over --calls back-to-back calls on rotating input
     copies, ceil(512 MB / bytes) + 1 of them, so logits come from HBM), plus
-    the same call on one warm copy. Plain workloads time ssd_verify; cache
+    the same call on one warm copy, and the calls replayed as HIP graphs
+    (t_graph_us: GPU time per call without host launch overhead, the
+    latency figure for launch-bound workloads). Plain workloads time ssd_verify; cache
     workloads time ssd_verify_round (cache build, sigma verification, lookup)
     on drafts drawn on the GPU from q_sigma (ssd_draft_sample).
     Bytes: single-read logits bytes of the call, and the early-exit minimum
@@ -386,6 +388,19 @@ def bench_report(args):
         timed(10, True)
         ts = timed(args.calls, True)
         warm = timed(max(20, args.calls // 4), False)
+        # the same calls replayed as HIP graphs (one graph per cycle over the
+        # copies): GPU time per call without the host's launch overhead
+        run = _replay_runner(call, ncopy, argparse.Namespace(eager=False))
+        n_graph = ncopy * max(1, -(-args.calls // ncopy))
+        run(ncopy)
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        run(n_graph)
+        g1.record()
+        torch.cuda.synchronize()
+        graph_us = g0.elapsed_time(g1) * 1e3 / n_graph
+        del run
         med, p10, p90 = ts[len(ts) // 2], ts[len(ts) // 10], ts[(9 * len(ts)) // 10]
         acc = outs[0]["accepted"].cpu().numpy()
         ok = acc >= 0
@@ -400,6 +415,7 @@ def bench_report(args):
             "calls": args.calls, "rotating_copies": ncopy,
             "t_call_us": {"median": round(med * 1e3, 2), "p10": round(p10 * 1e3, 2), "p90": round(p90 * 1e3, 2)},
             "warm_single_copy_us": round(warm[len(warm) // 2] * 1e3, 2),
+            "t_graph_us": round(graph_us, 2),
             "rows_per_s": round(B / (med / 1e3), 1),
             "bytes_single_read": bytes_call,
             "eff_gbps": round(bytes_call / (med / 1e3) / 1e9, 1),
