@@ -125,6 +125,17 @@ __device__ __forceinline__ void merge_row_partials(const StatsArgs& a, int b, fl
   else merge_rows<2>(pb, a.NR, a.S, a.c32, e_piv, e_s, nullptr);
 }
 
+// exp2((z - piv) * c32) of one token in the scaled form of the streaming
+// sums (one rounding in the argument, the pivot's product error restored by
+// a second factor), returned in double for the division by the row sum.
+// Its relative error (a few float ulps, plus |argument| * 2^-24) stays far
+// below the 1e-6 absolute margin that decides an accept test and the 1e-5
+// relative tolerance of the reported probabilities.
+__device__ __forceinline__ double token_mass(float z, float piv, float c32) {
+  const ScaledPivot sp = scaled_pivot(piv, c32);
+  return double(scaled_mass(z, c32, sp.P)) * double(sp.fix);
+}
+
 // The accept scan of batch row b (verify mode): merges the target rows'
 // partials, takes p and q at the drafted tokens, keeps d iff u*q(d) < p(d)
 // up to the first rejection, and fills the RowInfo of the row to sample
@@ -167,7 +178,7 @@ __device__ __forceinline__ RowInfo accept_scan(const StatsArgs& a, int b, bool w
       bad = (d < 0 || d >= a.V);
       if (!bad) {
         const double st = e_s[i];
-        pd = st > 0.0 ? exp2(double(zt - e_piv[i]) * double(a.c32)) / st : 0.0;
+        pd = st > 0.0 ? token_mass(zt, e_piv[i], a.c32) / st : 0.0;
         double pivd, sdn, wgt = 1.0;
         if (a.use_sigma) {
           pivd = double(pivot_of(float(sp0)));
@@ -177,7 +188,7 @@ __device__ __forceinline__ RowInfo accept_scan(const StatsArgs& a, int b, bool w
           pivd = double(e_piv[K + 1 + i]);
           sdn = e_s[K + 1 + i];
         }
-        qd = sdn > 0.0 ? wgt * exp2(double(zd - float(pivd)) * double(a.c32)) / sdn : 0.0;
+        qd = sdn > 0.0 ? wgt * token_mass(zd, float(pivd), a.c32) / sdn : 0.0;
         acc = double(ua) * qd < pd;
       }
     }
