@@ -362,7 +362,7 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
 
   // chunks whose candidates overflowed (ties): re-read them and keep exactly
   // their top F; the other entries >= T0 of such a chunk add to S_rest
-  if (s_anyovf) {
+  if (__builtin_expect(s_anyovf != 0, 0)) {   // rare: ties overflowed a chunk's slots
     const T* row = static_cast<const T*>(a.draft) + int64_t(b) * a.db + int64_t(k) * a.V;
     for (int cc = 0; cc < a.S; ++cc) {
       if (ld64<COH>(pp + cc * 4 + 2) != kOverflow) continue;   // uniform
@@ -425,7 +425,7 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
   int n2 = __builtin_amdgcn_readfirstlane(s_n2);   // uniform
   __syncthreads();
 
-  if (n2 > kFiltCap) {
+  if (__builtin_expect(n2 > kFiltCap, 0)) {
     // too many at or above Tmax: the row's F-th largest key, exactly, 8 bits
     // at a time from the top (it is >= Tmax, so only those are re-sorted)
     constexpr int KB = Dt<DT>::kKeyBits;
@@ -527,7 +527,7 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
     if (rank < F) st32<COH>(ct + rank, cand_idx(e));
     if (rank == F - 1) s_thrw = e;
   };
-  if (n2 <= 64) {
+  if (__builtin_expect(n2 <= 64, 1)) {
     // one wave, entry i in lane i, the others read with readlane
     if (w == 0) {
       const uint64_t e = lane < n2 ? s_list[lane] : 0ull;
