@@ -224,6 +224,20 @@ def main():
         assert torch.equal(o[1]["accepted"], sep_ref[j][0]) and torch.equal(o[1]["out_tokens"], sep_ref[j][1])
         assert torch.equal(o[2]["hit"], sep_ref[j][2])
 
+    # the round's launches timed one by one: HIP events recorded on the
+    # launching stream between the three launches (ssd_verify_round_marked),
+    # back-to-back calls over the rotating copies
+    n_mark = 60
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_mark)]
+    for i in range(n_mark):
+        j = i % ncopy
+        S.ssd_verify_round(tgts[j], dfts[j], F, C, toks, ua, ur, tau, out=rounds[j], marks=marks[i])
+    torch.cuda.synchronize()
+    launch_ms = {name: float(np.mean([m[k].elapsed_time(m[k + 1]) for m in marks[n_mark // 6:]]))
+                 for k, name in enumerate(("k_round_chunks", "k_cache_merge", "k_round_resid"))}
+    for j in range(ncopy):   # the marked calls wrote the same outputs
+        assert torch.equal(rounds[j]["accepted"], round_ref[j][0]) and torch.equal(rounds[j]["hit"], round_ref[j][2])
+
     if args.profile_loop:
         for i in range(args.profile_loop):
             step(i % ncopy)
@@ -251,12 +265,18 @@ def main():
                     "kernel": "ssd_build_cache (k_cache_chunk + k_cache_merge, bf16)",
                     "bytes_per_launch": bytes_build, "avg_launch_ms": round(dom_ms, 5)}
     else:
-        # the fused round is the step: its three launches read each logit once
-        # (target rows 0..K, draft rows 0..K) plus the residual rows again
-        roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(gbps / PEAK_HBM_GBS, 4), "traffic": measured_traffic(ROUND_BYTES_PROFILE),
-                    "kernel": "ssd_verify_round (k_round_chunks + k_cache_merge + k_round_resid, bf16)",
-                    "bytes_per_launch": step_bytes, "avg_launch_ms": round(ms_step, 5)}
+        # dominant kernel of the step: k_round_chunks, the one launch that
+        # streams every logit of the step once (target rows 0..K for the row
+        # statistics, draft rows 0..K for the cache), timed by the marks
+        dom_ms = launch_ms["k_round_chunks"]
+        dom_gbps = step_bytes / (dom_ms / 1e3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(dom_gbps / PEAK_HBM_GBS, 4),
+                    "traffic": measured_traffic(ROUND_BYTES_PROFILE, "k_round_chunks<1>"),
+                    "kernel": "k_round_chunks (cache chunk pass over draft rows 0..5 + row-statistics chunk pass "
+                              "over target rows 0..5, bf16)",
+                    "bytes_per_launch": step_bytes, "avg_launch_ms": round(dom_ms, 5),
+                    "launches_timed": n_mark - n_mark // 6}
 
     cpu, check = None, None
     if not args.no_cpu:
@@ -291,6 +311,11 @@ def main():
         "pct_peak_hbm": round(100 * gbps / PEAK_HBM_GBS, 2),
         "bytes_per_step": step_bytes,
         "roofline": roofline,
+        "step_roofline": ({"achieved": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBS, 4), "unit": "GB/s",
+                           "traffic": measured_traffic(ROUND_BYTES_PROFILE),
+                           "what": "the whole graph-replayed step (three launches, launch gaps included)"}
+                          if not args.separate else None),
+        "launch_ms": ({k: round(v, 5) for k, v in launch_ms.items()} if not args.separate else None),
         "per_call_ms": {"ssd_build_cache": round(t_build, 5), "ssd_verify_sigma": round(t_verify, 5),
                         "ssd_cache_lookup": round(t_lookup, 5)},
         "verify_only": {"ms": round(t_plain, 5), "rows_per_s": round(B / (t_plain / 1e3), 1),
@@ -690,9 +715,10 @@ HBM_BYTES_PROFILE = os.path.join(ROOT, "profiles", "ssd_build_cache_B64_K5_V1282
 ROUND_BYTES_PROFILE = os.path.join(ROOT, "profiles", "ssd_verify_round_B64_K5_V128256_bf16_hbm_bytes.md")
 
 
-def measured_traffic(profile):
-    """HBM bytes per call from a committed FETCH_SIZE / WRITE_SIZE counter
-    summary, or None when the kernel sources changed since it was taken."""
+def measured_traffic(profile, kernel=None):
+    """HBM bytes per call (or, with kernel, per launch of that kernel) from a
+    committed FETCH_SIZE / WRITE_SIZE counter summary, or None when the
+    kernel sources changed since it was taken."""
     import hashlib
     try:
         text = open(profile).read()
@@ -702,7 +728,11 @@ def measured_traffic(profile):
             h.update(open(os.path.join(ROOT, p), "rb").read())
     except (OSError, ValueError, KeyError, IndexError):
         return None
-    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["source_sha256"] else None
+    if h.hexdigest() != rec["source_sha256"]:
+        return None
+    if kernel is not None:
+        return rec.get("kernel_bytes", {}).get(kernel)
+    return rec["traffic_bytes_per_launch"]
 
 
 def _cpu_model():

@@ -359,6 +359,21 @@ SSD_API int ssd_verify_round(const void* target_logits, int64_t target_bstride,
                              int32_t* accepted, int32_t* out_tokens, uint8_t* hit, int32_t* slot,
                              void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* ssd_verify_round for callers that time its launches (profilers, the
+ * bench): marks is NULL or a host array of four hipEvent_t (created by the
+ * caller on the device of hip_stream), recorded on hip_stream before the
+ * chunk pass, after it, after the cache merge and after the residual
+ * launch, so that elapsed times between them give each launch's duration.
+ * Recording adds three event packets to the stream; everything else, the
+ * arguments and the outputs, are those of ssd_verify_round. */
+SSD_API int ssd_verify_round_marked(const void* target_logits, int64_t target_bstride,
+                                    const void* draft_logits, int64_t draft_bstride, int dtype,
+                                    int32_t B, int32_t K, int32_t V, float tau, const int32_t* F, float C,
+                                    const int32_t* draft_tokens, const float* u_acc, const float* u_res,
+                                    int32_t* cache_tokens, ssd_rowkey* thr, double* draft_stats,
+                                    int32_t* accepted, int32_t* out_tokens, uint8_t* hit, int32_t* slot,
+                                    void* workspace, size_t ws_bytes, void* hip_stream, void* const* marks);
+
 /* Cache hit of the realised outcome ([SSD-notes] framework: the round's
  * outcome (k, t*) hits iff it is among the prepared keys): hit[b] = 1 iff
  * t* = out_tokens[b, a] lies in segment a of cache_tokens row b, with

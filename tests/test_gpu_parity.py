@@ -631,3 +631,23 @@ def test_verify_round_extremes(S):
         d["target"][1] = -np.inf                      # a row without mass: empty p
         d["draft"][2, 0] = -np.inf                    # a draft row without mass
         _round_vs_separate(S, d, [4, 0, 64, 3], 0.0, f"round tau{tau}")
+
+
+def test_verify_round_marked_matches_round(S):
+    """ssd_verify_round_marked: the same outputs as ssd_verify_round, and the
+    four events recorded in launch order (non-negative elapsed times)."""
+    log("[gpu] verify round marked")
+    B, K, V = 9, 3, 20000
+    d = _random_case(77, B, K, V, "bf16", 0.8, Kd=K + 1)
+    F = [5, 4, 3, 6]
+    tgt, dft = to_dev(d["target"], torch), to_dev(d["draft"], torch)
+    toks, ua, ur = ivec(d["tokens"], torch), fvec(d["u_acc"], torch), fvec(d["u_res"], torch)
+    plain = S.ssd_verify_round(tgt, dft, F, 0.5, toks, ua, ur, d["tau"])
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    marked = S.ssd_verify_round(tgt, dft, F, 0.5, toks, ua, ur, d["tau"], marks=marks)
+    torch.cuda.synchronize()
+    for k in plain:
+        if isinstance(plain[k], torch.Tensor):
+            assert torch.equal(plain[k], marked[k]), k
+    for i in range(3):
+        assert marks[i].elapsed_time(marks[i + 1]) >= 0.0

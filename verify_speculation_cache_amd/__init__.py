@@ -31,8 +31,8 @@ EXPORTS = ("ssd_last_error", "ssd_fanout", "ssd_verify_workspace_size", "ssd_ver
            "ssd_draft_sample_workspace_size", "ssd_draft_sample",
            "ssd_verify_greedy_workspace_size", "ssd_verify_greedy", "ssd_fanout_uniform", "ssd_speedup",
            "ssd_cache_stats", "ssd_tree_rounds", "ssd_verify_tree_workspace_size", "ssd_verify_tree",
-           "ssd_verify_round_workspace_size", "ssd_verify_round", "ssd_noalloc_scratch_bytes",
-           "ssd_verify_noalloc")
+           "ssd_verify_round_workspace_size", "ssd_verify_round", "ssd_verify_round_marked",
+           "ssd_noalloc_scratch_bytes", "ssd_verify_noalloc")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -86,6 +86,9 @@ _SIGS = {
     "ssd_verify_round_workspace_size": (_sz, [_i32, _i32, _i32, ctypes.c_int]),
     "ssd_verify_round": (ctypes.c_int, [_vp, _i64, _vp, _i64, ctypes.c_int, _i32, _i32, _i32, _f32, _vp, _f32,
                                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ssd_verify_round_marked": (ctypes.c_int, [_vp, _i64, _vp, _i64, ctypes.c_int, _i32, _i32, _i32, _f32, _vp,
+                                               _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                               _vp, _vp]),
     "ssd_verify_tree_workspace_size": (_sz, [_i32, _i32, _i32, ctypes.c_int]),
     "ssd_verify_tree": (ctypes.c_int, [_vp, _i64, _vp, _i64, ctypes.c_int, _i32, _i32, _i32, _f32, _vp,
                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -510,11 +513,13 @@ def ssd_verify_round_workspace_size(B, K, V, dtype) -> int:
 
 
 def ssd_verify_round(target, draft, F: Sequence[int], C: float, draft_tokens, u_acc, u_res, tau: float, *,
-                     out: Optional[dict] = None, stream=None) -> dict:
+                     out: Optional[dict] = None, stream=None, marks=None) -> dict:
     """One verification round with the speculation cache: cache build on
     draft rows 0..K, sigma verification, and the hit of the outcome, in three
     launches. Returns the outputs of ssd_build_cache, ssd_verify and
-    ssd_cache_lookup in one dict."""
+    ssd_cache_lookup in one dict. marks: optional four torch.cuda.Event
+    objects, recorded before the chunk pass and after each launch
+    (ssd_verify_round_marked)."""
     torch = _torch()
     B, K = int(draft_tokens.shape[0]), int(draft_tokens.shape[1])
     V = int(target.shape[2])
@@ -539,7 +544,17 @@ def ssd_verify_round(target, draft, F: Sequence[int], C: float, draft_tokens, u_
                "hit": torch.empty(B, dtype=torch.uint8, device=dev),
                "slot": torch.empty(B, dtype=torch.int32, device=dev)}
     ws, wsz = _workspace(ssd_verify_round_workspace_size(B, K, V, dt), dev, ("round", B, K, V, dt), stream)
-    _check(lib().ssd_verify_round(
+    mk = None
+    if marks is not None:
+        if len(marks) != 4:
+            raise ValueError("marks: four events")
+        for ev in marks:
+            if ev.cuda_event == 0:   # torch creates an event at its first record
+                ev.record(torch.cuda.current_stream() if stream is None else stream)
+        mk = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(ev.cuda_event) for ev in marks])
+    fn = lib().ssd_verify_round if mk is None else (
+        lambda *args: lib().ssd_verify_round_marked(*args, mk))
+    _check(fn(
         tp, tb, dp, db, dt, B, K, V, float(tau), Fa, float(C),
         _dev(draft_tokens, torch.int32, (B, K), "draft_tokens"), _dev(u_acc, torch.float32, (B, K), "u_acc"),
         _dev(u_res, torch.float32, (B,), "u_res"),

@@ -662,13 +662,13 @@ SSD_API size_t ssd_verify_round_workspace_size(int32_t B, int32_t K, int32_t V, 
   return CacheWs(B, K, S).total + StatsWs(B, K + 1, S, K).total + ResidWs(B, pick_chunks_per_row(V)).total;
 }
 
-SSD_API int ssd_verify_round(const void* target_logits, int64_t target_bstride,
-                             const void* draft_logits, int64_t draft_bstride, int dtype,
-                             int32_t B, int32_t K, int32_t V, float tau, const int32_t* F, float C,
-                             const int32_t* draft_tokens, const float* u_acc, const float* u_res,
-                             int32_t* cache_tokens, ssd_rowkey* thr, double* draft_stats,
-                             int32_t* accepted, int32_t* out_tokens, uint8_t* hit, int32_t* slot,
-                             void* workspace, size_t ws_bytes, void* hip_stream) {
+SSD_API int ssd_verify_round_marked(const void* target_logits, int64_t target_bstride,
+                                    const void* draft_logits, int64_t draft_bstride, int dtype,
+                                    int32_t B, int32_t K, int32_t V, float tau, const int32_t* F, float C,
+                                    const int32_t* draft_tokens, const float* u_acc, const float* u_res,
+                                    int32_t* cache_tokens, ssd_rowkey* thr, double* draft_stats,
+                                    int32_t* accepted, int32_t* out_tokens, uint8_t* hit, int32_t* slot,
+                                    void* workspace, size_t ws_bytes, void* hip_stream, void* const* marks) {
   int st;
   if (!dtype_ok(dtype)) return fail(SSD_EDTYPE, "unknown dtype %d", dtype);
   if ((st = check_shape(B, K, V)) != SSD_OK) return st;
@@ -709,10 +709,19 @@ SSD_API int ssd_verify_round(const void* target_logits, int64_t target_bstride,
   }
   r.hit = hit;
   r.slot = slot;
-  hipStream_t stream = as_stream(hip_stream);
-  if ((st = hip_status(launch_round_chunks(a, dtype, stream), "round chunk launch")) != SSD_OK) return st;
-  if ((st = hip_status(launch_cache_merge(a.c, dtype, stream), "round merge launch")) != SSD_OK) return st;
-  return hip_status(launch_round_resid(rr, dtype, true, stream), "round residual launch");
+  return hip_status(launch_round(a, rr, dtype, as_stream(hip_stream), marks), "round launch");
+}
+
+SSD_API int ssd_verify_round(const void* target_logits, int64_t target_bstride,
+                             const void* draft_logits, int64_t draft_bstride, int dtype,
+                             int32_t B, int32_t K, int32_t V, float tau, const int32_t* F, float C,
+                             const int32_t* draft_tokens, const float* u_acc, const float* u_res,
+                             int32_t* cache_tokens, ssd_rowkey* thr, double* draft_stats,
+                             int32_t* accepted, int32_t* out_tokens, uint8_t* hit, int32_t* slot,
+                             void* workspace, size_t ws_bytes, void* hip_stream) {
+  return ssd_verify_round_marked(target_logits, target_bstride, draft_logits, draft_bstride, dtype, B, K, V, tau,
+                                 F, C, draft_tokens, u_acc, u_res, cache_tokens, thr, draft_stats, accepted,
+                                 out_tokens, hit, slot, workspace, ws_bytes, hip_stream, nullptr);
 }
 
 }  // extern "C"

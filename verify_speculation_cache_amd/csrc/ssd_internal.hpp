@@ -337,5 +337,10 @@ hipError_t launch_round_chunks(const RoundArgs& a, int dtype, hipStream_t st);
 hipError_t launch_cache_merge(const CacheArgs& a, int dtype, hipStream_t st);
 hipError_t launch_round_resid(const RoundResidArgs& a, int dtype, bool sigma, hipStream_t st);
 hipError_t launch_rows_resid(const RoundResidArgs& a, int dtype, bool sigma, hipStream_t st);
+// The three launches of a verification round; with marks (hipEvent_t[4],
+// else NULL) the events are recorded on st before the chunk pass and after
+// each launch.
+hipError_t launch_round(const RoundArgs& a, const RoundResidArgs& rr, int dtype, hipStream_t st,
+                        void* const* marks);
 
 }  // namespace ssd

@@ -86,4 +86,19 @@ hipError_t launch_round_resid(const RoundResidArgs& a, int dtype, bool sigma, hi
   return hipGetLastError();
 }
 
+hipError_t launch_round(const RoundArgs& a, const RoundResidArgs& rr, int dtype, hipStream_t st,
+                        void* const* marks) {
+  auto mark = [&](int i) -> hipError_t {
+    return marks != nullptr ? hipEventRecord(static_cast<hipEvent_t>(marks[i]), st) : hipSuccess;
+  };
+  hipError_t e;
+  if ((e = mark(0)) != hipSuccess) return e;
+  if ((e = launch_round_chunks(a, dtype, st)) != hipSuccess) return e;
+  if ((e = mark(1)) != hipSuccess) return e;
+  if ((e = launch_cache_merge(a.c, dtype, st)) != hipSuccess) return e;
+  if ((e = mark(2)) != hipSuccess) return e;
+  if ((e = launch_round_resid(rr, dtype, true, st)) != hipSuccess) return e;
+  return mark(3);
+}
+
 }  // namespace ssd
