@@ -596,11 +596,14 @@ __device__ __forceinline__ float chunk_rest_mass(const float (&x)[kPerThread], f
 }
 
 // Compacts one wave's candidates (entries >= f0; with CHECK also inside the
-// row) into its LDS staging list, in (entry, lane) order; entries past
-// kCandCap are counted but not kept. Returns the wave's count.
+// row) into its LDS staging lists, in (entry, lane) order: the value's raw
+// bits in wv and the token index in wi (the copy-out forms the keyed
+// records, so the rare taken branch stays short). Entries past kCandCap are
+// counted and written to the spare slot kCandCap, which is never read.
+// Returns the wave's count.
 template <int DT, bool CHECK>
 __device__ __forceinline__ uint32_t wave_compact(const float (&x)[kPerThread], float f0, int tid, int nvalid, int c0,
-                                                 uint64_t* wlist) {
+                                                 uint32_t* wv, int32_t* wi) {
   uint32_t cw = 0;
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
@@ -609,8 +612,10 @@ __device__ __forceinline__ uint32_t wave_compact(const float (&x)[kPerThread], f
     const uint64_t m = __builtin_amdgcn_ballot_w64(cand);
     if (m != 0) {   // wave-uniform
       if (cand) {
-        const uint32_t p = cw + __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
-        if (p < uint32_t(kCandCap)) wlist[p] = cand_bits(key_of<DT>(x[q]), c0 + loc);
+        const uint32_t p = min(cw + __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)),
+                               uint32_t(kCandCap));
+        wv[p] = __float_as_uint(x[q]);
+        wi[p] = c0 + loc;
       }
       cw += uint32_t(__popcll(m));
     }
@@ -646,7 +651,8 @@ __device__ __forceinline__ void cache_chunk_wg(const CacheArgs& a, uint32_t blk)
   __shared__ uint32_t sm_wthq[4];
   __shared__ int sm_wcnt[4];
   __shared__ double sm_ws[4];
-  __shared__ uint64_t sm_list[4][kCandCap];   // per-wave candidate staging
+  __shared__ uint32_t sm_lv[4][kCandCap + 1];   // per-wave candidate staging: value bits,
+  __shared__ int32_t sm_li[4][kCandCap + 1];    // token index (+1: spill slot)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int KP = a.K + 1;
@@ -756,9 +762,9 @@ __device__ __forceinline__ void cache_chunk_wg(const CacheArgs& a, uint32_t blk)
   // ---- candidates (per-wave compaction) and exp-mass of the rest ----
   uint32_t cw;
   if (nvalid < kChunk && f0 == -__builtin_inff())   // padding would pass the test
-    cw = wave_compact<DT, true>(x, f0, tid, nvalid, int(c0), sm_list[w]);
+    cw = wave_compact<DT, true>(x, f0, tid, nvalid, int(c0), sm_lv[w], sm_li[w]);
   else
-    cw = wave_compact<DT, false>(x, f0, tid, nvalid, int(c0), sm_list[w]);
+    cw = wave_compact<DT, false>(x, f0, tid, nvalid, int(c0), sm_lv[w], sm_li[w]);
   const float sn = chunk_rest_mass<DT>(x, f0, sp.P, c32);
   const double ws = wave_sum_u(double(sn));   // double across threads
   if (lane == 0) {
@@ -774,7 +780,8 @@ __device__ __forceinline__ void cache_chunk_wg(const CacheArgs& a, uint32_t blk)
   // ---- candidates out: each wave copies its list, in order ----
   if (!overflow) {
     uint64_t* out = reinterpret_cast<uint64_t*>(a.cand + (rowid * a.S + c) * kCandCap) + woff;
-    for (int i = lane; i < int(cw); i += 64) st64<COH>(out + i, sm_list[w][i]);
+    for (int i = lane; i < int(cw); i += 64)
+      st64<COH>(out + i, cand_bits(key_of<DT>(__uint_as_float(sm_lv[w][i])), sm_li[w][i]));
   }
   if (tid == 0) {
     const double s_rest = ((sm_ws[0] + sm_ws[1]) + (sm_ws[2] + sm_ws[3])) * double(sp.fix);

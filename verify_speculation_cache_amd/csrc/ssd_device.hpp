@@ -325,8 +325,13 @@ __device__ __forceinline__ float movf(float old, float v) {
 template <int CTRL, int ROWS = 0xF>
 __device__ __forceinline__ double movd(double v) {   // 0.0 where the row is masked
   const uint64_t b = uint64_t(__double_as_longlong(v));
-  const int lo = mov<CTRL, ROWS>(0, int(uint32_t(b)));
-  const int hi = mov<CTRL, ROWS>(0, int(uint32_t(b >> 32)));
+  // the quad permutes and mirrors write every lane, so `old` is never used
+  // there: passing the source saves materialising the zero (shifts and
+  // masked broadcasts leave lanes at `old`, which must stay 0)
+  constexpr bool all = ROWS == 0xF && (CTRL == kXor1 || CTRL == kXor2 || CTRL == kHalfMirror || CTRL == kMirror);
+  const int ol = all ? int(uint32_t(b)) : 0, oh = all ? int(uint32_t(b >> 32)) : 0;
+  const int lo = mov<CTRL, ROWS>(ol, int(uint32_t(b)));
+  const int hi = mov<CTRL, ROWS>(oh, int(uint32_t(b >> 32)));
   return __longlong_as_double(int64_t((uint64_t(uint32_t(hi)) << 32) | uint32_t(lo)));
 }
 __device__ __forceinline__ float lane63f(float v) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63)); }
@@ -338,16 +343,24 @@ __device__ __forceinline__ double lane63d(double v) {
 }
 }  // namespace dpp
 
-// wave max of a float, uniform result (fmaxf ignores NaN operands)
+// wave max of a float, uniform result (NaN operands are ignored, as fmaxf
+// does). The max runs on a signed-integer image of the bits that orders
+// floats as their values (-0 just below +0), so each step is one DPP max.
 __device__ __forceinline__ float wave_max_u(float v) {
   using namespace dpp;
-  v = fmaxf(v, movf<kXor1>(v, v));
-  v = fmaxf(v, movf<kXor2>(v, v));
-  v = fmaxf(v, movf<kHalfMirror>(v, v));
-  v = fmaxf(v, movf<kMirror>(v, v));
-  v = fmaxf(v, movf<kBcast15, 0xA>(v, v));
-  v = fmaxf(v, movf<kBcast31, 0xC>(v, v));
-  return lane63f(v);
+  int i = __float_as_int(v == v ? v : -__builtin_inff());
+  i ^= (i >> 31) & 0x7FFFFFFF;
+  auto mx = [](int a, int b) { return a > b ? a : b; };
+  const int id = int(0x80000000u);   // identity of the max for rows a row_mask leaves out
+  i = mx(i, mov<kXor1>(id, i));
+  i = mx(i, mov<kXor2>(id, i));
+  i = mx(i, mov<kHalfMirror>(id, i));
+  i = mx(i, mov<kMirror>(id, i));
+  i = mx(i, mov<kBcast15, 0xA>(id, i));
+  i = mx(i, mov<kBcast31, 0xC>(id, i));
+  i = __builtin_amdgcn_readlane(i, 63);
+  i ^= (i >> 31) & 0x7FFFFFFF;
+  return __int_as_float(i);
 }
 // wave min of an unsigned int, uniform result
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
