@@ -46,7 +46,50 @@ static int g_fail = 0;
 
 static void* fake(uintptr_t i) { return reinterpret_cast<void*>((i + 1) << 12); }
 
+// The launchers' magic-number division (make_fastdiv), evaluated as the
+// kernels do, against integer division: every divisor up to 4096 with
+// dividends near multiples of it and at the ends of [0, 2^31), powers of two
+// and a spread of large divisors.
+static void check_fastdiv() {
+  auto fd = [](uint32_t n, ssd::FastDiv f) {
+    return uint32_t(((uint64_t(n) * f.m >> 32) + n) >> f.s);
+  };
+  auto chk = [&](uint32_t n, uint32_t d, ssd::FastDiv f) {
+    if (fd(n, f) != n / d) {
+      std::fprintf(stderr, "FAIL fastdiv n=%u d=%u\n", n, d);
+      ++g_fail;
+    }
+  };
+  const uint32_t top = 0x7FFFFFFFu;
+  uint64_t x = 0x9E3779B97F4A7C15ull;   // xorshift dividends
+  auto next = [&]() { x ^= x << 13; x ^= x >> 7; x ^= x << 17; return uint32_t(x & top); };
+  for (uint32_t d = 1; d <= 4096; ++d) {
+    const ssd::FastDiv f = ssd::make_fastdiv(d);
+    for (uint32_t n = 0; n < 2 * d + 3; ++n) chk(n, d, f);
+    for (uint32_t q : {7u, 1000u, top / d - 1}) {
+      const uint64_t n0 = uint64_t(q) * d;
+      for (int o = -1; o <= 1; ++o)
+        if (int64_t(n0) + o >= 0 && int64_t(n0) + o <= int64_t(top)) chk(uint32_t(int64_t(n0) + o), d, f);
+    }
+    for (int t = 0; t < 64; ++t) chk(next(), d, f);
+    chk(top, d, f);
+  }
+  for (int k = 0; k <= 31; ++k) {
+    const uint32_t d = 1u << k;
+    const ssd::FastDiv f = ssd::make_fastdiv(d);
+    for (int t = 0; t < 256; ++t) chk(next(), d, f);
+    chk(top, d, f);
+    chk(d - 1, d, f);
+    if (d <= top) chk(d, d, f);
+  }
+  for (int t = 0; t < 200000; ++t) {
+    const uint32_t d = 1 + next();
+    chk(next(), d, ssd::make_fastdiv(d));
+  }
+}
+
 int main() {
+  check_fastdiv();
   // fan-out: every budget, K and a range of (a_p, r) sums to the budget
   std::vector<int32_t> F(SSD_MAX_K + 1);
   for (int K = 1; K <= SSD_MAX_K; K += 7)

@@ -85,7 +85,10 @@ hipError_t launch_cache_stats(const CacheStatsArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_cache(const CacheArgs& a, int dtype, hipStream_t st) {
+hipError_t launch_cache(const CacheArgs& a0, int dtype, hipStream_t st) {
+  CacheArgs a = a0;
+  a.div_pb = make_fastdiv(uint32_t((a.K + 1) * a.S));
+  a.div_s = make_fastdiv(uint32_t(a.S));
   const unsigned grid = unsigned(int64_t(a.B) * (a.K + 1) * a.S);
   const unsigned rows = unsigned(int64_t(a.B) * (a.K + 1));
   if (dtype == SSD_BF16) {

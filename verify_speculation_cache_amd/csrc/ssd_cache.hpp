@@ -639,11 +639,11 @@ template <> __device__ __forceinline__ uint32_t floor_key<1>(float v) {
   return k;
 }
 
-// The chunk pass of one workgroup; blk = (b * (K+1) + k) * S + c. COH: the
-// record and candidates are read by a merge in the same launch, so they are
-// stored with device-scope stores.
+// The chunk pass of one workgroup over chunk c of draft row k of batch row
+// b. COH: the record and candidates are read by a merge in the same launch,
+// so they are stored with device-scope stores.
 template <int DT, bool COH = false>
-__device__ __forceinline__ void cache_chunk_wg(const CacheArgs& a, uint32_t blk) {
+__device__ __forceinline__ void cache_chunk_at(const CacheArgs& a, int b, int k, int c) {
   using T = typename Dt<DT>::T;
   constexpr int PV = Dt<DT>::kPerVec;
   constexpr int NV = kPerThread / PV;
@@ -656,11 +656,6 @@ __device__ __forceinline__ void cache_chunk_wg(const CacheArgs& a, uint32_t blk)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int KP = a.K + 1;
-  const int per_b = KP * a.S;
-  const int b = blk / per_b;
-  const int rem = blk - b * per_b;
-  const int k = rem / a.S;
-  const int c = rem - k * a.S;
   const int F = a.F[k];
   const int64_t rowid = int64_t(b) * KP + k;
   const T* row = static_cast<const T*>(a.draft) + int64_t(b) * a.db + int64_t(k) * a.V;
@@ -790,6 +785,16 @@ __device__ __forceinline__ void cache_chunk_wg(const CacheArgs& a, uint32_t blk)
     st64<COH>(wp + 1, dbits(s_rest));
     st64<COH>(wp + 2, overflow ? kOverflow : uint64_t(uint32_t(n)));
   }
+}
+
+// The same for workgroup blk = (b * (K+1) + k) * S + c of a one-chunk-per-
+// workgroup grid.
+template <int DT, bool COH = false>
+__device__ __forceinline__ void cache_chunk_wg(const CacheArgs& a, uint32_t blk) {
+  const uint32_t b = fdiv(blk, a.div_pb);
+  const uint32_t rem = blk - b * uint32_t((a.K + 1) * a.S);
+  const uint32_t k = fdiv(rem, a.div_s);
+  cache_chunk_at<DT, COH>(a, int(b), int(k), int(rem - k * uint32_t(a.S)));
 }
 
 }  // namespace ssd

@@ -300,6 +300,11 @@ __device__ __forceinline__ void load_pair(ChunkVecs<DT, STRIDED, PT>& x, const t
   }
 }
 
+// n / d for n < 2^31 (make_fastdiv(d)); uniform operands stay on the scalar unit.
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  return (__umulhi(n, f.m) + n) >> f.s;
+}
+
 // ---- wave64 reductions on DPP lane moves (no LDS traffic) ----
 // Within each row of 16 lanes: quad swaps, half-row mirror, row mirror;
 // across rows: row_bcast15 / row_bcast31 fold rows 0+1 and 2+3, then 0..3.
@@ -325,13 +330,19 @@ __device__ __forceinline__ float movf(float old, float v) {
 template <int CTRL, int ROWS = 0xF>
 __device__ __forceinline__ double movd(double v) {   // 0.0 where the row is masked
   const uint64_t b = uint64_t(__double_as_longlong(v));
-  // the quad permutes and mirrors write every lane, so `old` is never used
-  // there: passing the source saves materialising the zero (shifts and
-  // masked broadcasts leave lanes at `old`, which must stay 0)
-  constexpr bool all = ROWS == 0xF && (CTRL == kXor1 || CTRL == kXor2 || CTRL == kHalfMirror || CTRL == kMirror);
-  const int ol = all ? int(uint32_t(b)) : 0, oh = all ? int(uint32_t(b >> 32)) : 0;
-  const int lo = mov<CTRL, ROWS>(ol, int(uint32_t(b)));
-  const int hi = mov<CTRL, ROWS>(oh, int(uint32_t(b >> 32)));
+  const int lo = mov<CTRL, ROWS>(0, int(uint32_t(b)));
+  const int hi = mov<CTRL, ROWS>(0, int(uint32_t(b >> 32)));
+  return __longlong_as_double(int64_t((uint64_t(uint32_t(hi)) << 32) | uint32_t(lo)));
+}
+// The same move for a reduction read from lane 63 only: no `old` operand.
+// The permutes write every lane; a row broadcast leaves the rows outside its
+// mask unwritten, and lane 63's chain (row 3, then rows 2 and 3) never reads
+// them, so no zero has to be placed first.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ double movd63(double v) {
+  const uint64_t b = uint64_t(__double_as_longlong(v));
+  const int lo = __builtin_amdgcn_mov_dpp(int(uint32_t(b)), CTRL, ROWS, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp(int(uint32_t(b >> 32)), CTRL, ROWS, 0xF, true);
   return __longlong_as_double(int64_t((uint64_t(uint32_t(hi)) << 32) | uint32_t(lo)));
 }
 __device__ __forceinline__ float lane63f(float v) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63)); }
@@ -389,12 +400,12 @@ __device__ __forceinline__ float wave_sum_uf(float v) {
 // wave sum of a double, uniform result (fixed order: deterministic)
 __device__ __forceinline__ double wave_sum_u(double v) {
   using namespace dpp;
-  v += movd<kXor1>(v);
-  v += movd<kXor2>(v);
-  v += movd<kHalfMirror>(v);
-  v += movd<kMirror>(v);
-  v += movd<kBcast15, 0xA>(v);
-  v += movd<kBcast31, 0xC>(v);
+  v += movd63<kXor1>(v);
+  v += movd63<kXor2>(v);
+  v += movd63<kHalfMirror>(v);
+  v += movd63<kMirror>(v);
+  v += movd63<kBcast15, 0xA>(v);
+  v += movd63<kBcast31, 0xC>(v);
   return lane63d(v);
 }
 // inclusive prefix sum of an int over lanes 0..63

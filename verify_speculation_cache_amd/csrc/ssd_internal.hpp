@@ -19,6 +19,26 @@ constexpr int kMaxRows = 2 * SSD_MAX_K + 1;     // rows one verify batch element
 
 inline int64_t chunks_per_row(int64_t V) { return (V + kChunk - 1) / kChunk; }
 
+// Division by a divisor 1 <= d <= 2^31 fixed at launch, for dividends n
+// below 2^31 (workgroup indices): with s = ceil(log2 d) and M =
+// ceil(2^(32+s) / d) = 2^32 + m (m < 2^32 since d > 2^(s-1)), n / d =
+// floor(n * M / 2^(32+s)) = (mulhi(n, m) + n) >> s, the sum staying below
+// 2^32. It is exact: with M * d = 2^(32+s) + e, 0 <= e < d <= 2^s, the term
+// n * e / (d * 2^(32+s)) is below 1/d, less than the gap from n/d to the
+// next integer. The launchers fill these from the argument block's own
+// sizes, so the kernels split a linear workgroup index with a scalar high
+// multiply, an add and a shift instead of a division.
+struct FastDiv {
+  uint32_t m, s;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f{0u, 0u};
+  if (d < 1 || d > (1u << 31)) return f;   // outside the sizes the launchers pass
+  while ((uint64_t(1) << f.s) < d) ++f.s;
+  f.m = uint32_t(((uint64_t(1) << (32 + f.s)) + d - 1) / d - (uint64_t(1) << 32));
+  return f;
+}
+
 // The row-statistics pass reads 64 entries per thread: twice the bytes per
 // workgroup, half the workgroups (dispatching workgroups, not HBM, bounds a
 // one-chunk-per-workgroup pass at this size).
@@ -114,6 +134,7 @@ struct StatsArgs {
   uint32_t* cnt;      // [B] (kCntStride apart)
   RowInfo* info;      // [B]
   uint64_t* zg;       // [B, K]: target | draft logit at the drafted token (floats)
+  FastDiv div_pb, div_s;   // by NR*S and by S: set by the launchers
 };
 
 struct ResidArgs {
@@ -157,6 +178,7 @@ struct CacheArgs {
   CachePartial* part;   // [B, K+1, S]
   Cand* cand;           // [B, K+1, S, kCandCap]
   uint32_t* cnt;        // [B, K+1] (kCntStride apart)
+  FastDiv div_pb, div_s;   // by (K+1)*S and by S: set by the launchers
 };
 
 struct SampleArgs {
@@ -318,6 +340,7 @@ struct RoundArgs {
   CacheArgs c;
   StatsArgs s;
   uint32_t ncw, nsw;    // cache and statistics workgroups per batch row
+  FastDiv div_pb;       // by ncw + nsw: set by the launcher
 };
 struct RoundResidArgs {
   ResidArgs r;

@@ -32,14 +32,18 @@ namespace ssd {
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_round_chunks(RoundArgs a) {
-  const uint32_t per_b = a.ncw + a.nsw;
-  const uint32_t b = blockIdx.x / per_b;
-  const uint32_t rem = blockIdx.x - b * per_b;
+  const uint32_t b = fdiv(blockIdx.x, a.div_pb);
+  const uint32_t rem = blockIdx.x - b * (a.ncw + a.nsw);
   // uniform per workgroup; the statistics chunks are 8192 entries here (32
   // per thread, as the cache chunks), which keeps the launch at the cache
   // pass's register budget
-  if (rem < a.ncw) cache_chunk_wg<DT>(a.c, b * a.ncw + rem);
-  else stats_chunk_wg<DT, kPerThread>(a.s, b * a.nsw + (rem - a.ncw));
+  if (rem < a.ncw) {
+    const uint32_t k = fdiv(rem, a.c.div_s);
+    cache_chunk_at<DT>(a.c, int(b), int(k), int(rem - k * uint32_t(a.c.S)));
+  } else {
+    const uint32_t r = fdiv(rem - a.ncw, a.s.div_s);
+    stats_chunk_at<DT, kPerThread>(a.s, int(b), int(r), int(rem - a.ncw - r * uint32_t(a.s.S)));
+  }
 }
 
 // Also the second launch of ssd_verify (after its statistics chunk pass),
@@ -59,7 +63,11 @@ __global__ __launch_bounds__(kThreads) void k_round_resid(RoundResidArgs a) {
   resid_row_wg<DT, SIG, PT>(a.r, inf, b, c4);
 }
 
-hipError_t launch_round_chunks(const RoundArgs& a, int dtype, hipStream_t st) {
+hipError_t launch_round_chunks(const RoundArgs& a0, int dtype, hipStream_t st) {
+  RoundArgs a = a0;
+  a.div_pb = make_fastdiv(a.ncw + a.nsw);
+  a.c.div_s = make_fastdiv(uint32_t(a.c.S));
+  a.s.div_s = make_fastdiv(uint32_t(a.s.S));
   const unsigned grid = unsigned(int64_t(a.c.B) * (a.ncw + a.nsw));
   if (dtype == SSD_BF16) hipLaunchKernelGGL(k_round_chunks<1>, dim3(grid), dim3(kThreads), 0, st, a);
   else hipLaunchKernelGGL(k_round_chunks<0>, dim3(grid), dim3(kThreads), 0, st, a);

@@ -12,7 +12,10 @@ __global__ __launch_bounds__(kThreads) void k_stats_chunks(StatsArgs a) {
   stats_chunk_wg<DT, PT>(a, blockIdx.x);
 }
 
-hipError_t launch_stats_chunks(const StatsArgs& a, int dtype, hipStream_t st) {
+hipError_t launch_stats_chunks(const StatsArgs& a0, int dtype, hipStream_t st) {
+  StatsArgs a = a0;
+  a.div_pb = make_fastdiv(uint32_t(a.NR * a.S));
+  a.div_s = make_fastdiv(uint32_t(a.S));
   const dim3 grid(unsigned(int64_t(a.B) * a.NR * a.S));
   const bool small = a.pt == kSmallPerThread;
   if (dtype == SSD_BF16) {

@@ -79,6 +79,10 @@ __device__ __forceinline__ void stats_chunk_at(const StatsArgs& a, int b, int r,
   if (row != nullptr) {  // uniform per workgroup
     using CV = ChunkVecs<DT, true, PT>;
     const int64_t c0 = int64_t(c) * kSpan;
+    CV cv;
+    cv.load(row, c0, a.V, (reinterpret_cast<uintptr_t>(row) & 15u) == 0, tid);
+    // the chunk's loads are in flight before the drafted token is read
+    __builtin_amdgcn_sched_barrier(0);
     // The workgroup whose chunk holds drafted token d_r (target row r < K)
     // also fetches z_t(d_r) and z_d(d_r) for the accept test, so the
     // epilogue finds them with the partials.
@@ -90,8 +94,6 @@ __device__ __forceinline__ void stats_chunk_at(const StatsArgs& a, int b, int r,
       gzt = load_one<DT>(a.target, int64_t(b) * a.tb + int64_t(r) * a.V + dtok);
       gzd = load_one<DT>(a.draft, int64_t(b) * a.db + int64_t(r) * a.V + dtok);
     }
-    CV cv;
-    cv.load(row, c0, a.V, (reinterpret_cast<uintptr_t>(row) & 15u) == 0, tid);
     float m;
     double sd;
     chunk_max_sum(cv, a.c32, sm_f, sm_s, m, sd);
@@ -108,11 +110,10 @@ __device__ __forceinline__ void stats_chunk_at(const StatsArgs& a, int b, int r,
 // workgroup grid.
 template <int DT, int PT = kStatsPerThread>
 __device__ __forceinline__ void stats_chunk_wg(const StatsArgs& a, uint32_t blk) {
-  const int per_b = a.NR * a.S;
-  const int b = blk / per_b;
-  const int rem = blk - b * per_b;
-  const int r = rem / a.S;
-  stats_chunk_at<DT, PT>(a, b, r, rem - r * a.S);
+  const uint32_t b = fdiv(blk, a.div_pb);
+  const uint32_t rem = blk - b * uint32_t(a.NR * a.S);
+  const uint32_t r = fdiv(rem, a.div_s);
+  stats_chunk_at<DT, PT>(a, int(b), int(r), int(rem - r * uint32_t(a.S)));
 }
 
 // Row max pivots and sums of the a.NR logit rows of batch row b, merged
