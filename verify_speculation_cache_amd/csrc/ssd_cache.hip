@@ -89,6 +89,7 @@ hipError_t launch_cache(const CacheArgs& a0, int dtype, hipStream_t st) {
   CacheArgs a = a0;
   a.div_pb = make_fastdiv(uint32_t((a.K + 1) * a.S));
   a.div_s = make_fastdiv(uint32_t(a.S));
+  a.div_kp = make_fastdiv(uint32_t(a.K + 1));
   const unsigned grid = unsigned(int64_t(a.B) * (a.K + 1) * a.S);
   const unsigned rows = unsigned(int64_t(a.B) * (a.K + 1));
   if (dtype == SSD_BF16) {
@@ -101,7 +102,9 @@ hipError_t launch_cache(const CacheArgs& a0, int dtype, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_cache_merge(const CacheArgs& a, int dtype, hipStream_t st) {
+hipError_t launch_cache_merge(const CacheArgs& a0, int dtype, hipStream_t st) {
+  CacheArgs a = a0;
+  a.div_kp = make_fastdiv(uint32_t(a.K + 1));
   const unsigned rows = unsigned(int64_t(a.B) * (a.K + 1));
   if (dtype == SSD_BF16) hipLaunchKernelGGL(k_cache_merge<1>, dim3(rows), dim3(kThreads), 0, st, a);
   else hipLaunchKernelGGL(k_cache_merge<0>, dim3(rows), dim3(kThreads), 0, st, a);

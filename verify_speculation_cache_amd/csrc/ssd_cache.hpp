@@ -176,8 +176,7 @@ struct HeldMap {
   int chunk, pos, step;   // this thread's chunk, first position, position step
 };
 __device__ __forceinline__ HeldMap held_map(int S, int tid) {
-  int lg = 0;
-  while ((1 << lg) < S && lg < 8) ++lg;
+  const int lg = S <= 1 ? 0 : min(8, 32 - __clz(S - 1));   // ceil(log2 S), at most 8
   const int P = kThreads >> lg;
   return HeldMap{tid / P, tid % P, P};
 }
@@ -260,8 +259,8 @@ template <int DT, bool COH = false>
 __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid) {
   using T = typename Dt<DT>::T;
   const int KP = a.K + 1;
-  const int b = int(rowid / KP);
-  const int k = int(rowid - int64_t(b) * KP);
+  const int b = int(fdiv(uint32_t(rowid), a.div_kp));   // rowid < 2^31 (the grid)
+  const int k = int(rowid) - b * KP;
   const int F = a.F[k];
   __shared__ uint64_t s_list[kFiltCap];
   __shared__ double s_exp[kFiltCap];

@@ -26,9 +26,9 @@ __global__ __launch_bounds__(kThreads) void k_greedy(GreedyArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int KP = a.K + 1;
   const int per_b = KP * a.S;
-  const int b = blockIdx.x / per_b;
+  const int b = int(fdiv(blockIdx.x, a.div_pb));
   const int rem = blockIdx.x - b * per_b;
-  const int r = rem / a.S;
+  const int r = int(fdiv(uint32_t(rem), a.div_s));
   const int c = rem - r * a.S;
   const T* row = static_cast<const T*>(a.target) + int64_t(b) * a.tb + int64_t(r) * a.V;
 
@@ -118,7 +118,10 @@ __global__ __launch_bounds__(kThreads) void k_greedy(GreedyArgs a) {
   }
 }
 
-hipError_t launch_greedy(const GreedyArgs& a, int dtype, hipStream_t st) {
+hipError_t launch_greedy(const GreedyArgs& a0, int dtype, hipStream_t st) {
+  GreedyArgs a = a0;
+  a.div_pb = make_fastdiv(uint32_t((a.K + 1) * a.S));
+  a.div_s = make_fastdiv(uint32_t(a.S));
   const unsigned grid = unsigned(int64_t(a.B) * (a.K + 1) * a.S);
   if (dtype == SSD_BF16) hipLaunchKernelGGL(k_greedy<1>, dim3(grid), dim3(kThreads), 0, st, a);
   else hipLaunchKernelGGL(k_greedy<0>, dim3(grid), dim3(kThreads), 0, st, a);

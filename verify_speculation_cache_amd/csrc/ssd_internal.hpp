@@ -150,6 +150,7 @@ struct ResidArgs {
   double* cmass;       // [B, S, 2]: residual mass, target mass per chunk (S chunks of kPickChunk
                        // for the one-path draw, of kChunk for the token-tree rounds)
   uint32_t* cnt;       // [B] (kCntStride apart)
+  FastDiv div_nw;      // by the first-phase workgroups per row: set by the launchers
   int32_t* tok_out;    // token written at tok_out[b * tok_stride + (tok_at_a ? a : 0)]
   int64_t tok_stride;
   int tok_at_a;
@@ -178,7 +179,7 @@ struct CacheArgs {
   CachePartial* part;   // [B, K+1, S]
   Cand* cand;           // [B, K+1, S, kCandCap]
   uint32_t* cnt;        // [B, K+1] (kCntStride apart)
-  FastDiv div_pb, div_s;   // by (K+1)*S and by S: set by the launchers
+  FastDiv div_pb, div_s, div_kp;   // by (K+1)*S, by S, by K+1: set by the launchers
 };
 
 struct SampleArgs {
@@ -191,6 +192,7 @@ struct SampleArgs {
   const float* u;           // [B, K]
   int32_t* tok_out;         // [B, K]
   RowPartial* part;         // [B*K, S]
+  FastDiv div_s2, div_k;    // by (S+1)/2 and by K: set by the launcher
 };
 
 struct LookupArgs {
@@ -258,6 +260,7 @@ struct GreedyArgs {
   int32_t* out_tokens;       // [B, K+1]
   uint64_t* part;            // [B, K+1, S]: chunk max (float bits) | argmax index << 32
   uint32_t* cnt;             // [B] (kCntStride apart)
+  FastDiv div_pb, div_s;     // by (K+1)*S and by S: set by the launcher
 };
 
 struct GreedyWs {
@@ -317,6 +320,7 @@ struct TreeArgs {
   TreeState* state;         // [B]
   double* cmass;            // [B, S, 2]
   uint32_t* cnt_round;      // [B] (kCntStride apart)
+  FastDiv div_pb, div_ss, div_s;   // by NR*SS, by SS, by S: set by the launchers
 };
 
 struct TreeWs {

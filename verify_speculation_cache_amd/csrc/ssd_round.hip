@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kThreads) void k_round_resid(RoundResidArgs a) {
   __shared__ double e_s[kMaxRows];
   __shared__ RowInfo sm_inf;
   const int nw = resid_wgs_per_row(a.r.S, PT);
-  const int b = blockIdx.x / nw;
+  const int b = int(fdiv(blockIdx.x, a.r.div_nw));
   const int c4 = blockIdx.x - b * nw;
   // the row's first workgroup also stores accepted[b], out_tokens, probs and
   // the optional row log-normalisers
@@ -82,7 +82,9 @@ static void launch_round_resid_t(const RoundResidArgs& a, unsigned grid, hipStre
     hipLaunchKernelGGL((k_round_resid<DT, SIG, kStatsPerThread>), dim3(grid), dim3(kThreads), 0, st, a);
 }
 
-hipError_t launch_round_resid(const RoundResidArgs& a, int dtype, bool sigma, hipStream_t st) {
+hipError_t launch_round_resid(const RoundResidArgs& a0, int dtype, bool sigma, hipStream_t st) {
+  RoundResidArgs a = a0;
+  a.r.div_nw = make_fastdiv(uint32_t(resid_wgs_per_row(a.r.S, a.r.span_pt)));
   const unsigned grid = unsigned(int64_t(a.r.B) * resid_wgs_per_row(a.r.S, a.r.span_pt));
   if (dtype == SSD_BF16) {
     if (sigma) launch_round_resid_t<1, true>(a, grid, st);

@@ -57,9 +57,9 @@ __global__ __launch_bounds__(kThreads) void k_sample_chunks(SampleArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int S2 = (a.S + 1) / 2;   // workgroups per row, two 8192-chunks each
-  const int64_t rowid = blockIdx.x / S2;
+  const int64_t rowid = fdiv(blockIdx.x, a.div_s2);
   const int c2 = int(blockIdx.x - rowid * S2);
-  const int b = int(rowid / a.K);
+  const int b = int(fdiv(uint32_t(rowid), a.div_k));
   const int i = int(rowid - int64_t(b) * a.K);
   const T* row = static_cast<const T*>(a.draft) + int64_t(b) * a.db + int64_t(i) * a.V;
   const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void k_sample_pick(SampleArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t rowid = blockIdx.x;
-  const int b = int(rowid / a.K);
+  const int b = int(fdiv(uint32_t(rowid), a.div_k));
   const int i = int(rowid - int64_t(b) * a.K);
   const T* row = static_cast<const T*>(a.draft) + int64_t(b) * a.db + int64_t(i) * a.V;
   const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
@@ -196,7 +196,10 @@ __global__ __launch_bounds__(kThreads) void k_sample_pick(SampleArgs a) {
 }
 
 template <int DT, bool SIG>
-static hipError_t launch_sample_t(const SampleArgs& a, hipStream_t st) {
+static hipError_t launch_sample_t(const SampleArgs& a0, hipStream_t st) {
+  SampleArgs a = a0;
+  a.div_s2 = make_fastdiv(uint32_t((a.S + 1) / 2));
+  a.div_k = make_fastdiv(uint32_t(a.K));
   const int64_t rows = int64_t(a.B) * a.K;
   hipLaunchKernelGGL((k_sample_chunks<DT, SIG>), dim3(unsigned(rows * ((a.S + 1) / 2))), dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();

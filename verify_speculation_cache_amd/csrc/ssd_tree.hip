@@ -77,9 +77,9 @@ __global__ __launch_bounds__(kThreads) void k_tree_stats(TreeArgs a) {
 
   const int tid = threadIdx.x;
   const int per_b = a.NR * a.SS;
-  const int b = blockIdx.x / per_b;
+  const int b = int(fdiv(blockIdx.x, a.div_pb));
   const int rem = blockIdx.x - b * per_b;
-  const int r = rem / a.SS;
+  const int r = int(fdiv(uint32_t(rem), a.div_ss));
   const int c = rem - r * a.SS;
 
   const typename Dt<DT>::T* row = tree_row<DT>(a, b, r);
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_round(TreeArgs a) {
   __shared__ int sm_bad;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int b = blockIdx.x / a.S;
+  const int b = int(fdiv(blockIdx.x, a.div_s));
   const int c = blockIdx.x - b * a.S;
   TreeState st;
   if (FIRST) {
@@ -333,14 +333,19 @@ __global__ __launch_bounds__(kThreads) void k_tree_round(TreeArgs a) {
   }
 }
 
-hipError_t launch_tree_stats(const TreeArgs& a, int dtype, hipStream_t st) {
+hipError_t launch_tree_stats(const TreeArgs& a0, int dtype, hipStream_t st) {
+  TreeArgs a = a0;
+  a.div_pb = make_fastdiv(uint32_t(a.NR * a.SS));
+  a.div_ss = make_fastdiv(uint32_t(a.SS));
   const unsigned grid = unsigned(int64_t(a.B) * a.NR * a.SS);
   if (dtype == SSD_BF16) hipLaunchKernelGGL(k_tree_stats<1>, dim3(grid), dim3(kThreads), 0, st, a);
   else hipLaunchKernelGGL(k_tree_stats<0>, dim3(grid), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_tree_round(const TreeArgs& a, int dtype, bool first, hipStream_t st) {
+hipError_t launch_tree_round(const TreeArgs& a0, int dtype, bool first, hipStream_t st) {
+  TreeArgs a = a0;
+  a.div_s = make_fastdiv(uint32_t(a.S));
   const unsigned grid = unsigned(int64_t(a.B) * a.S);
   if (dtype == SSD_BF16) {
     if (first) hipLaunchKernelGGL((k_tree_round<1, true>), dim3(grid), dim3(kThreads), 0, st, a);
