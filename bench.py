@@ -234,7 +234,7 @@ def main():
         S.ssd_verify_round(tgts[j], dfts[j], F, C, toks, ua, ur, tau, out=rounds[j], marks=marks[i])
     torch.cuda.synchronize()
     launch_ms = {name: float(np.mean([m[k].elapsed_time(m[k + 1]) for m in marks[n_mark // 6:]]))
-                 for k, name in enumerate(("k_round_chunks", "k_cache_merge", "k_round_resid"))}
+                 for k, name in enumerate(("k_round_chunks", "k_round_merge_stats", "k_round_resid"))}
     for j in range(ncopy):   # the marked calls wrote the same outputs
         assert torch.equal(rounds[j]["accepted"], round_ref[j][0]) and torch.equal(rounds[j]["hit"], round_ref[j][2])
 
@@ -265,17 +265,21 @@ def main():
                     "kernel": "ssd_build_cache (k_cache_chunk + k_cache_merge, bf16)",
                     "bytes_per_launch": bytes_build, "avg_launch_ms": round(dom_ms, 5)}
     else:
-        # dominant kernel of the step: k_round_chunks, the one launch that
-        # streams every logit of the step once (target rows 0..K for the row
-        # statistics, draft rows 0..K for the cache), timed by the marks
+        # dominant kernel of the step: k_round_chunks, the launch that
+        # streams draft rows 0..K for the cache and target rows 0..na-1 for
+        # the row statistics (na = floor(2(K+1)/3), the split documented with
+        # ssd_verify_round; the second launch streams the other target rows
+        # beside the cache merges), timed by the marks
+        na = 2 * (K + 1) // 3
+        dom_bytes = B * (K + 1 + na) * V * tgt0.element_size()
         dom_ms = launch_ms["k_round_chunks"]
-        dom_gbps = step_bytes / (dom_ms / 1e3) / 1e9
+        dom_gbps = dom_bytes / (dom_ms / 1e3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(dom_gbps / PEAK_HBM_GBS, 4),
                     "traffic": measured_traffic(ROUND_BYTES_PROFILE, "k_round_chunks<1>"),
-                    "kernel": "k_round_chunks (cache chunk pass over draft rows 0..5 + row-statistics chunk pass "
-                              "over target rows 0..5, bf16)",
-                    "bytes_per_launch": step_bytes, "avg_launch_ms": round(dom_ms, 5),
+                    "kernel": f"k_round_chunks (cache chunk pass over draft rows 0..{K} + row-statistics chunk "
+                              f"pass over target rows 0..{na - 1}, bf16)",
+                    "bytes_per_launch": dom_bytes, "avg_launch_ms": round(dom_ms, 5),
                     "launches_timed": n_mark - n_mark // 6}
 
     cpu, check = None, None

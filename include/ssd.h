@@ -338,10 +338,12 @@ SSD_API size_t ssd_verify_round_workspace_size(int32_t B, int32_t K, int32_t V, 
  * outputs are bit-identical to ssd_build_cache's; the row sums of the
  * verification add 8192-entry chunk partials (ssd_verify: 16384), so an
  * outcome can differ from the three calls' only where a decision lies within
- * rounding of its threshold. Three launches instead of five: the cache's and
- * the row statistics' chunk passes share one, the cache merge follows, and
- * each residual workgroup runs its batch row's accept scan before its share
- * of the draw (the lookup in the draw's last workgroup).
+ * rounding of its threshold. Three launches instead of five: the first
+ * streams draft rows 0..K for the cache and target rows 0..na-1 for the row
+ * statistics (na = floor(2(K+1)/3)); the second runs every cache merge
+ * beside the statistics of target rows na..K; and each residual workgroup
+ * runs its batch row's accept scan before its share of the draw (the lookup
+ * in the draw's last workgroup).
  *   target_logits device [B, K+1, V]; draft_logits device [B, >=K+1, V]
  *   F host int32 [K+1] (0 <= F_k <= min(V, 64)); C in [0, 1]
  *   draft_tokens device int32 [B, K] (drawn from q_sigma, e.g. by
@@ -362,8 +364,10 @@ SSD_API int ssd_verify_round(const void* target_logits, int64_t target_bstride,
 /* ssd_verify_round for callers that time its launches (profilers, the
  * bench): marks is NULL or a host array of four hipEvent_t (created by the
  * caller on the device of hip_stream), recorded on hip_stream before the
- * chunk pass, after it, after the cache merge and after the residual
- * launch, so that elapsed times between them give each launch's duration.
+ * first launch (the cache chunk pass with the statistics of target rows
+ * 0..na-1), after it, after the second (the cache merges with the
+ * statistics of target rows na..K) and after the residual launch, so that
+ * elapsed times between them give each launch's duration.
  * Recording adds three event packets to the stream; everything else, the
  * arguments and the outputs, are those of ssd_verify_round. */
 SSD_API int ssd_verify_round_marked(const void* target_logits, int64_t target_bstride,

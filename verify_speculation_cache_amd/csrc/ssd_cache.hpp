@@ -154,22 +154,32 @@ __device__ __forceinline__ uint32_t exact_top_f(const typename Dt<DT>::T* row, i
   return gmask | keep;
 }
 
-constexpr int kHold = 16;        // candidate slots each merge thread holds in registers
+constexpr int kHold = 16;        // candidate slots a merge thread holds in registers (own launch)
+constexpr int kHoldLean = 4;     // the same where the merge shares a launch with streaming work
 constexpr int kCountLds = 256;   // chunk candidate counts kept in LDS by the merge
-constexpr int kHeldChunks = 32;  // rows of at most this many chunks keep their candidates in registers
+constexpr int kHeldChunks = 32;  // rows of at most this many chunks use the chunk-major map
 
 // The candidate slots of one row, as seen by one merge thread. Rows of at
-// most kHeldChunks chunks are held in registers, chunk-major: with G the
-// chunk count rounded up to a power of two and P = 256 / G, thread tid
-// serves chunk tid / P at positions tid % P + P * i, i < kHold, which
-// covers every slot of the chunk. A thread's valid slots are a prefix of
-// its i, a chunk's candidates spread over its P threads, and one wave load
-// instruction reads 64 / P runs of P consecutive slots. They are loaded
-// once, in the round trip of the chunk records. Longer rows stream their
-// slots on every visit.
+// most kHeldChunks chunks use a chunk-major map: with G the chunk count
+// rounded up to a power of two and P = 256 / G, thread tid serves chunk
+// tid / P at positions tid % P + P * i, i < 128 / P, which covers every
+// slot of the chunk. A thread's valid slots are a prefix of its i, a
+// chunk's candidates spread over its P threads, and one wave load
+// instruction reads 64 / P runs of P consecutive slots. The first HOLD
+// positions (kHold, or kHoldLean where the merge shares a launch) are loaded
+// in the round trip of the chunk records and kept in registers (they hold
+// every candidate of a chunk with up to HOLD * P of them); later positions
+// are read when a visit reaches them, in the same order, and only while
+// some lane of the wave has one. Longer rows stream their slots on every
+// visit (thread tid: slots tid, tid + 256, ...). Either way each thread
+// meets its candidates in the same order for every HOLD, so both forms of
+// the merge give bit-identical results.
+template <int HOLD>
 struct RowCands {
-  uint64_t v[kHold];
-  uint32_t ok;   // bit i: slot i holds a written candidate
+  uint64_t v[HOLD];
+  uint32_t ok;          // bit i: slot i holds a written candidate
+  const uint64_t* base; // this thread's chunk's slots
+  int pos, step, nc;    // first position, position step, the chunk's candidate count
 };
 
 struct HeldMap {
@@ -181,22 +191,37 @@ __device__ __forceinline__ HeldMap held_map(int S, int tid) {
   return HeldMap{tid / P, tid % P, P};
 }
 
-// f(e) for every written candidate of the row, each visited by one thread.
-template <bool COH, typename Fn>
-__device__ __forceinline__ void visit(const RowCands& rc, bool held, const uint64_t* pp, const int* cnt_lds,
+// f(e) for every written candidate of the row, each visited by one thread
+// (a thread's candidates in the order of its positions).
+template <bool COH, int HOLD, typename Fn>
+__device__ __forceinline__ void visit(const RowCands<HOLD>& rc, bool held, const uint64_t* pp, const int* cnt_lds,
                                       const uint64_t* cl, int S, Fn f) {
   if (held) {
 #pragma unroll
-    for (int i = 0; i < kHold; ++i)
+    for (int i = 0; i < HOLD; ++i)
       if ((rc.ok >> i) & 1u) f(rc.v[i]);
+    for (int i0 = HOLD; rc.step * i0 < kCandCap; i0 += HOLD) {
+      if (__builtin_amdgcn_ballot_w64(rc.pos + rc.step * i0 < rc.nc) == 0) break;   // wave-uniform
+      uint64_t e[HOLD];
+      bool ok[HOLD];
+#pragma unroll
+      for (int i = 0; i < HOLD; ++i) {
+        const int p = rc.pos + rc.step * (i0 + i);
+        ok[i] = p < rc.nc;
+        e[i] = ok[i] ? ld64<COH>(rc.base + p) : 0ull;
+      }
+#pragma unroll
+      for (int i = 0; i < HOLD; ++i)
+        if (ok[i]) f(e[i]);
+    }
     return;
   }
   const int slots = S * kCandCap;
-  for (int base = 0; base < slots; base += kThreads * kHold) {
-    uint64_t e[kHold];
-    bool ok[kHold];
+  for (int base = 0; base < slots; base += kThreads * HOLD) {
+    uint64_t e[HOLD];
+    bool ok[HOLD];
 #pragma unroll
-    for (int i = 0; i < kHold; ++i) {
+    for (int i = 0; i < HOLD; ++i) {
       const int sidx = base + i * kThreads + int(threadIdx.x);
       ok[i] = false;
       if (sidx < slots) {
@@ -207,19 +232,21 @@ __device__ __forceinline__ void visit(const RowCands& rc, bool held, const uint6
       e[i] = ok[i] ? ld64<COH>(cl + sidx) : 0ull;
     }
 #pragma unroll
-    for (int i = 0; i < kHold; ++i)
+    for (int i = 0; i < HOLD; ++i)
       if (ok[i]) f(e[i]);
   }
 }
 
-// Every thread's held slots, loaded unconditionally (slots past a chunk's
-// count are masked out later; the chunk and position are clamped into the
-// row's slots, so there is no branch around the loads).
-template <bool COH>
-__device__ __forceinline__ void load_held(RowCands& rc, const uint64_t* cl, const HeldMap& hm, int S) {
-  const uint64_t* base = cl + min(hm.chunk, S - 1) * kCandCap;
+// Every thread's first HOLD slots, loaded unconditionally (slots past a
+// chunk's count are masked out later; the chunk and position are clamped
+// into the row's slots, so there is no branch around the loads).
+template <bool COH, int HOLD>
+__device__ __forceinline__ void load_held(RowCands<HOLD>& rc, const uint64_t* cl, const HeldMap& hm, int S) {
+  rc.base = cl + min(hm.chunk, S - 1) * kCandCap;
+  rc.pos = hm.pos;
+  rc.step = hm.step;
 #pragma unroll
-  for (int i = 0; i < kHold; ++i) rc.v[i] = ld64<COH>(base + min(hm.pos + hm.step * i, kCandCap - 1));
+  for (int i = 0; i < HOLD; ++i) rc.v[i] = ld64<COH>(rc.base + min(hm.pos + hm.step * i, kCandCap - 1));
 }
 
 // Appends e to the LDS list when keep holds: one LDS atomic per wave (the
@@ -255,7 +282,7 @@ __device__ __forceinline__ void wave_append(uint64_t e, bool keep, int lane, int
 // read them. COH: the chunk records and candidates were written by other
 // workgroups of the same launch, so they are read (and rewritten) with
 // device-scope accesses, and so are the cache tokens written.
-template <int DT, bool COH = false>
+template <int DT, bool COH = false, int HOLD = kHold>
 __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid) {
   using T = typename Dt<DT>::T;
   const int KP = a.K + 1;
@@ -297,9 +324,9 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
   const uint64_t r0 = ld64<COH>(pp + rl * 4), r1 = ld64<COH>(pp + rl * 4 + 1), r2 = ld64<COH>(pp + rl * 4 + 2);
   const uint64_t own_cnt = ld64<COH>(pp + min(hm.chunk, a.S - 1) * 4 + 2);
   __builtin_amdgcn_sched_barrier(0);
-  RowCands rc;
+  RowCands<HOLD> rc;
   rc.ok = 0;
-  load_held<COH>(rc, cl, hm, a.S);
+  load_held<COH, HOLD>(rc, cl, hm, a.S);
   __builtin_amdgcn_sched_barrier(0);
 
   // row max, the chunks' non-candidate mass (lane-local fold in chunk order,
@@ -369,8 +396,6 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
       const int nvalid = int(min(int64_t(kChunk), int64_t(a.V) - c0));
       uint32_t key_unused;
       const uint32_t sel = exact_top_f<DT>(row, c0, nvalid, F, tid, lane, w, sm_i2, sm_wcnt2, key_unused);
-      float x[kPerThread];
-      load_strided<DT>(row, c0, a.V, (reinterpret_cast<uintptr_t>(row) & 15u) == 0, tid, x);
       const float f0 = threshold_value<DT>(uint32_t(ld64<COH>(pp + cc * 4) >> 32));
       const int nt = __popc(sel);
       const int incl = wave_incl_scan_i(nt, lane);
@@ -380,14 +405,23 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
       for (int ww = 0; ww < w; ++ww) pos += sm_wcnt2[ww];
       const int nsel = (sm_wcnt2[0] + sm_wcnt2[1]) + (sm_wcnt2[2] + sm_wcnt2[3]);
       __syncthreads();
+      // the chunk again, a vector at a time (entry order as in the pass):
+      // selected entries to the slots, the rest at or above T0 to S_rest
+      constexpr int PV = Dt<DT>::kPerVec;
+#pragma unroll 1
+      for (int j = 0; j < kPerThread / PV; ++j) {
+        float v[PV];
+        load_vec<DT>(row, c0, nvalid, tid, j, v);
 #pragma unroll
-      for (int q = 0; q < kPerThread; ++q) {
-        const int loc = local_of<DT>(tid, q);
-        if ((sel >> q) & 1u) {
-          st64<COH>(clw + int64_t(cc) * kCandCap + pos, cand_bits(key_of<DT>(x[q]), int32_t(c0) + loc));
-          ++pos;
-        } else if (loc < nvalid && x[q] >= f0) {
-          s_unsel += double(__builtin_amdgcn_exp2f((x[q] - prow) * c32));
+        for (int e = 0; e < PV; ++e) {
+          const int q = j * PV + e;
+          const int loc = local_of<DT>(tid, q);
+          if ((sel >> q) & 1u) {
+            st64<COH>(clw + int64_t(cc) * kCandCap + pos, cand_bits(key_of<DT>(v[e]), int32_t(c0) + loc));
+            ++pos;
+          } else if (loc < nvalid && v[e] >= f0) {
+            s_unsel += double(__builtin_amdgcn_exp2f((v[e] - prow) * c32));
+          }
         }
       }
       if (tid == 0) {
@@ -398,7 +432,7 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
     }
     __threadfence();
     __syncthreads();
-    load_held<COH>(rc, cl, hm, a.S);   // the rewritten lists
+    load_held<COH, HOLD>(rc, cl, hm, a.S);   // the rewritten lists
   }
 
   if (held) {
@@ -406,8 +440,9 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
     // overflowed chunk was rewritten
     int nc = hm.chunk < a.S ? (own_cnt == kOverflow ? 0 : int(uint32_t(own_cnt))) : 0;
     if (s_anyovf && hm.chunk < a.S) nc = s_cnt[hm.chunk];
+    rc.nc = nc;
 #pragma unroll
-    for (int i = 0; i < kHold; ++i)
+    for (int i = 0; i < HOLD; ++i)
       if (hm.pos + hm.step * i < nc) rc.ok |= 1u << i;
   }
   int32_t* ct = a.cache_tokens + int64_t(b) * a.sumF + a.off[k];
@@ -415,7 +450,7 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
   // candidates at or above Tmax go to the ranked list; the others only add
   // to S_rest
   const uint32_t tcut = s_tmax;
-  visit<COH>(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
+  visit<COH, HOLD>(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
     const bool keep = F > 0 && cand_key(e) >= tcut;
     wave_append(e, keep, lane, &s_n2, s_list);
     if (!keep) s_unsel += cand_mass<DT>(e, prow, c32);
@@ -432,7 +467,7 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
       s_hist[tid] = 0;
       __syncthreads();
       const uint32_t prefix = s_prefix;
-      visit<COH>(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
+      visit<COH, HOLD>(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
         const uint32_t key = cand_key(e);
         const uint32_t hi = (shift + 8 < 32) ? (key >> (shift + 8)) : 0u;
         if (hi == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1);
@@ -479,7 +514,7 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
     const uint32_t cut = s_need == 0 && s_prefix == 0 ? tcut : s_prefix;   // the F-th key
     if (tid == 0) s_n2 = 0;
     __syncthreads();
-    visit<COH>(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
+    visit<COH, HOLD>(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
       if (cand_key(e) < tcut) return;   // already counted
       const bool keep = cand_key(e) >= cut;
       wave_append(e, keep, lane, &s_n2, s_list);
@@ -493,13 +528,13 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
       // more ties at the F-th key than the list holds: the needed ties are
       // the ones with the smallest indices (bitwise search for the index bound)
       int c = 0;
-      visit<COH>(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) { c += cand_key(e) > cut ? 1 : 0; });
+      visit<COH, HOLD>(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) { c += cand_key(e) > cut ? 1 : 0; });
       const int need = F - block_sum_i(c, sm_i2);
       int lim = 0;   // largest bound with fewer than `need` ties below it
       for (int bit = 30; bit >= 0; --bit) {
         const int cand = lim | (1 << bit);
         int cnt = 0;
-        visit<COH>(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
+        visit<COH, HOLD>(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
           cnt += (cand_key(e) == cut && cand_idx(e) < cand) ? 1 : 0;
         });
         if (block_sum_i(cnt, sm_i2) < need) lim = cand;
@@ -507,7 +542,7 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
       // ties with index <= lim are exactly `need` of them
       if (tid == 0) s_n2 = 0;
       __syncthreads();
-      visit<COH>(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
+      visit<COH, HOLD>(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
         if (cand_key(e) < cut) return;   // already counted
         const bool keep = cand_key(e) > cut || cand_idx(e) <= lim;
         wave_append(e, keep, lane, &s_n2, s_list);

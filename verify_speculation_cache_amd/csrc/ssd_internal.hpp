@@ -344,7 +344,8 @@ struct RoundArgs {
   CacheArgs c;
   StatsArgs s;
   uint32_t ncw, nsw;    // cache and statistics workgroups per batch row
-  FastDiv div_pb;       // by ncw + nsw: set by the launcher
+  uint32_t na;          // target rows whose statistics run in the first launch (the rest in the second)
+  FastDiv div_pb, div_pbb;   // by the first and second launch's chunk workgroups per batch row
 };
 struct RoundResidArgs {
   ResidArgs r;
@@ -361,6 +362,7 @@ hipError_t launch_cache_stats(const CacheStatsArgs& a, hipStream_t st);
 hipError_t launch_tree_stats(const TreeArgs& a, int dtype, hipStream_t st);
 hipError_t launch_tree_round(const TreeArgs& a, int dtype, bool first, hipStream_t st);
 hipError_t launch_round_chunks(const RoundArgs& a, int dtype, hipStream_t st);
+hipError_t launch_round_merge_stats(const RoundArgs& a, int dtype, hipStream_t st);
 hipError_t launch_cache_merge(const CacheArgs& a, int dtype, hipStream_t st);
 hipError_t launch_round_resid(const RoundResidArgs& a, int dtype, bool sigma, hipStream_t st);
 hipError_t launch_rows_resid(const RoundResidArgs& a, int dtype, bool sigma, hipStream_t st);

@@ -8,10 +8,19 @@
 // The separate entry points need five launches (cache chunk pass, cache
 // merge, row statistics, residual, lookup). Here three:
 //  k_round_chunks  the cache chunk pass over draft rows 0..K and the row
-//                  statistics' chunk pass over target rows 0..K in one grid
-//                  (they read different rows and depend on nothing), so the
-//                  two streams share one launch and one tail;
-//  k_cache_merge   the cache merge of every (b, k), as in the cache build;
+//                  statistics' chunk pass over target rows 0..na-1 in one
+//                  grid (they read different rows and depend on nothing), so
+//                  the two streams share one launch and one tail;
+//  k_round_merge_stats  the cache merge of every (b, k), as in the cache
+//                  build, first in the grid, then the statistics chunks of
+//                  target rows na..K: the merges' round trips run beside
+//                  streaming work instead of alone (the merge holds four
+//                  candidate slots per thread in registers here instead of
+//                  sixteen, so the launch stays near the streaming pass's
+//                  register budget, and visits them in the same order);
+//                  na = floor(2(K+1)/3) balanced the two launches best at
+//                  B=64 K=5 V=128256 (60.5 us per round against 61.2 for
+//                  half and 61.6 for a third of the rows);
 //  k_round_resid   every workgroup of batch row b first runs the row's accept
 //                  scan itself (it needs the sigma statistics of all K+1
 //                  merges and the target rows' chunk partials, a few KiB),
@@ -32,8 +41,9 @@ namespace ssd {
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_round_chunks(RoundArgs a) {
+  const uint32_t per_b = a.ncw + a.na * uint32_t(a.s.S);
   const uint32_t b = fdiv(blockIdx.x, a.div_pb);
-  const uint32_t rem = blockIdx.x - b * (a.ncw + a.nsw);
+  const uint32_t rem = blockIdx.x - b * per_b;
   // uniform per workgroup; the statistics chunks are 8192 entries here (32
   // per thread, as the cache chunks), which keeps the launch at the cache
   // pass's register budget
@@ -44,6 +54,24 @@ __global__ __launch_bounds__(kThreads) void k_round_chunks(RoundArgs a) {
     const uint32_t r = fdiv(rem - a.ncw, a.s.div_s);
     stats_chunk_at<DT, kPerThread>(a.s, int(b), int(r), int(rem - a.ncw - r * uint32_t(a.s.S)));
   }
+}
+
+// The cache merges of every (b, k) (first in the grid, so they start at
+// once), then the statistics chunks of target rows na..K: the merges' round
+// trips overlap the streaming workgroups.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_round_merge_stats(RoundArgs a) {
+  const uint32_t nmerge = uint32_t(a.c.B) * uint32_t(a.c.K + 1);
+  if (blockIdx.x < nmerge) {
+    cache_merge_wg<DT, false, kHoldLean>(a.c, blockIdx.x);
+    return;
+  }
+  const uint32_t j = blockIdx.x - nmerge;
+  const uint32_t per_b = (uint32_t(a.s.NR) - a.na) * uint32_t(a.s.S);
+  const uint32_t b = fdiv(j, a.div_pbb);
+  const uint32_t rem = j - b * per_b;
+  const uint32_t r = fdiv(rem, a.s.div_s);
+  stats_chunk_at<DT, kPerThread>(a.s, int(b), int(a.na + r), int(rem - r * uint32_t(a.s.S)));
 }
 
 // Also the second launch of ssd_verify (after its statistics chunk pass),
@@ -63,14 +91,30 @@ __global__ __launch_bounds__(kThreads) void k_round_resid(RoundResidArgs a) {
   resid_row_wg<DT, SIG, PT>(a.r, inf, b, c4);
 }
 
-hipError_t launch_round_chunks(const RoundArgs& a0, int dtype, hipStream_t st) {
+static RoundArgs round_divs(const RoundArgs& a0) {
   RoundArgs a = a0;
-  a.div_pb = make_fastdiv(a.ncw + a.nsw);
+  a.div_pb = make_fastdiv(a.ncw + a.na * uint32_t(a.s.S));
+  a.div_pbb = make_fastdiv((uint32_t(a.s.NR) - a.na) * uint32_t(a.s.S));
   a.c.div_s = make_fastdiv(uint32_t(a.c.S));
+  a.c.div_kp = make_fastdiv(uint32_t(a.c.K + 1));
   a.s.div_s = make_fastdiv(uint32_t(a.s.S));
-  const unsigned grid = unsigned(int64_t(a.c.B) * (a.ncw + a.nsw));
+  return a;
+}
+
+hipError_t launch_round_chunks(const RoundArgs& a0, int dtype, hipStream_t st) {
+  const RoundArgs a = round_divs(a0);
+  const unsigned grid = unsigned(int64_t(a.c.B) * (a.ncw + a.na * uint32_t(a.s.S)));
   if (dtype == SSD_BF16) hipLaunchKernelGGL(k_round_chunks<1>, dim3(grid), dim3(kThreads), 0, st, a);
   else hipLaunchKernelGGL(k_round_chunks<0>, dim3(grid), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_round_merge_stats(const RoundArgs& a0, int dtype, hipStream_t st) {
+  const RoundArgs a = round_divs(a0);
+  const unsigned grid =
+      unsigned(int64_t(a.c.B) * (a.c.K + 1) + int64_t(a.c.B) * (a.s.NR - int64_t(a.na)) * a.s.S);
+  if (dtype == SSD_BF16) hipLaunchKernelGGL(k_round_merge_stats<1>, dim3(grid), dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL(k_round_merge_stats<0>, dim3(grid), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -105,7 +149,7 @@ hipError_t launch_round(const RoundArgs& a, const RoundResidArgs& rr, int dtype,
   if ((e = mark(0)) != hipSuccess) return e;
   if ((e = launch_round_chunks(a, dtype, st)) != hipSuccess) return e;
   if ((e = mark(1)) != hipSuccess) return e;
-  if ((e = launch_cache_merge(a.c, dtype, st)) != hipSuccess) return e;
+  if ((e = launch_round_merge_stats(a, dtype, st)) != hipSuccess) return e;
   if ((e = mark(2)) != hipSuccess) return e;
   if ((e = launch_round_resid(rr, dtype, true, st)) != hipSuccess) return e;
   return mark(3);
