@@ -633,6 +633,40 @@ def test_verify_round_extremes(S):
         _round_vs_separate(S, d, [4, 0, 64, 3], 0.0, f"round tau{tau}")
 
 
+@pytest.mark.parametrize("V", [16 * 8192, 32 * 8192])
+def test_verify_round_tied_chunks(S, V):
+    """Chunks whose candidates (entries at or above the chunk bound) fill
+    more of their slots than the merge keeps in registers (four positions of
+    P = 256 / G threads: 64 slots at 16 chunks, 32 at 32), more than the 128
+    slots (the exact top-F rewrite), and ties spread over several chunks
+    (more than 64 kept candidates, ranked in LDS). The round's merge (four
+    held slots) and ssd_build_cache's (sixteen) must agree bit for bit, and
+    both with the oracle."""
+    log(f"[gpu] verify round tied chunks V={V}")
+    B, K = 5, 2
+    rng = np.random.default_rng(V + 17)
+    d = _random_case(V + 3, B, K, V, "f32", 0.9, Kd=K + 1)
+    dr = d["draft"]
+    c = 8192
+
+    def ties(b, k, chunk, n, val=20.0):   # far above every other logit of the row
+        pos = rng.choice(c, size=n, replace=False)
+        dr[b, k, chunk * c + pos] = val
+
+    for k in range(K + 1):
+        ties(0, k, 3, 100)               # 64 < n <= 128 at 16 chunks (32 < n at 32)
+        ties(1, k, 5, 200)               # past the 128 slots: the exact top-F rewrite
+        for ch in range(4):
+            ties(2, k, ch, 50)           # 200 ties at the row maximum over four chunks
+        ties(3, k, 1, 40)                # 32 < n <= 64: a continuation only at 32 chunks
+        ties(3, k, 2, 40, 19.0)
+    d["target"], d["draft"] = W.f32_to_bf16_bits(d["target"]), W.f32_to_bf16_bits(dr)
+    for b in range(B):
+        for i in range(K):
+            d["tokens"][b, i] = O.sample_draft(d["draft"][b, i], d["tau"], rng.random())
+    _round_vs_separate(S, d, [64, 40, 8], 0.5, f"round ties V={V}")
+
+
 def test_verify_round_marked_matches_round(S):
     """ssd_verify_round_marked: the same outputs as ssd_verify_round, and the
     four events recorded in launch order (non-negative elapsed times)."""
