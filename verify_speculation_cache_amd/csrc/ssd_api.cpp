@@ -696,7 +696,6 @@ SSD_API int ssd_verify_round_marked(const void* target_logits, int64_t target_bs
                           u_acc, &sig, accepted, out_tokens, nullptr, nullptr, ws + off_s, sw, kPerThread);
   a.s.S = int(S);
   a.ncw = uint32_t((K + 1) * S);
-  a.nsw = uint32_t((K + 1) * S);
   a.na = uint32_t(2 * (K + 1) / 3);   // target rows whose statistics share the cache's chunk pass
   RoundResidArgs rr{};
   rr.s = a.s;

@@ -102,15 +102,6 @@ hipError_t launch_cache(const CacheArgs& a0, int dtype, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_cache_merge(const CacheArgs& a0, int dtype, hipStream_t st) {
-  CacheArgs a = a0;
-  a.div_kp = make_fastdiv(uint32_t(a.K + 1));
-  const unsigned rows = unsigned(int64_t(a.B) * (a.K + 1));
-  if (dtype == SSD_BF16) hipLaunchKernelGGL(k_cache_merge<1>, dim3(rows), dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL(k_cache_merge<0>, dim3(rows), dim3(kThreads), 0, st, a);
-  return hipGetLastError();
-}
-
 hipError_t launch_lookup(const LookupArgs& a, hipStream_t st) {
   const unsigned rows_per_wg = kThreads / 64;
   const unsigned grid = unsigned((a.B + rows_per_wg - 1) / rows_per_wg);

@@ -343,7 +343,7 @@ struct TreeWs {
 struct RoundArgs {
   CacheArgs c;
   StatsArgs s;
-  uint32_t ncw, nsw;    // cache and statistics workgroups per batch row
+  uint32_t ncw;         // cache chunk workgroups per batch row
   uint32_t na;          // target rows whose statistics run in the first launch (the rest in the second)
   FastDiv div_pb, div_pbb;   // by the first and second launch's chunk workgroups per batch row
 };
@@ -363,7 +363,6 @@ hipError_t launch_tree_stats(const TreeArgs& a, int dtype, hipStream_t st);
 hipError_t launch_tree_round(const TreeArgs& a, int dtype, bool first, hipStream_t st);
 hipError_t launch_round_chunks(const RoundArgs& a, int dtype, hipStream_t st);
 hipError_t launch_round_merge_stats(const RoundArgs& a, int dtype, hipStream_t st);
-hipError_t launch_cache_merge(const CacheArgs& a, int dtype, hipStream_t st);
 hipError_t launch_round_resid(const RoundResidArgs& a, int dtype, bool sigma, hipStream_t st);
 hipError_t launch_rows_resid(const RoundResidArgs& a, int dtype, bool sigma, hipStream_t st);
 // The three launches of a verification round; with marks (hipEvent_t[4],
