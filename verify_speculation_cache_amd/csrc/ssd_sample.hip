@@ -97,10 +97,26 @@ __global__ __launch_bounds__(kThreads) void k_sample_chunks(SampleArgs a) {
       float v[PV];
       cv.get(j, v);
       const int i0 = int(c0) + ChunkVecs<DT, true, kStatsPerThread>::local(tid, j);
+      // a sigma member has a logit at or above the threshold value, so a
+      // vector whose maximum lies below it in every lane of the wave has
+      // none: its entries take weight 1 without the per-entry test (1 * ex
+      // is ex exactly, so the sums are unchanged)
+      bool member_possible = false;
+      if (SIG) {
+        float vmax = v[0];
 #pragma unroll
-      for (int e = 0; e < PV; ++e) {
-        const float ex = __builtin_amdgcn_exp2f((v[e] - pc[j / NVH]) * a.c32);
-        sum[j / NVH] += SIG ? sg.weight(v[e], i0 + e) * ex : ex;
+        for (int e = 1; e < PV; ++e) vmax = fmaxf(vmax, v[e]);
+        member_possible = __builtin_amdgcn_ballot_w64(vmax >= sg.val) != 0;
+      }
+      if (member_possible) {
+#pragma unroll
+        for (int e = 0; e < PV; ++e) {
+          const float ex = __builtin_amdgcn_exp2f((v[e] - pc[j / NVH]) * a.c32);
+          sum[j / NVH] += sg.weight(v[e], i0 + e) * ex;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < PV; ++e) sum[j / NVH] += __builtin_amdgcn_exp2f((v[e] - pc[j / NVH]) * a.c32);
       }
     }
     const double ws0 = wave_sum_u(double(sum[0]));
