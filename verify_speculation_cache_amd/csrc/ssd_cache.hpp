@@ -614,17 +614,29 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
 // Scaled exp-mass (scaled_mass) of the entries below f0 (the
 // non-candidates); the caller applies the chunk's fix. Entries past the row
 // end read as -inf and add nothing; with f0 = NaN (no candidates) every
-// entry counts.
+// entry counts. Bit j of cvec is set when vector j holds a candidate in some
+// lane of the wave (wave_compact's ballots): the other vectors skip the
+// per-entry test, since it passes every entry there (a padding entry it
+// would drop adds exp2(-inf) = 0 either way), and the sum is the same.
 template <int DT>
-__device__ __forceinline__ float chunk_rest_mass(const float (&x)[kPerThread], float f0, float P, float c32) {
+__device__ __forceinline__ float chunk_rest_mass(const float (&x)[kPerThread], float f0, float P, float c32,
+                                                 uint32_t cvec) {
   constexpr int PV = Dt<DT>::kPerVec;
   float sn = 0.0f;
 #pragma unroll
-  for (int q = 0; q < kPerThread; ++q) {
-    const float e = scaled_mass(x[q], c32, P);
-    sn += (x[q] >= f0) ? 0.0f : e;
+  for (int j = 0; j < kPerThread / PV; ++j) {
+    if (cvec & (1u << j)) {   // wave-uniform
+#pragma unroll
+      for (int e = 0; e < PV; ++e) {
+        const float m = scaled_mass(x[j * PV + e], c32, P);
+        sn += (x[j * PV + e] >= f0) ? 0.0f : m;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < PV; ++e) sn += scaled_mass(x[j * PV + e], c32, P);
+    }
     // a vector at a time: keeps the exp temporaries short-lived
-    if (q % PV == PV - 1) __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_sched_barrier(0);
   }
   return sn;
 }
@@ -634,11 +646,14 @@ __device__ __forceinline__ float chunk_rest_mass(const float (&x)[kPerThread], f
 // bits in wv and the token index in wi (the copy-out forms the keyed
 // records, so the rare taken branch stays short). Entries past kCandCap are
 // counted and written to the spare slot kCandCap, which is never read.
-// Returns the wave's count.
+// Returns the wave's count; bit j of cvec marks vector j (entries j PV ..
+// j PV + PV - 1 of every lane) as holding a candidate in some lane.
 template <int DT, bool CHECK>
 __device__ __forceinline__ uint32_t wave_compact(const float (&x)[kPerThread], float f0, int tid, int nvalid, int c0,
-                                                 uint32_t* wv, int32_t* wi) {
+                                                 uint32_t* wv, int32_t* wi, uint32_t& cvec) {
+  constexpr int PV = Dt<DT>::kPerVec;
   uint32_t cw = 0;
+  cvec = 0;
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
     const int loc = local_of<DT>(tid, q);
@@ -652,6 +667,7 @@ __device__ __forceinline__ uint32_t wave_compact(const float (&x)[kPerThread], f
         wi[p] = c0 + loc;
       }
       cw += uint32_t(__popcll(m));
+      cvec |= 1u << (q / PV);
     }
   }
   return cw;
@@ -789,12 +805,12 @@ __device__ __forceinline__ void cache_chunk_at(const CacheArgs& a, int b, int k,
   if (F > 0) f0 = (t0 <= key_of<DT>(-__builtin_inff())) ? -__builtin_inff() : value_of_key<DT>(t0);
 
   // ---- candidates (per-wave compaction) and exp-mass of the rest ----
-  uint32_t cw;
+  uint32_t cw, cvec;
   if (nvalid < kChunk && f0 == -__builtin_inff())   // padding would pass the test
-    cw = wave_compact<DT, true>(x, f0, tid, nvalid, int(c0), sm_lv[w], sm_li[w]);
+    cw = wave_compact<DT, true>(x, f0, tid, nvalid, int(c0), sm_lv[w], sm_li[w], cvec);
   else
-    cw = wave_compact<DT, false>(x, f0, tid, nvalid, int(c0), sm_lv[w], sm_li[w]);
-  const float sn = chunk_rest_mass<DT>(x, f0, sp.P, c32);
+    cw = wave_compact<DT, false>(x, f0, tid, nvalid, int(c0), sm_lv[w], sm_li[w], cvec);
+  const float sn = chunk_rest_mass<DT>(x, f0, sp.P, c32, cvec);
   const double ws = wave_sum_u(double(sn));   // double across threads
   if (lane == 0) {
     sm_wcnt[w] = int(cw);
