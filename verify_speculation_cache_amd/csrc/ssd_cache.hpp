@@ -237,6 +237,73 @@ __device__ __forceinline__ void visit(const RowCands<HOLD>& rc, bool held, const
   }
 }
 
+// The same candidates as visit, a batch at a time: fb(e, okm) gets up to
+// HOLD slots of the thread (bit i of okm: e[i] holds a written candidate),
+// in the order visit meets them. Every thread of the workgroup calls it and
+// fb is called by all lanes of a wave together.
+template <bool COH, int HOLD, typename Fb>
+__device__ __forceinline__ void visit_batches(const RowCands<HOLD>& rc, bool held, const uint64_t* pp,
+                                              const int* cnt_lds, const uint64_t* cl, int S, Fb fb) {
+  if (held) {
+    fb(rc.v, rc.ok);
+    for (int i0 = HOLD; rc.step * i0 < kCandCap; i0 += HOLD) {
+      if (__builtin_amdgcn_ballot_w64(rc.pos + rc.step * i0 < rc.nc) == 0) break;   // wave-uniform
+      uint64_t e[HOLD];
+      uint32_t okm = 0;
+#pragma unroll
+      for (int i = 0; i < HOLD; ++i) {
+        const int p = rc.pos + rc.step * (i0 + i);
+        const bool ok = p < rc.nc;
+        e[i] = ok ? ld64<COH>(rc.base + p) : 0ull;
+        okm |= ok ? 1u << i : 0u;
+      }
+      fb(e, okm);
+    }
+    return;
+  }
+  const int slots = S * kCandCap;
+  for (int base = 0; base < slots; base += kThreads * HOLD) {
+    uint64_t e[HOLD];
+    uint32_t okm = 0;
+#pragma unroll
+    for (int i = 0; i < HOLD; ++i) {
+      const int sidx = base + i * kThreads + int(threadIdx.x);
+      bool ok = false;
+      if (sidx < slots) {
+        const int cc = sidx / kCandCap;
+        const int n = cc < kCountLds ? cnt_lds[cc] : int(uint32_t(ld64<COH>(pp + cc * 4 + 2)));
+        ok = (sidx - cc * kCandCap) < n;
+      }
+      e[i] = ok ? ld64<COH>(cl + sidx) : 0ull;
+      okm |= ok ? 1u << i : 0u;
+    }
+    fb(e, okm);
+  }
+}
+
+// Appends the entries e[i] with bit i of km set to the LDS list: one prefix
+// count over the wave and one LDS atomic per wave and batch (entries past
+// kFiltCap are counted but not stored). Called by all lanes of a wave
+// together; the list order is the wave's lane order, then i.
+template <int HOLD>
+__device__ __forceinline__ void batch_append(const uint64_t (&e)[HOLD], uint32_t km, int lane, int* n,
+                                             uint64_t* list) {
+  const int cnt = __popc(km);
+  const int incl = wave_incl_scan_i(cnt, lane);
+  const int tot = __builtin_amdgcn_readlane(incl, 63);
+  if (tot == 0) return;   // wave-uniform
+  int base = 0;
+  if (lane == 0) base = atomicAdd(n, tot);
+  int slot = __builtin_amdgcn_readlane(base, 0) + incl - cnt;
+#pragma unroll
+  for (int i = 0; i < HOLD; ++i) {
+    if ((km >> i) & 1u) {
+      if (slot < kFiltCap) list[slot] = e[i];
+      ++slot;
+    }
+  }
+}
+
 // Every thread's first HOLD slots, loaded unconditionally (slots past a
 // chunk's count are masked out later; the chunk and position are clamped
 // into the row's slots, so there is no branch around the loads).
@@ -450,10 +517,16 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
   // candidates at or above Tmax go to the ranked list; the others only add
   // to S_rest
   const uint32_t tcut = s_tmax;
-  visit<COH, HOLD>(rc, held, pp, s_cnt, cl, a.S, [&](uint64_t e) {
-    const bool keep = F > 0 && cand_key(e) >= tcut;
-    wave_append(e, keep, lane, &s_n2, s_list);
-    if (!keep) s_unsel += cand_mass<DT>(e, prow, c32);
+  visit_batches<COH, HOLD>(rc, held, pp, s_cnt, cl, a.S, [&](const uint64_t (&e)[HOLD], uint32_t okm) {
+    uint32_t km = 0;
+#pragma unroll
+    for (int i = 0; i < HOLD; ++i) {
+      if ((okm >> i) & 1u) {
+        if (F > 0 && cand_key(e[i]) >= tcut) km |= 1u << i;
+        else s_unsel += cand_mass<DT>(e[i], prow, c32);
+      }
+    }
+    batch_append(e, km, lane, &s_n2, s_list);
   });
   __syncthreads();
   int n2 = __builtin_amdgcn_readfirstlane(s_n2);   // uniform
@@ -562,16 +635,20 @@ __device__ __forceinline__ void cache_merge_wg(const CacheArgs& a, int64_t rowid
     if (rank == F - 1) s_thrw = e;
   };
   if (__builtin_expect(n2 <= 64, 1)) {
-    // one wave, entry i in lane i, the others read with readlane
+    // entry i in lane i of every wave; wave w counts the larger keys among
+    // entries w, w + 4, ... (broadcast LDS reads), wave 0 adds the four
+    // counts (in s_hist, unused on this path) and places the entries
+    const uint64_t e = lane < n2 ? s_list[lane] : 0ull;
+    const uint64_t rk = rank_key(cand_key(e), cand_idx(e));
+    int part = 0;
+    for (int j = w; j < n2; j += 4) {
+      const uint64_t o = s_list[j];
+      part += rank_key(cand_key(o), cand_idx(o)) > rk ? 1 : 0;
+    }
+    s_hist[tid] = part;
+    __syncthreads();
     if (w == 0) {
-      const uint64_t e = lane < n2 ? s_list[lane] : 0ull;
-      const uint64_t rk = rank_key(cand_key(e), cand_idx(e));
-      int rank = 0;
-      for (int j = 0; j < n2; ++j) {
-        const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(rk)), j));
-        const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(rk >> 32)), j));
-        rank += ((uint64_t(hi) << 32) | lo) > rk ? 1 : 0;
-      }
+      const int rank = (s_hist[lane] + s_hist[64 + lane]) + (s_hist[128 + lane] + s_hist[192 + lane]);
       if (lane < n2) place(e, rank);
     }
   } else {
