@@ -157,7 +157,9 @@ SSD_API size_t ssd_verify_workspace_size(int32_t B, int32_t K, int32_t V, int dt
  *               0..K, then draft rows 0..K-1 (sigma form when sigma given)
  * Launches two kernels on hip_stream: the row statistics' chunk pass, then
  * one in which every workgroup of a batch row runs the row's accept scan
- * before its share of the draw. */
+ * before its share of the draw. Draws of 2048 or more workgroups (B times
+ * ceil(V / 16384)) run the accept scan once per batch row in a kernel of its
+ * own between the two (three launches). */
 SSD_API int ssd_verify(const void* target_logits, int64_t target_bstride,
                        const void* draft_logits, int64_t draft_bstride, int dtype,
                        int32_t B, int32_t K, int32_t V, float tau,
@@ -180,7 +182,7 @@ SSD_API int ssd_verify(const void* target_logits, int64_t target_bstride,
  * (ssd_verify_workspace_size) exceeds the array returns SSD_EINVAL with a
  * message. All calls on one GPU share the array: calls that may overlap in
  * time on one GPU (other streams, other threads) race and give wrong
- * results. Launches the fill kernel, then ssd_verify's two kernels, on
+ * results. Launches the fill kernel, then ssd_verify's kernels, on
  * hip_stream (the current device's). */
 #define SSD_NOALLOC_SCRATCH_BYTES (16u << 20)
 SSD_API size_t ssd_noalloc_scratch_bytes(void);
@@ -343,7 +345,9 @@ SSD_API size_t ssd_verify_round_workspace_size(int32_t B, int32_t K, int32_t V, 
  * statistics (na = floor(2(K+1)/3)); the second runs every cache merge
  * beside the statistics of target rows na..K; and each residual workgroup
  * runs its batch row's accept scan before its share of the draw (the lookup
- * in the draw's last workgroup).
+ * in the draw's last workgroup). As in ssd_verify, draws of 2048 or more
+ * workgroups take the accept scan once per batch row in a launch of its own
+ * before the residual launch.
  *   target_logits device [B, K+1, V]; draft_logits device [B, >=K+1, V]
  *   F host int32 [K+1] (0 <= F_k <= min(V, 64)); C in [0, 1]
  *   draft_tokens device int32 [B, K] (drawn from q_sigma, e.g. by
@@ -352,7 +356,7 @@ SSD_API size_t ssd_verify_round_workspace_size(int32_t B, int32_t K, int32_t V, 
  *   draft_stats double [B, K+1, 3] (as ssd_build_cache); accepted int32 [B],
  *   out_tokens int32 [B, K+1] (as ssd_verify); hit uint8 [B], slot int32 [B]
  *   or NULL (as ssd_cache_lookup).
- * Three kernel launches on hip_stream. */
+ * Three kernel launches on hip_stream (four for the large draws above). */
 SSD_API int ssd_verify_round(const void* target_logits, int64_t target_bstride,
                              const void* draft_logits, int64_t draft_bstride, int dtype,
                              int32_t B, int32_t K, int32_t V, float tau, const int32_t* F, float C,
@@ -367,7 +371,8 @@ SSD_API int ssd_verify_round(const void* target_logits, int64_t target_bstride,
  * first launch (the cache chunk pass with the statistics of target rows
  * 0..na-1), after it, after the second (the cache merges with the
  * statistics of target rows na..K) and after the residual launch, so that
- * elapsed times between them give each launch's duration.
+ * elapsed times between them give each launch's duration (the last interval
+ * holds the accept-scan launch too where there is one).
  * Recording adds three event packets to the stream; everything else, the
  * arguments and the outputs, are those of ssd_verify_round. */
 SSD_API int ssd_verify_round_marked(const void* target_logits, int64_t target_bstride,

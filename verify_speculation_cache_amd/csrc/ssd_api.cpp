@@ -375,7 +375,8 @@ SSD_API int ssd_verify(const void* target_logits, int64_t target_bstride,
                                         pt);
   hipStream_t stream = as_stream(hip_stream);
   // two launches: the statistics chunk pass, then per batch row the accept
-  // scan (repeated in each of the row's residual workgroups) and the draw
+  // scan (repeated in each of the row's residual workgroups, or for large
+  // draws once per row in a launch of its own) and the draw
   if ((st = hip_status(launch_stats_chunks(a, dtype, stream), "stats launch")) != SSD_OK) return st;
   const RoundResidArgs rr{verify_resid_args(a, u_res, resid_mass, ws + sw.total, rw), a};
   return hip_status(launch_round_resid(rr, dtype, sig, stream), "residual launch");

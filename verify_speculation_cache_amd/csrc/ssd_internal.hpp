@@ -61,6 +61,14 @@ inline int64_t pick_chunks_per_row(int64_t V) { return (V + kPickChunk - 1) / kP
 // instead: four times the workgroups with a quarter of the bytes each,
 // since at that size one workgroup's own loads, not HBM, set the time.
 constexpr int64_t kSmallGridWgs = 512;
+// Residual grids of at least this many workgroups (more than stay resident
+// at once) run the accept scan once per batch row in a launch of their own
+// and leave its RowInfo in the workspace; smaller grids repeat it in every
+// residual workgroup (no extra launch on the latency path).
+#ifndef SSD_SCAN_ONCE_WGS
+#define SSD_SCAN_ONCE_WGS 2048
+#endif
+constexpr int64_t kScanOnceWgs = SSD_SCAN_ONCE_WGS;
 constexpr int kSmallPerThread = kPickPerThread;   // 16: a span of one pick chunk
 inline int stats_pt(int64_t B, int64_t NR, int64_t V) {
   return B * NR * stats_chunks_per_row(V) < kSmallGridWgs ? kSmallPerThread : kStatsPerThread;

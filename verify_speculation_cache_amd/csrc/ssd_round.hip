@@ -27,7 +27,11 @@
 //                  then its share of the residual / bonus draw; the last
 //                  workgroup per row also looks the outcome up in the cache.
 //                  Repeating the small scan in each of the row's workgroups
-//                  costs less than a cross-workgroup hand-off of its result.
+//                  costs less than a cross-workgroup hand-off of its result
+//                  while the draw's workgroups are all resident at once;
+//                  draws of kScanOnceWgs or more workgroups (several
+//                  generations of them) instead run the scan once per row in
+//                  k_row_scan, a launch of its own, and read its RowInfo.
 // The arithmetic is that of the separate entry points: the cache is
 // bit-identical to ssd_build_cache's; the row statistics here sum 8192-entry
 // chunk partials (ssd_verify's pass sums 16384-entry ones, a register budget
@@ -75,20 +79,41 @@ __global__ __launch_bounds__(kThreads) void k_round_merge_stats(RoundArgs a) {
 }
 
 // Also the second launch of ssd_verify (after its statistics chunk pass),
-// with SIG as the caller's sigma switch and no lookup.
-template <int DT, bool SIG, int PT>
+// with SIG as the caller's sigma switch and no lookup. ONCE: k_row_scan ran
+// the accept scan before this launch and left each row's RowInfo in the
+// workspace (large grids).
+template <int DT, bool SIG, int PT, bool ONCE>
 __global__ __launch_bounds__(kThreads) void k_round_resid(RoundResidArgs a) {
-  __shared__ float e_piv[kMaxRows];
-  __shared__ double e_s[kMaxRows];
-  __shared__ RowInfo sm_inf;
   const int nw = resid_wgs_per_row(a.r.S, PT);
   const int b = int(fdiv(blockIdx.x, a.r.div_nw));
   const int c4 = blockIdx.x - b * nw;
-  // the row's first workgroup also stores accepted[b], out_tokens, probs and
-  // the optional row log-normalisers
-  const RowInfo inf = accept_scan<DT, true>(a.s, b, c4 == 0, e_piv, e_s, &sm_inf);
-  if (c4 == 0) write_row_lse(a.s, b, e_piv, e_s);
+  RowInfo inf;
+  if constexpr (ONCE) {
+    inf = a.r.info[b];   // the same address in every lane
+  } else {
+    __shared__ float e_piv[kMaxRows];
+    __shared__ double e_s[kMaxRows];
+    __shared__ RowInfo sm_inf;
+    // the row's first workgroup also stores accepted[b], out_tokens, probs
+    // and the optional row log-normalisers
+    inf = accept_scan<DT, true>(a.s, b, c4 == 0, e_piv, e_s, &sm_inf);
+    if (c4 == 0) write_row_lse(a.s, b, e_piv, e_s);
+  }
   resid_row_wg<DT, SIG, PT>(a.r, inf, b, c4);
+}
+
+// The accept scan of batch row b = blockIdx.x on its own (large grids): it
+// stores accepted[b], out_tokens (position a too, which the draw of the next
+// launch then overwrites), probs and the optional row log-normalisers, and
+// leaves the row's RowInfo in the workspace for k_round_resid<.., true>.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_row_scan(RoundResidArgs a) {
+  __shared__ float e_piv[kMaxRows];
+  __shared__ double e_s[kMaxRows];
+  const int b = blockIdx.x;
+  const RowInfo inf = accept_scan<DT, false>(a.s, b, true, e_piv, e_s, nullptr);
+  write_row_lse(a.s, b, e_piv, e_s);
+  if (threadIdx.x == 0) a.s.info[b] = inf;   // wave 0 holds the result
 }
 
 static RoundArgs round_divs(const RoundArgs& a0) {
@@ -119,23 +144,33 @@ hipError_t launch_round_merge_stats(const RoundArgs& a0, int dtype, hipStream_t 
 }
 
 template <int DT, bool SIG>
-static void launch_round_resid_t(const RoundResidArgs& a, unsigned grid, hipStream_t st) {
+static void launch_round_resid_t(const RoundResidArgs& a, unsigned grid, bool once, hipStream_t st) {
   if (a.r.span_pt == kSmallPerThread)
-    hipLaunchKernelGGL((k_round_resid<DT, SIG, kSmallPerThread>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((k_round_resid<DT, SIG, kSmallPerThread, false>), dim3(grid), dim3(kThreads), 0, st, a);
+  else if (once)
+    hipLaunchKernelGGL((k_round_resid<DT, SIG, kStatsPerThread, true>), dim3(grid), dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((k_round_resid<DT, SIG, kStatsPerThread>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((k_round_resid<DT, SIG, kStatsPerThread, false>), dim3(grid), dim3(kThreads), 0, st, a);
 }
 
 hipError_t launch_round_resid(const RoundResidArgs& a0, int dtype, bool sigma, hipStream_t st) {
   RoundResidArgs a = a0;
-  a.r.div_nw = make_fastdiv(uint32_t(resid_wgs_per_row(a.r.S, a.r.span_pt)));
-  const unsigned grid = unsigned(int64_t(a.r.B) * resid_wgs_per_row(a.r.S, a.r.span_pt));
+  const int64_t nw = resid_wgs_per_row(a.r.S, a.r.span_pt);
+  a.r.div_nw = make_fastdiv(uint32_t(nw));
+  const unsigned grid = unsigned(int64_t(a.r.B) * nw);
+  const bool once = a.r.span_pt != kSmallPerThread && int64_t(a.r.B) * nw >= kScanOnceWgs;
+  if (once) {
+    if (dtype == SSD_BF16) hipLaunchKernelGGL(k_row_scan<1>, dim3(unsigned(a.r.B)), dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL(k_row_scan<0>, dim3(unsigned(a.r.B)), dim3(kThreads), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (dtype == SSD_BF16) {
-    if (sigma) launch_round_resid_t<1, true>(a, grid, st);
-    else launch_round_resid_t<1, false>(a, grid, st);
+    if (sigma) launch_round_resid_t<1, true>(a, grid, once, st);
+    else launch_round_resid_t<1, false>(a, grid, once, st);
   } else {
-    if (sigma) launch_round_resid_t<0, true>(a, grid, st);
-    else launch_round_resid_t<0, false>(a, grid, st);
+    if (sigma) launch_round_resid_t<0, true>(a, grid, once, st);
+    else launch_round_resid_t<0, false>(a, grid, once, st);
   }
   return hipGetLastError();
 }
