@@ -168,6 +168,25 @@ def test_determinism(S):
         assert torch.equal(v, r2[k]), k
 
 
+def test_verify_large_draw_scan_once(S):
+    # 128 batch rows x 16 spans of 16384 entries = 2048 residual workgroups:
+    # the accept scan runs once per batch row in a launch of its own and the
+    # draw reads its result; every output (probs, Z, log-normalisers) of every
+    # row against the oracle, with two flagged rows and a fully masked target
+    # row among them
+    B, K, V = 128, 2, 262144
+    log(f"[gpu] verify large draw B={B} K={K} V={V} bf16")
+    d = _random_case(11, B, K, V, "bf16", 0.8)
+    d["tokens"][5, 1] = V
+    d["tokens"][77, 0] = -1
+    d["target"][9, 0, :] = W.f32_to_bf16_bits(np.full(V, -np.inf, dtype=np.float32))
+    got, _, _ = _run_verify(S, d, label="large-draw")
+    acc = got["accepted"].cpu().numpy()
+    out = got["out_tokens"].cpu().numpy()
+    assert acc[5] == -1 and acc[77] == -1 and np.all(out[[5, 77]] == -1)
+    assert acc[9] == 0 and out[9, 0] == -1
+
+
 # ---------------------------------------------------------------------------
 # residual sampling entry point
 # ---------------------------------------------------------------------------
