@@ -37,30 +37,32 @@ __global__ __launch_bounds__(kThreads) void k_greedy(GreedyArgs a) {
     const int64_t c0 = int64_t(c) * kStatsChunk;
     CV cv;
     cv.load(row, c0, a.V, (reinterpret_cast<uintptr_t>(row) & 15u) == 0, tid);
-    float m = -__builtin_inff();
+    float lm = -__builtin_inff();
 #pragma unroll
     for (int j = 0; j < CV::NV; ++j) {
       float v[PV];
       cv.get(j, v);
 #pragma unroll
-      for (int e = 0; e < PV; ++e) m = fmaxf(m, v[e]);
+      for (int e = 0; e < PV; ++e) lm = fmaxf(lm, v[e]);
     }
-    m = wave_max_u(m);
+    float m = wave_max_u(lm);
     if (lane == 0) sm_f[w] = m;
     __syncthreads();
     m = fmaxf(fmaxf(sm_f[0], sm_f[1]), fmaxf(sm_f[2], sm_f[3]));
     // smallest local index equal to the max (vector order is index order
-    // within a thread; across threads the minimum is taken)
+    // within a thread; across threads the minimum is taken); only a wave
+    // with a lane whose maximum is the chunk's can hold it
     int best = 0x7FFFFFFF;
+    if (__builtin_amdgcn_ballot_w64(lm == m) != 0) {   // wave-uniform
 #pragma unroll
-    for (int j = CV::NV - 1; j >= 0; --j) {
-      float v[PV];
-      cv.get(j, v);
+      for (int j = CV::NV - 1; j >= 0; --j) {
+        float v[PV];
+        cv.get(j, v);
 #pragma unroll
-      for (int e = PV - 1; e >= 0; --e) best = (v[e] == m) ? CV::local(tid, j) + e : best;
+        for (int e = PV - 1; e >= 0; --e) best = (v[e] == m) ? CV::local(tid, j) + e : best;
+      }
+      best = int(wave_min_u32(uint32_t(best)));
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) best = min(best, __shfl_xor(best, o));
     if (lane == 0) sm_i[w] = best;
     __syncthreads();
     if (tid == 0) {
