@@ -497,7 +497,7 @@ SSD_API int ssd_verify_greedy(const void* target_logits, int64_t target_bstride,
 
 SSD_API size_t ssd_draft_sample_workspace_size(int32_t B, int32_t K, int32_t V, int dtype) {
   if (check_shape(B, K, V) != SSD_OK || !dtype_ok(dtype)) return 0;
-  return SampleWs(int64_t(B) * K, chunks_per_row(V)).total;
+  return SampleWs(int64_t(B) * K, pick_chunks_per_row(V)).total;
 }
 
 SSD_API int ssd_draft_sample(const void* draft_logits, int64_t draft_bstride, int dtype,
@@ -512,10 +512,11 @@ SSD_API int ssd_draft_sample(const void* draft_logits, int64_t draft_bstride, in
     return fail(SSD_EINVAL, "sigma needs C in [0, 1] and thr");
   if (!draft_logits || !u || !tokens_out) return fail(SSD_EINVAL, "a required pointer is NULL");
   if (draft_bstride < 0) return fail(SSD_EINVAL, "negative batch stride");
-  const int64_t S = chunks_per_row(V);
+  // one partial per 4096-entry pick chunk, four per 16384-entry workgroup
+  const int64_t S = pick_chunks_per_row(V);
   const SampleWs sw(int64_t(B) * K, S);
   if ((st = check_ws(workspace, ws_bytes, sw.total)) != SSD_OK) return st;
-  if ((st = check_grid(int64_t(B) * K * S)) != SSD_OK) return st;
+  if ((st = check_grid(int64_t(B) * K * stats_chunks_per_row(V))) != SSD_OK) return st;
   char* ws = static_cast<char*>(workspace);
   SampleArgs a{};
   a.draft = draft_logits;

@@ -200,7 +200,7 @@ struct SampleArgs {
   const float* u;           // [B, K]
   int32_t* tok_out;         // [B, K]
   RowPartial* part;         // [B*K, S]
-  FastDiv div_s2, div_k;    // by (S+1)/2 and by K: set by the launcher
+  FastDiv div_s4, div_k;    // by (S+3)/4 and by K: set by the launcher
 };
 
 struct LookupArgs {

@@ -11,13 +11,14 @@
 //
 // The draw is by inverse CDF in token-index order: the smallest v whose
 // running mass exceeds u * Z. Two launches: k_sample_chunks, one workgroup
-// per (batch row b, position i, pair of 8192-chunks), sums each chunk's
-// weighted mass against the chunk's own max; k_sample_pick, one workgroup
-// per (b, i), rescales the chunk masses to the row max, finds the crossing
-// chunk and picks the token inside it. A row without mass (all logits -inf)
-// draws -1. The second launch replaces an arrival count in the first (the
-// last workgroup of a row drawing): that count and the draw's latency kept
-// workgroup slots of the streaming pass busy.
+// per (batch row b, position i, 16384-entry span), sums the weighted mass of
+// each of the span's four 4096-entry chunks against that chunk's own max;
+// k_sample_pick, one workgroup per (b, i), rescales the chunk masses to the
+// row max, finds the crossing chunk and picks the token inside it (16
+// entries per thread). A row without mass (all logits -inf) draws -1. The
+// second launch replaces an arrival count in the first (the last workgroup
+// of a row drawing): that count and the draw's latency kept workgroup slots
+// of the streaming pass busy.
 #include "ssd_cdf.hpp"
 
 namespace ssd {
@@ -50,90 +51,96 @@ __device__ __forceinline__ SigmaTest sigma_test(const SampleArgs& a, int b, int 
 template <int DT, bool SIG>
 __global__ __launch_bounds__(kThreads) void k_sample_chunks(SampleArgs a) {
   using T = typename Dt<DT>::T;
+  using CV = ChunkVecs<DT, true, kStatsPerThread>;
   constexpr int PV = Dt<DT>::kPerVec;
-  constexpr int NV2 = kStatsPerThread / PV;
-  __shared__ float sm_f[8];
-  __shared__ double sm_s[8];
+  constexpr int NQ = kStatsPerThread / kPickPerThread;   // pick chunks per span
+  constexpr int NVQ = CV::NV / NQ;                      // vectors per pick chunk
+  __shared__ float sm_f[4 * NQ];
+  __shared__ double sm_s[4 * NQ];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int S2 = (a.S + 1) / 2;   // workgroups per row, two 8192-chunks each
-  const int64_t rowid = fdiv(blockIdx.x, a.div_s2);
-  const int c2 = int(blockIdx.x - rowid * S2);
+  const int S4 = (a.S + NQ - 1) / NQ;   // workgroups per row
+  const int64_t rowid = fdiv(blockIdx.x, a.div_s4);
+  const int c4 = int(blockIdx.x - rowid * S4);
   const int b = int(fdiv(uint32_t(rowid), a.div_k));
   const int i = int(rowid - int64_t(b) * a.K);
   const T* row = static_cast<const T*>(a.draft) + int64_t(b) * a.db + int64_t(i) * a.V;
   const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
   const SigmaTest sg = sigma_test<DT, SIG>(a, b, i);
 
-  // max and weighted mass of two 8192-chunks: a workgroup reads 16384 entries (64 per thread, strided: vectors j <
-  // NV/2 lie in the first 8192, the others in the second) and writes one
-  // partial per 8192-chunk, so the draw below keeps 8192-entry chunks.
-  {
-    constexpr int NVH = NV2 / 2;
-    const int64_t c0 = int64_t(c2) * kStatsChunk;
-    ChunkVecs<DT, true, kStatsPerThread> cv;
-    cv.load(row, c0, a.V, aligned, tid);
-    float m[2] = {-__builtin_inff(), -__builtin_inff()};
+  // max and weighted mass of four 4096-chunks: a workgroup reads 16384
+  // entries (64 per thread, strided: vectors j < NVQ lie in the first
+  // 4096, the next NVQ in the second, and so on) and writes one partial per
+  // 4096-chunk, the chunks the draw picks in.
+  const int64_t c0 = int64_t(c4) * kStatsChunk;
+  CV cv;
+  cv.load(row, c0, a.V, aligned, tid);
+  float m[NQ];
 #pragma unroll
-    for (int j = 0; j < NV2; ++j) {
-      float v[PV];
-      cv.get(j, v);
+  for (int h = 0; h < NQ; ++h) m[h] = -__builtin_inff();
 #pragma unroll
-      for (int e = 0; e < PV; ++e) m[j / NVH] = fmaxf(m[j / NVH], v[e]);
+  for (int j = 0; j < CV::NV; ++j) {
+    float v[PV];
+    cv.get(j, v);
+#pragma unroll
+    for (int e = 0; e < PV; ++e) m[j / NVQ] = fmaxf(m[j / NVQ], v[e]);
+  }
+#pragma unroll
+  for (int h = 0; h < NQ; ++h) {
+    m[h] = wave_max_u(m[h]);
+    if (lane == 0) sm_f[4 * h + w] = m[h];
+  }
+  __syncthreads();
+  float pc[NQ];
+#pragma unroll
+  for (int h = 0; h < NQ; ++h) {
+    m[h] = fmaxf(fmaxf(sm_f[4 * h], sm_f[4 * h + 1]), fmaxf(sm_f[4 * h + 2], sm_f[4 * h + 3]));
+    pc[h] = pivot_of(m[h]);
+  }
+  float sum[NQ];
+#pragma unroll
+  for (int h = 0; h < NQ; ++h) sum[h] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CV::NV; ++j) {
+    float v[PV];
+    cv.get(j, v);
+    const int i0 = int(c0) + CV::local(tid, j);
+    // a sigma member has a logit at or above the threshold value, so a
+    // vector whose maximum lies below it in every lane of the wave has
+    // none: its entries take weight 1 without the per-entry test (1 * ex
+    // is ex exactly, so the sums are unchanged)
+    bool member_possible = false;
+    if (SIG) {
+      float vmax = v[0];
+#pragma unroll
+      for (int e = 1; e < PV; ++e) vmax = fmaxf(vmax, v[e]);
+      member_possible = __builtin_amdgcn_ballot_w64(vmax >= sg.val) != 0;
     }
-    m[0] = wave_max_u(m[0]);
-    m[1] = wave_max_u(m[1]);
-    if (lane == 0) {
-      sm_f[w] = m[0];
-      sm_f[4 + w] = m[1];
-    }
-    __syncthreads();
-    m[0] = fmaxf(fmaxf(sm_f[0], sm_f[1]), fmaxf(sm_f[2], sm_f[3]));
-    m[1] = fmaxf(fmaxf(sm_f[4], sm_f[5]), fmaxf(sm_f[6], sm_f[7]));
-    const float pc[2] = {pivot_of(m[0]), pivot_of(m[1])};
-    float sum[2] = {0.0f, 0.0f};
+    if (member_possible) {
 #pragma unroll
-    for (int j = 0; j < NV2; ++j) {
-      float v[PV];
-      cv.get(j, v);
-      const int i0 = int(c0) + ChunkVecs<DT, true, kStatsPerThread>::local(tid, j);
-      // a sigma member has a logit at or above the threshold value, so a
-      // vector whose maximum lies below it in every lane of the wave has
-      // none: its entries take weight 1 without the per-entry test (1 * ex
-      // is ex exactly, so the sums are unchanged)
-      bool member_possible = false;
-      if (SIG) {
-        float vmax = v[0];
-#pragma unroll
-        for (int e = 1; e < PV; ++e) vmax = fmaxf(vmax, v[e]);
-        member_possible = __builtin_amdgcn_ballot_w64(vmax >= sg.val) != 0;
+      for (int e = 0; e < PV; ++e) {
+        const float ex = __builtin_amdgcn_exp2f((v[e] - pc[j / NVQ]) * a.c32);
+        sum[j / NVQ] += sg.weight(v[e], i0 + e) * ex;
       }
-      if (member_possible) {
+    } else {
 #pragma unroll
-        for (int e = 0; e < PV; ++e) {
-          const float ex = __builtin_amdgcn_exp2f((v[e] - pc[j / NVH]) * a.c32);
-          sum[j / NVH] += sg.weight(v[e], i0 + e) * ex;
-        }
-      } else {
+      for (int e = 0; e < PV; ++e) sum[j / NVQ] += __builtin_amdgcn_exp2f((v[e] - pc[j / NVQ]) * a.c32);
+    }
+  }
 #pragma unroll
-        for (int e = 0; e < PV; ++e) sum[j / NVH] += __builtin_amdgcn_exp2f((v[e] - pc[j / NVH]) * a.c32);
-      }
-    }
-    const double ws0 = wave_sum_u(double(sum[0]));
-    const double ws1 = wave_sum_u(double(sum[1]));
-    if (lane == 0) {
-      sm_s[w] = ws0;
-      sm_s[4 + w] = ws1;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      const int cc = 2 * c2;
-      uint64_t* wp = reinterpret_cast<uint64_t*>(a.part + rowid * a.S + cc);
-      dev_store(wp, pack2(m[0], 0.0f));
-      dev_store(wp + 1, dbits((sm_s[0] + sm_s[1]) + (sm_s[2] + sm_s[3])));
-      if (cc + 1 < a.S) {
-        dev_store(wp + 2, pack2(m[1], 0.0f));
-        dev_store(wp + 3, dbits((sm_s[4] + sm_s[5]) + (sm_s[6] + sm_s[7])));
+  for (int h = 0; h < NQ; ++h) {
+    const double ws = wave_sum_u(double(sum[h]));
+    if (lane == 0) sm_s[4 * h + w] = ws;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int cq = NQ * c4;
+    uint64_t* wp = reinterpret_cast<uint64_t*>(a.part + rowid * a.S + cq);
+#pragma unroll
+    for (int h = 0; h < NQ; ++h) {
+      if (cq + h < a.S) {
+        dev_store(wp + 2 * h, pack2(m[h], 0.0f));
+        dev_store(wp + 2 * h + 1, dbits((sm_s[4 * h] + sm_s[4 * h + 1]) + (sm_s[4 * h + 2] + sm_s[4 * h + 3])));
       }
     }
   }
@@ -146,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void k_sample_pick(SampleArgs a) {
   __shared__ int sm_c;
   __shared__ double sm_pre, sm_target;
   __shared__ float sm_piv;
-  __shared__ PickLds<DT, 1> sm_pk;
+  __shared__ PickLds<DT, 1, kPickPerThread> sm_pk;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t rowid = blockIdx.x;
@@ -197,11 +204,11 @@ __global__ __launch_bounds__(kThreads) void k_sample_pick(SampleArgs a) {
   const int cs = sm_c;
   int tok = -1;
   if (cs >= 0) {
-    const int64_t c0 = int64_t(cs) * kChunk;
+    const int64_t c0 = int64_t(cs) * kPickChunk;
     const float P = sm_piv, c32 = a.c32;
-    ChunkVecs<DT, false> cv[1];
+    ChunkVecs<DT, false, kPickPerThread> cv[1];
     cv[0].load(row, c0, a.V, aligned, tid);
-    tok = chunk_pick<DT, 1>(cv, c0, sm_pre, sm_target,
+    tok = chunk_pick<DT, 1, kPickPerThread>(cv, c0, sm_pre, sm_target,
                             [&](const float (&x)[1], int idx) {
                               const float ex = __builtin_amdgcn_exp2f((x[0] - P) * c32);
                               return SIG ? sg.weight(x[0], idx) * ex : ex;
@@ -214,10 +221,12 @@ __global__ __launch_bounds__(kThreads) void k_sample_pick(SampleArgs a) {
 template <int DT, bool SIG>
 static hipError_t launch_sample_t(const SampleArgs& a0, hipStream_t st) {
   SampleArgs a = a0;
-  a.div_s2 = make_fastdiv(uint32_t((a.S + 1) / 2));
+  constexpr int NQ = kStatsPerThread / kPickPerThread;
+  const int S4 = (a.S + NQ - 1) / NQ;
+  a.div_s4 = make_fastdiv(uint32_t(S4));
   a.div_k = make_fastdiv(uint32_t(a.K));
   const int64_t rows = int64_t(a.B) * a.K;
-  hipLaunchKernelGGL((k_sample_chunks<DT, SIG>), dim3(unsigned(rows * ((a.S + 1) / 2))), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((k_sample_chunks<DT, SIG>), dim3(unsigned(rows * S4)), dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_sample_pick<DT, SIG>), dim3(unsigned(rows)), dim3(kThreads), 0, st, a);
