@@ -282,6 +282,7 @@ def main():
                     "bytes_per_launch": dom_bytes, "avg_launch_ms": round(dom_ms, 5),
                     "launches_timed": n_mark - n_mark // 6}
 
+    ceil = box_ceilings(dev)
     cpu, check = None, None
     if not args.no_cpu:
         src = outs[0] if args.separate else None
@@ -328,6 +329,7 @@ def main():
                         "pct_peak_hbm": round(100 * bytes_plain / (t_plain / 1e3) / 1e9 / PEAK_HBM_GBS, 2)},
         "verify_sigma_gbps": round(bytes_verify_sigma / (t_verify / 1e3) / 1e9, 1),
         "round_vs_separate_rows_differ": round_rows_differ,
+        "box_ceilings": dict(ceil, dominant_kernel_vs_copy=round(dom_gbps / ceil["copy_gbps"], 4)),
         "oracle_check": check,
         "mean_accepted_plus_1": round(float(np.mean(acc + 1)), 4),
         "hit_rate": round(float(np.mean(hit)), 4),
@@ -717,6 +719,36 @@ def bench_tree(args):
 
 HBM_BYTES_PROFILE = os.path.join(ROOT, "profiles", "ssd_build_cache_B64_K5_V128256_bf16_hbm_bytes.md")
 ROUND_BYTES_PROFILE = os.path.join(ROOT, "profiles", "ssd_verify_round_B64_K5_V128256_bf16_hbm_bytes.md")
+
+
+def box_ceilings(dev):
+    """What plain torch kernels reach on this machine's HBM, as context for the
+    roofline fractions (8 TB/s is the published peak): a device copy of a
+    512 MiB bf16 tensor (bytes read + written per second) and its float32
+    sum (bytes read per second), medians of 7 runs timed with events."""
+    import torch
+    nbytes = 512 << 20
+    x = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    y = torch.empty_like(x)
+
+    def med(fn, reps=7):
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[reps // 2]
+
+    t_copy = med(lambda: y.copy_(x))
+    t_sum = med(lambda: x.sum(dtype=torch.float32))
+    del x, y
+    torch.cuda.synchronize()
+    return {"copy_gbps": round(2 * nbytes / t_copy / 1e6, 1), "sum_read_gbps": round(nbytes / t_sum / 1e6, 1),
+            "what": "torch copy_ (read + write) and sum (read) of a 512 MiB bf16 tensor, median of 7"}
 
 
 def measured_traffic(profile, kernel=None):
