@@ -187,6 +187,15 @@ def test_verify_large_draw_scan_once(S):
     assert acc[9] == 0 and out[9, 0] == -1
 
 
+def test_verify_large_draw_scan_once_sigma(S):
+    # the same 2048-workgroup draw with sigma: cache build, sigma verification
+    # and lookup against the oracle on every row
+    B, K, V = 128, 2, 262144
+    log(f"[gpu] sigma verify large draw B={B} K={K} V={V} bf16")
+    d = _random_case(12, B, K, V, "bf16", 0.8, Kd=K + 1)
+    _cache_case(S, d, [6, 5, 9], 0.5, label="large-draw-sigma")
+
+
 # ---------------------------------------------------------------------------
 # residual sampling entry point
 # ---------------------------------------------------------------------------
