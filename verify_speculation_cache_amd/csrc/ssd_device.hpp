@@ -56,19 +56,6 @@ __device__ __forceinline__ uint64_t rank_key(uint32_t key, int32_t idx) {
   return (uint64_t(key) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(idx));
 }
 
-// Chunk of kChunk entries starting at c0, strided layout: thread t holds
-// vector g = j * kThreads + t (j = 0..NV-1) of kPerVec consecutive entries,
-// so each load instruction of a wave covers one contiguous 1 KiB span.
-template <int DT>
-struct Strided {
-  static constexpr int PV = Dt<DT>::kPerVec;
-  static constexpr int NV = kPerThread / PV;
-  __device__ static int64_t index(int64_t c0, int tid, int k) {
-    const int j = k / PV, e = k % PV;
-    return c0 + int64_t(j * kThreads + tid) * PV + e;
-  }
-};
-
 // Unpack one 16-byte vector into floats x[o .. o + kPerVec).
 template <int DT>
 __device__ __forceinline__ void unpack16(const uint4& r, float* x) {
@@ -80,81 +67,6 @@ __device__ __forceinline__ void unpack16(const uint4& r, float* x) {
       x[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
     } else {
       x[q] = __uint_as_float(w[q]);
-    }
-  }
-}
-
-// Entry i of a row as float, or -inf past the end. The index is clamped so
-// the load is unconditional (in bounds) and can be batched with the others.
-template <int DT>
-__device__ __forceinline__ float load_elem(const typename Dt<DT>::T* __restrict__ row, int64_t i,
-                                           int64_t V) {
-  const float v = Dt<DT>::to_f(row[i < V ? i : V - 1]);
-  return i < V ? v : -__builtin_inff();
-}
-
-// Load a chunk in the strided layout. `aligned`: the row start is 16-byte
-// aligned, so every vector lying wholly inside the row is one 16-byte load;
-// entries past the row end read as -inf, and a vector straddling the end (V
-// not a multiple of the vector width) or an unaligned row is read per entry.
-template <int DT>
-__device__ __forceinline__ void load_strided(const typename Dt<DT>::T* __restrict__ row, int64_t c0,
-                                             int64_t V, bool aligned, int tid, float (&x)[kPerThread]) {
-  using S = Strided<DT>;
-  constexpr int PV = S::PV;
-  const int64_t rem = V - c0;
-  if (aligned && rem >= kChunk) {
-    const uint4* p = reinterpret_cast<const uint4*>(row + c0);
-    uint4 raw[S::NV];
-#pragma unroll
-    for (int j = 0; j < S::NV; ++j) raw[j] = p[j * kThreads + tid];
-    // keep every load in flight before the first use (the scheduler would
-    // otherwise wait on the first load before issuing the rest)
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < S::NV; ++j) unpack16<DT>(raw[j], x + j * PV);
-  } else if (aligned) {
-    const int nvalid = int(rem);   // < kChunk
-    const uint4* p = reinterpret_cast<const uint4*>(row + c0);
-    uint4 raw[S::NV];
-#pragma unroll
-    for (int j = 0; j < S::NV; ++j) {
-      const int loc = (j * kThreads + tid) * PV;
-      raw[j] = (loc + PV <= nvalid) ? p[j * kThreads + tid] : make_uint4(0u, 0u, 0u, 0u);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < S::NV; ++j) unpack16<DT>(raw[j], x + j * PV);
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-      const int loc = ((k / PV) * kThreads + tid) * PV + (k % PV);
-      if (loc >= nvalid) x[k] = -__builtin_inff();
-    }
-    const int gs = nvalid / PV;   // vector straddling the end, if any
-    if ((nvalid % PV) != 0 && (gs % kThreads) == tid) {
-#pragma unroll
-      for (int j = 0; j < S::NV; ++j) {
-        if (j == gs / kThreads) {
-#pragma unroll
-          for (int e = 0; e < PV; ++e)
-            if (gs * PV + e < nvalid) x[j * PV + e] = Dt<DT>::to_f(row[c0 + gs * PV + e]);
-        }
-      }
-    }
-  } else {
-    // unaligned row (rare): per-entry loads at 32-bit offsets from the
-    // (uniform) chunk start, one vector's worth at a time to bound registers
-    const typename Dt<DT>::T* base = row + c0;
-    const int lim = rem < kChunk ? int(rem) : kChunk;
-#pragma unroll
-    for (int j = 0; j < S::NV; ++j) {
-#pragma unroll
-      for (int e = 0; e < PV; ++e) {
-        const int loc = (j * kThreads + tid) * PV + e;
-        const float v = Dt<DT>::to_f(base[loc < lim ? loc : lim - 1]);
-        x[j * PV + e] = loc < lim ? v : -__builtin_inff();
-      }
-      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -386,17 +298,6 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   v = mn(v, uint32_t(mov<kBcast31, 0xC>(id, int(v))));
   return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
 }
-// wave sum of a float, uniform result (fixed order: deterministic)
-__device__ __forceinline__ float wave_sum_uf(float v) {
-  using namespace dpp;
-  v += movf<kXor1>(0.0f, v);
-  v += movf<kXor2>(0.0f, v);
-  v += movf<kHalfMirror>(0.0f, v);
-  v += movf<kMirror>(0.0f, v);
-  v += movf<kBcast15, 0xA>(0.0f, v);
-  v += movf<kBcast31, 0xC>(0.0f, v);
-  return lane63f(v);
-}
 // wave sum of a double, uniform result (fixed order: deterministic)
 __device__ __forceinline__ double wave_sum_u(double v) {
   using namespace dpp;
@@ -472,14 +373,6 @@ __device__ __forceinline__ double lane_d(double v, int l) {
 }
 
 // ---- workgroup (4 waves) reductions; all threads must call ----
-__device__ __forceinline__ float block_max(float v, float* sm4) {
-  v = wave_max(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sm4[w] = v;
-  __syncthreads();
-  return fmaxf(fmaxf(sm4[0], sm4[1]), fmaxf(sm4[2], sm4[3]));
-}
 __device__ __forceinline__ double block_sum(double v, double* sm4) {
   v = wave_sum(v);
   const int w = threadIdx.x >> 6;
