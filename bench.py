@@ -224,9 +224,11 @@ def main():
         assert torch.equal(o[1]["accepted"], sep_ref[j][0]) and torch.equal(o[1]["out_tokens"], sep_ref[j][1])
         assert torch.equal(o[2]["hit"], sep_ref[j][2])
 
-    # the round's launches timed one by one: HIP events recorded on the
-    # launching stream between the three launches (ssd_verify_round_marked),
-    # back-to-back calls over the rotating copies
+    # the round's launches timed one by one (ssd_verify_round_marked): the
+    # first launch records its own start and end events (its execution
+    # time); events recorded on the launching stream after the second and
+    # the third give those launches with the gap before each; back-to-back
+    # calls over the rotating copies
     n_mark = 60
     marks = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_mark)]
     for i in range(n_mark):

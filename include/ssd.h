@@ -367,14 +367,16 @@ SSD_API int ssd_verify_round(const void* target_logits, int64_t target_bstride,
 
 /* ssd_verify_round for callers that time its launches (profilers, the
  * bench): marks is NULL or a host array of four hipEvent_t (created by the
- * caller on the device of hip_stream), recorded on hip_stream before the
- * first launch (the cache chunk pass with the statistics of target rows
- * 0..na-1), after it, after the second (the cache merges with the
- * statistics of target rows na..K) and after the residual launch, so that
- * elapsed times between them give each launch's duration (the last interval
- * holds the accept-scan launch too where there is one).
- * Recording adds three event packets to the stream; everything else, the
- * arguments and the outputs, are those of ssd_verify_round. */
+ * caller on the device of hip_stream, with timing). marks[0] and marks[1]
+ * are the start and the end of the first launch (the cache chunk pass with
+ * the statistics of target rows 0..na-1), recorded by that launch itself
+ * (hipExtLaunchKernel), so their interval is the kernel's execution time;
+ * marks[2] and marks[3] are recorded on hip_stream after the second launch
+ * (the cache merges with the statistics of target rows na..K) and after the
+ * residual launch, so those intervals also hold the gap before each launch
+ * (the last one the accept-scan launch too where there is one).
+ * Everything else, the arguments and the outputs, are those of
+ * ssd_verify_round. */
 SSD_API int ssd_verify_round_marked(const void* target_logits, int64_t target_bstride,
                                     const void* draft_logits, int64_t draft_bstride, int dtype,
                                     int32_t B, int32_t K, int32_t V, float tau, const int32_t* F, float C,

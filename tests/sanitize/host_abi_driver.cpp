@@ -23,7 +23,7 @@ hipError_t launch_greedy(const GreedyArgs&, int, hipStream_t) { ++g_launches; re
 hipError_t launch_cache_stats(const CacheStatsArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_tree_stats(const TreeArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_tree_round(const TreeArgs&, int, bool, hipStream_t) { ++g_launches; return hipSuccess; }
-hipError_t launch_round_chunks(const RoundArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_round_chunks(const RoundArgs&, int, hipStream_t, hipEvent_t, hipEvent_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_round_resid(const RoundResidArgs&, int, bool, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_rows_resid(const RoundResidArgs&, int, bool, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_round(const RoundArgs&, const RoundResidArgs&, int, hipStream_t, void* const*) {

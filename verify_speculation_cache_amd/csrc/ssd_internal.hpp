@@ -369,7 +369,10 @@ hipError_t launch_greedy(const GreedyArgs& a, int dtype, hipStream_t st);
 hipError_t launch_cache_stats(const CacheStatsArgs& a, hipStream_t st);
 hipError_t launch_tree_stats(const TreeArgs& a, int dtype, hipStream_t st);
 hipError_t launch_tree_round(const TreeArgs& a, int dtype, bool first, hipStream_t st);
-hipError_t launch_round_chunks(const RoundArgs& a, int dtype, hipStream_t st);
+// start / stop (may be null): events the launch itself records at the
+// kernel's start and end (hipExtLaunchKernel), for callers that time it
+hipError_t launch_round_chunks(const RoundArgs& a, int dtype, hipStream_t st, hipEvent_t start = nullptr,
+                               hipEvent_t stop = nullptr);
 hipError_t launch_round_merge_stats(const RoundArgs& a, int dtype, hipStream_t st);
 hipError_t launch_round_resid(const RoundResidArgs& a, int dtype, bool sigma, hipStream_t st);
 hipError_t launch_rows_resid(const RoundResidArgs& a, int dtype, bool sigma, hipStream_t st);

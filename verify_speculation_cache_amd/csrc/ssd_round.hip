@@ -37,6 +37,8 @@
 // chunk partials (ssd_verify's pass sums 16384-entry ones, a register budget
 // this launch cannot afford next to the cache pass), so accept decisions and
 // draws agree with ssd_verify's except at rounding-level ties.
+#include <hip/hip_ext.h>
+
 #include "ssd_cache.hpp"
 #include "ssd_resid.hpp"
 #include "ssd_stats.hpp"
@@ -126,11 +128,19 @@ static RoundArgs round_divs(const RoundArgs& a0) {
   return a;
 }
 
-hipError_t launch_round_chunks(const RoundArgs& a0, int dtype, hipStream_t st) {
+hipError_t launch_round_chunks(const RoundArgs& a0, int dtype, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   const RoundArgs a = round_divs(a0);
   const unsigned grid = unsigned(int64_t(a.c.B) * (a.ncw + a.na * uint32_t(a.s.S)));
-  if (dtype == SSD_BF16) hipLaunchKernelGGL(k_round_chunks<1>, dim3(grid), dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL(k_round_chunks<0>, dim3(grid), dim3(kThreads), 0, st, a);
+  if (start != nullptr || stop != nullptr) {
+    if (dtype == SSD_BF16)
+      hipExtLaunchKernelGGL(k_round_chunks<1>, dim3(grid), dim3(kThreads), 0, st, start, stop, 0, a);
+    else
+      hipExtLaunchKernelGGL(k_round_chunks<0>, dim3(grid), dim3(kThreads), 0, st, start, stop, 0, a);
+  } else if (dtype == SSD_BF16) {
+    hipLaunchKernelGGL(k_round_chunks<1>, dim3(grid), dim3(kThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(k_round_chunks<0>, dim3(grid), dim3(kThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 
@@ -181,9 +191,14 @@ hipError_t launch_round(const RoundArgs& a, const RoundResidArgs& rr, int dtype,
     return marks != nullptr ? hipEventRecord(static_cast<hipEvent_t>(marks[i]), st) : hipSuccess;
   };
   hipError_t e;
-  if ((e = mark(0)) != hipSuccess) return e;
-  if ((e = launch_round_chunks(a, dtype, st)) != hipSuccess) return e;
-  if ((e = mark(1)) != hipSuccess) return e;
+  // marks 0 and 1: the first launch's own start and end (recorded by the
+  // launch, so their interval is that kernel's execution time); marks 2
+  // and 3: recorded after the second and the last launch
+  if (marks != nullptr)
+    e = launch_round_chunks(a, dtype, st, static_cast<hipEvent_t>(marks[0]), static_cast<hipEvent_t>(marks[1]));
+  else
+    e = launch_round_chunks(a, dtype, st);
+  if (e != hipSuccess) return e;
   if ((e = launch_round_merge_stats(a, dtype, st)) != hipSuccess) return e;
   if ((e = mark(2)) != hipSuccess) return e;
   if ((e = launch_round_resid(rr, dtype, true, st)) != hipSuccess) return e;
