@@ -374,9 +374,11 @@ SSD_API int ssd_verify_round(const void* target_logits, int64_t target_bstride,
  * marks[2] and marks[3] are recorded on hip_stream after the second launch
  * (the cache merges with the statistics of target rows na..K) and after the
  * residual launch, so those intervals also hold the gap before each launch
- * (the last one the accept-scan launch too where there is one).
- * Everything else, the arguments and the outputs, are those of
- * ssd_verify_round. */
+ * (the last one the accept-scan launch too where there is one). With marks,
+ * call it on a stream that is not being captured into a graph (a launch
+ * that records its own events is not a graph node); with marks NULL it is
+ * ssd_verify_round. Everything else, the arguments and the outputs, are
+ * those of ssd_verify_round. */
 SSD_API int ssd_verify_round_marked(const void* target_logits, int64_t target_bstride,
                                     const void* draft_logits, int64_t draft_bstride, int dtype,
                                     int32_t B, int32_t K, int32_t V, float tau, const int32_t* F, float C,
